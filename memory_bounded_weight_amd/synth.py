@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for the paged block operator.
+
+This module holds no arithmetic of the method itself: it only draws seeded
+normal numbers and stores them as bfloat16 bit patterns.  Both the HIP path
+(through the tests and the benchmark) and the CPU oracle receive the SAME
+bytes from here.
+
+Recipe (the workloads of the paper are LTX-2.5 blocks whose checkpoint is
+not available; random weights of the same shapes stand in):
+  * generator: ``numpy.random.default_rng(seed)`` (PCG64), draws with
+    ``standard_normal(dtype=float32)`` in a fixed order;
+  * ``N(0, v)`` means variance ``v``: the float32 draw is multiplied by the
+    float32 value of sqrt(v), then rounded to bfloat16 (nearest, ties to
+    even);
+  * activations N(0, 1); weights N(0, 1/fan_in); biases N(0, 0.02);
+  * a stack of blocks draws block ``i``'s weights from
+    ``default_rng([seed, i])`` so one block can be regenerated alone.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BIAS_VAR = 0.02
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 bit patterns (nearest, ties to even).
+    Inputs are finite draws; no NaN handling is needed here."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    w = a.view(np.uint32)
+    lsb = (w >> np.uint32(16)) & np.uint32(1)
+    return ((w + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, var: float) -> np.ndarray:
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    z *= np.float32(math.sqrt(var))
+    return f32_to_bf16_bits(z)
+
+
+def linear_weights(rng, n_out: int, n_in: int):
+    """One Linear layer: W [n_out, n_in] ~ N(0, 1/n_in), b [n_out] ~ N(0, 0.02)."""
+    W = normal_bf16(rng, (n_out, n_in), 1.0 / n_in)
+    b = normal_bf16(rng, (n_out,), BIAS_VAR)
+    return W, b
+
+
+def linear_case(seed: int = 0, M: int = 64, K: int = 256, N: int = 512):
+    """Single paged linear: x [M,K] ~ N(0,1), W [N,K] ~ N(0,1/K), b [N] ~ N(0,0.02).
+    The default sizes are the 64 x 256 -> 512 parity case."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (M, K), 1.0)
+    W = normal_bf16(rng, (N, K), 1.0 / K)
+    b = normal_bf16(rng, (N,), BIAS_VAR)
+    return {"x": x, "W": W, "b": b}
+
+
+def ffn_case(seed: int = 0, M: int = 1024, d: int = 2048, hidden: int = 8192):
+    """FFN: x [M,d] ~ N(0,1); U [hidden,d] ~ N(0,1/d), a [hidden];
+    V [d,hidden] ~ N(0,1/hidden), b [d]."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (M, d), 1.0)
+    U, a = linear_weights(rng, hidden, d)
+    V, b = linear_weights(rng, d, hidden)
+    return {"x": x, "U": U, "a": a, "V": V, "b": b}
+
+
+def attn_weights(rng, d: int):
+    out = {}
+    for n in ("q", "k", "v", "o"):
+        W, b = linear_weights(rng, d, d)
+        out["W" + n] = W
+        out["b" + n] = b
+    return out
+
+
+def attn_case(seed: int = 0, M: int = 6144, Mc: int = 1024, d: int = 4096, cross: bool = True):
+    """Attention sub-blocks: x [M,d] ~ N(0,1), ctx [Mc,d] ~ N(0,1), then the
+    self-attention Wq,bq,Wk,bk,Wv,bv,Wo,bo and (if ``cross``) the
+    cross-attention ones, each W ~ N(0,1/d)."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (M, d), 1.0)
+    ctx = normal_bf16(rng, (Mc, d), 1.0) if cross else None
+    self_w = attn_weights(rng, d)
+    cross_w = attn_weights(rng, d) if cross else None
+    return {"x": x, "ctx": ctx, "self": self_w, "cross": cross_w}
+
+
+def block_weights(seed: int, index: int, d: int = 4096, hidden: int = 16384):
+    """Weights of block ``index`` of a synthetic stack: attention
+    Wq,bq,Wk,bk,Wv,bv,Wo,bo then FFN U,a,V,b."""
+    rng = np.random.default_rng([seed, index])
+    w = attn_weights(rng, d)
+    w["U"], w["a"] = linear_weights(rng, hidden, d)
+    w["V"], w["b"] = linear_weights(rng, d, hidden)
+    return w
+
+
+def stack_input(seed: int = 0, M: int = 8192, d: int = 4096):
+    rng = np.random.default_rng(seed)
+    return normal_bf16(rng, (M, d), 1.0)
