@@ -1,0 +1,339 @@
+/*
+ * psi.h -- C ABI of the MI355X paged BF16 block operator.
+ *
+ * Precision-Preserving Subtensor Inference (cited as [PSI]: "Precision-
+ * Preserving Subtensor Inference for a 22B Joint Audio-Video Generator under
+ * a Fixed GPU Working Set", arXiv 2611.08023) computes linear projections,
+ * the FFN and attention from weight sub-block PAGES that are copied from
+ * pinned host memory into a fixed, reusable device ARENA.  The managed
+ * device footprint is bounded by the pages, the declared live state and a
+ * bounded workspace ([PSI] sec. II-A, eq. (1)):
+ *
+ *     M_managed <= S_live + W + n_pages * P + eps
+ *
+ * Conventions for every entry point:
+ *   - Return value: PSI_OK (0) or a negative PSI_E_* code.  On error nothing
+ *     has been enqueued and the arena/journal state is unchanged; a message
+ *     is available from psi_last_error() (thread-local).
+ *   - BF16 values are passed as uint16_t bit patterns (bfloat16).
+ *   - Pointers named *_dev are device pointers owned by the caller (the
+ *     declared live state).  Pointers named *_host point to pinned host
+ *     memory (hipHostMalloc / torch pin_memory), owned by the caller, which
+ *     must stay valid and unmodified until the compute stream has passed
+ *     the operation (psi_arena_sync).
+ *   - Streams are hipStream_t passed as void*; NULL means the null stream.
+ *   - All operators are asynchronous on the arena's compute stream: a call
+ *     returns after enqueueing.  Page copies run on a library-owned copy
+ *     stream and are ordered with cross-stream events ([PSI] sec. II-D).
+ *   - Matrices are row-major; weights use the Linear layout W[out, in], so
+ *     a projection computes y = x W^T + b.
+ *   - One arena per host thread; an arena is not thread-safe.
+ */
+#ifndef PSI_H
+#define PSI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int psi_status;
+
+/* ---------------------------------------------------------------- status */
+#define PSI_OK 0
+#define PSI_E_INVALID (-1)           /* bad shape, pointer or flag; masked/causal attention unsupported */
+#define PSI_E_ARENA_TOO_SMALL (-2)   /* n_pages * (P + side) + W exceeds the arena */
+#define PSI_E_SCRATCH_EXHAUSTED (-3) /* an operator's tiles do not fit the arena scratch ([PSI] Table V) */
+#define PSI_E_PAGE_TOO_SMALL (-4)    /* a weight tile does not fit one page ([PSI] Table V) */
+#define PSI_E_PAGE_BUSY (-5)         /* second unreleased request for a page ([PSI] sec. II-A, rule 2) */
+#define PSI_E_NOT_PINNED (-6)        /* host pointer is not pinned (page-locked) memory */
+#define PSI_E_ALIGN (-7)             /* pointer or leading dimension not 16-byte aligned */
+#define PSI_E_JOURNAL_KEY (-8)       /* journal key missing, duplicated, or size mismatch */
+#define PSI_E_HIP (-9)               /* HIP runtime error */
+#define PSI_E_STATE (-10)            /* page released/acquired in the wrong lifecycle state */
+#define PSI_E_JOURNAL_FULL (-11)     /* journal host store capacity exceeded */
+
+/* ------------------------------------------------------------ arena flags */
+#define PSI_ARENA_SYNC_COPY 0x1u /* page copies on the compute stream (transport control) */
+#define PSI_ARENA_PROFILE 0x2u   /* time every kernel launch and page copy with HIP events */
+#define PSI_ARENA_DRY_RUN 0x4u   /* no device memory and no HIP calls: plans, lifecycle and
+                                    byte accounting only (host-side tests) */
+
+/* --------------------------------------------------------- operator flags */
+#define PSI_OP_BASELINE_BIAS 0x1u /* [PSI] sec. III-A baseline: round the product to BF16,
+                                     then add the bias (default: bias added in fp32) */
+#define PSI_OP_RESIDUAL 0x2u      /* y = B(f(x) + f(B(acc + b))) */
+#define PSI_OP_STORE_ACC 0x4u     /* also store the final fp32 accumulator to acc_dev */
+#define PSI_OP_BF16_SOFTMAX 0x8u  /* attention: BF16 softmax numerator weights (the
+                                     [PSI] sec. III-A baseline); default fp32-faithful */
+
+/* -------------------------------------------------------- matrix layouts */
+#define PSI_SPLIT_ROWS 0 /* page p = rows [p*block, (p+1)*block) of W: an output-column
+                            partition of y = x W^T ([PSI] sec. IV-B projections) */
+#define PSI_SPLIT_COLS 1 /* page p = columns [p*block, (p+1)*block) of W stored as a
+                            contiguous [rows, block] slice: a K-split with a carried fp32
+                            accumulator ([PSI] sec. II-B eq. (2), bias added once) */
+
+#define PSI_MAX_PAGES 8
+
+typedef struct psi_arena psi_arena;
+typedef struct psi_journal psi_journal;
+
+/* Arena description ([PSI] Fig. 1: two pages, workspace, state/scratch). */
+typedef struct psi_arena_desc {
+  size_t arena_bytes;     /* A: the single device allocation */
+  size_t page_bytes;      /* P: capacity of one weight page */
+  int n_pages;            /* reusable page slots, 1..PSI_MAX_PAGES (the paper uses 2) */
+  size_t workspace_bytes; /* W: fixed library workspace (reserved, may be 0) */
+  size_t side_bytes;      /* per-page side slot for the page's bias slice; 0 -> 64 KiB */
+  void* compute_stream;   /* hipStream_t the operators run on (caller-owned) */
+  unsigned flags;         /* PSI_ARENA_* */
+} psi_arena_desc;
+
+/* Byte offsets of the carve inside the arena (256-byte aligned). */
+typedef struct psi_arena_layout {
+  size_t page_off[PSI_MAX_PAGES];
+  size_t side_off[PSI_MAX_PAGES];
+  size_t side_bytes;
+  size_t workspace_off;
+  size_t scratch_off;
+  size_t scratch_bytes;
+  size_t total_bytes;
+} psi_arena_layout;
+
+/* Accounting ([PSI] sec. IV-A/IV-C: arena, scratch high-water, bytes moved,
+ * blocking synchronisations). */
+typedef struct psi_stats {
+  size_t arena_bytes;
+  size_t page_bytes;
+  size_t workspace_bytes;
+  size_t scratch_bytes;
+  size_t scratch_high_water;
+  uint64_t bytes_h2d;       /* page + bias bytes copied host -> device */
+  uint64_t page_copies;     /* page submissions */
+  uint64_t event_waits;     /* cross-stream waits enqueued */
+  uint64_t host_syncs;      /* blocking host synchronisations performed */
+  uint64_t kernel_launches;
+  /* PSI_ARENA_PROFILE only (0 otherwise): summed device time per kind */
+  double gemm_ms;
+  uint64_t gemm_launches;
+  double gemm_flops;        /* algorithmic 2*M*N*K of the timed GEMM launches */
+  double attn_ms;
+  uint64_t attn_launches;
+  double attn_flops;        /* algorithmic 4*Mq*Mk*dh per head of the timed launches */
+  double copy_ms;           /* summed page-copy time on the copy stream */
+  uint64_t copy_bytes_timed;
+} psi_stats;
+
+/* A weight matrix W[rows, cols] in pinned host memory, already packed into
+ * page-contiguous slices by psi_pack_matrix ([PSI] Fig. 1 "checkpoint
+ * slices"): page p starts at byte offset p * block * (split == ROWS ? cols :
+ * rows) * 2.  The last page may be narrower (ragged). */
+typedef struct psi_matrix {
+  const void* pages_host;   /* pinned, packed image of W (rows*cols bf16) */
+  const uint16_t* bias_host;/* pinned [rows] bf16, or NULL for no bias */
+  int rows;                 /* output features */
+  int cols;                 /* input features */
+  int split;                /* PSI_SPLIT_ROWS or PSI_SPLIT_COLS */
+  int block;                /* rows (ROWS) or columns (COLS) per page */
+  int resident;             /* 0: streamed through the arena pages.  1: the image and
+                               bias are DEVICE pointers (weights already resident in
+                               HBM); pages are consumed in place, nothing is copied and
+                               no page slot is used (the resident-weight comparison) */
+} psi_matrix;
+
+/* ------------------------------------------------------------ host utils */
+
+/* Pack a row-major W[rows, cols] (any host memory) into the page image
+ * layout of psi_matrix; dst must hold rows*cols bf16.  Host-only. */
+psi_status psi_pack_matrix(const uint16_t* W, int rows, int cols, int split, int block,
+                           void* dst);
+
+/* Number of pages and bytes of page p of a matrix.  Host-only. */
+int psi_matrix_pages(const psi_matrix* m);
+size_t psi_matrix_page_bytes(const psi_matrix* m, int p);
+
+/* Compute the arena carve without allocating.  Fails with
+ * PSI_E_ARENA_TOO_SMALL when the pages, side slots and workspace exceed
+ * arena_bytes.  Host-only. */
+psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out);
+
+/* Scratch and page feasibility of each operator for a given arena, without
+ * allocating or enqueueing anything (host-only).  *scratch_needed receives
+ * the scratch bytes the operator would use.  Errors: PSI_E_PAGE_TOO_SMALL
+ * when a page slice exceeds P, PSI_E_SCRATCH_EXHAUSTED when the scratch
+ * does not fit, PSI_E_INVALID for bad shapes. */
+psi_status psi_linear_plan(const psi_arena_desc* d, int M, int K, const psi_matrix* W,
+                           int acc_external, size_t* scratch_needed);
+psi_status psi_ffn_plan(const psi_arena_desc* d, int M, int dmodel, const psi_matrix* U,
+                        const psi_matrix* V, int token_chunks, int acc_external,
+                        size_t* scratch_needed);
+psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                         const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                         const psi_matrix* Wo, int acc_external, size_t* scratch_needed);
+
+/* Thread-local message describing the last error. */
+const char* psi_last_error(void);
+/* Library version string. */
+const char* psi_version(void);
+
+/* ----------------------------------------------------------------- arena */
+
+/* [PSI] sec. II-A, Fig. 1: one device allocation of arena_bytes carved into
+ * n_pages page slots (+ a side slot each for bias slices), the workspace
+ * and scratch.  Creates the copy stream and per-slot events.  *out is the
+ * caller's handle until psi_arena_destroy.  Errors: PSI_E_INVALID,
+ * PSI_E_ARENA_TOO_SMALL, PSI_E_HIP. */
+psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out);
+
+/* Synchronises the compute and copy streams and frees the one allocation. */
+psi_status psi_arena_destroy(psi_arena* a);
+
+/* Blocks the host until every enqueued page copy and operator completed. */
+psi_status psi_arena_sync(psi_arena* a);
+
+/* Copies the accounting counters (synchronises first if PSI_ARENA_PROFILE,
+ * to read the event timers). */
+psi_status psi_arena_stats(psi_arena* a, psi_stats* out);
+
+/* Zeroes the counters and the scratch high-water mark. */
+psi_status psi_arena_reset_stats(psi_arena* a);
+
+/* Device address of the arena base (for footprint checks). */
+psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_out);
+
+/* ------------------------------------------------------------ page API */
+
+/* Slice request ([PSI] sec. II-D): take the next page slot in round-robin
+ * order and enqueue an H2D copy of `bytes` from pinned host memory into it
+ * (free -> filling).  The copy waits for the slot's previous release event.
+ * Errors: PSI_E_PAGE_TOO_SMALL (bytes > P), PSI_E_PAGE_BUSY (the slot still
+ * has an unreleased request), PSI_E_NOT_PINNED, PSI_E_ALIGN. */
+psi_status psi_page_submit(psi_arena* a, const void* host_pinned, size_t bytes, int* page_out);
+
+/* Makes the compute stream wait for the page's copy (filling -> consuming)
+ * and returns its device address, so caller kernels may consume it. */
+psi_status psi_page_acquire(psi_arena* a, int page, void** dev_out);
+
+/* Ends the request: records the release event after every use enqueued so
+ * far on the compute stream; the next copy into this slot waits for it
+ * ([PSI] sec. II-D).  Releasing a page that was never acquired acquires it
+ * implicitly.  Errors: PSI_E_STATE for a free page. */
+psi_status psi_page_release(psi_arena* a, int page);
+
+/* ------------------------------------------------------------- operators */
+
+/* Paged projection y = B(x W^T + b) ([PSI] sec. III-A numerics, sec. IV-B
+ * output-column groups).
+ *   x_dev [M, K] bf16 (16-byte aligned rows: K % 8 == 0)
+ *   W: PSI_SPLIT_ROWS -> each page computes y[:, page columns] directly;
+ *      PSI_SPLIT_COLS -> K-split, fp32 accumulator carried in page order in
+ *      acc_dev (or arena scratch when acc_dev is NULL and it fits), bias
+ *      added once after the last page.
+ *   acc_dev nullable [M, N] fp32; y_dev [M, N] bf16 (N = W->rows).
+ *   flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL (y = B(x + ...), needs
+ *   K == N; y may alias x), PSI_OP_STORE_ACC. */
+psi_status psi_linear_paged(psi_arena* a, const uint16_t* x_dev, int M, int K,
+                            const psi_matrix* W, float* acc_dev, uint16_t* y_dev,
+                            unsigned flags);
+
+/* Paged FFN F(X) = phi(X U^T + a) V^T + b ([PSI] sec. II-B eq. (2)) with the
+ * declared BF16 writes of sec. III-A: pre-GELU B(acc + a), post-GELU
+ * B(phi(.)), output B(ACC + b).
+ *   U: [h, d] PSI_SPLIT_ROWS with block t_h (hidden tile J); bias a [h].
+ *   V: [d, h] PSI_SPLIT_COLS with the same block t_h; bias b [d].
+ *   Each U_J page, then each V_J page, serves all token_chunks chunks of x
+ *   before release (page reuse across token chunks); the hidden tile H_J
+ *   lives in arena scratch, the fp32 accumulator in acc_dev or scratch.
+ *   y_dev may alias x_dev (with PSI_OP_RESIDUAL: y = B(x + F(x))). */
+psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x_dev, int M, int d,
+                         const psi_matrix* U, const psi_matrix* V, int token_chunks,
+                         float* acc_dev, uint16_t* y_dev, unsigned flags);
+
+/* Paged attention sub-block ([PSI] sec. II-B eqs. (3)-(4)): per head group
+ * g (heads_per_group = Wq->block / head_dim): Q_g = x Wq_g^T + bq_g,
+ * K_g/V_g from ctx (cross-attention) or x (self), fp32 online-softmax
+ * attention per head (unmasked, noncausal, dropout-free), then
+ * ACC += O_g Wo[:, g]^T in group order, y = B(ACC + bo) (+ residual).
+ *   Wq, Wk, Wv: [d, d] PSI_SPLIT_ROWS, block = heads_per_group*head_dim;
+ *   Wo: [d, d] PSI_SPLIT_COLS with the same block.  head_dim must be 128.
+ *   ctx_dev nullable [Mc, d]; y_dev may alias x_dev. */
+psi_status psi_attn_paged(psi_arena* a, const uint16_t* x_dev, int M,
+                          const uint16_t* ctx_dev, int Mc, int heads, int head_dim,
+                          const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                          const psi_matrix* Wo, float* acc_dev, uint16_t* y_dev,
+                          unsigned flags);
+
+/* One synthetic transformer block in place: x_tmp = x + Attn(x) (self),
+ * then x = x_tmp + FFN(x_tmp), both with the residual write.  If `fence`
+ * is non-NULL, the FFN's output write first waits for every journal copy
+ * enqueued so far (the journal's reads of x are previous consumers,
+ * [PSI] sec. II-D). */
+typedef struct psi_block_weights {
+  psi_matrix Wq, Wk, Wv, Wo; /* attention projections */
+  psi_matrix U, V;           /* FFN */
+} psi_block_weights;
+psi_status psi_block_paged(psi_arena* a, uint16_t* x_dev, uint16_t* x_tmp_dev, int M,
+                           int heads, int head_dim, const psi_block_weights* w,
+                           int token_chunks, float* acc_dev, psi_journal* fence,
+                           unsigned flags);
+
+/* --------------------------------------------------------------- journal */
+
+/* Indexed host journal of BF16 state ([PSI] sec. II-D, sec. III-B):
+ * key = (step, block, branch, role).  Commit copies device bytes to a
+ * pinned ring slot on the journal's own stream after the producer's work,
+ * then moves them into the host store; reload moves them back after the
+ * consumer's previous work.  Byte-preserving. */
+typedef struct psi_key {
+  int32_t step;
+  int32_t block;
+  int32_t branch;
+  int32_t role;
+} psi_key;
+
+typedef struct psi_journal_desc {
+  size_t ring_slot_bytes; /* pinned staging slot size (e.g. 8 MiB) */
+  int ring_slots;         /* >= 2 */
+  size_t store_bytes;     /* host store capacity, allocated and touched up front */
+  unsigned flags;         /* PSI_JOURNAL_SYNC: blocking transport on the caller's stream */
+} psi_journal_desc;
+#define PSI_JOURNAL_SYNC 0x1u
+
+psi_status psi_journal_create(const psi_journal_desc* d, psi_journal** out);
+psi_status psi_journal_destroy(psi_journal* j);
+
+/* Enqueue a byte copy of dev[0, bytes) into the store under key k, ordered
+ * after all work enqueued so far on `producer`.  Errors: PSI_E_JOURNAL_KEY
+ * for a duplicate key, PSI_E_JOURNAL_FULL. */
+psi_status psi_journal_commit(psi_journal* j, psi_key k, const void* dev, size_t bytes,
+                              void* producer_stream);
+
+/* Enqueue the reload of key k into dev, ordered after all work enqueued so
+ * far on `consumer`; `consumer` then waits for the reload.  Errors:
+ * PSI_E_JOURNAL_KEY when the key is missing or sizes differ. */
+psi_status psi_journal_reload(psi_journal* j, psi_key k, void* dev, size_t bytes,
+                              void* consumer_stream);
+
+/* Make `stream` wait until every commit enqueued so far has finished
+ * reading its device buffer (device-buffer overwrites follow the journal's
+ * copies). */
+psi_status psi_journal_fence(psi_journal* j, void* stream);
+
+/* Block the host until every enqueued commit and reload is complete. */
+psi_status psi_journal_sync(psi_journal* j);
+
+/* Copy a committed entry to host memory (synchronises first). */
+psi_status psi_journal_read(psi_journal* j, psi_key k, void* host_dst, size_t bytes);
+
+/* Bytes moved and entries held. */
+psi_status psi_journal_counters(psi_journal* j, uint64_t* bytes_d2h, uint64_t* bytes_h2d,
+                                uint64_t* entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSI_H */

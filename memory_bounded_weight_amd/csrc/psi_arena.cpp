@@ -1,0 +1,329 @@
+// psi_arena.cpp -- the fixed device arena and the weight-page lifecycle.
+//
+// [PSI] sec. II-A and Fig. 1 ("Precision-Preserving Subtensor Inference for
+// a 22B Joint Audio-Video Generator under a Fixed GPU Working Set", arXiv
+// 2611.08023): all managed device memory is ONE allocation carved into
+// reusable pages, a workspace and scratch.  [PSI] sec. II-D: a page has at
+// most one outstanding slice request; its lifecycle is free -> filling ->
+// ready -> consuming; copy completion permits consumption and completion of
+// the last consumer permits the next write.  Here the copy runs on a
+// library stream and records `ready`; consumers on the compute stream wait
+// on `ready`; release records `release` on the compute stream after every
+// enqueued use, and the next copy into the slot waits on it.  The host
+// never blocks to enforce this.
+#include <cstring>
+
+#include "psi_internal.h"
+
+namespace psi {
+
+psi_status check_pinned(const void* p, const char* what) {
+  if (!p) return PSI_OK;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    return fail(PSI_E_NOT_PINNED, std::string(what) + " is not pinned host memory");
+  }
+  if (attr.type != hipMemoryTypeHost)
+    return fail(PSI_E_NOT_PINNED, std::string(what) + " is not pinned host memory (type " +
+                                      std::to_string((int)attr.type) + ")");
+  return PSI_OK;
+}
+
+void* scratch_alloc(psi_arena* a, size_t bytes, psi_status* st) {
+  size_t off = a->scratch_top;
+  size_t end = off + align_up(bytes, kAlign);
+  if (end > a->layout.scratch_bytes) {
+    *st = fail(PSI_E_SCRATCH_EXHAUSTED, "scratch exhausted: need " + std::to_string(end) +
+                                            " B of " + std::to_string(a->layout.scratch_bytes));
+    return nullptr;
+  }
+  *st = PSI_OK;
+  a->scratch_top = end;
+  if (end > a->stats.scratch_high_water) a->stats.scratch_high_water = end;
+  if (a->dry) return nullptr;
+  return a->base + a->layout.scratch_off + off;
+}
+
+void scratch_reset(psi_arena* a, size_t mark) { a->scratch_top = mark; }
+
+static hipEvent_t pool_event(psi_arena* a) {
+  if (!a->event_pool.empty()) {
+    hipEvent_t e = a->event_pool.back();
+    a->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const void* side_host,
+                          size_t side_bytes, int* page_out, bool pinned_check) {
+  if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
+  if (bytes > a->desc.page_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
+                                          " B > " + std::to_string(a->desc.page_bytes) + " B");
+  if (side_bytes > a->layout.side_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, "bias slice exceeds the page side slot");
+  const int s = a->next_slot;
+  psi_page_slot& slot = a->slots[s];
+  if (slot.state != psi_page_slot::FREE)
+    return fail(PSI_E_PAGE_BUSY, "page " + std::to_string(s) + " still has an unreleased request");
+  if (!a->dry && pinned_check) {
+    psi_status st = check_pinned(host, "page slice");
+    if (st) return st;
+    if (side_host && (st = check_pinned(side_host, "bias slice"))) return st;
+  }
+  if (!a->dry) {
+    const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
+    hipStream_t cs = sync ? a->compute : a->copy;
+    if (!sync && slot.released_once) {
+      PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
+      a->stats.event_waits++;
+    }
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (a->desc.flags & PSI_ARENA_PROFILE) {
+      t0 = pool_event(a);
+      t1 = pool_event(a);
+      if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
+      PSI_HIP(hipEventRecord(t0, cs));
+    }
+    PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, cs));
+    if (side_host && side_bytes)
+      PSI_HIP(hipMemcpyAsync(slot.side_dev, side_host, side_bytes, hipMemcpyHostToDevice, cs));
+    if (t0) {
+      PSI_HIP(hipEventRecord(t1, cs));
+      a->pending.push_back({t0, t1, 2, (double)(bytes + side_bytes)});
+    }
+    PSI_HIP(hipEventRecord(slot.ready, cs));
+  }
+  slot.state = psi_page_slot::FILLING;
+  a->stats.bytes_h2d += bytes + side_bytes;
+  a->stats.page_copies++;
+  a->next_slot = (s + 1) % a->desc.n_pages;
+  if (page_out) *page_out = s;
+  return PSI_OK;
+}
+
+psi_status page_acquire(psi_arena* a, int page) {
+  if (page < 0 || page >= a->desc.n_pages) return fail(PSI_E_INVALID, "bad page index");
+  psi_page_slot& slot = a->slots[page];
+  if (slot.state == psi_page_slot::FREE)
+    return fail(PSI_E_STATE, "page " + std::to_string(page) + " has no outstanding request");
+  if (slot.state == psi_page_slot::CONSUMING) return PSI_OK;
+  if (!a->dry && !(a->desc.flags & PSI_ARENA_SYNC_COPY)) {
+    PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready, 0));
+    a->stats.event_waits++;
+  }
+  slot.state = psi_page_slot::CONSUMING;
+  return PSI_OK;
+}
+
+psi_status page_release(psi_arena* a, int page) {
+  if (page < 0 || page >= a->desc.n_pages) return fail(PSI_E_INVALID, "bad page index");
+  psi_page_slot& slot = a->slots[page];
+  if (slot.state == psi_page_slot::FREE)
+    return fail(PSI_E_STATE, "page " + std::to_string(page) + " released while free");
+  if (slot.state == psi_page_slot::FILLING) {
+    psi_status st = page_acquire(a, page);
+    if (st) return st;
+  }
+  if (!a->dry) PSI_HIP(hipEventRecord(slot.release, a->compute));
+  slot.released_once = true;
+  slot.state = psi_page_slot::FREE;
+  return PSI_OK;
+}
+
+static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (*fn)(const void*, hipStream_t),
+                               const void* args) {
+  a->stats.kernel_launches++;
+  if (a->dry) return PSI_OK;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  if (a->desc.flags & PSI_ARENA_PROFILE) {
+    t0 = pool_event(a);
+    t1 = pool_event(a);
+    if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
+    PSI_HIP(hipEventRecord(t0, a->compute));
+  }
+  hipError_t e = fn(args, a->compute);
+  if (e != hipSuccess) return hip_fail(e, kind == 0 ? "gemm launch" : "attention launch");
+  if (t0) {
+    PSI_HIP(hipEventRecord(t1, a->compute));
+    a->pending.push_back({t0, t1, kind, work});
+  }
+  return PSI_OK;
+}
+
+static hipError_t gemm_thunk(const void* p, hipStream_t s) {
+  return launch_gemm(*static_cast<const GemmArgs*>(p), s);
+}
+static hipError_t attn_thunk(const void* p, hipStream_t s) {
+  return launch_attention(*static_cast<const AttnArgs*>(p), s);
+}
+
+psi_status run_gemm(psi_arena* a, const GemmArgs& g) {
+  double flops = 2.0 * g.M * (double)g.N * g.K;
+  return timed_launch(a, 0, flops, gemm_thunk, &g);
+}
+
+psi_status run_attention(psi_arena* a, const AttnArgs& g) {
+  double flops = 4.0 * g.Mq * (double)g.Mk * 128.0 * g.heads;
+  return timed_launch(a, 1, flops, attn_thunk, &g);
+}
+
+static psi_status harvest(psi_arena* a) {
+  if (a->dry) return PSI_OK;
+  PSI_HIP(hipStreamSynchronize(a->copy));
+  PSI_HIP(hipStreamSynchronize(a->compute));
+  a->stats.host_syncs += 2;
+  for (const psi_timed& t : a->pending) {
+    float ms = 0.0f;
+    PSI_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+    if (t.kind == 0) {
+      a->stats.gemm_ms += ms;
+      a->stats.gemm_launches++;
+      a->stats.gemm_flops += t.work;
+    } else if (t.kind == 1) {
+      a->stats.attn_ms += ms;
+      a->stats.attn_launches++;
+      a->stats.attn_flops += t.work;
+    } else {
+      a->stats.copy_ms += ms;
+      a->stats.copy_bytes_timed += (uint64_t)t.work;
+    }
+    a->event_pool.push_back(t.start);
+    a->event_pool.push_back(t.stop);
+  }
+  a->pending.clear();
+  return PSI_OK;
+}
+
+}  // namespace psi
+
+using namespace psi;
+
+extern "C" {
+
+psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
+  if (!out) return fail(PSI_E_INVALID, "psi_arena_create: null out");
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  psi_arena* a = new psi_arena();
+  a->desc = *d;
+  a->layout = L;
+  a->dry = d->flags & PSI_ARENA_DRY_RUN;
+  a->compute = static_cast<hipStream_t>(d->compute_stream);
+  a->stats.arena_bytes = d->arena_bytes;
+  a->stats.page_bytes = d->page_bytes;
+  a->stats.workspace_bytes = d->workspace_bytes;
+  a->stats.scratch_bytes = L.scratch_bytes;
+  if (!a->dry) {
+    hipError_t e = hipGetDevice(&a->device);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&a->base), d->arena_bytes);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy, hipStreamNonBlocking);
+    for (int i = 0; e == hipSuccess && i < d->n_pages; ++i) {
+      e = hipEventCreateWithFlags(&a->slots[i].ready, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].release, hipEventDisableTiming);
+      a->slots[i].dev = a->base + L.page_off[i];
+      a->slots[i].side_dev = a->base + L.side_off[i];
+    }
+    if (e != hipSuccess) {
+      psi_status r = hip_fail(e, "psi_arena_create");
+      psi_arena_destroy(a);
+      return r;
+    }
+  }
+  *out = a;
+  return PSI_OK;
+}
+
+psi_status psi_arena_destroy(psi_arena* a) {
+  if (!a) return PSI_OK;
+  psi_status st = PSI_OK;
+  if (!a->dry) {
+    if (a->copy) (void)hipStreamSynchronize(a->copy);
+    (void)hipStreamSynchronize(a->compute);
+    for (psi_timed& t : a->pending) {
+      a->event_pool.push_back(t.start);
+      a->event_pool.push_back(t.stop);
+    }
+    for (hipEvent_t e : a->event_pool) (void)hipEventDestroy(e);
+    for (int i = 0; i < a->desc.n_pages; ++i) {
+      if (a->slots[i].ready) (void)hipEventDestroy(a->slots[i].ready);
+      if (a->slots[i].release) (void)hipEventDestroy(a->slots[i].release);
+    }
+    if (a->copy) (void)hipStreamDestroy(a->copy);
+    if (a->base) {
+      hipError_t e = hipFree(a->base);
+      if (e != hipSuccess) st = hip_fail(e, "hipFree(arena)");
+    }
+  }
+  delete a;
+  return st;
+}
+
+psi_status psi_arena_sync(psi_arena* a) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (a->dry) return PSI_OK;
+  PSI_HIP(hipStreamSynchronize(a->copy));
+  PSI_HIP(hipStreamSynchronize(a->compute));
+  a->stats.host_syncs += 2;
+  return PSI_OK;
+}
+
+psi_status psi_arena_stats(psi_arena* a, psi_stats* out) {
+  if (!a || !out) return fail(PSI_E_INVALID, "null argument");
+  if ((a->desc.flags & PSI_ARENA_PROFILE) && !a->pending.empty()) {
+    psi_status st = harvest(a);
+    if (st) return st;
+  }
+  *out = a->stats;
+  return PSI_OK;
+}
+
+psi_status psi_arena_reset_stats(psi_arena* a) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (!a->pending.empty()) {
+    psi_status st = harvest(a);
+    if (st) return st;
+  }
+  psi_stats s;
+  std::memset(&s, 0, sizeof s);
+  s.arena_bytes = a->stats.arena_bytes;
+  s.page_bytes = a->stats.page_bytes;
+  s.workspace_bytes = a->stats.workspace_bytes;
+  s.scratch_bytes = a->stats.scratch_bytes;
+  s.scratch_high_water = a->scratch_top;
+  a->stats = s;
+  return PSI_OK;
+}
+
+psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_out) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (base_out) *base_out = a->base;
+  if (bytes_out) *bytes_out = a->desc.arena_bytes;
+  return PSI_OK;
+}
+
+psi_status psi_page_submit(psi_arena* a, const void* host_pinned, size_t bytes, int* page_out) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  return page_submit_ex(a, host_pinned, bytes, nullptr, 0, page_out, true);
+}
+
+psi_status psi_page_acquire(psi_arena* a, int page, void** dev_out) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  psi_status st = page_acquire(a, page);
+  if (st) return st;
+  if (dev_out) *dev_out = a->dry ? nullptr : a->slots[page].dev;
+  return PSI_OK;
+}
+
+psi_status psi_page_release(psi_arena* a, int page) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  return page_release(a, page);
+}
+
+}  // extern "C"

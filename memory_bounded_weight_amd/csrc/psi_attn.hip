@@ -1,0 +1,236 @@
+// psi_attn.hip -- row-blocked attention with fp32 online softmax, gfx950.
+//
+// [PSI] sec. II-B eqs. (3)-(4) ("Precision-Preserving Subtensor Inference
+// for a 22B Joint Audio-Video Generator under a Fixed GPU Working Set",
+// arXiv 2611.08023): for every query, keys are processed in disjoint tiles
+// T while a running maximum m, normaliser l and weighted value sum z are
+// kept; for each tile m' = max(m, max_T s_j), eta = e^(m - m'),
+// l' = eta l + sum_T e^(s_j - m'), z' = eta z + sum_T e^(s_j - m') v_j.
+// After the last tile z / l is dense softmax attention (unmasked,
+// noncausal, no dropout, at least one key).
+//
+// Layout of the work (head_dim 128, 64 keys per tile):
+//   * one workgroup = 4 waves = 128 queries of one head; each wave owns 32
+//     queries;
+//   * scores are computed transposed, S^T = K Q^T, with the 32x32x16 BF16
+//     MFMA: in its accumulator layout a lane holds ONE query (column) and
+//     16 keys, so m, l and the rescale factor of a query live in one lane
+//     (and its partner lane l^32), with no cross-lane shuffles of the
+//     output accumulator;
+//   * the output is also accumulated transposed, O^T = V^T P^T: V^T comes
+//     from the value projection, which writes V transposed, and P^T is fed
+//     straight from the score registers as the B operand;
+//   * the softmax weights stay fp32-faithful on the BF16 matrix cores by
+//     splitting p = hi + lo into two BF16 numbers and issuing two MFMAs
+//     (the FP32 accumulation of modified PSI, sec. III-A); with bf16_p set
+//     only hi is used (the BF16-numerator baseline).
+#include "psi_internal.h"
+
+namespace psi {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t f2bf(float v) {
+  uint32_t w = __float_as_uint(v);
+  if ((w & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  w += 0x7FFFu + ((w >> 16) & 1u);
+  return (uint16_t)(w >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+constexpr int DH = 128;       // head dimension
+constexpr int KT = 64;        // keys per tile
+constexpr int QB = 128;       // queries per workgroup
+constexpr int KS = DH + 8;    // K tile row stride in LDS (elements): 272 B
+constexpr int VS = KT + 4;    // V^T tile row stride in LDS (elements): 136 B
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DH * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int h = blockIdx.y;
+  const int qrow = blockIdx.x * QB + wave * 32 + l32;  // this lane's query
+  const bool qvalid = qrow < p.Mq;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][kk*16 + half*8 + 0..7].
+  bf16x8 qf[DH / 16];
+  {
+    const uint16_t* qp = p.q + (long)qrow * p.ldq + h * DH + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      u16x8 v = qvalid ? *reinterpret_cast<const u16x8*>(qp + kk * 16) : (u16x8)0;
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // Global -> register staging of one key tile: K rows (keys) and V^T rows
+  // (channels of this head), 16-byte chunks, 4 of each per thread.
+  uint4 rk[4], rv[4];
+  const uint16_t* kbase = p.k + h * DH;
+  const uint16_t* vbase = p.vt + (long)h * DH * p.ldvt;
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + i * kThreads;          // 0..1023
+      int r = c >> 4, col = (c & 15) * 8;  // K tile: 64 rows x 16 chunks
+      int key = key0 + r;
+      rk[i] = key < p.Mk ? *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + col)
+                         : make_uint4(0, 0, 0, 0);
+      int vr = c >> 3, vcol = (c & 7) * 8;  // V^T tile: 128 rows x 8 chunks
+      int vkey = key0 + vcol;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (vkey < p.Mk) {
+        v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+        if (vkey + 8 > p.Mk) {  // ragged key tail inside the chunk: zero the rest
+          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (vkey + t >= p.Mk) e[t] = 0;
+        }
+      }
+      rv[i] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + i * kThreads;
+      int r = c >> 4, col = (c & 15) * 8;
+      *reinterpret_cast<uint4*>(&k_lds[buf][r * KS + col]) = rk[i];
+      int vr = c >> 3, vcol = (c & 7) * 8;
+      uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][vr * VS + vcol]);  // 8-byte aligned rows
+      dst[0] = make_uint2(rv[i].x, rv[i].y);
+      dst[1] = make_uint2(rv[i].z, rv[i].w);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+
+  const int ntiles = (p.Mk + KT - 1) / KT;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int key0 = t * KT;
+    if (t + 1 < ntiles) load_tile(key0 + KT);
+
+    // S^T for 64 keys x this wave's 32 queries: two 32x32 accumulator tiles.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < DH / 16; ++kk) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[cur][(kb * 32 + l32) * KS + kk * 16 + half * 8]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+      }
+    }
+    // scale, mask the key tail, tile maximum of this query
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int key = key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        float v = key < p.Mk ? s[kb][r] * p.alpha : -INFINITY;
+        s[kb][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float eta = __expf(m_run - m_new);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __expf(s[kb][r] - m_new);
+        s[kb][r] = e;
+        lsum += e;
+      }
+    lsum += __shfl_xor(lsum, 32);
+    l_run = eta * l_run + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= eta;
+
+    // O^T += V^T P^T over 4 groups of 16 keys.  Slot j of a lane's B operand
+    // holds score register i = (g%2)*8 + j of tile g/2, i.e. key
+    // 16g + 4*half + j (j < 4) or 16g + 8 + 4*half + (j-4) (j >= 4); the A
+    // operand (V^T) uses the same key for the same slot.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float pv = s[g >> 1][(g & 1) * 8 + j];
+        uint16_t hb = f2bf(pv);
+        hi[j] = hb;
+        lo[j] = f2bf(pv - bf2f(hb));
+      }
+      const bf16x8 bhi = __builtin_bit_cast(bf16x8, hi);
+      const bf16x8 blo = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+        const uint16_t* vr = &v_lds[cur][(dt * 32 + l32) * VS + 16 * g + 4 * half];
+        uint2 x0 = *reinterpret_cast<const uint2*>(vr);
+        uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
+        uint4 av = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, o[dt], 0, 0, 0);
+        if (!p.bf16_p) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, o[dt], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // O = B(z / l).  O^T layout: lane holds query qrow, channels
+  // dt*32 + 8*(r/4) + 4*half + (r%4): four consecutive channels per store.
+  if (qvalid) {
+    uint16_t* op = p.q + (long)qrow * p.ldq + h * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = dt * 32 + 8 * rg + 4 * half;
+        uint16_t b0 = f2bf(o[dt][rg * 4 + 0] / l_run);
+        uint16_t b1 = f2bf(o[dt][rg * 4 + 1] / l_run);
+        uint16_t b2 = f2bf(o[dt][rg * 4 + 2] / l_run);
+        uint16_t b3 = f2bf(o[dt][rg * 4 + 3] / l_run);
+        uint2 w = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16));
+        *reinterpret_cast<uint2*>(op + c0) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.Mq <= 0) return hipSuccess;
+  dim3 grid((a.Mq + QB - 1) / QB, a.heads);
+  hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace psi

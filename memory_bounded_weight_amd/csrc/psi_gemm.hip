@@ -1,0 +1,214 @@
+// psi_gemm.hip -- page-sliced BF16 GEMM for gfx950 (CDNA4).
+//
+// Computes C[M,N] = A[M,K] * B[N,K]^T with fp32 accumulation on the matrix
+// cores (v_mfma_f32_32x32x16_bf16), operands staged through LDS with a
+// double buffer, and a fused epilogue:
+//   * carried fp32 accumulator: the MFMA accumulators start from acc_in, so
+//     a K-split over weight pages continues one accumulation chain per
+//     output in page order ([PSI] sec. II-B eq. (2): disjoint
+//     down-projection sum, output bias added once);
+//   * bias in fp32 before the single BF16 write (modified PSI, [PSI] sec.
+//     III-A) or after rounding the product (baseline PSI);
+//   * tanh-GELU between the two declared BF16 writes of the up-projection
+//     ([PSI] sec. III-A);
+//   * residual write B(f(x) + f(y)).
+// [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint
+// Audio-Video Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+//
+// Determinism: one fixed instruction sequence per output element for every
+// shape (no split-K inside a launch, no atomics), so the same operands give
+// the same bits on every run and for every page partition of the output.
+#include "psi_internal.h"
+
+namespace psi {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// Round to bfloat16, nearest with ties to even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint16_t f2bf(float v) {
+  uint32_t w = __float_as_uint(v);
+  if ((w & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  w += 0x7FFFu + ((w >> 16) & 1u);
+  return (uint16_t)(w >> 16);
+}
+
+// tanh-GELU, phi(v) = v/2 (1 + tanh(c (v + 0.044715 v^3))), c = sqrt(2/pi),
+// written as v / (1 + exp(-2u)) so that neither tail cancels.
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float c = 0.7978845608028654f;
+  float u = c * (v + 0.044715f * v * v * v);
+  return v / (1.0f + expf(-2.0f * u));
+}
+
+constexpr int kThreads = 256;  // 4 waves of 64
+
+template <int BM, int BN, int BK>
+struct Tile {
+  static constexpr int LDS = BK + 8;            // padded row stride (elements)
+  static constexpr int A_CHUNKS = BM * BK / 8;  // 16-byte chunks per tile
+  static constexpr int B_CHUNKS = BN * BK / 8;
+  static constexpr int A_PER_T = A_CHUNKS / kThreads;
+  static constexpr int B_PER_T = B_CHUNKS / kThreads;
+  static constexpr int WM = BM / 2;  // wave tile (2 x 2 waves)
+  static constexpr int WN = BN / 2;
+  static constexpr int TM = WM / 32;  // MFMA tiles per wave
+  static constexpr int TN = WN / 32;
+  static_assert(A_CHUNKS % kThreads == 0 && B_CHUNKS % kThreads == 0, "tile/threads");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+};
+
+template <int BM, int BN, int BK>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  using T = Tile<BM, BN, BK>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * T::LDS];
+
+  // Tile order: consecutive workgroups walk down M for a fixed N column
+  // band, so the B slice (the weight page) of a band is re-read from L2.
+  const int bid = blockIdx.x;
+  const int tm = bid % tiles_m;
+  const int tn = bid / tiles_m;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  constexpr int CPR = BK / 8;  // chunks per row
+  uint4 ra[T::A_PER_T], rb[T::B_PER_T];
+
+  auto load_global = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < T::A_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      int r = c / CPR, kc = (c % CPR) * 8;
+      int gr = m0 + r, gk = k0 + kc;
+      if (gr < p.M && gk < p.K)
+        ra[i] = *reinterpret_cast<const uint4*>(p.A + (long)gr * p.lda + gk);
+      else
+        ra[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      int r = c / CPR, kc = (c % CPR) * 8;
+      int gr = n0 + r, gk = k0 + kc;
+      if (gr < p.N && gk < p.K)
+        rb[i] = *reinterpret_cast<const uint4*>(p.B + (long)gr * p.ldb + gk);
+      else
+        rb[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_lds = [&](int buf) {
+    uint16_t* sa = smem[buf];
+    uint16_t* sb = smem[buf] + BM * T::LDS;
+#pragma unroll
+    for (int i = 0; i < T::A_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      int r = c / CPR, kc = (c % CPR) * 8;
+      *reinterpret_cast<uint4*>(sa + r * T::LDS + kc) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      int r = c / CPR, kc = (c % CPR) * 8;
+      *reinterpret_cast<uint4*>(sb + r * T::LDS + kc) = rb[i];
+    }
+  };
+
+  // Accumulators, C layout of the 32x32 MFMA: lane holds column l32 and
+  // rows 8*(i/4) + 4*half + (i%4), i = 0..15.
+  f32x16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = 0.0f;
+        if (p.acc_in) {
+          int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          int gn = n0 + wn * T::WN + j * 32 + l32;
+          if (gm < p.M && gn < p.N) v = p.acc_in[(long)gm * p.ld_acc_in + gn];
+        }
+        acc[i][j][r] = v;
+      }
+
+  const int nk = (p.K + BK - 1) / BK;
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_global((kt + 1) * BK);
+    const uint16_t* sa = smem[cur] + (wm * T::WM) * T::LDS;
+    const uint16_t* sb = smem[cur] + BM * T::LDS + (wn * T::WN) * T::LDS;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kofs = ks * 16 + half * 8;
+      bf16x8 af[T::TM], bfr[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + (i * 32 + l32) * T::LDS + kofs);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (j * 32 + l32) * T::LDS + kofs);
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        const int gn = n0 + wn * T::WN + j * 32 + l32;
+        if (gm >= p.M || gn >= p.N) continue;
+        const float v = acc[i][j][r];
+        if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
+        if (p.out) {
+          float t;
+          if (p.bias) {
+            const float bv = bf2f(p.bias[p.bias_on_m ? gm : gn]);
+            t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
+          } else {
+            t = v;
+          }
+          uint16_t y = f2bf(t);
+          if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
+          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
+          p.out[(long)gm * p.ldo + gn] = y;
+        }
+      }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  constexpr int BM = 128, BN = 128, BK = 64;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace psi

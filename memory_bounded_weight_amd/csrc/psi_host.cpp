@@ -1,0 +1,251 @@
+// psi_host.cpp -- host-only parts of the runtime: error reporting, page-image
+// packing, arena carve and operator feasibility plans.  Nothing here touches
+// the device, so all of it runs (and is tested) without a GPU.
+//
+// [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint
+// Audio-Video Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+#include <cstring>
+#include <string>
+
+#include "psi_internal.h"
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+namespace psi {
+
+psi_status fail(psi_status code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+psi_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return PSI_E_HIP;
+}
+
+psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split) {
+  if (!m) return fail(PSI_E_INVALID, std::string(name) + ": null matrix");
+  if (m->rows <= 0 || m->cols <= 0 || m->block <= 0)
+    return fail(PSI_E_INVALID, std::string(name) + ": non-positive rows/cols/block");
+  if (m->split != PSI_SPLIT_ROWS && m->split != PSI_SPLIT_COLS)
+    return fail(PSI_E_INVALID, std::string(name) + ": unknown split");
+  if (expect_split >= 0 && m->split != expect_split)
+    return fail(PSI_E_INVALID, std::string(name) + (expect_split == PSI_SPLIT_ROWS
+                                                         ? ": must be split by rows (output columns)"
+                                                         : ": must be split by columns (K-split)"));
+  if (m->cols % 8 != 0 || (m->split == PSI_SPLIT_COLS && m->block % 8 != 0))
+    return fail(PSI_E_ALIGN, std::string(name) + ": K extents must be multiples of 8 (16-byte rows)");
+  if (!m->pages_host) return fail(PSI_E_INVALID, std::string(name) + ": null page image");
+  return PSI_OK;
+}
+
+int matrix_page_extent(const psi_matrix* m, int p) {
+  int total = m->split == PSI_SPLIT_ROWS ? m->rows : m->cols;
+  int start = p * m->block;
+  int ext = total - start;
+  return ext < m->block ? ext : m->block;
+}
+
+MatrixInfo matrix_info(const psi_matrix* m) {
+  MatrixInfo mi;
+  int total = m->split == PSI_SPLIT_ROWS ? m->rows : m->cols;
+  mi.pages = (total + m->block - 1) / m->block;
+  size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
+  mi.max_page_bytes = (size_t)(m->block < total ? m->block : total) * other * 2;
+  return mi;
+}
+
+const void* matrix_page_ptr(const psi_matrix* m, int p) {
+  size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
+  return static_cast<const char*>(m->pages_host) + (size_t)p * m->block * other * 2;
+}
+
+}  // namespace psi
+
+using namespace psi;
+
+extern "C" {
+
+const char* psi_last_error(void) { return g_last_error.c_str(); }
+
+const char* psi_version(void) { return "psi-mi355x 0.1 (gfx950)"; }
+
+psi_status psi_pack_matrix(const uint16_t* W, int rows, int cols, int split, int block, void* dst) {
+  if (!W || !dst || rows <= 0 || cols <= 0 || block <= 0)
+    return fail(PSI_E_INVALID, "psi_pack_matrix: bad arguments");
+  uint16_t* out = static_cast<uint16_t*>(dst);
+  if (split == PSI_SPLIT_ROWS) {
+    // row blocks of a row-major matrix are already contiguous
+    if (out != W) std::memmove(out, W, (size_t)rows * cols * 2);
+    return PSI_OK;
+  }
+  if (split != PSI_SPLIT_COLS) return fail(PSI_E_INVALID, "psi_pack_matrix: unknown split");
+  if (out == W) return fail(PSI_E_INVALID, "psi_pack_matrix: column split cannot be packed in place");
+  size_t off = 0;
+  for (int c0 = 0; c0 < cols; c0 += block) {
+    int w = cols - c0 < block ? cols - c0 : block;
+    for (int r = 0; r < rows; ++r) {
+      std::memcpy(out + off, W + (size_t)r * cols + c0, (size_t)w * 2);
+      off += (size_t)w;
+    }
+  }
+  return PSI_OK;
+}
+
+int psi_matrix_pages(const psi_matrix* m) {
+  if (!m || m->block <= 0) return 0;
+  return matrix_info(m).pages;
+}
+
+size_t psi_matrix_page_bytes(const psi_matrix* m, int p) {
+  if (!m || p < 0 || p >= psi_matrix_pages(m)) return 0;
+  size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
+  return (size_t)matrix_page_extent(m, p) * other * 2;
+}
+
+psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out) {
+  if (!d || !out) return fail(PSI_E_INVALID, "psi_arena_plan: null argument");
+  if (d->n_pages < 1 || d->n_pages > PSI_MAX_PAGES)
+    return fail(PSI_E_INVALID, "psi_arena_plan: n_pages must be 1.." + std::to_string(PSI_MAX_PAGES));
+  if (d->page_bytes == 0 || d->arena_bytes == 0)
+    return fail(PSI_E_INVALID, "psi_arena_plan: zero arena or page size");
+  psi_arena_layout L;
+  std::memset(&L, 0, sizeof L);
+  L.side_bytes = align_up(d->side_bytes ? d->side_bytes : kDefaultSide, kAlign);
+  size_t off = 0;
+  for (int i = 0; i < d->n_pages; ++i) {
+    L.page_off[i] = off;
+    off += align_up(d->page_bytes, kAlign);
+  }
+  for (int i = 0; i < d->n_pages; ++i) {
+    L.side_off[i] = off;
+    off += L.side_bytes;
+  }
+  L.workspace_off = off;
+  off += align_up(d->workspace_bytes, kAlign);
+  if (off > d->arena_bytes)
+    return fail(PSI_E_ARENA_TOO_SMALL,
+                "arena of " + std::to_string(d->arena_bytes) + " B cannot hold " +
+                    std::to_string(d->n_pages) + " pages of " + std::to_string(d->page_bytes) +
+                    " B, their side slots and " + std::to_string(d->workspace_bytes) + " B workspace");
+  L.scratch_off = off;
+  L.scratch_bytes = (d->arena_bytes - off) / kAlign * kAlign;
+  L.total_bytes = d->arena_bytes;
+  *out = L;
+  return PSI_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- plans
+namespace psi {
+
+static psi_status page_fit(const psi_arena_desc* d, const psi_arena_layout& L, const psi_matrix* m,
+                           const char* name, size_t side_need) {
+  if (m->resident) return PSI_OK;  // consumed in place, never copied into a page
+  MatrixInfo mi = matrix_info(m);
+  if (mi.max_page_bytes > d->page_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, std::string("weight tile exceeds page: ") + name + " needs " +
+                                          std::to_string(mi.max_page_bytes) + " B per page, page is " +
+                                          std::to_string(d->page_bytes) + " B");
+  if (side_need > L.side_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, std::string("bias slice of ") + name + " (" +
+                                          std::to_string(side_need) + " B) exceeds the side slot (" +
+                                          std::to_string(L.side_bytes) + " B)");
+  return PSI_OK;
+}
+
+static size_t bias_side_bytes(const psi_matrix* m) {
+  if (!m->bias_host) return 0;
+  // ROWS: each page carries its slice; COLS: the last page carries all of it
+  return m->split == PSI_SPLIT_ROWS ? (size_t)(m->block < m->rows ? m->block : m->rows) * 2
+                                    : (size_t)m->rows * 2;
+}
+
+static psi_status scratch_fit(const psi_arena_layout& L, size_t need, const char* what) {
+  if (need > L.scratch_bytes)
+    return fail(PSI_E_SCRATCH_EXHAUSTED, std::string("scratch exhausted: ") + what + " needs " +
+                                             std::to_string(need) + " B, scratch is " +
+                                             std::to_string(L.scratch_bytes) + " B");
+  return PSI_OK;
+}
+
+}  // namespace psi
+
+extern "C" {
+
+psi_status psi_linear_plan(const psi_arena_desc* d, int M, int K, const psi_matrix* W,
+                           int acc_external, size_t* scratch_needed) {
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  if ((st = check_matrix(W, "W", -1))) return st;
+  if (M < 0 || K <= 0 || K != W->cols) return fail(PSI_E_INVALID, "linear: x is [M, K] with K == W.cols");
+  if ((st = page_fit(d, L, W, "W", bias_side_bytes(W)))) return st;
+  size_t need = 0;
+  if (W->split == PSI_SPLIT_COLS && !acc_external) need += align_up((size_t)M * W->rows * 4, kAlign);
+  if ((st = scratch_fit(L, need, "linear accumulator"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
+psi_status psi_ffn_plan(const psi_arena_desc* d, int M, int dmodel, const psi_matrix* U,
+                        const psi_matrix* V, int token_chunks, int acc_external,
+                        size_t* scratch_needed) {
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  if ((st = check_matrix(U, "U", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(V, "V", PSI_SPLIT_COLS))) return st;
+  if (M < 0 || dmodel <= 0 || U->cols != dmodel || V->rows != dmodel || V->cols != U->rows)
+    return fail(PSI_E_INVALID, "ffn: need U [h, d] and V [d, h]");
+  if (U->block != V->block) return fail(PSI_E_INVALID, "ffn: U and V must share the hidden tile");
+  if (U->block % 8 != 0) return fail(PSI_E_ALIGN, "ffn: hidden tile must be a multiple of 8");
+  if (token_chunks < 1) return fail(PSI_E_INVALID, "ffn: token_chunks must be >= 1");
+  if ((st = page_fit(d, L, U, "U", bias_side_bytes(U)))) return st;
+  if ((st = page_fit(d, L, V, "V", bias_side_bytes(V)))) return st;
+  size_t need = align_up((size_t)M * U->block * 2, kAlign);  // hidden tile H_J, all rows
+  if (!acc_external) need += align_up((size_t)M * dmodel * 4, kAlign);
+  if ((st = scratch_fit(L, need, "FFN hidden tile and accumulator"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
+psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                         const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                         const psi_matrix* Wo, int acc_external, size_t* scratch_needed) {
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  if (head_dim != 128) return fail(PSI_E_INVALID, "attention: head_dim must be 128");
+  if (heads <= 0 || M < 0 || Mc < 0) return fail(PSI_E_INVALID, "attention: bad sizes");
+  const int dm = heads * head_dim;
+  if ((st = check_matrix(Wq, "Wq", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(Wk, "Wk", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(Wv, "Wv", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(Wo, "Wo", PSI_SPLIT_COLS))) return st;
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  for (const psi_matrix* m : ms)
+    if (m->rows != dm || m->cols != dm)
+      return fail(PSI_E_INVALID, "attention: projections must be [heads*head_dim, heads*head_dim]");
+  const int gw = Wq->block;
+  if (gw % head_dim != 0 || Wk->block != gw || Wv->block != gw || Wo->block != gw)
+    return fail(PSI_E_INVALID, "attention: all four matrices need the same head-group block "
+                               "(a multiple of head_dim)");
+  const char* names[4] = {"Wq", "Wk", "Wv", "Wo"};
+  for (int i = 0; i < 4; ++i)
+    if ((st = page_fit(d, L, ms[i], names[i], bias_side_bytes(ms[i])))) return st;
+  const int Ms = Mc > 0 ? Mc : M;
+  if (Ms < 1 && M > 0) return fail(PSI_E_INVALID, "attention: at least one key per row is required");
+  size_t ldvt = align_up((size_t)Ms, 64);
+  size_t need = align_up((size_t)M * gw * 2, kAlign) + align_up((size_t)Ms * gw * 2, kAlign) +
+                align_up((size_t)gw * ldvt * 2, kAlign);
+  if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
+  if ((st = scratch_fit(L, need, "attention Q/K/V head-group tiles"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
+}  // extern "C"

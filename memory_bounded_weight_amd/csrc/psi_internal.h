@@ -1,0 +1,139 @@
+// psi_internal.h -- shared declarations of the paged-operator runtime.
+//
+// [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint
+// Audio-Video Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "psi.h"
+
+namespace psi {
+
+// ------------------------------------------------------------- errors
+psi_status fail(psi_status code, const std::string& msg);
+psi_status hip_fail(hipError_t e, const char* what);
+#define PSI_HIP(call)                                     \
+  do {                                                    \
+    hipError_t e_ = (call);                               \
+    if (e_ != hipSuccess) return ::psi::hip_fail(e_, #call); \
+  } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr size_t kAlign = 256;
+constexpr size_t kDefaultSide = 64 * 1024;
+
+// ------------------------------------------------------------- kernels
+enum GemmEpilogue : int {
+  EPI_ACC = 0,   // store fp32 accumulator only
+  EPI_BIAS = 1,  // out = B(acc + bias)  [+ residual]
+  EPI_GELU = 2,  // out = B(phi(f(B(acc + bias))))
+};
+
+// C[M,N] = A[M,K] * B[N,K]^T (both operands K-contiguous bf16), fp32
+// accumulation on MFMA, optional carried initial accumulator and fused
+// epilogue.  All pointers are device pointers; leading dimensions are in
+// elements.
+struct GemmArgs {
+  const uint16_t* A;
+  long lda;
+  const uint16_t* B;
+  long ldb;
+  int M, N, K;
+  const float* acc_in;  // nullable [M, ld_acc]: initial accumulator
+  long ld_acc_in;
+  float* acc_out;       // nullable: fp32 accumulator store
+  long ld_acc_out;
+  const uint16_t* bias; // nullable
+  int bias_on_m;        // bias indexed by row (1) or column (0)
+  uint16_t* out;        // nullable bf16 output
+  long ldo;
+  const uint16_t* resid;// nullable residual, indexed like out (may alias out)
+  long ldr;
+  int epi;
+  int baseline_bias;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  uint16_t* q;         // [Mq, ldq]; head h occupies columns h*128..h*128+127; O overwrites it
+  long ldq;
+  const uint16_t* k;   // [Mk, ldk]
+  long ldk;
+  const uint16_t* vt;  // [heads*128, ldvt]: V transposed (row = channel, column = key)
+  long ldvt;
+  int Mq, Mk, heads;
+  float alpha;         // 1/sqrt(128) rounded to fp32
+  int bf16_p;          // 1: softmax weights rounded to BF16 before P*V
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------- planning
+struct MatrixInfo {
+  int pages;
+  size_t max_page_bytes;
+};
+psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split);
+MatrixInfo matrix_info(const psi_matrix* m);
+const void* matrix_page_ptr(const psi_matrix* m, int p);
+int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COLS) in page p
+
+}  // namespace psi
+
+// ------------------------------------------------------------- arena
+struct psi_page_slot {
+  enum State { FREE = 0, FILLING = 1, CONSUMING = 2 };
+  State state = FREE;
+  hipEvent_t ready = nullptr;    // recorded on the copy stream after the copy
+  hipEvent_t release = nullptr;  // recorded on the compute stream after the last consumer
+  bool released_once = false;
+  void* dev = nullptr;
+  void* side_dev = nullptr;
+};
+
+struct psi_timed {
+  hipEvent_t start, stop;
+  int kind;      // 0 gemm, 1 attention, 2 copy
+  double work;   // flops (kernels) or bytes (copies)
+};
+
+struct psi_arena {
+  psi_arena_desc desc{};
+  psi_arena_layout layout{};
+  bool dry = false;
+  char* base = nullptr;
+  hipStream_t compute = nullptr;
+  hipStream_t copy = nullptr;
+  psi_page_slot slots[PSI_MAX_PAGES];
+  int next_slot = 0;
+  // scratch stack (offsets relative to layout.scratch_off)
+  size_t scratch_top = 0;
+  psi_stats stats{};
+  // profiling
+  std::vector<psi_timed> pending;
+  std::vector<hipEvent_t> event_pool;
+  int device = 0;
+};
+
+namespace psi {
+// Scratch bump allocation inside the arena; nullptr in a dry run.
+void* scratch_alloc(psi_arena* a, size_t bytes, psi_status* st);
+void scratch_reset(psi_arena* a, size_t mark);
+
+// Internal page request carrying an optional side (bias) slice.
+psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const void* side_host,
+                          size_t side_bytes, int* page_out, bool check_pinned);
+psi_status page_acquire(psi_arena* a, int page);
+psi_status page_release(psi_arena* a, int page);
+
+// Kernel launch through the arena (profiling, counters).
+psi_status run_gemm(psi_arena* a, const GemmArgs& g);
+psi_status run_attention(psi_arena* a, const AttnArgs& g);
+
+psi_status check_pinned(const void* p, const char* what);
+}  // namespace psi

@@ -1,0 +1,248 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load and export every entry point ``include/psi.h``
+declares; the arena carve, the operator feasibility plans and the page
+lifecycle are host logic and are checked here through a dry-run arena
+(``PSI_ARENA_DRY_RUN``: no device memory, no HIP calls, no compute).
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from memory_bounded_weight_amd import psi
+
+MiB = 1 << 20
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "psi.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psi_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(psi.EXPORTS) == declared
+    out = subprocess.run(["nm", "-D", "--defined-only", psi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (psi_\w+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    assert "gfx950" in psi.psi_version()
+
+
+def test_library_has_gfx950_code_object():
+    """The shared library embeds an offload bundle for gfx950."""
+    blob = open(psi.LIB_PATH, "rb").read()
+    assert b"__CLANG_OFFLOAD_BUNDLE__" in blob
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def desc(arena_mib, page_mib, n_pages=2, ws_mib=0, flags=psi.PSI_ARENA_DRY_RUN):
+    return psi.arena_desc(int(arena_mib * MiB), int(page_mib * MiB), n_pages, int(ws_mib * MiB), 0,
+                          None, flags)
+
+
+# ------------------------------------------------------------------ carve
+
+def test_arena_carve_paper_split():
+    """[PSI] sec. IV-A / Fig. 1: 80 MiB = 8 + 8 pages + 8 workspace + 56
+    state/scratch; here the two 64 KiB bias side slots come out of the
+    56 MiB (they are the bounded metadata term of eq. (1))."""
+    L = psi.psi_arena_plan(desc(80, 8, 2, 8))
+    assert L.page_off[0] == 0 and L.page_off[1] == 8 * MiB
+    assert L.side_off[0] == 16 * MiB and L.side_bytes == 64 * 1024
+    assert L.workspace_off == 16 * MiB + 128 * 1024
+    assert L.scratch_off == 24 * MiB + 128 * 1024
+    assert L.scratch_bytes == 56 * MiB - 128 * 1024
+    assert L.total_bytes == 80 * MiB
+
+
+def test_arena_too_small():
+    with pytest.raises(psi.PsiError) as e:
+        psi.psi_arena_plan(desc(16, 8, 2, 8))
+    assert e.value.status == psi.PSI_E_ARENA_TOO_SMALL
+    with pytest.raises(psi.PsiError) as e:
+        psi.psi_arena_plan(desc(80, 8, 0))
+    assert e.value.status == psi.PSI_E_INVALID
+
+
+# ---------------------------------------------------- matrices and packing
+
+def test_pack_matrix_column_pages():
+    rng = np.random.default_rng(0)
+    W = rng.integers(0, 65535, size=(6, 40), dtype=np.uint16)
+    out = np.zeros(6 * 40, np.uint16)
+    psi.psi_pack_matrix(W, 6, 40, psi.PSI_SPLIT_COLS, 16, out)
+    pages = [W[:, 0:16], W[:, 16:32], W[:, 32:40]]
+    assert np.array_equal(out, np.concatenate([p.ravel() for p in pages]))
+    out2 = np.zeros(6 * 40, np.uint16)
+    psi.psi_pack_matrix(W, 6, 40, psi.PSI_SPLIT_ROWS, 4, out2)
+    assert np.array_equal(out2, W.ravel())
+    m = psi.make_matrix(out, None, 6, 40, psi.PSI_SPLIT_COLS, 16)
+    assert psi.psi_matrix_pages(m) == 3
+    assert [psi.psi_matrix_page_bytes(m, p) for p in range(3)] == [6 * 16 * 2, 6 * 16 * 2, 6 * 8 * 2]
+
+
+def fake_matrix(rows, cols, split, block, bias=True):
+    # plans never dereference the image; any non-null address works
+    return psi.make_matrix(0x1000, 0x2000 if bias else None, rows, cols, split, block)
+
+
+def cfg5_attn(block_cols=1024):
+    return [fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, block_cols) for _ in range(3)] + \
+           [fake_matrix(4096, 4096, psi.PSI_SPLIT_COLS, block_cols)]
+
+
+def cfg5_ffn(tile=1024):
+    return (fake_matrix(16384, 4096, psi.PSI_SPLIT_ROWS, tile),
+            fake_matrix(4096, 16384, psi.PSI_SPLIT_COLS, tile))
+
+
+@pytest.mark.parametrize("arena,page,expect", [
+    (48, 8, psi.PSI_E_SCRATCH_EXHAUSTED),
+    (64, 8, psi.PSI_E_SCRATCH_EXHAUSTED),
+    (80, 8, psi.PSI_OK),
+    (96, 8, psi.PSI_OK),
+    (80, 4, psi.PSI_E_PAGE_TOO_SMALL),
+    (96, 16, psi.PSI_OK),
+])
+def test_capacity_outcomes_like_table_v(arena, page, expect):
+    """[PSI] Table V lists six arena/page capacities for one block with tiles
+    held fixed: 48/8 and 64/8 exhaust scratch, 80/8, 96/8, 96/16 complete,
+    80/4 fails because a weight tile exceeds the page.  With this build's
+    tiles (8-head groups, 1,024-channel FFN tiles, 8,192 tokens, 8 MiB
+    workspace) the same six settings give the same outcome pattern."""
+    d = desc(arena, page, 2, 8, 0)
+    Wq, Wk, Wv, Wo = cfg5_attn()
+    st_a, need_a = psi.psi_attn_plan(d, 8192, 0, 32, 128, Wq, Wk, Wv, Wo, True)
+    U, V = cfg5_ffn()
+    st_f, need_f = psi.psi_ffn_plan(d, 8192, 4096, U, V, 1, True)
+    worst = st_a if st_a != psi.PSI_OK else st_f
+    assert worst == expect, (st_a, st_f, psi.psi_last_error())
+    if expect == psi.PSI_OK:
+        assert need_a == 3 * 8192 * 1024 * 2  # Q, K, V^T of one 8-head group
+        assert need_f == 8192 * 1024 * 2      # one hidden tile for all tokens
+
+
+def test_plan_errors_and_scratch_accumulator():
+    d = desc(32, 8, 2, 0, 0)  # the FFN d=2048 configuration: 32 MiB arena, 8 MiB pages
+    U = fake_matrix(8192, 2048, psi.PSI_SPLIT_ROWS, 2048)
+    V = fake_matrix(2048, 8192, psi.PSI_SPLIT_COLS, 2048)
+    st, need = psi.psi_ffn_plan(d, 1024, 2048, U, V, 1, False)  # fp32 ACC in the arena
+    assert st == psi.PSI_OK and need == 1024 * 2048 * 2 + 1024 * 2048 * 4
+    st, _ = psi.psi_ffn_plan(d, 1024, 2048, V, U, 1, False)
+    assert st == psi.PSI_E_INVALID
+    U2 = fake_matrix(8192, 2048, psi.PSI_SPLIT_ROWS, 4096)  # 16 MiB tile > 8 MiB page
+    V2 = fake_matrix(2048, 8192, psi.PSI_SPLIT_COLS, 4096)
+    st, _ = psi.psi_ffn_plan(d, 1024, 2048, U2, V2, 1, True)
+    assert st == psi.PSI_E_PAGE_TOO_SMALL
+    st, _ = psi.psi_ffn_plan(d, 4096, 2048, U, V, 1, False)  # ACC 32 MiB no longer fits
+    assert st == psi.PSI_E_SCRATCH_EXHAUSTED
+    Wq, Wk, Wv, Wo = cfg5_attn()
+    st, _ = psi.psi_attn_plan(desc(80, 8, 2, 8, 0), 8192, 0, 32, 64, Wq, Wk, Wv, Wo, True)
+    assert st == psi.PSI_E_INVALID  # head_dim 128 only
+    Wk_bad = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 512)
+    st, _ = psi.psi_attn_plan(desc(80, 8, 2, 8, 0), 8192, 0, 32, 128, Wq, Wk_bad, Wv, Wo, True)
+    assert st == psi.PSI_E_INVALID
+    odd = fake_matrix(64, 36, psi.PSI_SPLIT_ROWS, 16)
+    st, _ = psi.psi_linear_plan(desc(1, 0.25, 2, 0, 0), 8, 36, odd, True)
+    assert st == psi.PSI_E_ALIGN
+
+
+# ------------------------------------------------------- page lifecycle
+
+def test_page_lifecycle_dry_run():
+    """[PSI] sec. II-A rule 2 and sec. II-D: at most one unreleased request
+    per page; free -> filling -> consuming -> free; releasing a free page is
+    an error; a slice larger than a page is rejected."""
+    a = psi.psi_arena_create(desc(1, 0.25, 2))
+    try:
+        host = np.zeros(4096, np.uint8)
+        p0 = psi.psi_page_submit(a, host, 4096)
+        p1 = psi.psi_page_submit(a, host, 4096)
+        assert (p0, p1) == (0, 1)
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_page_submit(a, host, 4096)
+        assert e.value.status == psi.PSI_E_PAGE_BUSY
+        psi.psi_page_acquire(a, p0)
+        psi.psi_page_release(a, p0)
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_page_release(a, p0)
+        assert e.value.status == psi.PSI_E_STATE
+        assert psi.psi_page_submit(a, host, 4096) == 0  # round robin reuses slot 0
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_page_submit(a, np.zeros(MiB, np.uint8), MiB)
+        assert e.value.status == psi.PSI_E_PAGE_TOO_SMALL
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 3 and s.bytes_h2d == 3 * 4096
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_ffn_streams_every_page_once_dry_run():
+    """Page reuse across token chunks: with 4 chunks of 1,024 tokens each
+    U_J and V_J page is copied exactly once (32 pages = 256 MiB of weights,
+    plus the bias slices), never once per chunk."""
+    a = psi.psi_arena_create(desc(80, 8, 2, 8))
+    try:
+        U, V = cfg5_ffn()
+        fake = 0x10000  # device pointers are not touched in a dry run
+        psi.psi_ffn_paged(a, fake, 4096, 4096, U, V, 4, fake, fake, psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 32
+        assert s.bytes_h2d == 256 * MiB + 16384 * 2 + 4096 * 2
+        assert s.kernel_launches == 32 * 4
+        assert s.scratch_high_water == 4096 * 1024 * 2
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_attention_page_order_dry_run():
+    """Self- plus cross-attention with 8-head groups: 4 pages per group per
+    sub-block, 32 pages = 256 MiB for the two sub-blocks."""
+    a = psi.psi_arena_create(desc(80, 8, 2, 8))
+    try:
+        Wq, Wk, Wv, Wo = cfg5_attn()
+        fake = 0x10000
+        psi.psi_attn_paged(a, fake, 6144, None, 0, 32, 128, Wq, Wk, Wv, Wo, fake, fake,
+                           psi.PSI_OP_RESIDUAL)
+        psi.psi_attn_paged(a, fake, 6144, fake, 1024, 32, 128, Wq, Wk, Wv, Wo, fake, fake,
+                           psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 32
+        assert s.bytes_h2d == 256 * MiB + 2 * (4 * 4096 * 2)
+        assert s.kernel_launches == 2 * 4 * 5  # 4 GEMMs + 1 attention per group
+        assert s.scratch_high_water == 3 * 6144 * 1024 * 2
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_checkpoint_size_independence_dry_run():
+    """[PSI] sec. II-A: the managed footprint does not depend on checkpoint
+    size -- stacks of 2, 4 and 8 blocks give the same arena peak and scratch
+    high-water mark; only the bytes streamed grow."""
+    peaks, streamed = [], []
+    for nblocks in (2, 4, 8):
+        a = psi.psi_arena_create(desc(80, 8, 2, 8))
+        try:
+            Wq, Wk, Wv, Wo = cfg5_attn()
+            U, V = cfg5_ffn()
+            bw = psi.psi_block_weights(Wq, Wk, Wv, Wo, U, V)
+            for _ in range(nblocks):
+                psi.psi_block_paged(a, 0x10000, 0x20000, 8192, 32, 128, bw, 1, 0x30000, None, 0)
+            s = psi.psi_arena_stats(a)
+            peaks.append((s.arena_bytes, s.scratch_high_water))
+            streamed.append(s.bytes_h2d)
+        finally:
+            psi.psi_arena_destroy(a)
+    assert peaks[0] == peaks[1] == peaks[2]
+    assert streamed[1] == 2 * streamed[0] and streamed[2] == 4 * streamed[0]

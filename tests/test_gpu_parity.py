@@ -1,0 +1,394 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Floating-point outputs: max relative error <= 2e-2 on BF16 outputs and
+<= 1e-4 on fp32 accumulators compared on identical inputs (relative to
+max(|ref|, rms(ref))).  Bitwise where the accumulation order cannot matter
+(integer lattice, the paper's eq. (5) example) and GPU-vs-GPU for every
+partition of the same operator.
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bounded_weight_amd import synth
+from tests.gpu_util import MiB, assert_bf16_close, dev, empty_bf16, f, host, make_arena, rel_err
+
+pytestmark = pytest.mark.gpu
+
+KiB = 1024
+
+
+@pytest.fixture(scope="module")
+def P(psi_lib):
+    return psi_lib
+
+
+def run_linear(P, x, W, b, split, block, arena_bytes=None, page_bytes=None, flags=0,
+               want_acc=False, n_pages=2):
+    M, K = x.shape
+    N = W.shape[0]
+    m = P.pinned_matrix(W, b, split, block)
+    pb = page_bytes or max(P.psi_matrix_page_bytes(m, p) for p in range(P.psi_matrix_pages(m)))
+    side = 64 * KiB
+    ab = arena_bytes or (n_pages * (pb + side) + (M * N * 4 if split == P.PSI_SPLIT_COLS else 0) + 4096)
+    a = make_arena(ab, pb, n_pages)
+    try:
+        xd = dev(x)
+        y = empty_bf16(M, N)
+        acc = torch.zeros(M, N, dtype=torch.float32, device="cuda") if want_acc else None
+        if want_acc:
+            flags |= P.PSI_OP_STORE_ACC
+        P.psi_linear_paged(a, xd, M, K, m, acc, y, flags)
+        P.psi_arena_sync(a)
+        out = host(y)
+        return (out, acc.cpu().numpy()) if want_acc else out
+    finally:
+        P.psi_arena_destroy(a)
+
+
+# ----------------------------------------------------------------- linear
+
+def test_linear_single_paged_case(P):
+    """Single paged linear, x [64,256], W [512,256] in 4 output-column pages
+    of 128 rows, arena of 2 pages (64 KiB each), seed 0."""
+    c = synth.linear_case(seed=0)
+    y, acc = run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_ROWS, 128, page_bytes=64 * KiB,
+                        arena_bytes=2 * (64 * KiB + 64 * KiB), want_acc=True)
+    yr, accr = oracle.linear(c["x"], c["W"], c["b"], want_acc=True)
+    assert_bf16_close(y, yr)
+    assert rel_err(acc, accr).max() <= 1e-4  # identical inputs: fp32 accumulators
+
+
+@pytest.mark.parametrize("variant,expect", [(0, 129 / 128), (1, 1.0)])
+def test_linear_eq5_bitwise(P, variant, expect):
+    """[PSI] eq. (5) through the GPU epilogue: the accumulator is exactly
+    257/256, so the fp32-bias variant gives 129/128 and the baseline variant
+    (product rounded first) gives 1, bitwise."""
+    x = synth.f32_to_bf16_bits(np.array([[1.0, 2.0 ** -8] + [0.0] * 6], np.float32))
+    W = synth.f32_to_bf16_bits(np.array([[1.0, 1.0] + [0.0] * 6], np.float32))
+    b = synth.f32_to_bf16_bits(np.array([2.0 ** -8], np.float32))
+    flags = P.PSI_OP_BASELINE_BIAS if variant else 0
+    y = run_linear(P, x, W, b, P.PSI_SPLIT_ROWS, 1, flags=flags)
+    assert f(y)[0, 0] == np.float32(expect)
+    assert np.array_equal(y, oracle.linear(x, W, b, variant=variant))
+
+
+@pytest.mark.parametrize("split,block", [("rows", 64), ("rows", 72), ("cols", 128), ("cols", 136)])
+def test_linear_integer_lattice_bitwise(P, split, block):
+    """Pin P7 on the GPU: operands in {-2..2}, small integer biases, K = 4096:
+    every partial sum is exact, so the GPU equals the oracle bitwise for
+    output-column pages and for the K-split with a carried accumulator,
+    including ragged M, ragged last pages and blocks that are not tile
+    multiples."""
+    rng = np.random.default_rng(17)
+    M, K, N = 150, 4096, 200
+    bits = lambda a: synth.f32_to_bf16_bits(a.astype(np.float32))
+    x = bits(rng.integers(-2, 3, size=(M, K)))
+    W = bits(rng.integers(-2, 3, size=(N, K)))
+    b = bits(rng.integers(-8, 9, size=(N,)))
+    sp = P.PSI_SPLIT_ROWS if split == "rows" else P.PSI_SPLIT_COLS
+    y, acc = run_linear(P, x, W, b, sp, block, want_acc=True)
+    yr, accr = oracle.linear(x, W, b, want_acc=True)
+    assert np.array_equal(acc, accr)
+    assert np.array_equal(y, yr)
+
+
+def test_linear_parity_ragged(P):
+    c = synth.linear_case(seed=3, M=333, K=520, N=392)
+    for sp, blk in ((P.PSI_SPLIT_ROWS, 96), (P.PSI_SPLIT_COLS, 200)):
+        y, acc = run_linear(P, c["x"], c["W"], c["b"], sp, blk, want_acc=True)
+        yr, accr = oracle.linear(c["x"], c["W"], c["b"], want_acc=True)
+        assert_bf16_close(y, yr)
+        assert rel_err(acc, accr).max() <= 1e-4
+
+
+def test_linear_partitions_bitwise_gpu(P):
+    """Pin P3 on the GPU ([PSI] sec. IV-B): output-column pages of 1, 2 and 4
+    per matrix, and K-splits whose pages are multiples of 16 (the MFMA K
+    step), all reproduce the single-page result bitwise."""
+    c = synth.linear_case(seed=4, M=256, K=1024, N=512)
+    ref = run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_ROWS, 512)
+    for blk in (256, 128):
+        assert np.array_equal(run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_ROWS, blk), ref)
+    for blk in (1024, 512, 256, 64, 48):
+        assert np.array_equal(run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_COLS, blk), ref)
+
+
+def test_linear_sync_copy_and_one_page_bitwise(P):
+    """Transport control ([PSI] sec. IV-C): copies on the compute stream, or a
+    single page slot, give the same bytes as the asynchronous two-page
+    streamer."""
+    c = synth.linear_case(seed=5, M=128, K=512, N=512)
+    ref = run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_ROWS, 128)
+    m = P.pinned_matrix(c["W"], c["b"], P.PSI_SPLIT_ROWS, 128)
+    for n_pages, fl in ((2, P.PSI_ARENA_SYNC_COPY), (1, 0), (3, 0)):
+        a = make_arena(n_pages * (128 * KiB + 64 * KiB), 128 * KiB, n_pages, 0, fl)
+        try:
+            y = empty_bf16(128, 512)
+            P.psi_linear_paged(a, dev(c["x"]), 128, 512, m, None, y, 0)
+            P.psi_arena_sync(a)
+            assert np.array_equal(host(y), ref)
+        finally:
+            P.psi_arena_destroy(a)
+
+
+def test_linear_rejects_pageable_and_busy(P):
+    c = synth.linear_case(seed=6, M=16, K=64, N=64)
+    a = make_arena(2 * (16 * KiB + 64 * KiB), 16 * KiB)
+    try:
+        m = P.make_matrix(c["W"], None, 64, 64, P.PSI_SPLIT_ROWS, 32)  # numpy: pageable
+        with pytest.raises(P.PsiError) as e:
+            P.psi_linear_paged(a, dev(c["x"]), 16, 64, m, None, empty_bf16(16, 64), 0)
+        assert e.value.status == P.PSI_E_NOT_PINNED
+        pinned = torch.empty(4096, dtype=torch.int16, pin_memory=True)
+        p0 = P.psi_page_submit(a, pinned, 8192)
+        P.psi_page_submit(a, pinned, 8192)
+        with pytest.raises(P.PsiError) as e:
+            P.psi_page_submit(a, pinned, 8192)
+        assert e.value.status == P.PSI_E_PAGE_BUSY
+        d0 = P.psi_page_acquire(a, p0)
+        assert d0 != 0
+        P.psi_page_release(a, p0)
+        P.psi_page_release(a, 1)
+        P.psi_arena_sync(a)
+    finally:
+        P.psi_arena_destroy(a)
+
+
+def test_page_bytes_roundtrip(P):
+    """A submitted page holds exactly the host bytes once its copy is
+    complete (byte-preserving transport)."""
+    a = make_arena(2 * (64 * KiB + 64 * KiB), 64 * KiB)
+    try:
+        src = torch.empty(32 * 1024, dtype=torch.int16, pin_memory=True)
+        src.copy_(torch.randint(-32768, 32767, (32 * 1024,), dtype=torch.int16))
+        out = torch.empty(32 * 1024, dtype=torch.int16, device="cuda")
+        for _ in range(3):
+            p = P.psi_page_submit(a, src, 64 * KiB)
+            ptr = P.psi_page_acquire(a, p)
+            s = torch.cuda.current_stream()
+            torch.cuda.synchronize()
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_int, ctypes.c_void_p]
+            assert hip.hipMemcpyAsync(out.data_ptr(), ptr, 64 * KiB, 3, s.cuda_stream) == 0
+            P.psi_page_release(a, p)
+            P.psi_arena_sync(a)
+            assert torch.equal(out.cpu(), src)
+            src.copy_(src.roll(7))
+    finally:
+        P.psi_arena_destroy(a)
+
+
+# -------------------------------------------------------------------- FFN
+
+def run_ffn(P, c, tile, chunks=1, arena_bytes=None, page_bytes=None, acc_external=True, flags=0,
+            want_acc=False):
+    x, U, a_, V, b = c["x"], c["U"], c["a"], c["V"], c["b"]
+    M, d = x.shape
+    h = U.shape[0]
+    mu = P.pinned_matrix(U, a_, P.PSI_SPLIT_ROWS, tile)
+    mv = P.pinned_matrix(V, b, P.PSI_SPLIT_COLS, tile)
+    pb = page_bytes or max(tile * d * 2, 4096)
+    ab = arena_bytes or (2 * (pb + 64 * KiB) + M * tile * 2 + (0 if acc_external else M * d * 4) + 8192)
+    ar = make_arena(ab, pb)
+    try:
+        xd = dev(x)
+        y = empty_bf16(M, d)
+        acc = torch.zeros(M, d, dtype=torch.float32, device="cuda") if acc_external else None
+        if want_acc:
+            flags |= P.PSI_OP_STORE_ACC
+        P.psi_ffn_paged(ar, xd, M, d, mu, mv, chunks, acc, y, flags)
+        P.psi_arena_sync(ar)
+        out = host(y)
+        return (out, acc.cpu().numpy()) if want_acc else out
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def test_ffn_parity_ragged(P):
+    c = synth.ffn_case(seed=1, M=200, d=256, hidden=1024)
+    y = run_ffn(P, c, 256, chunks=3)
+    yr = oracle.ffn(c["x"], c["U"], c["a"], c["V"], c["b"])
+    assert_bf16_close(y, yr)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_ffn_parity_residual_inplace(P, residual):
+    c = synth.ffn_case(seed=2, M=130, d=128, hidden=512)
+    x, M, d = c["x"], 130, 128
+    mu = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, 128)
+    mv = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, 128)
+    ar = make_arena(4 * MiB, 256 * KiB)
+    try:
+        xd = dev(x)
+        fl = P.PSI_OP_RESIDUAL if residual else 0
+        P.psi_ffn_paged(ar, xd, M, d, mu, mv, 2, None, xd, fl)  # y aliases x, ACC in scratch
+        P.psi_arena_sync(ar)
+        yr = oracle.ffn(x, c["U"], c["a"], c["V"], c["b"], residual=residual)
+        assert_bf16_close(host(xd), yr)
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def test_ffn_partitions_bitwise_gpu(P):
+    """[PSI] eq. (2) on the GPU: hidden tiles of 128/256/512 channels and
+    1/2/4 token chunks give bitwise-identical outputs."""
+    c = synth.ffn_case(seed=3, M=256, d=256, hidden=1024)
+    ref = run_ffn(P, c, 512, chunks=1)
+    for tile in (256, 128):
+        for ch in (1, 2, 4):
+            assert np.array_equal(run_ffn(P, c, tile, chunks=ch), ref), (tile, ch)
+    assert np.array_equal(run_ffn(P, c, 256, chunks=2, acc_external=False), ref)
+
+
+def test_ffn_baseline_bias_variant(P):
+    """The baseline variant (pre-GELU product rounded before the bias) follows
+    the oracle's baseline variant within tolerance and differs from the
+    modified variant somewhere (the effect [PSI] sec. IV-B measures)."""
+    c = synth.ffn_case(seed=4, M=64, d=256, hidden=512)
+    yb = run_ffn(P, c, 256, flags=P.PSI_OP_BASELINE_BIAS)
+    ym = run_ffn(P, c, 256)
+    assert_bf16_close(yb, oracle.ffn(c["x"], c["U"], c["a"], c["V"], c["b"], variant=1))
+    assert np.count_nonzero(yb != ym) > 0
+
+
+def test_gelu_epilogue_exhaustive(P):
+    """Pin P6 on the GPU: every finite bf16 value v goes through the fused
+    up-projection epilogue (x = v, U = e_0, a = 0, so pre = v exactly) and
+    the down-projection with V = I returns B(phi(v)) unchanged; the GPU's
+    fp32 GELU may differ from the oracle's double GELU by at most one bf16
+    ulp, on a small fraction of inputs."""
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    u = u[np.isfinite(f(u))]
+    M = u.size
+    d = h = 8
+    x = np.zeros((M, d), np.uint16)
+    x[:, 0] = u
+    one = synth.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    U = np.zeros((h, d), np.uint16)
+    U[0, 0] = one
+    V = np.zeros((d, h), np.uint16)
+    for i in range(d):
+        V[i, i] = one
+    zero = np.zeros(h, np.uint16)
+    c = {"x": x, "U": U, "a": zero, "V": V, "b": zero}
+    y = run_ffn(P, c, 8, chunks=1)
+    ref = oracle.gelu_bf16(u)
+    got = y[:, 0]
+    # the down-projection adds +0 to a -0 hidden value, so zeros compare by value
+    same = (got == ref) | ((f(got) == 0) & (f(ref) == 0))
+    mism = np.nonzero(~same)[0]
+    ulps = np.abs(got[mism].astype(np.int32) - ref[mism].astype(np.int32))
+    assert np.all(ulps <= 1), ulps.max()
+    assert mism.size <= M // 100, mism.size
+
+
+# ---------------------------------------------------------------- attention
+
+def attn_mats(P, w, group_cols):
+    return (P.pinned_matrix(w["Wq"], w["bq"], P.PSI_SPLIT_ROWS, group_cols),
+            P.pinned_matrix(w["Wk"], w["bk"], P.PSI_SPLIT_ROWS, group_cols),
+            P.pinned_matrix(w["Wv"], w["bv"], P.PSI_SPLIT_ROWS, group_cols),
+            P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, group_cols))
+
+
+def run_attn(P, x, w, heads, group_heads, ctx=None, flags=0, residual=True, arena_bytes=None):
+    M, d = x.shape
+    Mc = 0 if ctx is None else ctx.shape[0]
+    gw = group_heads * 128
+    mats = attn_mats(P, w, gw)
+    pb = gw * d * 2
+    Ms = Mc or M
+    scratch = (M + Ms) * gw * 2 + gw * (((Ms + 63) // 64) * 64) * 2 + 4 * 4096
+    ar = make_arena(arena_bytes or (2 * (pb + 64 * KiB) + scratch), pb)
+    try:
+        xd = dev(x)
+        cd = dev(ctx) if ctx is not None else None
+        y = empty_bf16(M, d)
+        acc = torch.zeros(M, d, dtype=torch.float32, device="cuda")
+        fl = flags | (P.PSI_OP_RESIDUAL if residual else 0)
+        P.psi_attn_paged(ar, xd, M, cd, Mc, heads, 128, *mats, acc, y, fl)
+        P.psi_arena_sync(ar)
+        return host(y)
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def test_attention_parity_ragged_self_and_cross(P):
+    rng = np.random.default_rng(8)
+    d, heads = 256, 2
+    x = synth.normal_bf16(rng, (200, d), 1.0)
+    ctx = synth.normal_bf16(rng, (77, d), 1.0)
+    w = synth.attn_weights(rng, d)
+    args = (w["Wq"], w["bq"], w["Wk"], w["bk"], w["Wv"], w["bv"], w["Wo"], w["bo"], heads, 128)
+    for gh in (1, 2):
+        y = run_attn(P, x, w, heads, gh)
+        assert_bf16_close(y, oracle.attn_sublayer(x, *args), what=f"self gh={gh}")
+        yc = run_attn(P, x, w, heads, gh, ctx=ctx)
+        assert_bf16_close(yc, oracle.attn_sublayer(x, *args, ctx=ctx), what=f"cross gh={gh}")
+
+
+def test_attention_head_groups_bitwise_gpu(P):
+    """Head groups of 1, 2 and 4 heads give bitwise-identical sub-block
+    outputs (the group partition of the projections and the ordered
+    O-projection K-split)."""
+    rng = np.random.default_rng(9)
+    d, heads = 512, 4
+    x = synth.normal_bf16(rng, (160, d), 1.0)
+    w = synth.attn_weights(rng, d)
+    ref = run_attn(P, x, w, heads, 4)
+    for gh in (2, 1):
+        assert np.array_equal(run_attn(P, x, w, heads, gh), ref)
+
+
+def _identity_bits(n):
+    one = synth.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    I = np.zeros((n, n), np.uint16)
+    I[np.arange(n), np.arange(n)] = one
+    return I
+
+
+@pytest.mark.parametrize("Mc", [1, 64, 128])
+def test_attention_uniform_weights_bitwise(P, Mc):
+    """Pin P8 on the GPU: with Wq = Wk = 0 every score is 0, every weight is
+    exp(0) = 1 (hi = 1, lo = 0), so O is the mean of the value rows; with
+    integer values and a power-of-two key count (1, 64, 128) every sum is
+    exact and the GPU equals the oracle bitwise (Wv = Wo = I)."""
+    rng = np.random.default_rng(10)
+    d, heads = 256, 2
+    bits = lambda a: synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+    x = bits(rng.integers(-4, 5, size=(96, d)))
+    ctx = bits(rng.integers(-4, 5, size=(Mc, d)))
+    z = np.zeros((d, d), np.uint16)
+    zb = np.zeros(d, np.uint16)
+    I = _identity_bits(d)
+    w = {"Wq": z, "bq": zb, "Wk": z, "bk": zb, "Wv": I, "bv": zb, "Wo": I, "bo": zb}
+    y = run_attn(P, x, w, heads, 1, ctx=ctx)
+    yr = oracle.attn_sublayer(x, z, zb, z, zb, I, zb, I, zb, heads, 128, ctx=ctx)
+    assert np.array_equal(y, yr)
+    mean_b = f(bits(f(ctx).astype(np.float64).mean(axis=0)))  # O is written as BF16
+    assert np.array_equal(f(y), f(bits(f(x).astype(np.float64) + mean_b[None, :])))
+
+
+def test_attention_bf16_softmax_variant(P):
+    """The BF16-numerator variant (baseline) is within tolerance of the
+    oracle but further from it than the default fp32-faithful weights."""
+    rng = np.random.default_rng(11)
+    d, heads = 256, 2
+    x = synth.normal_bf16(rng, (128, d), 1.0)
+    w = synth.attn_weights(rng, d)
+    yr = oracle.attn_sublayer(x, w["Wq"], w["bq"], w["Wk"], w["bk"], w["Wv"], w["bv"], w["Wo"],
+                              w["bo"], heads, 128, residual=False)
+    y32 = run_attn(P, x, w, heads, 1, residual=False)
+    y16 = run_attn(P, x, w, heads, 1, residual=False, flags=P.PSI_OP_BF16_SOFTMAX)
+    assert_bf16_close(y32, yr)
+    assert_bf16_close(y16, yr)
+    e32 = np.linalg.norm(f(y32) - f(yr)) / np.linalg.norm(f(yr))
+    e16 = np.linalg.norm(f(y16) - f(yr)) / np.linalg.norm(f(yr))
+    assert e32 < e16
