@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged BF16 block operator on one MI355X.
+
+Default workload: a stack of 8 synthetic transformer blocks (d 4096, 32
+heads of 128, FFN 16384, biases; ~3.2 GB of random BF16 weights in pinned
+host memory), 8192 tokens, fixed 80 MiB arena (2 x 8 MiB pages, 8 MiB
+workspace, scratch), each block output journaled to the host.  One step is
+one invocation of the stack (all 8 blocks); the default 11 timed steps
+mirror the paper's eleven transformer invocations, all on the same input.
+
+Every step streams every weight page from pinned host memory into the
+arena: the metric is TFLOP/s of the paged block operators, reported with
+the fraction of the binding roofline min(MFMA BF16 peak, H2D GB/s x
+FLOP/byte), where H2D GB/s is measured in the same run.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported (the build
+runs on one GPU) and exits with a message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MiB = 1 << 20
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def measure_h2d_gbps(torch, nbytes=256 * MiB, reps=5):
+    """Best of `reps` pinned host -> device copies of `nbytes` (hipMemcpyAsync)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps + 1):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src, non_blocking=True)
+        e.record()
+        e.synchronize()
+        best = max(best, nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+# ------------------------------------------------------------------ workloads
+
+def build_workload(args, torch, psi, synth):
+    """Returns a dict with the step callable, its FLOPs and H2D bytes."""
+    stream = torch.cuda.current_stream().cuda_stream
+    flags = 0 if args.no_profile else psi.PSI_ARENA_PROFILE
+    if args.sync_copy:
+        flags |= psi.PSI_ARENA_SYNC_COPY
+    W = {}
+    live = []
+    if args.workload == "stack8":
+        M, d, heads, hid, nblk = 8192, 4096, 32, 16384, 8
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 8 * MiB, 0, stream, flags))
+        t0 = time.time()
+        blocks = []
+        for b in range(nblk):
+            w = synth.block_weights(args.seed, b, d, hid)
+            blocks.append(psi.block_weights(w, 1024, 1024, resident=args.resident))
+            del w
+        log(f"bench: generated and pinned {nblk} blocks in {time.time() - t0:.1f}s")
+        x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
+        x = torch.empty_like(x0)
+        xt = torch.empty_like(x0)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        live += [x0, x, xt, acc]
+        journal = None
+        if not args.no_journal:
+            store = (args.steps + args.warmup) * nblk * M * d * 2
+            journal = psi.psi_journal_create(8 * MiB, 4, store)
+        flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
+        h2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2
+        state = {"step": 0}
+
+        def step():
+            x.copy_(x0)
+            s = state["step"]
+            for b in range(nblk):
+                psi.psi_block_paged(arena, x, xt, M, heads, 128, blocks[b], 1, acc, journal, 0)
+                if journal:
+                    psi.psi_journal_commit(journal, psi.key(s, b, 0, 0), x, M * d * 2, stream)
+            state["step"] += 1
+
+        return dict(step=step, arena=arena, journal=journal, flops=flops_block * nblk,
+                    h2d=h2d_block * nblk, live=live, keep=blocks,
+                    config={"workload": "stack of 8 synthetic blocks (self-attention + FFN)",
+                            "tokens": M, "d_model": d, "heads": heads, "head_dim": 128,
+                            "ffn_hidden": hid, "blocks": nblk, "arena_MiB": 80, "page_MiB": 8,
+                            "workspace_MiB": 8, "head_group": 8, "ffn_tile": 1024,
+                            "journal": not args.no_journal, "resident_weights": args.resident})
+    if args.workload in ("ffn2048", "ffn4096"):
+        if args.workload == "ffn2048":
+            M, d, hid, tile, chunks, arena_mib, ws, acc_ext = 1024, 2048, 8192, 2048, 1, 32, 0, False
+        else:
+            M, d, hid, tile, chunks, arena_mib, ws, acc_ext = 4096, 4096, 16384, 1024, 4, 80, 8, True
+        c = synth.ffn_case(args.seed, M, d, hid)
+        U = psi.pinned_matrix(c["U"], c["a"], psi.PSI_SPLIT_ROWS, tile)
+        V = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_COLS, tile)
+        if args.resident:
+            U, V = psi.resident_matrix(U), psi.resident_matrix(V)
+        arena = psi.psi_arena_create(psi.arena_desc(arena_mib * MiB, 8 * MiB, 2, ws * MiB, 0, stream, flags))
+        x = torch.from_numpy(c["x"].view("int16")).cuda()
+        y = torch.empty_like(x)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda") if acc_ext else None
+        live += [x, y] + ([acc] if acc_ext else [])
+
+        def step():
+            psi.psi_ffn_paged(arena, x, M, d, U, V, chunks, acc, y, 0)
+
+        return dict(step=step, arena=arena, journal=None, flops=2 * 2.0 * M * d * hid,
+                    h2d=2 * d * hid * 2 + (hid + d) * 2, live=live, keep=(U, V),
+                    config={"workload": f"paged FFN d={d} hidden={hid}", "tokens": M,
+                            "token_chunks": chunks, "ffn_tile": tile, "arena_MiB": arena_mib,
+                            "page_MiB": 8, "resident_weights": args.resident})
+    if args.workload == "attn4096":
+        M, Mc, d, heads = 6144, 1024, 4096, 32
+        c = synth.attn_case(args.seed, M, Mc, d, cross=True)
+        mats = {}
+        for part in ("self", "cross"):
+            w = c[part]
+            ms = [psi.pinned_matrix(w["W" + n], w["b" + n], psi.PSI_SPLIT_ROWS, 1024) for n in "qkv"]
+            ms.append(psi.pinned_matrix(w["Wo"], w["bo"], psi.PSI_SPLIT_COLS, 1024))
+            if args.resident:
+                ms = [psi.resident_matrix(m) for m in ms]
+            mats[part] = ms
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 8 * MiB, 0, stream, flags))
+        x0 = torch.from_numpy(c["x"].view("int16")).cuda()
+        ctx = torch.from_numpy(c["ctx"].view("int16")).cuda()
+        x = torch.empty_like(x0)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        live += [x0, ctx, x, acc]
+
+        def step():
+            x.copy_(x0)
+            psi.psi_attn_paged(arena, x, M, None, 0, heads, 128, *mats["self"], acc, x, psi.PSI_OP_RESIDUAL)
+            psi.psi_attn_paged(arena, x, M, ctx, Mc, heads, 128, *mats["cross"], acc, x, psi.PSI_OP_RESIDUAL)
+
+        fl = (4 * 2.0 * M * d * d + 4.0 * M * M * 128 * heads) + \
+             (2 * 2.0 * M * d * d + 2 * 2.0 * Mc * d * d + 4.0 * M * Mc * 128 * heads)
+        return dict(step=step, arena=arena, journal=None, flops=fl, h2d=8 * d * d * 2 + 8 * d * 2,
+                    live=live, keep=mats,
+                    config={"workload": "paged attention sub-blocks (self + cross)", "tokens": M,
+                            "context_tokens": Mc, "d_model": d, "heads": heads, "head_dim": 128,
+                            "head_group": 8, "arena_MiB": 80, "page_MiB": 8,
+                            "resident_weights": args.resident})
+    raise ValueError(args.workload)
+
+
+def cpu_baseline(seed, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the default workload:
+    the FFN sub-block of block 0 (Linear 4096->16384, GELU, Linear
+    16384->4096, residual) on a few token rows.  Returns TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from memory_bounded_weight_amd import synth
+    threads = oracle.threads()
+    w = synth.block_weights(seed, 0)
+    x = synth.stack_input(seed)
+    per_row = 2 * 2.0 * 4096 * 16384
+    rows = max(threads, 8)
+    t0 = time.perf_counter()
+    oracle.ffn(np.ascontiguousarray(x[:rows]), w["U"], w["a"], w["V"], w["b"], residual=True)
+    dt = time.perf_counter() - t0
+    if dt < budget_s / 4:
+        rows2 = int(rows * min(budget_s / max(dt, 1e-3), 64)) // threads * threads
+        rows2 = max(rows2, rows)
+        t0 = time.perf_counter()
+        oracle.ffn(np.ascontiguousarray(x[:rows2]), w["U"], w["a"], w["V"], w["b"], residual=True)
+        dt = time.perf_counter() - t0
+        rows = rows2
+    return {"value": per_row * rows / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"FFN sub-block of block 0 (4096->16384->4096, residual) on {rows} of 8192 "
+                      f"token rows; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=11)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", choices=WORKLOADS, default="stack8")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--resident", action="store_true", help="weights pre-loaded in HBM (no H2D)")
+    ap.add_argument("--no-profile", action="store_true", help="no per-launch event timing")
+    ap.add_argument("--no-journal", action="store_true")
+    ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); multi-GPU page sharding is a design, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from memory_bounded_weight_amd import psi, synth
+
+    torch.cuda.set_device(0)
+    h2d_gbps = measure_h2d_gbps(torch)
+    log(f"bench: pinned H2D {h2d_gbps:.1f} GB/s")
+    wl = build_workload(args, torch, psi, synth)
+    arena, journal, step = wl["arena"], wl["journal"], wl["step"]
+
+    def sync_all():
+        torch.cuda.synchronize()
+        psi.psi_arena_sync(arena)
+        if journal:
+            psi.psi_journal_sync(journal)
+
+    for i in range(args.warmup):
+        step()
+    sync_all()
+    psi.psi_arena_reset_stats(arena)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sync_all()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    sync_all()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    st = psi.psi_arena_stats(arena)
+
+    total_flops = wl["flops"] * args.steps
+    value = total_flops / wall / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    ai = wl["flops"] / wl["h2d"]
+    if args.resident:
+        roof = MFMA_BF16_PEAK_TFLOPS
+        binding = {"bound": "mfma", "roof_tflops": roof, "frac": value / roof}
+    else:
+        roof = min(MFMA_BF16_PEAK_TFLOPS, h2d_gbps * ai / 1e3)
+        binding = {"bound": "h2d" if roof < MFMA_BF16_PEAK_TFLOPS else "mfma",
+                   "h2d_GBps_measured": round(h2d_gbps, 2), "flop_per_h2d_byte": round(ai, 1),
+                   "roof_tflops": round(roof, 2), "frac": round(value / roof, 4),
+                   "h2d_bytes_per_step": wl["h2d"]}
+
+    roofline = None
+    if not args.no_profile:
+        kinds = [("gemm", st.gemm_ms, st.gemm_launches, st.gemm_flops),
+                 ("attention", st.attn_ms, st.attn_launches, st.attn_flops)]
+        name, ms, n, fl = max(kinds, key=lambda k: k[1])
+        if n:
+            achieved = fl / (ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "launches": n, "avg_launch_us": round(ms * 1e3 / n, 2),
+                        "flops_per_launch": fl / n}
+        other = [k for k in kinds if k[0] != name and k[2]]
+        if other:
+            o = other[0]
+            roofline["other_kernel"] = {"kernel": o[0], "achieved": round(o[3] / (o[1] * 1e-3) / 1e12, 2),
+                                        "avg_launch_us": round(o[1] * 1e3 / o[2], 2), "launches": o[2]}
+        if st.copy_ms > 0:
+            binding["page_copy_GBps"] = round(st.copy_bytes_timed / (st.copy_ms * 1e-3) / 1e9, 2)
+            binding["copy_busy_frac"] = round(st.copy_ms / (wall * 1e3), 4)
+
+    live_bytes = sum(t.numel() * t.element_size() for t in wl["live"])
+    footprint = {"arena_bytes": st.arena_bytes, "scratch_high_water": st.scratch_high_water,
+                 "declared_live_state_bytes": live_bytes,
+                 "torch_peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+                 "page_copies": st.page_copies, "bytes_h2d": st.bytes_h2d,
+                 "host_syncs": st.host_syncs}
+
+    extra = {}
+    if journal:
+        d2h, _, entries = psi.psi_journal_counters(journal)
+        extra["journal"] = {"entries": entries, "bytes_d2h": d2h}
+        if args.steps >= 2 and wl["config"].get("blocks"):
+            n = wl["config"]["tokens"] * wl["config"]["d_model"] * 2
+            a = np.empty(n, np.uint8)
+            b = np.empty(n, np.uint8)
+            last = wl["config"]["blocks"] - 1
+            psi.psi_journal_read(journal, psi.key(args.warmup, last), a, n)
+            psi.psi_journal_read(journal, psi.key(args.warmup + args.steps - 1, last), b, n)
+            extra["invocations_bitwise_equal"] = bool(np.array_equal(a, b))
+            extra["output_finite"] = bool(np.isfinite((a.view(np.uint16).astype(np.uint32) << 16)
+                                                      .view(np.float32)).all())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.seed)
+
+    out = {
+        "metric": "TFLOP/s of paged BF16 block ops at fixed arena; % of binding roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "event_ms_per_step": round(ev_ms / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": wl["config"],
+        "binding_roofline": binding,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "footprint": footprint,
+        **extra,
+    }
+    print(json.dumps(out), flush=True)
+    if journal:
+        psi.psi_journal_destroy(journal)
+    psi.psi_arena_destroy(arena)
+
+
+if __name__ == "__main__":
+    main()

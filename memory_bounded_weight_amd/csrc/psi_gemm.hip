@@ -36,12 +36,16 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
   return (uint16_t)(w >> 16);
 }
 
-// tanh-GELU, phi(v) = v/2 (1 + tanh(c (v + 0.044715 v^3))), c = sqrt(2/pi),
-// written as v / (1 + exp(-2u)) so that neither tail cancels.
+// tanh-GELU, phi(v) = v/2 (1 + tanh(z)), z = sqrt(2/pi) (v + 0.044715 v^3),
+// through 1 + tanh(z) = 2 / (1 + e^(-2z)) = 2 e^(2z) / (1 + e^(2z)); the
+// second form for z < 0 neither cancels nor overflows, so the tiny negative
+// values of the left tail keep their relative precision.
 __device__ __forceinline__ float gelu_tanh(float v) {
   const float c = 0.7978845608028654f;
-  float u = c * (v + 0.044715f * v * v * v);
-  return v / (1.0f + expf(-2.0f * u));
+  const float z = c * (v + 0.044715f * v * v * v);
+  if (z >= 0.0f) return v / (1.0f + expf(-2.0f * z));
+  const float e = expf(2.0f * z);
+  return v * e / (1.0f + e);
 }
 
 constexpr int kThreads = 256;  // 4 waves of 64

@@ -56,6 +56,8 @@ def use_library(path: str):
 
 
 def _configure(lib):
+    lib.orc_threads.restype = ctypes.c_int
+    lib.orc_threads.argtypes = []
     lib.orc_f.restype = ctypes.c_float
     lib.orc_f.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_from_float.restype = ctypes.c_uint16
@@ -107,6 +109,11 @@ def _f32(a, name="array"):
 
 
 # ---------------------------------------------------------------- scalars
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().orc_threads())
+
 
 def bf16_to_float(u) -> np.ndarray:
     """f(): widen bf16 bit patterns to float32 (exact)."""

@@ -35,9 +35,13 @@
  * y = x W^T + b.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below will use (reported with timings). */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* BF16 rounding, [PSI] sec. II-C eq. (5)                               */
@@ -141,10 +145,18 @@ void orc_linear(const uint16_t* x, int M, int K, const uint16_t* W, int N,
 /* tanh-GELU, [PSI] sec. II-B eq. (2): "coordinatewise tanh-GELU"      */
 /* ------------------------------------------------------------------ */
 
-/* phi(v) = v/2 * (1 + tanh( sqrt(2/pi) * (v + 0.044715 v^3) )), in double. */
+/* phi(v) = v/2 * (1 + tanh(z)),  z = sqrt(2/pi) * (v + 0.044715 v^3), in
+ * double.  The factor 1 + tanh(z) is evaluated through the identity
+ * 1 + tanh(z) = 2 / (1 + e^(-2z)) = 2 e^(2z) / (1 + e^(2z)) (second form for
+ * z < 0): written literally, 1 + tanh(z) cancels for z below about -19 (tanh
+ * rounds to -1) and the real value of phi, a tiny negative number, would be
+ * lost. */
 double orc_gelu_tanh_double(double v) {
   const double c = sqrt(2.0 / M_PI);
-  return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+  const double z = c * (v + 0.044715 * v * v * v);
+  if (z >= 0.0) return v / (1.0 + exp(-2.0 * z));
+  const double e = exp(2.0 * z);
+  return v * e / (1.0 + e);
 }
 
 /* H = B(phi(f(u))) for each element, rounded once from double. */

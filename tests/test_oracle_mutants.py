@@ -22,7 +22,10 @@ MUTANTS = {
     "linear_variants_swapped": ("else if (variant == 1)", "else if (variant == 0)"),
     "rounding_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
     "rounding_truncates": ("kept += 1u;", "kept += 0u;"),
-    "gelu_wrong_sign": ("0.5 * v * (1.0 + tanh", "0.5 * v * (1.0 - tanh"),
+    "gelu_wrong_sign": ("v / (1.0 + exp(-2.0 * z))", "v / (1.0 + exp(2.0 * z))"),
+    "gelu_negative_branch_dropped": ("return v * e / (1.0 + e);", "return v * e;"),
+    "gelu_literal_tanh_cancels": ("  if (z >= 0.0) return v / (1.0 + exp(-2.0 * z));",
+                                  "  return 0.5 * v * (1.0 + tanh(z));"),
     "gelu_cubic_dropped": ("(v + 0.044715 * v * v * v)", "(v)"),
     "ffn_skips_gelu": ("orc_gelu_bf16(pre, (size_t)M * h, H);",
                        "memcpy(H, pre, (size_t)M * h * sizeof(uint16_t));"),
