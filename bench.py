@@ -65,7 +65,11 @@ def build_workload(args, torch, psi, synth):
     live = []
     if args.workload == "stack8":
         M, d, heads, hid, nblk = 8192, 4096, 32, 16384, 8
-        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 8 * MiB, 0, stream, flags))
+        # 80 MiB = pages x 8 MiB + workspace + scratch: two pages leave the
+        # paper's 8 MiB workspace; three pages take its place (no kernel here
+        # uses a workspace), scratch keeps its 56 MiB
+        ws = 8 * MiB if args.pages == 2 else max(0, 80 * MiB - 56 * MiB - args.pages * 8 * MiB)
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, ws, 0, stream, flags))
         t0 = time.time()
         blocks = []
         for b in range(nblk):
@@ -87,6 +91,10 @@ def build_workload(args, torch, psi, synth):
         state = {"step": 0}
 
         def step():
+            if journal:
+                # the journal's copies of the previous invocation's outputs read x:
+                # the overwrite below must follow them
+                psi.psi_journal_fence(journal, stream)
             x.copy_(x0)
             s = state["step"]
             for b in range(nblk):
@@ -100,7 +108,8 @@ def build_workload(args, torch, psi, synth):
                     config={"workload": "stack of 8 synthetic blocks (self-attention + FFN)",
                             "tokens": M, "d_model": d, "heads": heads, "head_dim": 128,
                             "ffn_hidden": hid, "blocks": nblk, "arena_MiB": 80, "page_MiB": 8,
-                            "workspace_MiB": 8, "head_group": 8, "ffn_tile": 1024,
+                            "pages": args.pages, "workspace_MiB": ws // MiB, "head_group": 8,
+                            "ffn_tile": 1024,
                             "journal": not args.no_journal, "resident_weights": args.resident})
     if args.workload in ("ffn2048", "ffn4096"):
         if args.workload == "ffn2048":
@@ -201,6 +210,7 @@ def main():
     ap.add_argument("--no-journal", action="store_true")
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pages", type=int, default=2, help="page slots in the 80 MiB arena (2 or 3)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

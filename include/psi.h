@@ -44,7 +44,7 @@ typedef int psi_status;
 /* ---------------------------------------------------------------- status */
 #define PSI_OK 0
 #define PSI_E_INVALID (-1)           /* bad shape, pointer or flag; masked/causal attention unsupported */
-#define PSI_E_ARENA_TOO_SMALL (-2)   /* n_pages * (P + side) + W exceeds the arena */
+#define PSI_E_ARENA_TOO_SMALL (-2)   /* n_pages * P + 2 bias slots + W exceeds the arena */
 #define PSI_E_SCRATCH_EXHAUSTED (-3) /* an operator's tiles do not fit the arena scratch ([PSI] Table V) */
 #define PSI_E_PAGE_TOO_SMALL (-4)    /* a weight tile does not fit one page ([PSI] Table V) */
 #define PSI_E_PAGE_BUSY (-5)         /* second unreleased request for a page ([PSI] sec. II-A, rule 2) */
@@ -87,7 +87,8 @@ typedef struct psi_arena_desc {
   size_t page_bytes;      /* P: capacity of one weight page */
   int n_pages;            /* reusable page slots, 1..PSI_MAX_PAGES (the paper uses 2) */
   size_t workspace_bytes; /* W: fixed library workspace (reserved, may be 0) */
-  size_t side_bytes;      /* per-page side slot for the page's bias slice; 0 -> 64 KiB */
+  size_t bias_slot_bytes; /* each of the two bias slots (an operator's biases are staged
+                             in one slot, slots alternate between operators); 0 -> 64 KiB */
   void* compute_stream;   /* hipStream_t the operators run on (caller-owned) */
   unsigned flags;         /* PSI_ARENA_* */
 } psi_arena_desc;
@@ -95,8 +96,8 @@ typedef struct psi_arena_desc {
 /* Byte offsets of the carve inside the arena (256-byte aligned). */
 typedef struct psi_arena_layout {
   size_t page_off[PSI_MAX_PAGES];
-  size_t side_off[PSI_MAX_PAGES];
-  size_t side_bytes;
+  size_t bias_off[2];
+  size_t bias_slot_bytes;
   size_t workspace_off;
   size_t scratch_off;
   size_t scratch_bytes;
@@ -156,7 +157,7 @@ int psi_matrix_pages(const psi_matrix* m);
 size_t psi_matrix_page_bytes(const psi_matrix* m, int p);
 
 /* Compute the arena carve without allocating.  Fails with
- * PSI_E_ARENA_TOO_SMALL when the pages, side slots and workspace exceed
+ * PSI_E_ARENA_TOO_SMALL when the pages, bias slots and workspace exceed
  * arena_bytes.  Host-only. */
 psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out);
 
@@ -182,10 +183,10 @@ const char* psi_version(void);
 /* ----------------------------------------------------------------- arena */
 
 /* [PSI] sec. II-A, Fig. 1: one device allocation of arena_bytes carved into
- * n_pages page slots (+ a side slot each for bias slices), the workspace
- * and scratch.  Creates the copy stream and per-slot events.  *out is the
- * caller's handle until psi_arena_destroy.  Errors: PSI_E_INVALID,
- * PSI_E_ARENA_TOO_SMALL, PSI_E_HIP. */
+ * n_pages page slots, two bias slots (the bounded metadata term eps of
+ * eq. (1)), the workspace and scratch.  Creates the copy stream and the
+ * per-slot events.  *out is the caller's handle until psi_arena_destroy.
+ * Errors: PSI_E_INVALID, PSI_E_ARENA_TOO_SMALL, PSI_E_HIP. */
 psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out);
 
 /* Synchronises the compute and copy streams and frees the one allocation. */
@@ -283,10 +284,18 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x_dev, uint16_t* x_tmp_dev, i
 /* --------------------------------------------------------------- journal */
 
 /* Indexed host journal of BF16 state ([PSI] sec. II-D, sec. III-B):
- * key = (step, block, branch, role).  Commit copies device bytes to a
- * pinned ring slot on the journal's own stream after the producer's work,
- * then moves them into the host store; reload moves them back after the
- * consumer's previous work.  Byte-preserving. */
+ * key = (step, block, branch, role).  Commit copies device bytes to the
+ * host store on the journal's own stream after the producer's work; reload
+ * copies them back after the consumer's previous work.  Byte-preserving.
+ * Store modes:
+ *   default           the store is pinned host memory; commits and reloads
+ *                     are single DMA copies straight to/from the entry
+ *   PSI_JOURNAL_RING  the store is pageable memory; bytes are staged
+ *                     through a pinned ring of ring_slots x ring_slot_bytes
+ *                     and moved by a host commit after each copy (the
+ *                     paper's pinned-ring transport)
+ *   PSI_JOURNAL_SYNC  transport control: copies on the caller's stream and
+ *                     the host blocks until each one completes */
 typedef struct psi_key {
   int32_t step;
   int32_t block;
@@ -295,12 +304,13 @@ typedef struct psi_key {
 } psi_key;
 
 typedef struct psi_journal_desc {
-  size_t ring_slot_bytes; /* pinned staging slot size (e.g. 8 MiB) */
-  int ring_slots;         /* >= 2 */
+  size_t ring_slot_bytes; /* staging slot size (ring mode / sync mode), e.g. 8 MiB */
+  int ring_slots;         /* >= 2 in ring mode */
   size_t store_bytes;     /* host store capacity, allocated and touched up front */
-  unsigned flags;         /* PSI_JOURNAL_SYNC: blocking transport on the caller's stream */
+  unsigned flags;         /* PSI_JOURNAL_SYNC, PSI_JOURNAL_RING */
 } psi_journal_desc;
 #define PSI_JOURNAL_SYNC 0x1u
+#define PSI_JOURNAL_RING 0x2u
 
 psi_status psi_journal_create(const psi_journal_desc* d, psi_journal** out);
 psi_status psi_journal_destroy(psi_journal* j);

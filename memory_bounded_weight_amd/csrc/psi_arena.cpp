@@ -59,14 +59,12 @@ static hipEvent_t pool_event(psi_arena* a) {
   return e;
 }
 
-psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const void* side_host,
-                          size_t side_bytes, int* page_out, bool pinned_check) {
+psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
+                          bool pinned_check) {
   if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
   if (bytes > a->desc.page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
                                           " B > " + std::to_string(a->desc.page_bytes) + " B");
-  if (side_bytes > a->layout.side_bytes)
-    return fail(PSI_E_PAGE_TOO_SMALL, "bias slice exceeds the page side slot");
   const int s = a->next_slot;
   psi_page_slot& slot = a->slots[s];
   if (slot.state != psi_page_slot::FREE)
@@ -74,7 +72,6 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const vo
   if (!a->dry && pinned_check) {
     psi_status st = check_pinned(host, "page slice");
     if (st) return st;
-    if (side_host && (st = check_pinned(side_host, "bias slice"))) return st;
   }
   if (!a->dry) {
     const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
@@ -91,19 +88,80 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const vo
       PSI_HIP(hipEventRecord(t0, cs));
     }
     PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, cs));
-    if (side_host && side_bytes)
-      PSI_HIP(hipMemcpyAsync(slot.side_dev, side_host, side_bytes, hipMemcpyHostToDevice, cs));
     if (t0) {
       PSI_HIP(hipEventRecord(t1, cs));
-      a->pending.push_back({t0, t1, 2, (double)(bytes + side_bytes)});
+      a->pending.push_back({t0, t1, 2, (double)bytes});
     }
     PSI_HIP(hipEventRecord(slot.ready, cs));
   }
   slot.state = psi_page_slot::FILLING;
-  a->stats.bytes_h2d += bytes + side_bytes;
+  a->stats.bytes_h2d += bytes;
   a->stats.page_copies++;
   a->next_slot = (s + 1) % a->desc.n_pages;
   if (page_out) *page_out = s;
+  return PSI_OK;
+}
+
+psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_t** dev_out,
+                       int* slot_out) {
+  *slot_out = -1;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i)
+    if (parts[i].host && parts[i].bytes) total += align_up(parts[i].bytes, kAlign);
+  for (int i = 0; i < n; ++i) dev_out[i] = nullptr;
+  if (total == 0) return PSI_OK;
+  if (total > a->layout.bias_slot_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, "the operator's biases exceed a bias slot");
+  const int s = a->next_bias;
+  psi_page_slot& slot = a->bias_slots[s];
+  if (slot.state != psi_page_slot::FREE)
+    return fail(PSI_E_STATE, "bias slot " + std::to_string(s) + " still in use");
+  const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
+  hipStream_t cs = sync ? a->compute : a->copy;
+  if (!a->dry && !sync && slot.released_once) {
+    PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
+    a->stats.event_waits++;
+  }
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!parts[i].host || !parts[i].bytes) continue;
+    char* dst = a->dry ? nullptr : static_cast<char*>(slot.dev) + off;
+    if (!a->dry) PSI_HIP(hipMemcpyAsync(dst, parts[i].host, parts[i].bytes, hipMemcpyHostToDevice, cs));
+    dev_out[i] = reinterpret_cast<const uint16_t*>(dst);
+    off += align_up(parts[i].bytes, kAlign);
+    a->stats.bytes_h2d += parts[i].bytes;
+  }
+  if (!a->dry) PSI_HIP(hipEventRecord(slot.ready, cs));
+  slot.state = psi_page_slot::FILLING;
+  a->next_bias = (s + 1) % 2;
+  *slot_out = s;
+  return PSI_OK;
+}
+
+psi_status bias_acquire(psi_arena* a, int s) {
+  if (s < 0) return PSI_OK;
+  psi_page_slot& slot = a->bias_slots[s];
+  if (slot.state == psi_page_slot::FILLING) {
+    if (!a->dry && !(a->desc.flags & PSI_ARENA_SYNC_COPY)) {
+      PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready, 0));
+      a->stats.event_waits++;
+    }
+    slot.state = psi_page_slot::CONSUMING;
+  }
+  return PSI_OK;
+}
+
+psi_status bias_release(psi_arena* a, int s) {
+  if (s < 0) return PSI_OK;
+  psi_page_slot& slot = a->bias_slots[s];
+  if (slot.state == psi_page_slot::FREE) return PSI_OK;
+  if (slot.state == psi_page_slot::FILLING) {
+    psi_status st = bias_acquire(a, s);
+    if (st) return st;
+  }
+  if (!a->dry) PSI_HIP(hipEventRecord(slot.release, a->compute));
+  slot.released_once = true;
+  slot.state = psi_page_slot::FREE;
   return PSI_OK;
 }
 
@@ -228,7 +286,11 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
       e = hipEventCreateWithFlags(&a->slots[i].ready, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].release, hipEventDisableTiming);
       a->slots[i].dev = a->base + L.page_off[i];
-      a->slots[i].side_dev = a->base + L.side_off[i];
+    }
+    for (int i = 0; e == hipSuccess && i < 2; ++i) {
+      e = hipEventCreateWithFlags(&a->bias_slots[i].ready, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&a->bias_slots[i].release, hipEventDisableTiming);
+      a->bias_slots[i].dev = a->base + L.bias_off[i];
     }
     if (e != hipSuccess) {
       psi_status r = hip_fail(e, "psi_arena_create");
@@ -254,6 +316,10 @@ psi_status psi_arena_destroy(psi_arena* a) {
     for (int i = 0; i < a->desc.n_pages; ++i) {
       if (a->slots[i].ready) (void)hipEventDestroy(a->slots[i].ready);
       if (a->slots[i].release) (void)hipEventDestroy(a->slots[i].release);
+    }
+    for (int i = 0; i < 2; ++i) {
+      if (a->bias_slots[i].ready) (void)hipEventDestroy(a->bias_slots[i].ready);
+      if (a->bias_slots[i].release) (void)hipEventDestroy(a->bias_slots[i].release);
     }
     if (a->copy) (void)hipStreamDestroy(a->copy);
     if (a->base) {
@@ -310,7 +376,7 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
 
 psi_status psi_page_submit(psi_arena* a, const void* host_pinned, size_t bytes, int* page_out) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
-  return page_submit_ex(a, host_pinned, bytes, nullptr, 0, page_out, true);
+  return page_submit_ex(a, host_pinned, bytes, page_out, true);
 }
 
 psi_status psi_page_acquire(psi_arena* a, int page, void** dev_out) {

@@ -30,16 +30,18 @@ namespace psi {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
+// Round to bfloat16, nearest with ties to even (output values; finite).
 __device__ __forceinline__ uint16_t f2bf(float v) {
   uint32_t w = __float_as_uint(v);
   if ((w & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   w += 0x7FFFu + ((w >> 16) & 1u);
   return (uint16_t)(w >> 16);
 }
-__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 
 constexpr int DH = 128;       // head dimension
 constexpr int KT = 64;        // keys per tile
@@ -48,7 +50,9 @@ constexpr int KS = DH + 8;    // K tile row stride in LDS (elements): 272 B
 constexpr int VS = KT + 4;    // V^T tile row stride in LDS (elements): 136 B
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
+// Two waves per SIMD (<= 256 registers each): while one wave runs its
+// softmax arithmetic the other keeps the matrix cores busy.
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DH * VS];
 
@@ -60,6 +64,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
   const int h = blockIdx.y;
   const int qrow = blockIdx.x * QB + wave * 32 + l32;  // this lane's query
   const bool qvalid = qrow < p.Mq;
+  // scores in exp2 units: s * log2(e) = dot * (alpha * log2(e))
+  const float c = p.alpha * 1.4426950408889634f;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][kk*16 + half*8 + 0..7].
   bf16x8 qf[DH / 16];
@@ -80,12 +86,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
   auto load_tile = [&](int key0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c = tid + i * kThreads;          // 0..1023
-      int r = c >> 4, col = (c & 15) * 8;  // K tile: 64 rows x 16 chunks
+      int c2 = tid + i * kThreads;           // 0..1023
+      int r = c2 >> 4, col = (c2 & 15) * 8;  // K tile: 64 rows x 16 chunks
       int key = key0 + r;
       rk[i] = key < p.Mk ? *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + col)
                          : make_uint4(0, 0, 0, 0);
-      int vr = c >> 3, vcol = (c & 7) * 8;  // V^T tile: 128 rows x 8 chunks
+      int vr = c2 >> 3, vcol = (c2 & 7) * 8;  // V^T tile: 128 rows x 8 chunks
       int vkey = key0 + vcol;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (vkey < p.Mk) {
@@ -103,16 +109,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c = tid + i * kThreads;
-      int r = c >> 4, col = (c & 15) * 8;
+      int c2 = tid + i * kThreads;
+      int r = c2 >> 4, col = (c2 & 15) * 8;
       *reinterpret_cast<uint4*>(&k_lds[buf][r * KS + col]) = rk[i];
-      int vr = c >> 3, vcol = (c & 7) * 8;
+      int vr = c2 >> 3, vcol = (c2 & 7) * 8;
       uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][vr * VS + vcol]);  // 8-byte aligned rows
       dst[0] = make_uint2(rv[i].x, rv[i].y);
       dst[1] = make_uint2(rv[i].z, rv[i].w);
     }
   };
 
+  // Running maximum m (in raw dot-product units), normaliser l, and the
+  // output accumulator z (= O^T), all fp32.
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 o[DH / 32];
 #pragma unroll
@@ -142,36 +150,44 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
-    // scale, mask the key tail, tile maximum of this query
+    // mask the key tail; tile maximum of this query (max commutes with the
+    // positive scale, so it is taken on the raw dot products)
     float mt = -INFINITY;
+    const bool tail = key0 + KT > p.Mk;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int key = key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-        float v = key < p.Mk ? s[kb][r] * p.alpha : -INFINITY;
-        s[kb][r] = v;
-        mt = fmaxf(mt, v);
+        if (tail) {
+          int key = key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          if (key >= p.Mk) s[kb][r] = -INFINITY;
+        }
+        mt = fmaxf(mt, s[kb][r]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    const float eta = __expf(m_run - m_new);
+    const float mc = m_new * c;
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = __expf(s[kb][r] - m_new);
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
         s[kb][r] = e;
         lsum += e;
       }
     lsum += __shfl_xor(lsum, 32);
-    l_run = eta * l_run + lsum;
+    // rescale only when some query's maximum moved (eta = 1 exactly otherwise)
+    const float eta = __builtin_amdgcn_exp2f(m_run * c - mc);
+    if (__any(m_new != m_run)) {
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= eta;
+      l_run *= eta;
+    }
+    l_run += lsum;
     m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= eta;
 
     // O^T += V^T P^T over 4 groups of 16 keys.  Slot j of a lane's B operand
     // holds score register i = (g%2)*8 + j of tile g/2, i.e. key
@@ -179,16 +195,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs p) {
     // operand (V^T) uses the same key for the same slot.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      u16x8 hi, lo;
+      bf16x8 bhi, blo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float pv = s[g >> 1][(g & 1) * 8 + j];
-        uint16_t hb = f2bf(pv);
-        hi[j] = hb;
-        lo[j] = f2bf(pv - bf2f(hb));
+      for (int j = 0; j < 8; j += 2) {
+        f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
+        bf16x2 hi = __builtin_convertvector(pv, bf16x2);  // round to nearest even
+        f32x2 hf = __builtin_convertvector(hi, f32x2);
+        f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};      // exact
+        bf16x2 lo = __builtin_convertvector(rem, bf16x2);
+        bhi[j] = hi[0];
+        bhi[j + 1] = hi[1];
+        blo[j] = lo[0];
+        blo[j + 1] = lo[1];
       }
-      const bf16x8 bhi = __builtin_bit_cast(bf16x8, hi);
-      const bf16x8 blo = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
         const uint16_t* vr = &v_lds[cur][(dt * 32 + l32) * VS + 16 * g + 4 * half];

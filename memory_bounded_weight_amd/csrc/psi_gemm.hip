@@ -48,7 +48,7 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return v * e / (1.0f + e);
 }
 
-constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kThreads = 256;  // 4 waves of 64, arranged 2 x 2
 
 template <int BM, int BN, int BK>
 struct Tile {
@@ -59,22 +59,30 @@ struct Tile {
   static constexpr int B_PER_T = B_CHUNKS / kThreads;
   static constexpr int WM = BM / 2;  // wave tile (2 x 2 waves)
   static constexpr int WN = BN / 2;
-  static constexpr int TM = WM / 32;  // MFMA tiles per wave
+  static constexpr int TM = WM / 32;  // 32x32 MFMA tiles per wave
   static constexpr int TN = WN / 32;
+  static constexpr int STAGE = (BM + BN) * LDS;  // elements per LDS stage
   static_assert(A_CHUNKS % kThreads == 0 && B_CHUNKS % kThreads == 0, "tile/threads");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
 };
 
-template <int BM, int BN, int BK>
+// STAGES = 2: double-buffered LDS, one barrier per K tile.
+// STAGES = 1: one LDS buffer (half the LDS, so two workgroups fit a CU),
+// the register stage still prefetches the next K tile.
+template <int BM, int BN, int BK, int STAGES>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   using T = Tile<BM, BN, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * T::LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * T::STAGE];
 
-  // Tile order: consecutive workgroups walk down M for a fixed N column
-  // band, so the B slice (the weight page) of a band is re-read from L2.
-  const int bid = blockIdx.x;
-  const int tm = bid % tiles_m;
-  const int tn = bid / tiles_m;
+  // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own
+  // L2).  Remap so that every XCD owns a contiguous range of logical tiles,
+  // and walk that range with N fastest: concurrently running tiles of an
+  // XCD then share their A row bands (and the page's B bands) in its L2.
+  const int nt = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
+  const int tm = t / tiles_n;
+  const int tn = t % tiles_n;
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  constexpr int CPR = BK / 8;  // chunks per row
+  constexpr int CPR = BK / 8;  // 16-byte chunks per row
   uint4 ra[T::A_PER_T], rb[T::B_PER_T];
 
   auto load_global = [&](int k0) {
@@ -111,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     }
   };
   auto store_lds = [&](int buf) {
-    uint16_t* sa = smem[buf];
-    uint16_t* sb = smem[buf] + BM * T::LDS;
+    uint16_t* sa = smem + buf * T::STAGE;
+    uint16_t* sb = sa + BM * T::LDS;
 #pragma unroll
     for (int i = 0; i < T::A_PER_T; ++i) {
       int c = tid + i * kThreads;
@@ -135,15 +143,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
     for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = 0.0f;
-        if (p.acc_in) {
-          int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          int gn = n0 + wn * T::WN + j * 32 + l32;
-          if (gm < p.M && gn < p.N) v = p.acc_in[(long)gm * p.ld_acc_in + gn];
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (p.acc_in) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const int gn = n0 + wn * T::WN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          if (gm < p.M && gn < p.N) acc[i][j][r] = p.acc_in[(long)gm * p.ld_acc_in + gn];
         }
-        acc[i][j][r] = v;
       }
+  }
 
   const int nk = (p.K + BK - 1) / BK;
   load_global(0);
@@ -151,10 +164,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+    const int cur = STAGES == 2 ? (kt & 1) : 0;
     if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const uint16_t* sa = smem[cur] + (wm * T::WM) * T::LDS;
-    const uint16_t* sb = smem[cur] + BM * T::LDS + (wn * T::WN) * T::LDS;
+    const uint16_t* sa = smem + cur * T::STAGE + (wm * T::WM) * T::LDS;
+    const uint16_t* sb = smem + cur * T::STAGE + BM * T::LDS + (wn * T::WN) * T::LDS;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kofs = ks * 16 + half * 8;
@@ -171,7 +184,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         for (int j = 0; j < T::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+    if (STAGES == 1) __syncthreads();
+    if (kt + 1 < nk) store_lds(STAGES == 2 ? (cur ^ 1) : 0);
     __syncthreads();
   }
 
@@ -179,18 +193,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j)
+    for (int j = 0; j < T::TN; ++j) {
+      const int gn = n0 + wn * T::WN + j * 32 + l32;
+      if (gn >= p.N) continue;
+      const float bn = (p.bias && !p.bias_on_m) ? bf2f(p.bias[gn]) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-        const int gn = n0 + wn * T::WN + j * 32 + l32;
-        if (gm >= p.M || gn >= p.N) continue;
+        if (gm >= p.M) continue;
         const float v = acc[i][j][r];
         if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
         if (p.out) {
           float t;
           if (p.bias) {
-            const float bv = bf2f(p.bias[p.bias_on_m ? gm : gn]);
+            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
             t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
           } else {
             t = v;
@@ -201,18 +217,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
           p.out[(long)gm * p.ldo + gn] = y;
         }
       }
+    }
+}
+
+template <int BM, int BN, int BK, int STAGES>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, STAGES>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile configurations (every one gives the same bits: each output sees the
+// same ascending sequence of k16 MFMA steps whatever the tile).
+//   1: 256x256, 2: 256x128, 3: 128x256, 4: 128x128 (double-buffered LDS)
+//   5: 256x128, 6: 128x256 with one LDS stage (two workgroups per CU)
+// Measured on MI355X: the 128x128 tile, at two waves per SIMD (two
+// workgroups per CU), is the fastest on every page shape of this path;
+// the single-wave large tiles are latency-bound.
+int gemm_auto_config(int M, int N) {
+  (void)M;
+  (void)N;
+  return 4;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  constexpr int BM = 128, BN = 128, BK = 64;
-  const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
-                     tiles_m, tiles_n);
-  return hipGetLastError();
+  int cfg = a.config > 0 ? a.config : gemm_auto_config(a.M, a.N);
+  switch (cfg) {
+    case 1: return launch_cfg<256, 256, 64, 2>(a, s);
+    case 2: return launch_cfg<256, 128, 64, 2>(a, s);
+    case 3: return launch_cfg<128, 256, 64, 2>(a, s);
+    case 5: return launch_cfg<256, 128, 64, 1>(a, s);
+    case 6: return launch_cfg<128, 256, 64, 1>(a, s);
+    default: return launch_cfg<128, 128, 64, 2>(a, s);
+  }
 }
 
 }  // namespace psi

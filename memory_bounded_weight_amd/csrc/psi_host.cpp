@@ -113,15 +113,15 @@ psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out) {
     return fail(PSI_E_INVALID, "psi_arena_plan: zero arena or page size");
   psi_arena_layout L;
   std::memset(&L, 0, sizeof L);
-  L.side_bytes = align_up(d->side_bytes ? d->side_bytes : kDefaultSide, kAlign);
+  L.bias_slot_bytes = align_up(d->bias_slot_bytes ? d->bias_slot_bytes : kDefaultSide, kAlign);
   size_t off = 0;
   for (int i = 0; i < d->n_pages; ++i) {
     L.page_off[i] = off;
     off += align_up(d->page_bytes, kAlign);
   }
-  for (int i = 0; i < d->n_pages; ++i) {
-    L.side_off[i] = off;
-    off += L.side_bytes;
+  for (int i = 0; i < 2; ++i) {
+    L.bias_off[i] = off;
+    off += L.bias_slot_bytes;
   }
   L.workspace_off = off;
   off += align_up(d->workspace_bytes, kAlign);
@@ -129,7 +129,7 @@ psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out) {
     return fail(PSI_E_ARENA_TOO_SMALL,
                 "arena of " + std::to_string(d->arena_bytes) + " B cannot hold " +
                     std::to_string(d->n_pages) + " pages of " + std::to_string(d->page_bytes) +
-                    " B, their side slots and " + std::to_string(d->workspace_bytes) + " B workspace");
+                    " B, two bias slots and " + std::to_string(d->workspace_bytes) + " B workspace");
   L.scratch_off = off;
   L.scratch_bytes = (d->arena_bytes - off) / kAlign * kAlign;
   L.total_bytes = d->arena_bytes;
@@ -142,26 +142,25 @@ psi_status psi_arena_plan(const psi_arena_desc* d, psi_arena_layout* out) {
 // ---------------------------------------------------------------- plans
 namespace psi {
 
-static psi_status page_fit(const psi_arena_desc* d, const psi_arena_layout& L, const psi_matrix* m,
-                           const char* name, size_t side_need) {
+static psi_status page_fit(const psi_arena_desc* d, const psi_matrix* m, const char* name) {
   if (m->resident) return PSI_OK;  // consumed in place, never copied into a page
   MatrixInfo mi = matrix_info(m);
   if (mi.max_page_bytes > d->page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, std::string("weight tile exceeds page: ") + name + " needs " +
                                           std::to_string(mi.max_page_bytes) + " B per page, page is " +
                                           std::to_string(d->page_bytes) + " B");
-  if (side_need > L.side_bytes)
-    return fail(PSI_E_PAGE_TOO_SMALL, std::string("bias slice of ") + name + " (" +
-                                          std::to_string(side_need) + " B) exceeds the side slot (" +
-                                          std::to_string(L.side_bytes) + " B)");
   return PSI_OK;
 }
 
-static size_t bias_side_bytes(const psi_matrix* m) {
-  if (!m->bias_host) return 0;
-  // ROWS: each page carries its slice; COLS: the last page carries all of it
-  return m->split == PSI_SPLIT_ROWS ? (size_t)(m->block < m->rows ? m->block : m->rows) * 2
-                                    : (size_t)m->rows * 2;
+// Bytes an operator stages in its bias slot (streamed matrices with a bias).
+static psi_status bias_fit(const psi_arena_layout& L, const psi_matrix* const* ms, int n) {
+  size_t need = 0;
+  for (int i = 0; i < n; ++i)
+    if (ms[i]->bias_host && !ms[i]->resident) need += align_up((size_t)ms[i]->rows * 2, kAlign);
+  if (need > L.bias_slot_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, "the operator's biases (" + std::to_string(need) +
+                                          " B) exceed a bias slot (" + std::to_string(L.bias_slot_bytes) + " B)");
+  return PSI_OK;
 }
 
 static psi_status scratch_fit(const psi_arena_layout& L, size_t need, const char* what) {
@@ -183,7 +182,8 @@ psi_status psi_linear_plan(const psi_arena_desc* d, int M, int K, const psi_matr
   if (st) return st;
   if ((st = check_matrix(W, "W", -1))) return st;
   if (M < 0 || K <= 0 || K != W->cols) return fail(PSI_E_INVALID, "linear: x is [M, K] with K == W.cols");
-  if ((st = page_fit(d, L, W, "W", bias_side_bytes(W)))) return st;
+  if ((st = page_fit(d, W, "W"))) return st;
+  if ((st = bias_fit(L, &W, 1))) return st;
   size_t need = 0;
   if (W->split == PSI_SPLIT_COLS && !acc_external) need += align_up((size_t)M * W->rows * 4, kAlign);
   if ((st = scratch_fit(L, need, "linear accumulator"))) return st;
@@ -204,8 +204,9 @@ psi_status psi_ffn_plan(const psi_arena_desc* d, int M, int dmodel, const psi_ma
   if (U->block != V->block) return fail(PSI_E_INVALID, "ffn: U and V must share the hidden tile");
   if (U->block % 8 != 0) return fail(PSI_E_ALIGN, "ffn: hidden tile must be a multiple of 8");
   if (token_chunks < 1) return fail(PSI_E_INVALID, "ffn: token_chunks must be >= 1");
-  if ((st = page_fit(d, L, U, "U", bias_side_bytes(U)))) return st;
-  if ((st = page_fit(d, L, V, "V", bias_side_bytes(V)))) return st;
+  if ((st = page_fit(d, U, "U")) || (st = page_fit(d, V, "V"))) return st;
+  const psi_matrix* uv[2] = {U, V};
+  if ((st = bias_fit(L, uv, 2))) return st;
   size_t need = align_up((size_t)M * U->block * 2, kAlign);  // hidden tile H_J, all rows
   if (!acc_external) need += align_up((size_t)M * dmodel * 4, kAlign);
   if ((st = scratch_fit(L, need, "FFN hidden tile and accumulator"))) return st;
@@ -236,7 +237,8 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
                                "(a multiple of head_dim)");
   const char* names[4] = {"Wq", "Wk", "Wv", "Wo"};
   for (int i = 0; i < 4; ++i)
-    if ((st = page_fit(d, L, ms[i], names[i], bias_side_bytes(ms[i])))) return st;
+    if ((st = page_fit(d, ms[i], names[i]))) return st;
+  if ((st = bias_fit(L, ms, 4))) return st;
   const int Ms = Mc > 0 ? Mc : M;
   if (Ms < 1 && M > 0) return fail(PSI_E_INVALID, "attention: at least one key per row is required");
   size_t ldvt = align_up((size_t)Ms, 64);

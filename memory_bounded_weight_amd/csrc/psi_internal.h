@@ -57,8 +57,10 @@ struct GemmArgs {
   long ldr;
   int epi;
   int baseline_bias;
+  int config;           // tile configuration; 0 = chosen from the shape
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+int gemm_auto_config(int M, int N);
 
 struct AttnArgs {
   uint16_t* q;         // [Mq, ldq]; head h occupies columns h*128..h*128+127; O overwrites it
@@ -93,7 +95,6 @@ struct psi_page_slot {
   hipEvent_t release = nullptr;  // recorded on the compute stream after the last consumer
   bool released_once = false;
   void* dev = nullptr;
-  void* side_dev = nullptr;
 };
 
 struct psi_timed {
@@ -111,6 +112,8 @@ struct psi_arena {
   hipStream_t copy = nullptr;
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
+  psi_page_slot bias_slots[2];  // same lifecycle as pages, one per operator, alternating
+  int next_bias = 0;
   // scratch stack (offsets relative to layout.scratch_off)
   size_t scratch_top = 0;
   psi_stats stats{};
@@ -125,11 +128,23 @@ namespace psi {
 void* scratch_alloc(psi_arena* a, size_t bytes, psi_status* st);
 void scratch_reset(psi_arena* a, size_t mark);
 
-// Internal page request carrying an optional side (bias) slice.
-psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, const void* side_host,
-                          size_t side_bytes, int* page_out, bool check_pinned);
+// Page request (slice copy into the next round-robin page slot).
+psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
+                          bool check_pinned);
 psi_status page_acquire(psi_arena* a, int page);
 psi_status page_release(psi_arena* a, int page);
+
+// An operator's biases: one request into the next bias slot (several
+// pinned host arrays, each placed 256-byte aligned); *dev_out[i] receives
+// the device address of part i.  slot_out is -1 when nothing was copied.
+struct BiasPart {
+  const void* host;
+  size_t bytes;
+};
+psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_t** dev_out,
+                       int* slot_out);
+psi_status bias_acquire(psi_arena* a, int slot);
+psi_status bias_release(psi_arena* a, int slot);
 
 // Kernel launch through the arena (profiling, counters).
 psi_status run_gemm(psi_arena* a, const GemmArgs& g);

@@ -9,11 +9,15 @@
 // previous-consumer dependencies.  Asynchronous transport stages state
 // through a pinned host ring.
 //
-// Here: two library streams alternate over the pinned ring slots (slot s
-// belongs to stream s % 2, so stream order alone makes slot reuse follow
-// the previous host commit); a D2H copy into the slot is followed on the
-// same stream by a host callback that moves the bytes into the store.
-// The store is allocated and touched when the journal is created.
+// Default mode: the store is pinned host memory, so a commit is one DMA
+// copy into the entry's location on the journal's D2H stream (the "host
+// commit" is the index update) and a reload is one DMA copy back on its
+// H2D stream.  Ring mode (PSI_JOURNAL_RING): the store is pageable; two
+// library streams alternate over the pinned ring slots (slot s belongs to
+// stream s % 2, so stream order alone makes slot reuse follow the previous
+// host commit); a D2H copy into the slot is followed on the same stream by a
+// host callback that moves the bytes into the store.  The store is
+// allocated and touched when the journal is created.
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -50,8 +54,9 @@ void host_copy_cb(void* arg) {
 
 struct psi_journal {
   psi_journal_desc desc{};
-  char* ring = nullptr;   // pinned
-  char* store = nullptr;  // pageable, pre-touched
+  bool ring_mode = false;
+  char* ring = nullptr;   // pinned staging (ring and sync modes)
+  char* store = nullptr;  // pinned (default) or pageable, pre-touched (ring mode)
   size_t store_top = 0;
   std::map<psi_key, Entry, KeyLess> index;
   hipStream_t stream[2] = {nullptr, nullptr};
@@ -72,21 +77,36 @@ psi_status psi_journal_destroy(psi_journal* j);
 
 psi_status psi_journal_create(const psi_journal_desc* d, psi_journal** out) {
   if (!d || !out) return fail(PSI_E_INVALID, "psi_journal_create: null argument");
-  if (d->ring_slot_bytes == 0 || d->ring_slots < 2)
-    return fail(PSI_E_INVALID, "journal: need ring_slots >= 2 and a non-empty slot");
+  const bool ring_mode = d->flags & PSI_JOURNAL_RING;
+  const bool sync = d->flags & PSI_JOURNAL_SYNC;
+  if ((ring_mode || sync) && (d->ring_slot_bytes == 0 || d->ring_slots < 2))
+    return fail(PSI_E_INVALID, "journal: ring and sync modes need ring_slots >= 2 and a non-empty slot");
   psi_journal* j = new psi_journal();
   j->desc = *d;
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&j->ring), d->ring_slot_bytes * d->ring_slots,
-                               hipHostMallocDefault);
-  if (e != hipSuccess) {
-    delete j;
-    return hip_fail(e, "hipHostMalloc(journal ring)");
+  j->ring_mode = ring_mode;
+  hipError_t e = hipSuccess;
+  if (ring_mode || sync) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&j->ring), d->ring_slot_bytes * d->ring_slots,
+                      hipHostMallocDefault);
+    if (e != hipSuccess) {
+      delete j;
+      return hip_fail(e, "hipHostMalloc(journal ring)");
+    }
   }
   if (d->store_bytes) {
-    j->store = static_cast<char*>(std::malloc(d->store_bytes));
-    if (!j->store) {
-      psi_journal_destroy(j);
-      return fail(PSI_E_INVALID, "journal: cannot allocate the host store");
+    if (ring_mode) {
+      j->store = static_cast<char*>(std::malloc(d->store_bytes));
+      if (!j->store) {
+        psi_journal_destroy(j);
+        return fail(PSI_E_INVALID, "journal: cannot allocate the host store");
+      }
+    } else {
+      e = hipHostMalloc(reinterpret_cast<void**>(&j->store), d->store_bytes, hipHostMallocDefault);
+      if (e != hipSuccess) {
+        j->store = nullptr;
+        psi_journal_destroy(j);
+        return hip_fail(e, "hipHostMalloc(journal store)");
+      }
     }
     std::memset(j->store, 0, d->store_bytes);  // touch every page now, not during commits
   }
@@ -119,7 +139,10 @@ psi_status psi_journal_destroy(psi_journal* j) {
   }
   if (j->dep) (void)hipEventDestroy(j->dep);
   if (j->ring) (void)hipHostFree(j->ring);
-  std::free(j->store);
+  if (j->ring_mode)
+    std::free(j->store);
+  else if (j->store)
+    (void)hipHostFree(j->store);
   delete j;
   return PSI_OK;
 }
@@ -144,6 +167,13 @@ psi_status psi_journal_commit(psi_journal* j, psi_key k, const void* dev, size_t
       PSI_HIP(hipStreamSynchronize(prod));
       std::memcpy(j->store + ent.off + off, j->ring, n);
     }
+  } else if (!j->ring_mode) {
+    // one DMA copy straight into the pinned entry, after the producer's work
+    PSI_HIP(hipEventRecord(j->dep, prod));
+    PSI_HIP(hipStreamWaitEvent(j->stream[0], j->dep, 0));
+    PSI_HIP(hipMemcpyAsync(j->store + ent.off, src, bytes, hipMemcpyDeviceToHost, j->stream[0]));
+    PSI_HIP(hipEventRecord(j->read_done[0], j->stream[0]));
+    j->used[0] = true;
   } else {
     PSI_HIP(hipEventRecord(j->dep, prod));
     for (int i = 0; i < 2; ++i) PSI_HIP(hipStreamWaitEvent(j->stream[i], j->dep, 0));
@@ -189,6 +219,16 @@ psi_status psi_journal_reload(psi_journal* j, psi_key k, void* dev, size_t bytes
       PSI_HIP(hipMemcpyAsync(dst + off, j->ring, n, hipMemcpyHostToDevice, cons));
     }
     PSI_HIP(hipStreamSynchronize(cons));
+  } else if (!j->ring_mode) {
+    // the overwrite of dev follows its previous consumers on `cons`, and the
+    // entry's commit (both on the journal's streams) precedes the read
+    PSI_HIP(hipEventRecord(j->dep, cons));
+    PSI_HIP(hipEventRecord(j->cross[0], j->stream[0]));
+    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->dep, 0));
+    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->cross[0], 0));
+    PSI_HIP(hipMemcpyAsync(dst, j->store + ent.off, bytes, hipMemcpyHostToDevice, j->stream[1]));
+    PSI_HIP(hipEventRecord(j->write_done[1], j->stream[1]));
+    PSI_HIP(hipStreamWaitEvent(cons, j->write_done[1], 0));
   } else {
     // the overwrite of dev follows its previous consumers on `cons`, and
     // every earlier host commit (on either stream) precedes the reads of

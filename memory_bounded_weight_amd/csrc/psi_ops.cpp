@@ -16,30 +16,49 @@ namespace {
 struct PageReq {
   const void* host;  // device address when `resident`
   size_t bytes;
-  const void* side;
-  size_t side_bytes;
   bool resident;
 };
 
-// Page requests of a matrix: ROWS pages carry their bias slice; a COLS
-// (K-split) matrix carries its whole bias on the last page, because the
-// bias is added once after the last partial sum ([PSI] sec. II-B).
 void matrix_requests(const psi_matrix* m, std::vector<PageReq>& out) {
   const int n = psi_matrix_pages(m);
-  for (int p = 0; p < n; ++p) {
-    PageReq r{matrix_page_ptr(m, p), psi_matrix_page_bytes(m, p), nullptr, 0, m->resident != 0};
-    if (m->bias_host) {
-      if (m->split == PSI_SPLIT_ROWS) {
-        r.side = m->bias_host + (size_t)p * m->block;
-        r.side_bytes = (size_t)matrix_page_extent(m, p) * 2;
-      } else if (p == n - 1) {
-        r.side = m->bias_host;
-        r.side_bytes = (size_t)m->rows * 2;
-      }
-    }
-    out.push_back(r);
-  }
+  for (int p = 0; p < n; ++p)
+    out.push_back(PageReq{matrix_page_ptr(m, p), psi_matrix_page_bytes(m, p), m->resident != 0});
 }
+
+// The biases of an operator's matrices, staged together in one bias slot
+// (resident matrices are used in place).  A split-by-rows page uses the
+// slice of its output rows; a K-split matrix adds its whole bias once,
+// after the last partial sum ([PSI] sec. II-B).
+class OpBiases {
+ public:
+  psi_status stage(psi_arena* a, const psi_matrix* const* ms, int n) {
+    a_ = a;
+    BiasPart parts[4];
+    const uint16_t* dev[4];
+    for (int i = 0; i < n; ++i) {
+      const bool copy = ms[i]->bias_host && !ms[i]->resident;
+      parts[i] = BiasPart{copy ? ms[i]->bias_host : nullptr, copy ? (size_t)ms[i]->rows * 2 : 0};
+    }
+    psi_status st = bias_submit(a, parts, n, dev, &slot_);
+    if (st) return st;
+    for (int i = 0; i < n; ++i) ptr_[i] = ms[i]->resident ? ms[i]->bias_host : dev[i];
+    return PSI_OK;
+  }
+  // Device address of matrix i's bias (nullable); the compute stream
+  // first waits for the bias copy.
+  psi_status get(int i, const uint16_t** out) {
+    psi_status st = bias_acquire(a_, slot_);
+    if (st) return st;
+    *out = ptr_[i];
+    return PSI_OK;
+  }
+  psi_status release() { return bias_release(a_, slot_); }
+
+ private:
+  psi_arena* a_ = nullptr;
+  int slot_ = -1;
+  const uint16_t* ptr_[4] = {nullptr, nullptr, nullptr, nullptr};
+};
 
 // Streams a list of page requests through the arena's slots: requests are
 // submitted as soon as their (round-robin) slot is free, so the copy of the
@@ -58,28 +77,25 @@ class PageFeeder {
       }
       if (a_->slots[a_->next_slot].state != psi_page_slot::FREE) break;
       int s = -1;
-      psi_status st = page_submit_ex(a_, r.host, r.bytes, r.side, r.side_bytes, &s, false);
+      psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false);
       if (st) return st;
       slot_[submitted_++] = s;
     }
     return PSI_OK;
   }
-  // Waits (on the compute stream) for request i and returns its page/side.
-  psi_status take(size_t i, const uint16_t** page, const uint16_t** side) {
+  // Waits (on the compute stream) for request i and returns its page.
+  psi_status take(size_t i, const uint16_t** page) {
     psi_status st = feed();
     if (st) return st;
     const PageReq& r = reqs_[i];
     if (r.resident) {
       *page = static_cast<const uint16_t*>(r.host);
-      *side = static_cast<const uint16_t*>(r.side);
       return PSI_OK;
     }
     if (i >= submitted_) return fail(PSI_E_STATE, "page request not submitted (slots exhausted)");
     st = page_acquire(a_, slot_[i]);
     if (st) return st;
     *page = static_cast<const uint16_t*>(a_->dry ? nullptr : a_->slots[slot_[i]].dev);
-    *side = r.side ? static_cast<const uint16_t*>(a_->dry ? nullptr : a_->slots[slot_[i]].side_dev)
-                   : nullptr;
     return PSI_OK;
   }
   psi_status give_back(size_t i) {
@@ -161,24 +177,28 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * N * 4, &st));
     if (st) return st;
   }
+  OpBiases bias;
+  if ((st = bias.stage(a, &W, 1))) return st;
   std::vector<PageReq> reqs;
   matrix_requests(W, reqs);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
+  const uint16_t* b = nullptr;
   const int n = (int)reqs.size();
   for (int p = 0; p < n; ++p) {
-    const uint16_t *page, *side;
-    if ((st = feeder.take(p, &page, &side))) return st;
+    const uint16_t* page;
+    if ((st = feeder.take(p, &page))) return st;
     const int ext = matrix_page_extent(W, p);
     GemmArgs g = gemm_args();
     g.M = M;
     g.baseline_bias = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
     if (W->split == PSI_SPLIT_ROWS) {
       const int c0 = p * W->block;
+      if ((st = bias.get(0, &b))) return st;
       g.A = x; g.lda = K;
       g.B = page; g.ldb = K;
       g.N = ext; g.K = K;
-      g.bias = side;
+      g.bias = b ? b + c0 : nullptr;
       g.out = y + c0; g.ldo = N;
       if (resid) { g.resid = x + c0; g.ldr = K; }
       if (flags & PSI_OP_STORE_ACC) { g.acc_out = acc_dev + c0; g.ld_acc_out = N; }
@@ -190,7 +210,8 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
       g.N = N; g.K = ext;
       if (p > 0) { g.acc_in = acc; g.ld_acc_in = N; }
       if (last) {
-        g.bias = side;
+        if ((st = bias.get(0, &b))) return st;
+        g.bias = b;
         g.out = y; g.ldo = N;
         if (resid) { g.resid = x; g.ldr = K; }
         if (flags & PSI_OP_STORE_ACC) { g.acc_out = acc; g.ld_acc_out = N; }
@@ -202,7 +223,7 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
     if ((st = run_gemm(a, g))) return st;
     if ((st = feeder.give_back(p))) return st;
   }
-  return PSI_OK;
+  return bias.release();
 }
 
 psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
@@ -230,6 +251,9 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * d * 4, &st));
     if (st) return st;
   }
+  const psi_matrix* ms[2] = {U, V};
+  OpBiases bias;
+  if ((st = bias.stage(a, ms, 2))) return st;
   // Request order U_0, V_0, U_1, V_1, ...: each hidden tile J is produced
   // for all tokens from U_J, then consumed by V_J ([PSI] eq. (2)).
   std::vector<PageReq> ru, rv, reqs;
@@ -244,19 +268,21 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
   const int rows_per = (M + chunks - 1) / chunks;
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
+  const uint16_t *ba = nullptr, *bb = nullptr;
   for (int J = 0; J < nJ; ++J) {
     const int ext = matrix_page_extent(U, J);
     const bool last = J == nJ - 1;
-    const uint16_t *page, *side;
+    const uint16_t* page;
     // up-projection + bias + BF16 + GELU + BF16 for every token chunk
-    if ((st = feeder.take(2 * J, &page, &side))) return st;
+    if ((st = feeder.take(2 * J, &page))) return st;
+    if ((st = bias.get(0, &ba))) return st;
     for (int r0 = 0; r0 < M; r0 += rows_per) {
       const int mr = M - r0 < rows_per ? M - r0 : rows_per;
       GemmArgs g = gemm_args();
       g.A = x + (size_t)r0 * d; g.lda = d;
       g.B = page; g.ldb = d;
       g.M = mr; g.N = ext; g.K = d;
-      g.bias = side;
+      g.bias = ba ? ba + (size_t)J * th : nullptr;
       g.out = H + (size_t)r0 * th; g.ldo = th;
       g.epi = EPI_GELU;
       g.baseline_bias = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
@@ -264,7 +290,8 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
     }
     if ((st = feeder.give_back(2 * J))) return st;
     // down-projection: carried fp32 accumulator, bias once after the last tile
-    if ((st = feeder.take(2 * J + 1, &page, &side))) return st;
+    if ((st = feeder.take(2 * J + 1, &page))) return st;
+    if (last && (st = bias.get(1, &bb))) return st;
     for (int r0 = 0; r0 < M; r0 += rows_per) {
       const int mr = M - r0 < rows_per ? M - r0 : rows_per;
       GemmArgs g = gemm_args();
@@ -273,7 +300,7 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
       g.M = mr; g.N = d; g.K = ext;
       if (J > 0) { g.acc_in = acc + (size_t)r0 * d; g.ld_acc_in = d; }
       if (last) {
-        g.bias = side;
+        g.bias = bb;
         g.out = y + (size_t)r0 * d; g.ldo = d;
         if (resid) { g.resid = x + (size_t)r0 * d; g.ldr = d; }
         if (flags & PSI_OP_STORE_ACC) { g.acc_out = acc + (size_t)r0 * d; g.ld_acc_out = d; }
@@ -285,7 +312,7 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
     }
     if ((st = feeder.give_back(2 * J + 1))) return st;
   }
-  return PSI_OK;
+  return bias.release();
 }
 
 psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
@@ -313,7 +340,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   const uint16_t* src = ctx ? ctx : x;
   const int Ms = ctx ? Mc : M;
   const long ldvt = (long)align_up((size_t)Ms, 64);
-  const int bb = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  const int bbase = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
   ScratchMark mark(a);
   uint16_t* Q = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * gw * 2, &st));
   if (st) return st;
@@ -326,6 +353,9 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * dm * 4, &st));
     if (st) return st;
   }
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  OpBiases bias;
+  if ((st = bias.stage(a, ms, 4))) return st;
   std::vector<PageReq> rq, rk, rv, ro, reqs;
   matrix_requests(Wq, rq);
   matrix_requests(Wk, rk);
@@ -341,37 +371,43 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
+  const uint16_t* bq[4];
   for (int g = 0; g < nG; ++g) {
     const int ext = matrix_page_extent(Wq, g);
     const bool last = g == nG - 1;
-    const uint16_t *page, *side;
+    const size_t c0 = (size_t)g * gw;
+    const uint16_t* page;
+    if (g == 0)
+      for (int i = 0; i < 4; ++i)
+        if ((st = bias.get(i, &bq[i]))) return st;
     // Q_g = x Wq_g^T + bq_g
-    if ((st = feeder.take(4 * g, &page, &side))) return st;
+    if ((st = feeder.take(4 * g, &page))) return st;
     {
       GemmArgs G = gemm_args();
       G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
       G.M = M; G.N = ext; G.K = dm;
-      G.bias = side; G.out = Q; G.ldo = gw; G.baseline_bias = bb;
+      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q; G.ldo = gw; G.baseline_bias = bbase;
       if ((st = run_gemm(a, G))) return st;
     }
     if ((st = feeder.give_back(4 * g))) return st;
     // K_g = src Wk_g^T + bk_g
-    if ((st = feeder.take(4 * g + 1, &page, &side))) return st;
+    if ((st = feeder.take(4 * g + 1, &page))) return st;
     {
       GemmArgs G = gemm_args();
       G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
       G.M = Ms; G.N = ext; G.K = dm;
-      G.bias = side; G.out = Kb; G.ldo = gw; G.baseline_bias = bb;
+      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb; G.ldo = gw; G.baseline_bias = bbase;
       if ((st = run_gemm(a, G))) return st;
     }
     if ((st = feeder.give_back(4 * g + 1))) return st;
     // V_g^T = Wv_g src^T + bv_g (bias along rows): written transposed
-    if ((st = feeder.take(4 * g + 2, &page, &side))) return st;
+    if ((st = feeder.take(4 * g + 2, &page))) return st;
     {
       GemmArgs G = gemm_args();
       G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
       G.M = ext; G.N = Ms; G.K = dm;
-      G.bias = side; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt; G.baseline_bias = bb;
+      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
+      G.baseline_bias = bbase;
       if ((st = run_gemm(a, G))) return st;
     }
     if ((st = feeder.give_back(4 * g + 2))) return st;
@@ -387,15 +423,15 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
       if ((st = run_attention(a, A))) return st;
     }
     // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
-    if ((st = feeder.take(4 * g + 3, &page, &side))) return st;
+    if ((st = feeder.take(4 * g + 3, &page))) return st;
     {
       GemmArgs G = gemm_args();
       G.A = Q; G.lda = gw; G.B = page; G.ldb = ext;
       G.M = M; G.N = dm; G.K = ext;
-      G.baseline_bias = bb;
+      G.baseline_bias = bbase;
       if (g > 0) { G.acc_in = acc; G.ld_acc_in = dm; }
       if (last) {
-        G.bias = side; G.out = y; G.ldo = dm;
+        G.bias = bq[3]; G.out = y; G.ldo = dm;
         if (flags & PSI_OP_RESIDUAL) { G.resid = x; G.ldr = dm; }
         if (flags & PSI_OP_STORE_ACC) { G.acc_out = acc; G.ld_acc_out = dm; }
       } else {
@@ -405,7 +441,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     }
     if ((st = feeder.give_back(4 * g + 3))) return st;
   }
-  return PSI_OK;
+  return bias.release();
 }
 
 psi_status psi_journal_fence(psi_journal* j, void* stream);

@@ -52,6 +52,7 @@ PSI_SPLIT_ROWS = 0
 PSI_SPLIT_COLS = 1
 PSI_MAX_PAGES = 8
 PSI_JOURNAL_SYNC = 0x1
+PSI_JOURNAL_RING = 0x2
 
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
@@ -61,13 +62,13 @@ _u = ctypes.c_uint
 
 class psi_arena_desc(ctypes.Structure):
     _fields_ = [("arena_bytes", _sz), ("page_bytes", _sz), ("n_pages", _i),
-                ("workspace_bytes", _sz), ("side_bytes", _sz), ("compute_stream", _vp),
+                ("workspace_bytes", _sz), ("bias_slot_bytes", _sz), ("compute_stream", _vp),
                 ("flags", _u)]
 
 
 class psi_arena_layout(ctypes.Structure):
-    _fields_ = [("page_off", _sz * PSI_MAX_PAGES), ("side_off", _sz * PSI_MAX_PAGES),
-                ("side_bytes", _sz), ("workspace_off", _sz), ("scratch_off", _sz),
+    _fields_ = [("page_off", _sz * PSI_MAX_PAGES), ("bias_off", _sz * 2),
+                ("bias_slot_bytes", _sz), ("workspace_off", _sz), ("scratch_off", _sz),
                 ("scratch_bytes", _sz), ("total_bytes", _sz)]
 
 
@@ -212,9 +213,9 @@ def psi_matrix_page_bytes(m: psi_matrix, p: int) -> int:
     return _lib.psi_matrix_page_bytes(ctypes.byref(m), p)
 
 
-def arena_desc(arena_bytes, page_bytes, n_pages=2, workspace_bytes=0, side_bytes=0,
+def arena_desc(arena_bytes, page_bytes, n_pages=2, workspace_bytes=0, bias_slot_bytes=0,
                compute_stream=None, flags=0) -> psi_arena_desc:
-    return psi_arena_desc(arena_bytes, page_bytes, n_pages, workspace_bytes, side_bytes,
+    return psi_arena_desc(arena_bytes, page_bytes, n_pages, workspace_bytes, bias_slot_bytes,
                           compute_stream or None, flags)
 
 
@@ -406,20 +407,15 @@ def resident_matrix(m: psi_matrix) -> psi_matrix:
 
 def block_weights(w: dict, group_cols: int, hidden_tile: int, resident: bool = False) -> psi_block_weights:
     """psi_block_weights from a dict of host bf16 arrays (Wq..bo, U, a, V, b);
-    ``resident`` places the page images in device memory instead."""
-    bw = psi_block_weights()
-    keep = []
-    for name in ("Wq", "Wk", "Wv"):
-        m = pinned_matrix(w[name], w["b" + name[1]], PSI_SPLIT_ROWS, group_cols)
-        setattr(bw, name, m)
-        keep.append(m)
-    bw.Wo = pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_COLS, group_cols)
-    bw.U = pinned_matrix(w["U"], w["a"], PSI_SPLIT_ROWS, hidden_tile)
-    bw.V = pinned_matrix(w["V"], w["b"], PSI_SPLIT_COLS, hidden_tile)
-    keep += [bw.Wo, bw.U, bw.V]
+    ``resident`` places the page images in device memory instead.  The
+    returned structure holds (copies of) the six psi_matrix values and keeps
+    the Python objects that own their buffers alive."""
+    mats = {n: pinned_matrix(w[n], w["b" + n[1]], PSI_SPLIT_ROWS, group_cols) for n in ("Wq", "Wk", "Wv")}
+    mats["Wo"] = pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_COLS, group_cols)
+    mats["U"] = pinned_matrix(w["U"], w["a"], PSI_SPLIT_ROWS, hidden_tile)
+    mats["V"] = pinned_matrix(w["V"], w["b"], PSI_SPLIT_COLS, hidden_tile)
     if resident:
-        keep = [resident_matrix(m) for m in keep]
-        for name, m in zip(("Wq", "Wk", "Wv", "Wo", "U", "V"), keep):
-            setattr(bw, name, m)
-    bw._keepalive = keep
+        mats = {n: resident_matrix(m) for n, m in mats.items()}
+    bw = psi_block_weights(mats["Wq"], mats["Wk"], mats["Wv"], mats["Wo"], mats["U"], mats["V"])
+    bw._keepalive = mats
     return bw

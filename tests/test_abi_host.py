@@ -55,15 +55,26 @@ def desc(arena_mib, page_mib, n_pages=2, ws_mib=0, flags=psi.PSI_ARENA_DRY_RUN):
 
 def test_arena_carve_paper_split():
     """[PSI] sec. IV-A / Fig. 1: 80 MiB = 8 + 8 pages + 8 workspace + 56
-    state/scratch; here the two 64 KiB bias side slots come out of the
-    56 MiB (they are the bounded metadata term of eq. (1))."""
+    state/scratch; here the two 64 KiB bias slots come out of the 56 MiB
+    (they are the bounded metadata term of eq. (1))."""
     L = psi.psi_arena_plan(desc(80, 8, 2, 8))
     assert L.page_off[0] == 0 and L.page_off[1] == 8 * MiB
-    assert L.side_off[0] == 16 * MiB and L.side_bytes == 64 * 1024
+    assert L.bias_off[0] == 16 * MiB and L.bias_off[1] == 16 * MiB + 64 * 1024
+    assert L.bias_slot_bytes == 64 * 1024
     assert L.workspace_off == 16 * MiB + 128 * 1024
     assert L.scratch_off == 24 * MiB + 128 * 1024
     assert L.scratch_bytes == 56 * MiB - 128 * 1024
     assert L.total_bytes == 80 * MiB
+
+
+def test_arena_three_pages_same_footprint():
+    """The 8 MiB workspace reassigned to a third page slot keeps the 80 MiB
+    arena and the scratch size of the two-page carve."""
+    L2 = psi.psi_arena_plan(desc(80, 8, 2, 8))
+    L3 = psi.psi_arena_plan(desc(80, 8, 3, 0))
+    assert L3.page_off[2] == 16 * MiB and L3.bias_off[0] == 24 * MiB
+    assert L3.scratch_bytes == L2.scratch_bytes
+    assert L3.total_bytes == 80 * MiB
 
 
 def test_arena_too_small():

@@ -1,0 +1,115 @@
+"""GPU tests of the block operator and a small stack of blocks.
+
+Parity on identical inputs: every block's input is the GPU's own (journaled)
+output of the previous block, so each block is compared with the oracle on
+exactly the bytes it consumed, as the paper's same-input probes do
+([PSI] sec. IV-B).  Scheduling controls ([PSI] sec. IV-C, Table V): copies on
+the compute stream, 2 vs 3 pages, and the ring journal all give
+bitwise-identical saved states; two invocations on the same input are
+bitwise identical.
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bounded_weight_amd import synth
+from tests.gpu_util import MiB, assert_bf16_close, dev, host, make_arena
+
+pytestmark = pytest.mark.gpu
+
+D, HEADS, HID, M = 256, 2, 512, 160
+
+
+@pytest.fixture(scope="module")
+def P(psi_lib):
+    return psi_lib
+
+
+@pytest.fixture(scope="module")
+def stack():
+    """Three small blocks (d 256, 2 heads of 128, FFN 512) and an input."""
+    blocks = [synth.block_weights(5, b, D, HID) for b in range(3)]
+    x0 = synth.stack_input(5, M, D)
+    return blocks, x0
+
+
+def run_stack(P, blocks_host, x0, steps=1, n_pages=2, arena_flags=0, journal_flags=0,
+              group_heads=1, tile=256):
+    gw = group_heads * 128
+    bws = [P.block_weights(w, gw, tile) for w in blocks_host]
+    page = max(gw * D * 2, tile * D * 2)
+    scratch = 3 * M * gw * 2 + 2 * 64 * 1024 + M * tile * 2 + 64 * 1024
+    ar = make_arena(n_pages * page + 2 * 64 * 1024 + scratch, page, n_pages, 0, arena_flags)
+    j = P.psi_journal_create(1 * MiB, 2, steps * len(bws) * M * D * 2 + MiB, journal_flags)
+    s = torch.cuda.current_stream().cuda_stream
+    try:
+        xd0 = dev(x0)
+        x = torch.empty_like(xd0)
+        xt = torch.empty_like(xd0)
+        acc = torch.empty(M, D, dtype=torch.float32, device="cuda")
+        for st in range(steps):
+            P.psi_journal_fence(j, s)
+            x.copy_(xd0)
+            for b, bw in enumerate(bws):
+                P.psi_block_paged(ar, x, xt, M, HEADS, 128, bw, 2, acc, j, 0)
+                P.psi_journal_commit(j, P.key(st, b), x, M * D * 2, s)
+        P.psi_arena_sync(ar)
+        outs = []
+        for st in range(steps):
+            per = []
+            for b in range(len(bws)):
+                o = np.empty((M, D), np.uint16)
+                P.psi_journal_read(j, P.key(st, b), o, o.nbytes)
+                per.append(o)
+            outs.append(per)
+        return outs
+    finally:
+        P.psi_journal_destroy(j)
+        P.psi_arena_destroy(ar)
+
+
+def test_block_single_parity(P, stack):
+    blocks, x0 = stack
+    w = blocks[0]
+    bw = P.block_weights(w, 128, 256)
+    ar = make_arena(4 * MiB, 256 * 1024)
+    try:
+        x = dev(x0)
+        xt = torch.empty_like(x)
+        P.psi_block_paged(ar, x, xt, M, HEADS, 128, bw, 1, None, None, 0)
+        P.psi_arena_sync(ar)
+        assert_bf16_close(host(x), oracle.block(x0, w, HEADS, 128), what="block")
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def test_stack_parity_identical_inputs(P, stack):
+    blocks, x0 = stack
+    outs = run_stack(P, blocks, x0)[0]
+    inp = x0
+    for b, w in enumerate(blocks):
+        assert_bf16_close(outs[b], oracle.block(inp, w, HEADS, 128), what=f"block {b}")
+        inp = outs[b]
+
+
+def test_stack_invocations_and_controls_bitwise(P, stack):
+    blocks, x0 = stack
+    ref = run_stack(P, blocks, x0, steps=2)
+    for b in range(3):
+        assert np.array_equal(ref[0][b], ref[1][b])
+    variants = {
+        "sync copies": dict(arena_flags=P.PSI_ARENA_SYNC_COPY),
+        "3 pages": dict(n_pages=3),
+        "ring journal": dict(journal_flags=P.PSI_JOURNAL_RING),
+        "sync journal": dict(journal_flags=P.PSI_JOURNAL_SYNC),
+        "2-head groups": dict(group_heads=2),
+        "hidden tile 128": dict(tile=128),
+    }
+    for name, kw in variants.items():
+        got = run_stack(P, blocks, x0, **kw)[0]
+        for b in range(3):
+            assert np.array_equal(got[b], ref[0][b]), f"{name}: block {b} differs"

@@ -126,7 +126,7 @@ def test_linear_sync_copy_and_one_page_bitwise(P):
     ref = run_linear(P, c["x"], c["W"], c["b"], P.PSI_SPLIT_ROWS, 128)
     m = P.pinned_matrix(c["W"], c["b"], P.PSI_SPLIT_ROWS, 128)
     for n_pages, fl in ((2, P.PSI_ARENA_SYNC_COPY), (1, 0), (3, 0)):
-        a = make_arena(n_pages * (128 * KiB + 64 * KiB), 128 * KiB, n_pages, 0, fl)
+        a = make_arena(n_pages * 128 * KiB + 2 * 64 * KiB, 128 * KiB, n_pages, 0, fl)
         try:
             y = empty_bf16(128, 512)
             P.psi_linear_paged(a, dev(c["x"]), 128, 512, m, None, y, 0)
@@ -392,3 +392,27 @@ def test_attention_bf16_softmax_variant(P):
     e32 = np.linalg.norm(f(y32) - f(yr)) / np.linalg.norm(f(yr))
     e16 = np.linalg.norm(f(y16) - f(yr)) / np.linalg.norm(f(yr))
     assert e32 < e16
+
+
+# ---------------------------------------------------------- arena reuse
+
+def test_operators_back_to_back_share_arena(P):
+    """Several operators in one arena, enqueued without host syncs: page
+    slots and the two bias slots are reused across operators in event order,
+    and every output matches its own oracle."""
+    cases = [synth.linear_case(seed=s, M=96, K=256, N=384) for s in (11, 12, 13)]
+    mats = [P.pinned_matrix(c["W"], c["b"], P.PSI_SPLIT_ROWS, 128) for c in cases]
+    ar = make_arena(2 * 64 * KiB + 2 * 64 * KiB + 64 * KiB, 64 * KiB)
+    try:
+        ys = []
+        for c, m in zip(cases, mats):
+            y = empty_bf16(96, 384)
+            P.psi_linear_paged(ar, dev(c["x"]), 96, 256, m, None, y, 0)
+            ys.append(y)
+        P.psi_arena_sync(ar)
+        for c, y in zip(cases, ys):
+            assert_bf16_close(host(y), oracle.linear(c["x"], c["W"], c["b"]))
+        s = P.psi_arena_stats(ar)
+        assert s.page_copies == 9
+    finally:
+        P.psi_arena_destroy(ar)
