@@ -169,6 +169,22 @@ def build_workload(args, torch, psi, synth):
     raise ValueError(args.workload)
 
 
+def committed_traffic(kernel_source, profile):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None when the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    try:
+        src = open(os.path.join(ROOT, kernel_source), "rb").read()
+        fields = dict(l.split(": ", 1) for l in open(os.path.join(ROOT, profile)).read().splitlines()
+                      if ": " in l and l.split(": ", 1)[0] in ("source_sha256", "traffic_bytes_per_launch"))
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(seed, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the default workload:
     the FFN sub-block of block 0 (Linear 4096->16384, GELU, Linear
@@ -210,7 +226,10 @@ def main():
     ap.add_argument("--no-journal", action="store_true")
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pages", type=int, default=2, help="page slots in the 80 MiB arena (2 or 3)")
+    ap.add_argument("--pages", type=int, default=3,
+                    help="page slots in the 80 MiB arena: 2 (+8 MiB workspace) or 3 (no workspace)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -225,6 +244,16 @@ def main():
     from memory_bounded_weight_amd import psi, synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: reads 512 MiB, writes 512 MiB
+        a = torch.ones(512 * MiB, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 512 * MiB,
+                          "bytes_written": 512 * MiB, "launches": 3}))
+        return
     h2d_gbps = measure_h2d_gbps(torch)
     log(f"bench: pinned H2D {h2d_gbps:.1f} GB/s")
     wl = build_workload(args, torch, psi, synth)
@@ -274,9 +303,14 @@ def main():
         name, ms, n, fl = max(kinds, key=lambda k: k[1])
         if n:
             achieved = fl / (ms * 1e-3) / 1e12
+            traffic = None
+            if name == "gemm" and args.workload == "stack8" and not args.resident:
+                traffic = committed_traffic("memory_bounded_weight_amd/csrc/psi_gemm.hip",
+                                            "profiles/gemm_traffic_stack8.md")
             roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": traffic,
                         "launches": n, "avg_launch_us": round(ms * 1e3 / n, 2),
                         "flops_per_launch": fl / n}
         other = [k for k in kinds if k[0] != name and k[2]]

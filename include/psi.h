@@ -205,6 +205,19 @@ psi_status psi_arena_reset_stats(psi_arena* a);
 /* Device address of the arena base (for footprint checks). */
 psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_out);
 
+/* Stage probes ([PSI] sec. III-C and sec. IV-B compare stage tensors of a
+ * block on identical inputs).  With a journal attached, every following
+ * operator also commits its intermediate BF16 stage tensors under
+ * key (step, block, branch = head group or hidden tile, role):
+ *   PSI_ROLE_ATTN_O   attention output O_g of head group g, [M, group cols]
+ *   PSI_ROLE_FFN_H    FFN hidden tile H_J (after GELU), [M, tile]
+ * and the compute stream waits for each copy before the scratch holding
+ * the tensor is reused (probes cost time; they are a diagnostic).  Pass
+ * NULL to detach.  Errors: PSI_E_INVALID. */
+#define PSI_ROLE_ATTN_O 16
+#define PSI_ROLE_FFN_H 17
+psi_status psi_arena_set_probe(psi_arena* a, psi_journal* j, int32_t step, int32_t block);
+
 /* ------------------------------------------------------------ page API */
 
 /* Slice request ([PSI] sec. II-D): take the next page slot in round-robin

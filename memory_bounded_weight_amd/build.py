@@ -23,6 +23,28 @@ HIPCC_FLAGS = [
 ]
 
 
+def hip_runtime_dir():
+    """Directory of the HIP runtime the library must share with its caller.
+
+    PyTorch-ROCm ships its own libamdhip64.so; a process must not hold two
+    HIP runtimes (their streams would not be ordered with each other), so the
+    library links against torch's copy when torch is installed, else the
+    system ROCm one.  PSI_HIP_RUNTIME_DIR overrides."""
+    d = os.environ.get("PSI_HIP_RUNTIME_DIR")
+    if d:
+        return d
+    try:
+        import importlib.util
+        spec = importlib.util.find_spec("torch")
+        if spec and spec.origin:
+            lib = os.path.join(os.path.dirname(spec.origin), "lib")
+            if os.path.exists(os.path.join(lib, "libamdhip64.so")):
+                return lib
+    except Exception:
+        pass
+    return "/opt/rocm/lib"
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -45,7 +67,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             _wait(procs.pop(0), verbose)
     for p in procs:
         _wait(p, verbose)
-    link = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", LIB + ".tmp", *objs]
+    rt = hip_runtime_dir()
+    clangxx = os.environ.get("PSI_CLANGXX", "/opt/rocm/llvm/bin/clang++")
+    # plain host link (no implicit --hip-link, which would add the system
+    # runtime): the device code is already embedded in the objects
+    link = [clangxx, "-shared", "-fPIC", "-o", LIB + ".tmp", *objs,
+            "-L" + rt, "-l:libamdhip64.so", "-Wl,-rpath," + rt, "-Wl,--no-undefined"]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

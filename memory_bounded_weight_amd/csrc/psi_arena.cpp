@@ -17,6 +17,14 @@
 
 namespace psi {
 
+psi_status probe_commit(psi_arena* a, int32_t branch, int32_t role, const void* dev, size_t bytes) {
+  if (!a->probe || a->dry) return PSI_OK;
+  psi_key k{a->probe_step, a->probe_block, branch, role};
+  psi_status st = psi_journal_commit(a->probe, k, dev, bytes, a->compute);
+  if (st) return st;
+  return psi_journal_fence(a->probe, a->compute);
+}
+
 psi_status check_pinned(const void* p, const char* what) {
   if (!p) return PSI_OK;
   hipPointerAttribute_t attr;
@@ -371,6 +379,14 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
   if (!a) return fail(PSI_E_INVALID, "null arena");
   if (base_out) *base_out = a->base;
   if (bytes_out) *bytes_out = a->desc.arena_bytes;
+  return PSI_OK;
+}
+
+psi_status psi_arena_set_probe(psi_arena* a, psi_journal* j, int32_t step, int32_t block) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  a->probe = j;
+  a->probe_step = step;
+  a->probe_block = block;
   return PSI_OK;
 }
 

@@ -220,6 +220,189 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     }
 }
 
+// Deep-prefetch variant: K tiles are fetched two iterations ahead into two
+// register stages (the loop is unrolled by two so stage indices are
+// compile-time), loads are branch-free (rows past M or N are clamped to
+// the last row: they only feed outputs that are never stored; the K tail
+// is zeroed with a select), and LDS is double-buffered.
+template <int BM, int BN, int BK>
+__global__ __launch_bounds__(kThreads) void gemm_kernel_pf(GemmArgs p, int tiles_m, int tiles_n) {
+  using T = Tile<BM, BN, BK>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+
+  const int nt = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
+  const int tm = t / tiles_n;
+  const int tn = t % tiles_n;
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  constexpr int CPR = BK / 8;
+  // per-thread chunk coordinates (row within the tile, k offset)
+  const uint16_t* pa[T::A_PER_T];
+  const uint16_t* pb[T::B_PER_T];
+  int ka[T::A_PER_T], kb[T::B_PER_T];
+#pragma unroll
+  for (int i = 0; i < T::A_PER_T; ++i) {
+    int c = tid + i * kThreads;
+    int r = m0 + c / CPR;
+    r = r < p.M ? r : p.M - 1;
+    ka[i] = (c % CPR) * 8;
+    pa[i] = p.A + (long)r * p.lda;
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_PER_T; ++i) {
+    int c = tid + i * kThreads;
+    int r = n0 + c / CPR;
+    r = r < p.N ? r : p.N - 1;
+    kb[i] = (c % CPR) * 8;
+    pb[i] = p.B + (long)r * p.ldb;
+  }
+  uint4 ra[2][T::A_PER_T], rb[2][T::B_PER_T];
+
+  auto load = [&](int k0, uint4* xa, uint4* xb) {
+#pragma unroll
+    for (int i = 0; i < T::A_PER_T; ++i) {
+      const int gk = k0 + ka[i];
+      const bool ok = gk < p.K;
+      uint4 v = *reinterpret_cast<const uint4*>(pa[i] + (ok ? gk : 0));
+      xa[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_T; ++i) {
+      const int gk = k0 + kb[i];
+      const bool ok = gk < p.K;
+      uint4 v = *reinterpret_cast<const uint4*>(pb[i] + (ok ? gk : 0));
+      xb[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf, const uint4* xa, const uint4* xb) {
+    uint16_t* sa = smem + buf * T::STAGE;
+    uint16_t* sb = sa + BM * T::LDS;
+#pragma unroll
+    for (int i = 0; i < T::A_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(sa + (c / CPR) * T::LDS + (c % CPR) * 8) = xa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_PER_T; ++i) {
+      int c = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(sb + (c / CPR) * T::LDS + (c % CPR) * 8) = xb[i];
+    }
+  };
+
+  f32x16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (p.acc_in) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const int gn = n0 + wn * T::WN + j * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          if (gm < p.M && gn < p.N) acc[i][j][r] = p.acc_in[(long)gm * p.ld_acc_in + gn];
+        }
+      }
+  }
+
+  auto compute = [&](int buf) {
+    const uint16_t* sa = smem + buf * T::STAGE + (wm * T::WM) * T::LDS;
+    const uint16_t* sb = smem + buf * T::STAGE + BM * T::LDS + (wn * T::WN) * T::LDS;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kofs = ks * 16 + half * 8;
+      bf16x8 af[T::TM], bfr[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + (i * 32 + l32) * T::LDS + kofs);
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (j * 32 + l32) * T::LDS + kofs);
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (p.K + BK - 1) / BK;
+  // prologue: tile 0 in LDS buffer 0, tile 1 in register stage 1
+  load(0, ra[0], rb[0]);
+  store(0, ra[0], rb[0]);
+  if (nk > 1) load(BK, ra[1], rb[1]);
+  __syncthreads();
+
+  // iteration kt: issue tile kt+2 into register stage kt&1, compute tile kt
+  // from LDS buffer kt&1, then move tile kt+1 (register stage (kt+1)&1) into
+  // LDS buffer (kt+1)&1.
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) load((kt + 2) * BK, ra[0], rb[0]);
+    compute(0);
+    if (kt + 1 < nk) store(1, ra[1], rb[1]);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) load((kt + 3) * BK, ra[1], rb[1]);
+    compute(1);
+    if (kt + 2 < nk) store(0, ra[0], rb[0]);
+    __syncthreads();
+  }
+
+  // Epilogue.
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int gn = n0 + wn * T::WN + j * 32 + l32;
+      if (gn >= p.N) continue;
+      const float bn = (p.bias && !p.bias_on_m) ? bf2f(p.bias[gn]) : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        if (gm >= p.M) continue;
+        const float v = acc[i][j][r];
+        if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
+        if (p.out) {
+          float t;
+          if (p.bias) {
+            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
+            t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
+          } else {
+            t = v;
+          }
+          uint16_t y = f2bf(t);
+          if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
+          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
+          p.out[(long)gm * p.ldo + gn] = y;
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int BK>
+hipError_t launch_pf(const GemmArgs& a, hipStream_t s) {
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_kernel_pf<BM, BN, BK>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int STAGES>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
@@ -235,6 +418,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 // same ascending sequence of k16 MFMA steps whatever the tile).
 //   1: 256x256, 2: 256x128, 3: 128x256, 4: 128x128 (double-buffered LDS)
 //   5: 256x128, 6: 128x256 with one LDS stage (two workgroups per CU)
+//   7: 128x128 (BK 64), 8: 128x128 (BK 32), 9: 256x128 (BK 32), 10: 128x256
+//      (BK 32): two register stages, tiles fetched two iterations ahead
 // Measured on MI355X: the 128x128 tile, at two waves per SIMD (two
 // workgroups per CU), is the fastest on every page shape of this path;
 // the single-wave large tiles are latency-bound.
@@ -253,6 +438,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     case 3: return launch_cfg<128, 256, 64, 2>(a, s);
     case 5: return launch_cfg<256, 128, 64, 1>(a, s);
     case 6: return launch_cfg<128, 256, 64, 1>(a, s);
+    case 7: return launch_pf<128, 128, 64>(a, s);
+    case 8: return launch_pf<128, 128, 32>(a, s);
+    case 9: return launch_pf<256, 128, 32>(a, s);
+    case 10: return launch_pf<128, 256, 32>(a, s);
     default: return launch_cfg<128, 128, 64, 2>(a, s);
   }
 }

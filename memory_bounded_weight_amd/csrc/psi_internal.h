@@ -117,6 +117,9 @@ struct psi_arena {
   // scratch stack (offsets relative to layout.scratch_off)
   size_t scratch_top = 0;
   psi_stats stats{};
+  // stage probes
+  psi_journal* probe = nullptr;
+  int32_t probe_step = 0, probe_block = 0;
   // profiling
   std::vector<psi_timed> pending;
   std::vector<hipEvent_t> event_pool;
@@ -151,4 +154,9 @@ psi_status run_gemm(psi_arena* a, const GemmArgs& g);
 psi_status run_attention(psi_arena* a, const AttnArgs& g);
 
 psi_status check_pinned(const void* p, const char* what);
+
+// Stage probe: journal a device tensor of the current operator (no-op when
+// no probe journal is attached) and make the compute stream wait for the
+// copy before the buffer is reused.
+psi_status probe_commit(psi_arena* a, int32_t branch, int32_t role, const void* dev, size_t bytes);
 }  // namespace psi

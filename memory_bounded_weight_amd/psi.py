@@ -22,6 +22,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"HIP library {LIB_PATH} is not built; run "
                       "`python -m memory_bounded_weight_amd.build` (or __graft_entry__.build())")
 
+try:  # bind to the process's HIP runtime (torch's) before loading the library
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
@@ -47,6 +52,9 @@ PSI_OP_BASELINE_BIAS = 0x1
 PSI_OP_RESIDUAL = 0x2
 PSI_OP_STORE_ACC = 0x4
 PSI_OP_BF16_SOFTMAX = 0x8
+
+PSI_ROLE_ATTN_O = 16
+PSI_ROLE_FFN_H = 17
 
 PSI_SPLIT_ROWS = 0
 PSI_SPLIT_COLS = 1
@@ -133,6 +141,7 @@ _sig("psi_arena_sync", [_vp])
 _sig("psi_arena_stats", [_vp, _P(psi_stats)])
 _sig("psi_arena_reset_stats", [_vp])
 _sig("psi_arena_device_base", [_vp, _P(_vp), _P(_sz)])
+_sig("psi_arena_set_probe", [_vp, _vp, ctypes.c_int32, ctypes.c_int32])
 _sig("psi_page_submit", [_vp, _vp, _sz, _P(_i)])
 _sig("psi_page_acquire", [_vp, _i, _P(_vp)])
 _sig("psi_page_release", [_vp, _i])
@@ -154,7 +163,7 @@ _sig("psi_journal_counters", [_vp, _P(ctypes.c_uint64), _P(ctypes.c_uint64), _P(
 EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_arena_plan",
            "psi_linear_plan", "psi_ffn_plan", "psi_attn_plan", "psi_last_error", "psi_version",
            "psi_arena_create", "psi_arena_destroy", "psi_arena_sync", "psi_arena_stats",
-           "psi_arena_reset_stats", "psi_arena_device_base", "psi_page_submit",
+           "psi_arena_reset_stats", "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
            "psi_attn_paged", "psi_block_paged", "psi_journal_create", "psi_journal_destroy",
            "psi_journal_commit", "psi_journal_reload", "psi_journal_fence", "psi_journal_sync",
@@ -281,6 +290,10 @@ def psi_arena_device_base(arena: int):
     b, n = _vp(), _sz()
     _check(_lib.psi_arena_device_base(arena, ctypes.byref(b), ctypes.byref(n)), "psi_arena_device_base")
     return b.value or 0, n.value
+
+
+def psi_arena_set_probe(arena: int, journal, step: int = 0, block: int = 0):
+    return _check(_lib.psi_arena_set_probe(arena, journal or None, step, block), "psi_arena_set_probe")
 
 
 def psi_page_submit(arena: int, host_pinned, nbytes: int) -> int:

@@ -257,3 +257,14 @@ def test_checkpoint_size_independence_dry_run():
             psi.psi_arena_destroy(a)
     assert peaks[0] == peaks[1] == peaks[2]
     assert streamed[1] == 2 * streamed[0] and streamed[2] == 4 * streamed[0]
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds to the HIP runtime of the process (torch's copy),
+    so torch's streams and the library's are one runtime's streams."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    hsa = {l.split()[-1] for l in maps if "libhsa-runtime64" in l}
+    assert len(hip) == 1, hip
+    assert len(hsa) <= 1, hsa

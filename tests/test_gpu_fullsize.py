@@ -1,0 +1,157 @@
+"""Parity at the full workload sizes, on sampled outputs the oracle computes
+one by one, in the launch configuration the benchmark times (80 MiB arena,
+8 MiB pages, 8-head groups, 1,024-channel FFN tiles).
+
+Rows of an FFN are independent, so sampled rows of x go through the
+oracle directly.  Attention rows depend on every key; the paged operator's
+stage probes journal each head group's output O_g, so the oracle checks
+(a) head 0 of O on sampled query rows against its own projections of that
+head, and (b) the output projection + residual on the GPU's O (identical
+inputs, as the paper's same-input probes do, [PSI] sec. IV-B).
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bounded_weight_amd import synth
+from tests.gpu_util import MiB, assert_bf16_close, dev, host, make_arena, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P(psi_lib):
+    return psi_lib
+
+
+def sample_rows(M, n, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=n - 2, replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows))
+
+
+def read_probe(P, j, role, branch, M, cols, step=0, block=0):
+    out = np.empty((M, cols), np.uint16)
+    P.psi_journal_read(j, P.key(step, block, branch, role), out, out.nbytes)
+    return out
+
+
+def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0):
+    """(a) head 0 on sampled rows against the oracle's own projections of
+    head 0; (b) output projection + residual on the journaled O."""
+    M, d = x_in.shape
+    O = np.concatenate([read_probe(P, j, P.PSI_ROLE_ATTN_O, g, M, gw, step) for g in range(d // gw)],
+                       axis=1)
+    src = x_in if ctx is None else ctx
+    h0 = slice(0, 128)
+    K0 = oracle.linear(src, np.ascontiguousarray(w["Wk"][h0]), w["bk"][h0].copy())
+    V0 = oracle.linear(src, np.ascontiguousarray(w["Wv"][h0]), w["bv"][h0].copy())
+    Q0 = oracle.linear(np.ascontiguousarray(x_in[rows]), np.ascontiguousarray(w["Wq"][h0]),
+                       w["bq"][h0].copy())
+    O0 = oracle.attention(Q0, K0, V0, 1, 128)
+    assert_bf16_close(O[rows][:, h0], O0, what="attention head 0")
+    ref = oracle.residual(x_in[rows], oracle.linear(np.ascontiguousarray(O[rows]), w["Wo"], w["bo"]))
+    assert_bf16_close(y[rows], ref, what="output projection + residual")
+
+
+def test_fullsize_block_8192_tokens(P):
+    """One block of the 8-block stack at full size (8,192 tokens, d 4,096,
+    32 heads, FFN 16,384) in the benchmark's 80 MiB / 8 MiB arena."""
+    M, d, heads, hid = 8192, 4096, 32, 16384
+    w = synth.block_weights(0, 0, d, hid)
+    x0 = synth.stack_input(0, M, d)
+    bw = P.block_weights(w, 1024, 1024)
+    s = torch.cuda.current_stream().cuda_stream
+    ar = make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
+    j = P.psi_journal_create(8 * MiB, 2, (4 + 16) * M * 1024 * 2 + MiB, 0)
+    try:
+        P.psi_arena_set_probe(ar, j, 0, 0)
+        x = dev(x0)
+        xt = torch.empty_like(x)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        P.psi_block_paged(ar, x, xt, M, heads, 128, bw, 1, acc, j, 0)
+        P.psi_arena_sync(ar)
+        P.psi_journal_sync(j)
+        y_attn, y = host(xt), host(x)
+        rows = sample_rows(M, 12)
+        check_attention(P, j, x0, y_attn, w, heads, 1024, rows)
+        # FFN on the GPU's own attention output (identical inputs), and its
+        # first hidden tile from the stage probe
+        xr = np.ascontiguousarray(y_attn[rows])
+        assert_bf16_close(y[rows], oracle.ffn(xr, w["U"], w["a"], w["V"], w["b"], residual=True),
+                          what="FFN sub-block")
+        H0 = read_probe(P, j, P.PSI_ROLE_FFN_H, 0, M, 1024)
+        pre = oracle.linear(xr, np.ascontiguousarray(w["U"][:1024]), w["a"][:1024].copy())
+        assert_bf16_close(H0[rows], oracle.gelu_bf16(pre), what="hidden tile 0")
+    finally:
+        P.psi_arena_set_probe(ar, None)
+        P.psi_journal_destroy(j)
+        P.psi_arena_destroy(ar)
+
+
+def test_fullsize_attention_self_and_cross(P):
+    """Attention sub-blocks at full size: 6,144 tokens self-attention, then
+    cross-attention to 1,024 conditioning tokens, 32 heads of 128, 8-head
+    groups, 80 MiB arena."""
+    M, Mc, d, heads = 6144, 1024, 4096, 32
+    c = synth.attn_case(0, M, Mc, d, cross=True)
+    s = torch.cuda.current_stream().cuda_stream
+    ar = make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
+    j = P.psi_journal_create(8 * MiB, 2, 2 * 4 * M * 1024 * 2 + MiB, 0)
+    try:
+        x = dev(c["x"])
+        ctx = dev(c["ctx"])
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        mats = {}
+        for part in ("self", "cross"):
+            w = c[part]
+            mats[part] = [P.pinned_matrix(w["W" + n], w["b" + n], P.PSI_SPLIT_ROWS, 1024) for n in "qkv"] + \
+                         [P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, 1024)]
+        P.psi_arena_set_probe(ar, j, 0, 0)
+        y1 = torch.empty_like(x)
+        P.psi_attn_paged(ar, x, M, None, 0, heads, 128, *mats["self"], acc, y1, P.PSI_OP_RESIDUAL)
+        P.psi_arena_set_probe(ar, j, 1, 0)
+        y2 = torch.empty_like(x)
+        P.psi_attn_paged(ar, y1, M, ctx, Mc, heads, 128, *mats["cross"], acc, y2, P.PSI_OP_RESIDUAL)
+        P.psi_arena_sync(ar)
+        P.psi_journal_sync(j)
+        rows = sample_rows(M, 12, seed=1)
+        y1h, y2h = host(y1), host(y2)
+        check_attention(P, j, c["x"], y1h, c["self"], heads, 1024, rows, step=0)
+        check_attention(P, j, y1h, y2h, c["cross"], heads, 1024, rows, ctx=c["ctx"], step=1)
+    finally:
+        P.psi_arena_set_probe(ar, None)
+        P.psi_journal_destroy(j)
+        P.psi_arena_destroy(ar)
+
+
+@pytest.mark.parametrize("cfg", ["d2048", "d4096"])
+def test_fullsize_ffn(P, cfg):
+    """FFN at d 2,048 / 8,192 hidden / 1,024 tokens in a 32 MiB arena with the
+    fp32 accumulator in the arena, and at d 4,096 / 16,384 / 4,096 tokens in
+    4 token chunks in an 80 MiB arena, on sampled rows."""
+    if cfg == "d2048":
+        M, d, hid, tile, chunks, arena, ws, ext = 1024, 2048, 8192, 2048, 1, 32, 0, False
+    else:
+        M, d, hid, tile, chunks, arena, ws, ext = 4096, 4096, 16384, 1024, 4, 80, 8, True
+    c = synth.ffn_case(0, M, d, hid)
+    U = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, tile)
+    V = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, tile)
+    ar = make_arena(arena * MiB, 8 * MiB, 2, ws * MiB)
+    try:
+        x = dev(c["x"])
+        y = torch.empty_like(x)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda") if ext else None
+        P.psi_ffn_paged(ar, x, M, d, U, V, chunks, acc, y, 0)
+        P.psi_arena_sync(ar)
+        s = P.psi_arena_stats(ar)
+        assert s.page_copies == 2 * hid // tile  # every page streamed exactly once
+        rows = sample_rows(M, 10, seed=2)
+        yr = oracle.ffn(np.ascontiguousarray(c["x"][rows]), c["U"], c["a"], c["V"], c["b"])
+        assert_bf16_close(host(y)[rows], yr, what=f"FFN {cfg}")
+    finally:
+        P.psi_arena_destroy(ar)
