@@ -124,7 +124,7 @@ typedef struct psi_stats {
   double attn_ms;
   uint64_t attn_launches;
   double attn_flops;        /* algorithmic 4*Mq*Mk*dh per head of the timed launches */
-  double copy_ms;           /* summed page-copy time on the copy stream */
+  double copy_ms;           /* busy time of the busier of the two page-copy streams */
   uint64_t copy_bytes_timed;
 } psi_stats;
 

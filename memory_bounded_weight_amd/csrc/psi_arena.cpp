@@ -83,24 +83,41 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
   }
   if (!a->dry) {
     const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
-    hipStream_t cs = sync ? a->compute : a->copy;
-    if (!sync && slot.released_once) {
-      PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
-      a->stats.event_waits++;
+    if (sync) {
+      PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, a->compute));
+      PSI_HIP(hipEventRecord(slot.ready, a->compute));
+    } else {
+      // Two halves on two copy streams: each DMA engine pays the per-copy
+      // start-up once while the other one streams, so back-to-back 8 MiB
+      // pages keep the host link near its bulk rate.
+      const size_t h0 = bytes > (1u << 20) ? (bytes / 2 + 255) / 256 * 256 : bytes;
+      hipStream_t cs[2] = {a->copy, a->copy1};
+      const size_t off[2] = {0, h0};
+      const size_t len[2] = {h0, bytes - h0};
+      for (int i = 0; i < 2; ++i) {
+        if (len[i] == 0) continue;
+        if (slot.released_once) {
+          PSI_HIP(hipStreamWaitEvent(cs[i], slot.release, 0));
+          a->stats.event_waits++;
+        }
+        hipEvent_t t0 = nullptr, t1 = nullptr;
+        if (a->desc.flags & PSI_ARENA_PROFILE) {
+          t0 = pool_event(a);
+          t1 = pool_event(a);
+          if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
+          PSI_HIP(hipEventRecord(t0, cs[i]));
+        }
+        PSI_HIP(hipMemcpyAsync(static_cast<char*>(slot.dev) + off[i], static_cast<const char*>(host) + off[i],
+                               len[i], hipMemcpyHostToDevice, cs[i]));
+        if (t0) {
+          PSI_HIP(hipEventRecord(t1, cs[i]));
+          a->pending.push_back({t0, t1, 2 + i, (double)len[i]});
+        }
+      }
+      PSI_HIP(hipEventRecord(slot.ready, cs[0]));
+      if (len[1]) PSI_HIP(hipEventRecord(slot.ready1, cs[1]));
+      slot.split = len[1] != 0;
     }
-    hipEvent_t t0 = nullptr, t1 = nullptr;
-    if (a->desc.flags & PSI_ARENA_PROFILE) {
-      t0 = pool_event(a);
-      t1 = pool_event(a);
-      if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
-      PSI_HIP(hipEventRecord(t0, cs));
-    }
-    PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, cs));
-    if (t0) {
-      PSI_HIP(hipEventRecord(t1, cs));
-      a->pending.push_back({t0, t1, 2, (double)bytes});
-    }
-    PSI_HIP(hipEventRecord(slot.ready, cs));
   }
   slot.state = psi_page_slot::FILLING;
   a->stats.bytes_h2d += bytes;
@@ -182,6 +199,10 @@ psi_status page_acquire(psi_arena* a, int page) {
   if (!a->dry && !(a->desc.flags & PSI_ARENA_SYNC_COPY)) {
     PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready, 0));
     a->stats.event_waits++;
+    if (slot.split) {
+      PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready1, 0));
+      a->stats.event_waits++;
+    }
   }
   slot.state = psi_page_slot::CONSUMING;
   return PSI_OK;
@@ -242,8 +263,9 @@ psi_status run_attention(psi_arena* a, const AttnArgs& g) {
 static psi_status harvest(psi_arena* a) {
   if (a->dry) return PSI_OK;
   PSI_HIP(hipStreamSynchronize(a->copy));
+  PSI_HIP(hipStreamSynchronize(a->copy1));
   PSI_HIP(hipStreamSynchronize(a->compute));
-  a->stats.host_syncs += 2;
+  a->stats.host_syncs += 3;
   for (const psi_timed& t : a->pending) {
     float ms = 0.0f;
     PSI_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
@@ -256,7 +278,9 @@ static psi_status harvest(psi_arena* a) {
       a->stats.attn_launches++;
       a->stats.attn_flops += t.work;
     } else {
-      a->stats.copy_ms += ms;
+      // copy_ms = busy time of the busier copy stream
+      a->copy_ms_stream[t.kind - 2] += ms;
+      a->stats.copy_ms = a->copy_ms_stream[0] > a->copy_ms_stream[1] ? a->copy_ms_stream[0] : a->copy_ms_stream[1];
       a->stats.copy_bytes_timed += (uint64_t)t.work;
     }
     a->event_pool.push_back(t.start);
@@ -290,8 +314,10 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
     hipError_t e = hipGetDevice(&a->device);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&a->base), d->arena_bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy1, hipStreamNonBlocking);
     for (int i = 0; e == hipSuccess && i < d->n_pages; ++i) {
       e = hipEventCreateWithFlags(&a->slots[i].ready, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].ready1, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].release, hipEventDisableTiming);
       a->slots[i].dev = a->base + L.page_off[i];
     }
@@ -315,6 +341,7 @@ psi_status psi_arena_destroy(psi_arena* a) {
   psi_status st = PSI_OK;
   if (!a->dry) {
     if (a->copy) (void)hipStreamSynchronize(a->copy);
+    if (a->copy1) (void)hipStreamSynchronize(a->copy1);
     (void)hipStreamSynchronize(a->compute);
     for (psi_timed& t : a->pending) {
       a->event_pool.push_back(t.start);
@@ -323,6 +350,7 @@ psi_status psi_arena_destroy(psi_arena* a) {
     for (hipEvent_t e : a->event_pool) (void)hipEventDestroy(e);
     for (int i = 0; i < a->desc.n_pages; ++i) {
       if (a->slots[i].ready) (void)hipEventDestroy(a->slots[i].ready);
+      if (a->slots[i].ready1) (void)hipEventDestroy(a->slots[i].ready1);
       if (a->slots[i].release) (void)hipEventDestroy(a->slots[i].release);
     }
     for (int i = 0; i < 2; ++i) {
@@ -330,6 +358,7 @@ psi_status psi_arena_destroy(psi_arena* a) {
       if (a->bias_slots[i].release) (void)hipEventDestroy(a->bias_slots[i].release);
     }
     if (a->copy) (void)hipStreamDestroy(a->copy);
+    if (a->copy1) (void)hipStreamDestroy(a->copy1);
     if (a->base) {
       hipError_t e = hipFree(a->base);
       if (e != hipSuccess) st = hip_fail(e, "hipFree(arena)");
@@ -343,8 +372,9 @@ psi_status psi_arena_sync(psi_arena* a) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
   if (a->dry) return PSI_OK;
   PSI_HIP(hipStreamSynchronize(a->copy));
+  PSI_HIP(hipStreamSynchronize(a->copy1));
   PSI_HIP(hipStreamSynchronize(a->compute));
-  a->stats.host_syncs += 2;
+  a->stats.host_syncs += 3;
   return PSI_OK;
 }
 
@@ -372,6 +402,7 @@ psi_status psi_arena_reset_stats(psi_arena* a) {
   s.scratch_bytes = a->stats.scratch_bytes;
   s.scratch_high_water = a->scratch_top;
   a->stats = s;
+  a->copy_ms_stream[0] = a->copy_ms_stream[1] = 0.0;
   return PSI_OK;
 }
 

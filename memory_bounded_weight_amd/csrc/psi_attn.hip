@@ -10,8 +10,8 @@
 // noncausal, no dropout, at least one key).
 //
 // Layout of the work (head_dim 128, 64 keys per tile):
-//   * one workgroup = 4 waves = 128 queries of one head; each wave owns 32
-//     queries;
+//   * one workgroup = 4 or 8 waves = 128 or 256 queries of one head; each
+//     wave owns 32 queries;
 //   * scores are computed transposed, S^T = K Q^T, with the 32x32x16 BF16
 //     MFMA: in its accumulator layout a lane holds ONE query (column) and
 //     16 keys, so m, l and the rescale factor of a query live in one lane
@@ -45,14 +45,18 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
 
 constexpr int DH = 128;       // head dimension
 constexpr int KT = 64;        // keys per tile
-constexpr int QB = 128;       // queries per workgroup
 constexpr int KS = DH + 8;    // K tile row stride in LDS (elements): 272 B
 constexpr int VS = KT + 4;    // V^T tile row stride in LDS (elements): 136 B
-constexpr int kThreads = 256;
 
-// Two waves per SIMD (<= 256 registers each): while one wave runs its
-// softmax arithmetic the other keeps the matrix cores busy.
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
+// One workgroup = QB/32 waves = QB queries of one head.  Two waves per SIMD
+// (<= 256 registers each): while one wave runs its softmax arithmetic the
+// other keeps the matrix cores busy.  BF16P selects the BF16-numerator
+// variant (one MFMA per P.V step instead of hi + lo).
+template <int QB, bool BF16P>
+__global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
+  constexpr int NT = QB * 2;  // threads
+  constexpr int KCH = KT * DH / 8 / NT;  // 16-byte K chunks per thread and tile
+  constexpr int VCH = DH * KT / 8 / NT;  // 16-byte V^T chunks per thread and tile
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DH * VS];
 
@@ -67,53 +71,62 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   // scores in exp2 units: s * log2(e) = dot * (alpha * log2(e))
   const float c = p.alpha * 1.4426950408889634f;
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][kk*16 + half*8 + 0..7].
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][kk*16 + half*8 + 0..7]
+  // (rows past Mq read the last row; their outputs are not stored).
   bf16x8 qf[DH / 16];
   {
-    const uint16_t* qp = p.q + (long)qrow * p.ldq + h * DH + half * 8;
+    const int qr = qvalid ? qrow : p.Mq - 1;
+    const uint16_t* qp = p.q + (long)qr * p.ldq + h * DH + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < DH / 16; ++kk) {
-      u16x8 v = qvalid ? *reinterpret_cast<const u16x8*>(qp + kk * 16) : (u16x8)0;
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int kk = 0; kk < DH / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + kk * 16));
   }
 
   // Global -> register staging of one key tile: K rows (keys) and V^T rows
-  // (channels of this head), 16-byte chunks, 4 of each per thread.
-  uint4 rk[4], rv[4];
+  // (channels of this head), 16-byte chunks.  In full tiles every load is
+  // in range; the last (ragged) tile clamps K rows (their scores are masked)
+  // and zeroes V^T entries past the last key (their weights are 0 and the
+  // padding of V^T is not initialised).
+  uint4 rk[KCH], rv[VCH];
   const uint16_t* kbase = p.k + h * DH;
   const uint16_t* vbase = p.vt + (long)h * DH * p.ldvt;
-  auto load_tile = [&](int key0) {
+  auto load_tile = [&](int key0, bool ragged) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c2 = tid + i * kThreads;           // 0..1023
-      int r = c2 >> 4, col = (c2 & 15) * 8;  // K tile: 64 rows x 16 chunks
-      int key = key0 + r;
-      rk[i] = key < p.Mk ? *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + col)
-                         : make_uint4(0, 0, 0, 0);
-      int vr = c2 >> 3, vcol = (c2 & 7) * 8;  // V^T tile: 128 rows x 8 chunks
-      int vkey = key0 + vcol;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (vkey < p.Mk) {
-        v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
-        if (vkey + 8 > p.Mk) {  // ragged key tail inside the chunk: zero the rest
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = tid + i * NT;
+      int key = key0 + (c2 >> 4);
+      if (ragged) key = key < p.Mk ? key : p.Mk - 1;
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 & 15) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = tid + i * NT;
+      int vr = c2 >> 3, vkey = key0 + (c2 & 7) * 8;
+      if (!ragged) {
+        rv[i] = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+      } else {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (vkey < p.Mk) {
+          v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
           uint16_t* e = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
           for (int t = 0; t < 8; ++t)
             if (vkey + t >= p.Mk) e[t] = 0;
         }
+        rv[i] = v;
       }
-      rv[i] = v;
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c2 = tid + i * kThreads;
-      int r = c2 >> 4, col = (c2 & 15) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[buf][r * KS + col]) = rk[i];
-      int vr = c2 >> 3, vcol = (c2 & 7) * 8;
-      uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][vr * VS + vcol]);  // 8-byte aligned rows
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = tid + i * NT;
+      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 >> 4) * KS + (c2 & 15) * 8]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = tid + i * NT;
+      uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][(c2 >> 3) * VS + (c2 & 7) * 8]);  // 8-byte aligned rows
       dst[0] = make_uint2(rv[i].x, rv[i].y);
       dst[1] = make_uint2(rv[i].z, rv[i].w);
     }
@@ -128,16 +141,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
 
-  const int ntiles = (p.Mk + KT - 1) / KT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int key0 = t * KT;
-    if (t + 1 < ntiles) load_tile(key0 + KT);
-
+  // one key tile: scores, online-softmax update, P.V
+  auto tile = [&](int cur, int key0, bool ragged) {
     // S^T for 64 keys x this wave's 32 queries: two 32x32 accumulator tiles.
     f32x16 s[2];
 #pragma unroll
@@ -150,20 +155,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
-    // mask the key tail; tile maximum of this query (max commutes with the
-    // positive scale, so it is taken on the raw dot products)
+    if (ragged) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= p.Mk) s[kb][r] = -INFINITY;
+    }
+    // tile maximum of this query (max commutes with the positive scale, so
+    // it is taken on the raw dot products)
     float mt = -INFINITY;
-    const bool tail = key0 + KT > p.Mk;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (tail) {
-          int key = key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          if (key >= p.Mk) s[kb][r] = -INFINITY;
-        }
-        mt = fmaxf(mt, s[kb][r]);
-      }
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
     const float mc = m_new * c;
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
       }
     lsum += __shfl_xor(lsum, 32);
     // rescale only when some query's maximum moved (eta = 1 exactly otherwise)
-    const float eta = __builtin_amdgcn_exp2f(m_run * c - mc);
     if (__any(m_new != m_run)) {
+      const float eta = __builtin_amdgcn_exp2f(m_run * c - mc);
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
@@ -200,29 +205,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
       for (int j = 0; j < 8; j += 2) {
         f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
         bf16x2 hi = __builtin_convertvector(pv, bf16x2);  // round to nearest even
-        f32x2 hf = __builtin_convertvector(hi, f32x2);
-        f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};      // exact
-        bf16x2 lo = __builtin_convertvector(rem, bf16x2);
         bhi[j] = hi[0];
         bhi[j + 1] = hi[1];
-        blo[j] = lo[0];
-        blo[j + 1] = lo[1];
+        if (!BF16P) {
+          f32x2 hf = __builtin_convertvector(hi, f32x2);
+          f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};  // exact
+          bf16x2 lo = __builtin_convertvector(rem, bf16x2);
+          blo[j] = lo[0];
+          blo[j + 1] = lo[1];
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
         const uint16_t* vr = &v_lds[cur][(dt * 32 + l32) * VS + 16 * g + 4 * half];
         uint2 x0 = *reinterpret_cast<const uint2*>(vr);
         uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
-        uint4 av = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, o[dt], 0, 0, 0);
-        if (!p.bf16_p) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, o[dt], 0, 0, 0);
+        if (!BF16P) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, o[dt], 0, 0, 0);
       }
     }
+  };
 
+  const int nfull = p.Mk / KT;          // tiles with every key in range
+  const int ntiles = (p.Mk + KT - 1) / KT;
+  load_tile(0, nfull == 0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < nfull; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntiles) load_tile((t + 1) * KT, t + 1 >= nfull);
+    tile(cur, t * KT, false);
     if (t + 1 < ntiles) store_tile(cur ^ 1);
     __syncthreads();
   }
+  if (nfull < ntiles) tile(nfull & 1, nfull * KT, true);
 
   // O = B(z / l).  O^T layout: lane holds query qrow, channels
   // dt*32 + 8*(r/4) + 4*half + (r%4): four consecutive channels per store.
@@ -243,13 +260,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   }
 }
 
+template <int QB, bool BF16P>
+hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.Mq + QB - 1) / QB, a.heads);
+  hipLaunchKernelGGL((attn_kernel<QB, BF16P>), grid, dim3(QB * 2), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Mq <= 0) return hipSuccess;
-  dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  // 256-query workgroups (8 waves sharing each K/V tile) when they still
+  // give every CU a workgroup, else 128-query ones
+  const bool big = a.config == 2 || (a.config == 0 && ((a.Mq + 255) / 256) * a.heads >= 256);
+  if (big) return a.bf16_p ? launch_q<256, true>(a, s) : launch_q<256, false>(a, s);
+  return a.bf16_p ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
 }
 
 }  // namespace psi

@@ -72,6 +72,7 @@ struct AttnArgs {
   int Mq, Mk, heads;
   float alpha;         // 1/sqrt(128) rounded to fp32
   int bf16_p;          // 1: softmax weights rounded to BF16 before P*V
+  int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query workgroups
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
@@ -91,15 +92,17 @@ int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COL
 struct psi_page_slot {
   enum State { FREE = 0, FILLING = 1, CONSUMING = 2 };
   State state = FREE;
-  hipEvent_t ready = nullptr;    // recorded on the copy stream after the copy
+  hipEvent_t ready = nullptr;    // recorded on copy stream 0 after its half of the copy
+  hipEvent_t ready1 = nullptr;   // recorded on copy stream 1 after the other half
   hipEvent_t release = nullptr;  // recorded on the compute stream after the last consumer
   bool released_once = false;
+  bool split = false;            // the last copy used both copy streams
   void* dev = nullptr;
 };
 
 struct psi_timed {
   hipEvent_t start, stop;
-  int kind;      // 0 gemm, 1 attention, 2 copy
+  int kind;      // 0 gemm, 1 attention, 2 copy on stream 0, 3 copy on stream 1
   double work;   // flops (kernels) or bytes (copies)
 };
 
@@ -109,7 +112,8 @@ struct psi_arena {
   bool dry = false;
   char* base = nullptr;
   hipStream_t compute = nullptr;
-  hipStream_t copy = nullptr;
+  hipStream_t copy = nullptr;   // page copies (first half) and bias copies
+  hipStream_t copy1 = nullptr;  // second half of each page copy (a second DMA engine)
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
   psi_page_slot bias_slots[2];  // same lifecycle as pages, one per operator, alternating
@@ -123,6 +127,7 @@ struct psi_arena {
   // profiling
   std::vector<psi_timed> pending;
   std::vector<hipEvent_t> event_pool;
+  double copy_ms_stream[2] = {0.0, 0.0};
   int device = 0;
 };
 
