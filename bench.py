@@ -84,7 +84,7 @@ def build_workload(args, torch, psi, synth):
         live += [x0, x, xt, acc]
         journal = None
         if not args.no_journal:
-            store = (args.steps + args.warmup) * nblk * M * d * 2
+            store = (args.steps + args.warmup + (1 if args.trace else 0)) * nblk * M * d * 2
             journal = psi.psi_journal_create(8 * MiB, 4, store)
         flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
         h2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2
@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages", type=int, default=3,
                     help="page slots in the 80 MiB arena: 2 (+8 MiB workspace) or 3 (no workspace)")
+    ap.add_argument("--trace", metavar="FILE",
+                    help="after the timed steps, run one more step with the device timeline on and write "
+                         "it to FILE as JSON (kind 0 GEMM, 1 attention, 2/3 page copy stream 0/1)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -281,6 +284,12 @@ def main():
     wall = t1 - t0
     ev_ms = ev0.elapsed_time(ev1)
     st = psi.psi_arena_stats(arena)
+    if args.trace and not args.no_profile:
+        psi.psi_arena_trace_start(arena, 1 << 16)
+        step()
+        sync_all()
+        with open(args.trace, "w") as f:
+            json.dump(psi.psi_arena_trace_read(arena, 1 << 16), f)
 
     total_flops = wl["flops"] * args.steps
     value = total_flops / wall / 1e12

@@ -202,6 +202,28 @@ psi_status psi_arena_stats(psi_arena* a, psi_stats* out);
 /* Zeroes the counters and the scratch high-water mark. */
 psi_status psi_arena_reset_stats(psi_arena* a);
 
+/* Device timeline of a profiled arena (PSI_ARENA_PROFILE), for overlap
+ * analysis of the page lifecycle of [PSI] sec. II-D: every timed GEMM and
+ * attention launch and every timed half-page copy, with its start relative
+ * to a base event.
+ *   psi_arena_trace_start synchronises the arena's streams, records the base
+ *   event on the compute stream and starts keeping up to `capacity` events
+ *   (older ones are not overwritten: later events are dropped once full).
+ *   psi_arena_trace_read synchronises (to read the timers), copies up to
+ *   `capacity` events into `out` (caller-owned host array) and stores the
+ *   number recorded in *count.
+ * Errors: PSI_E_INVALID without PSI_ARENA_PROFILE or for a null arena;
+ * PSI_E_HIP if an event cannot be created or read. */
+typedef struct psi_trace_event {
+  int32_t kind;     /* 0 GEMM, 1 attention, 2 / 3 page copy on copy stream 0 / 1 */
+  int32_t reserved;
+  double start_ms;  /* from the base event */
+  double dur_ms;
+  double work;      /* algorithmic FLOPs (kernels) or bytes (copies) */
+} psi_trace_event;
+psi_status psi_arena_trace_start(psi_arena* a, size_t capacity);
+psi_status psi_arena_trace_read(psi_arena* a, psi_trace_event* out, size_t capacity, size_t* count);
+
 /* Device address of the arena base (for footprint checks). */
 psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_out);
 

@@ -87,36 +87,30 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
       PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, a->compute));
       PSI_HIP(hipEventRecord(slot.ready, a->compute));
     } else {
-      // Two halves on two copy streams: each DMA engine pays the per-copy
-      // start-up once while the other one streams, so back-to-back 8 MiB
-      // pages keep the host link near its bulk rate.
-      const size_t h0 = bytes > (1u << 20) ? (bytes / 2 + 255) / 256 * 256 : bytes;
-      hipStream_t cs[2] = {a->copy, a->copy1};
-      const size_t off[2] = {0, h0};
-      const size_t len[2] = {h0, bytes - h0};
-      for (int i = 0; i < 2; ++i) {
-        if (len[i] == 0) continue;
-        if (slot.released_once) {
-          PSI_HIP(hipStreamWaitEvent(cs[i], slot.release, 0));
-          a->stats.event_waits++;
-        }
-        hipEvent_t t0 = nullptr, t1 = nullptr;
-        if (a->desc.flags & PSI_ARENA_PROFILE) {
-          t0 = pool_event(a);
-          t1 = pool_event(a);
-          if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
-          PSI_HIP(hipEventRecord(t0, cs[i]));
-        }
-        PSI_HIP(hipMemcpyAsync(static_cast<char*>(slot.dev) + off[i], static_cast<const char*>(host) + off[i],
-                               len[i], hipMemcpyHostToDevice, cs[i]));
-        if (t0) {
-          PSI_HIP(hipEventRecord(t1, cs[i]));
-          a->pending.push_back({t0, t1, 2 + i, (double)len[i]});
-        }
+      // Whole pages, alternating between the two copy streams (two DMA
+      // engines): while one engine pays the start-up of its next copy (the
+      // release wait and the command set-up), the other one is streaming,
+      // so back-to-back 8 MiB pages keep the host link near its bulk rate.
+      const int ci = a->next_copy;
+      hipStream_t cs = ci ? a->copy1 : a->copy;
+      a->next_copy = ci ^ 1;
+      if (slot.released_once) {
+        PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
+        a->stats.event_waits++;
       }
-      PSI_HIP(hipEventRecord(slot.ready, cs[0]));
-      if (len[1]) PSI_HIP(hipEventRecord(slot.ready1, cs[1]));
-      slot.split = len[1] != 0;
+      hipEvent_t t0 = nullptr, t1 = nullptr;
+      if (a->desc.flags & PSI_ARENA_PROFILE) {
+        t0 = pool_event(a);
+        t1 = pool_event(a);
+        if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
+        PSI_HIP(hipEventRecord(t0, cs));
+      }
+      PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, cs));
+      if (t0) {
+        PSI_HIP(hipEventRecord(t1, cs));
+        a->pending.push_back({t0, t1, 2 + ci, (double)bytes});
+      }
+      PSI_HIP(hipEventRecord(slot.ready, cs));
     }
   }
   slot.state = psi_page_slot::FILLING;
@@ -199,10 +193,6 @@ psi_status page_acquire(psi_arena* a, int page) {
   if (!a->dry && !(a->desc.flags & PSI_ARENA_SYNC_COPY)) {
     PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready, 0));
     a->stats.event_waits++;
-    if (slot.split) {
-      PSI_HIP(hipStreamWaitEvent(a->compute, slot.ready1, 0));
-      a->stats.event_waits++;
-    }
   }
   slot.state = psi_page_slot::CONSUMING;
   return PSI_OK;
@@ -283,6 +273,11 @@ static psi_status harvest(psi_arena* a) {
       a->stats.copy_ms = a->copy_ms_stream[0] > a->copy_ms_stream[1] ? a->copy_ms_stream[0] : a->copy_ms_stream[1];
       a->stats.copy_bytes_timed += (uint64_t)t.work;
     }
+    if (a->trace_base && a->trace.size() < a->trace_cap) {
+      float off = 0.0f;
+      PSI_HIP(hipEventElapsedTime(&off, a->trace_base, t.start));
+      a->trace.push_back(psi_trace_event{t.kind, 0, (double)off, (double)ms, t.work});
+    }
     a->event_pool.push_back(t.start);
     a->event_pool.push_back(t.stop);
   }
@@ -317,7 +312,6 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy1, hipStreamNonBlocking);
     for (int i = 0; e == hipSuccess && i < d->n_pages; ++i) {
       e = hipEventCreateWithFlags(&a->slots[i].ready, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].ready1, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].release, hipEventDisableTiming);
       a->slots[i].dev = a->base + L.page_off[i];
     }
@@ -348,9 +342,9 @@ psi_status psi_arena_destroy(psi_arena* a) {
       a->event_pool.push_back(t.stop);
     }
     for (hipEvent_t e : a->event_pool) (void)hipEventDestroy(e);
+    if (a->trace_base) (void)hipEventDestroy(a->trace_base);
     for (int i = 0; i < a->desc.n_pages; ++i) {
       if (a->slots[i].ready) (void)hipEventDestroy(a->slots[i].ready);
-      if (a->slots[i].ready1) (void)hipEventDestroy(a->slots[i].ready1);
       if (a->slots[i].release) (void)hipEventDestroy(a->slots[i].release);
     }
     for (int i = 0; i < 2; ++i) {
@@ -403,6 +397,33 @@ psi_status psi_arena_reset_stats(psi_arena* a) {
   s.scratch_high_water = a->scratch_top;
   a->stats = s;
   a->copy_ms_stream[0] = a->copy_ms_stream[1] = 0.0;
+  return PSI_OK;
+}
+
+psi_status psi_arena_trace_start(psi_arena* a, size_t capacity) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (!(a->desc.flags & PSI_ARENA_PROFILE)) return fail(PSI_E_INVALID, "trace needs PSI_ARENA_PROFILE");
+  if (a->dry) return PSI_OK;
+  psi_status st = harvest(a);  // synchronises the three streams
+  if (st) return st;
+  if (!a->trace_base) PSI_HIP(hipEventCreate(&a->trace_base));
+  PSI_HIP(hipEventRecord(a->trace_base, a->compute));
+  a->trace.clear();
+  a->trace.reserve(capacity < (1u << 20) ? capacity : (1u << 20));
+  a->trace_cap = capacity;
+  return PSI_OK;
+}
+
+psi_status psi_arena_trace_read(psi_arena* a, psi_trace_event* out, size_t capacity, size_t* count) {
+  if (!a || (capacity && !out)) return fail(PSI_E_INVALID, "null argument");
+  if (!(a->desc.flags & PSI_ARENA_PROFILE)) return fail(PSI_E_INVALID, "trace needs PSI_ARENA_PROFILE");
+  if (!a->pending.empty()) {
+    psi_status st = harvest(a);
+    if (st) return st;
+  }
+  const size_t n = a->trace.size() < capacity ? a->trace.size() : capacity;
+  for (size_t i = 0; i < n; ++i) out[i] = a->trace[i];
+  if (count) *count = a->trace.size();
   return PSI_OK;
 }
 

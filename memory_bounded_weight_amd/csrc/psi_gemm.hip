@@ -1,8 +1,7 @@
 // psi_gemm.hip -- page-sliced BF16 GEMM for gfx950 (CDNA4).
 //
 // Computes C[M,N] = A[M,K] * B[N,K]^T with fp32 accumulation on the matrix
-// cores (v_mfma_f32_32x32x16_bf16), operands staged through LDS with a
-// double buffer, and a fused epilogue:
+// cores (v_mfma_f32_32x32x16_bf16) and a fused epilogue:
 //   * carried fp32 accumulator: the MFMA accumulators start from acc_in, so
 //     a K-split over weight pages continues one accumulation chain per
 //     output in page order ([PSI] sec. II-B eq. (2): disjoint
@@ -15,9 +14,19 @@
 // [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint
 // Audio-Video Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
 //
+// Main kernel: operand tiles move from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging) through a ring of S LDS
+// stages, so S-1 K tiles are in flight while the matrix cores work on the
+// current one.  LDS rows are unpadded; the 16-byte chunks of a row are
+// XOR-swizzled by the row index so that the MFMA fragment reads
+// (ds_read_b128 down 32 rows) hit distinct banks.  Fragments of the next
+// k16 step are read while the MFMAs of the current step run.
+//
 // Determinism: one fixed instruction sequence per output element for every
 // shape (no split-K inside a launch, no atomics), so the same operands give
-// the same bits on every run and for every page partition of the output.
+// the same bits on every run and for every page partition of the output;
+// all tile configurations below give identical bits (each output sees the
+// same ascending sequence of k16 MFMA steps with the same lane mapping).
 #include "psi_internal.h"
 
 namespace psi {
@@ -48,401 +57,335 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return v * e / (1.0f + e);
 }
 
-constexpr int kThreads = 256;  // 4 waves of 64, arranged 2 x 2
+// Epilogue of one wave's TM x TN block of 32x32 accumulator tiles.  C layout
+// of the 32x32 MFMA: lane holds column l32 and rows
+// 8*(r/4) + 4*half + (r%4), r = 0..15.
+template <int TM, int TN>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
+                                         int l32) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gn = nb + j * 32 + l32;
+      if (gn >= p.N) continue;
+      const float bn = (p.bias && !p.bias_on_m) ? bf2f(p.bias[gn]) : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = mb + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        if (gm >= p.M) continue;
+        const float v = acc[i][j][r];
+        if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
+        if (p.out) {
+          float t;
+          if (p.bias) {
+            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
+            t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
+          } else {
+            t = v;
+          }
+          uint16_t y = f2bf(t);
+          if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
+          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
+          p.out[(long)gm * p.ldo + gn] = y;
+        }
+      }
+    }
+}
 
-template <int BM, int BN, int BK>
-struct Tile {
-  static constexpr int LDS = BK + 8;            // padded row stride (elements)
-  static constexpr int A_CHUNKS = BM * BK / 8;  // 16-byte chunks per tile
-  static constexpr int B_CHUNKS = BN * BK / 8;
-  static constexpr int A_PER_T = A_CHUNKS / kThreads;
-  static constexpr int B_PER_T = B_CHUNKS / kThreads;
-  static constexpr int WM = BM / 2;  // wave tile (2 x 2 waves)
-  static constexpr int WN = BN / 2;
-  static constexpr int TM = WM / 32;  // 32x32 MFMA tiles per wave
-  static constexpr int TN = WN / 32;
-  static constexpr int STAGE = (BM + BN) * LDS;  // elements per LDS stage
-  static_assert(A_CHUNKS % kThreads == 0 && B_CHUNKS % kThreads == 0, "tile/threads");
-  static_assert(TM >= 1 && TN >= 1, "wave tile");
-};
+// Accumulators start from acc_in (carried K-split chain) or zero.
+template <int TM, int TN>
+__device__ __forceinline__ void init_acc(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
+                                         int l32) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (!p.acc_in) return;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gn = nb + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = mb + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        if (gm < p.M && gn < p.N) acc[i][j][r] = p.acc_in[(long)gm * p.ld_acc_in + gn];
+      }
+    }
+}
 
-// STAGES = 2: double-buffered LDS, one barrier per K tile.
-// STAGES = 1: one LDS buffer (half the LDS, so two workgroups fit a CU),
-// the register stage still prefetches the next K tile.
-template <int BM, int BN, int BK, int STAGES>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  using T = Tile<BM, BN, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * T::STAGE];
-
-  // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own
-  // L2).  Remap so that every XCD owns a contiguous range of logical tiles,
-  // and walk that range with N fastest: concurrently running tiles of an
-  // XCD then share their A row bands (and the page's B bands) in its L2.
-  const int nt = tiles_m * tiles_n;
+// Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).
+// Remap so that every XCD owns a contiguous range of logical tiles, walked
+// with N fastest: concurrently running tiles of an XCD then share their A
+// row bands (and the page's B bands) in its L2.
+__device__ __forceinline__ int xcd_tile(int nt) {
   int t = blockIdx.x;
   if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
-  const int tm = t / tiles_n;
-  const int tn = t % tiles_n;
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
+  return t;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// s_waitcnt immediate for gfx9: vmcnt = n (6 bits), expcnt and lgkmcnt not
+// waited on.
+#define PSI_VMCNT(n) ((((n) & 0xF)) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+#define PSI_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel.  BM x BN workgroup tile, WGM x WGN waves (each
+// (BM/WGM) x (BN/WGN)), BK = 64, S LDS stages.  Requires K % 64 == 0 and
+// 16-byte aligned rows (checked by the dispatcher).
+//
+// Stage layout: A rows [0, BM) then B rows [BM, BM+BN), 128 bytes per row;
+// chunk c (8 elements) of row r sits at chunk position c ^ ((r / 2) % 8).
+// One global_load_lds_dwordx4 moves 64 chunks = 8 rows: lane l fetches the
+// global chunk that belongs at LDS position l of those 8 rows.
+//
+// Pipeline (per K tile kt): stage kt+S-1 is issued into the buffer that
+// stage kt-1 used (all waves left it at the previous barrier); before the
+// last k16 step of tile kt each wave waits until its own loads of stage kt+1
+// have landed (vmcnt) and the workgroup meets at a barrier, after which the
+// first fragments of tile kt+1 are read while the last MFMAs of kt run.
+template <int BM, int BN, int WGM, int WGN, int S>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr int BK = 64, NW = WGM * WGN;
+  constexpr int CPR = BK / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;        // rows per load instruction
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int LA = BM / RPI / NW, LB = BN / RPI / NW, NL = LA + LB;  // loads per wave per stage
+  static_assert(LA * RPI * NW == BM && LB * RPI * NW == BN, "tile rows must split evenly over the waves");
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32, KS = BK / 16;
+  static_assert(S >= 2 && S <= 4, "stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
+
+  const int t = xcd_tile(tiles_m * tiles_n);
+  const int m0 = (t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // Global sources of this lane's chunks (rows past M or N clamped to the
+  // last row: they feed only outputs the epilogue discards).
+  const uint16_t* ga[LA];
+  const uint16_t* gb[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int r = (j * NW + wave) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ ((r / 2) % CPR);
+    const int gr = min(m0 + r, p.M - 1);
+    ga[j] = p.A + (long)gr * p.lda + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int r = (j * NW + wave) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ ((r / 2) % CPR);
+    const int gr = min(n0 + r, p.N - 1);
+    gb[j] = p.B + (long)gr * p.ldb + c * 8;
+  }
+  auto issue = [&](int kt) {
+    uint16_t* st = smem + (kt % S) * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(ga[j] + k0), PSI_LDS(st + (j * NW + wave) * RPI * BK), 16, 0,
+                                       0);
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(gb[j] + k0),
+                                       PSI_LDS(st + BM * BK + (j * NW + wave) * RPI * BK), 16, 0, 0);
+  };
+  // Let n stages of this wave's loads stay in flight (loads retire in order).
+  auto wait_stages = [&](int n) {
+    if (S >= 4 && n >= 2) __builtin_amdgcn_s_waitcnt(PSI_VMCNT(2 * NL));
+    else if (S >= 3 && n >= 1) __builtin_amdgcn_s_waitcnt(PSI_VMCNT(NL));
+    else __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0));
+  };
+  // Fragment reads: row r of the wave's block, logical chunk 2*ks + half.
+  // Rows 32 apart share the swizzle, so one per-lane term serves all tiles.
+  int offa[TM], offb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) offa[i] = (wm * WM + i * 32 + l32) * BK;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) offb[j] = BM * BK + (wn * WN + j * 32 + l32) * BK;
+  const int swz = (l32 / 2) % CPR;
+  auto frags = [&](const uint16_t* st, int ks, bf16x8* af, bf16x8* bf) {
+    const int pc = ((ks * 2 + half) ^ swz) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + offa[i] + pc);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + offb[j] + pc);
+  };
+
+  f32x16 acc[TM][TN];
+  init_acc<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
+
+  const int nk = p.K / BK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
+  wait_stages(min(S - 2, nk - 1));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  bf16x8 fa[2][TM], fb[2][TN];
+  frags(smem, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* st = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < KS) {
+        frags(st, ks + 1, fa[nxt], fb[nxt]);
+      } else if (kt + 1 < nk) {
+        wait_stages(min(S - 2, nk - 2 - kt));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        frags(smem + ((kt + 1) % S) * STAGE, 0, fa[nxt], fb[nxt]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+      if (ks == 0 && kt + S - 1 < nk) issue(kt + S - 1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0));
+  epilogue<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel for any K and 8-element-aligned rows: 128 x 128 x 64
+// tile, 2 x 2 waves of 64 x 64, padded LDS rows (BK + 8), the next K tile
+// loaded into registers while the current one is multiplied, K tail zeroed.
+constexpr int kRegThreads = 256;
+
+__global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr int BM = 128, BN = 128, BK = 64, LDS = BK + 8, CPR = BK / 8;
+  constexpr int A_PER_T = BM * BK / 8 / kRegThreads, B_PER_T = BN * BK / 8 / kRegThreads;
+  constexpr int WM = 64, WN = 64, TM = 2, TN = 2, STAGE = (BM + BN) * LDS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int t = xcd_tile(tiles_m * tiles_n);
+  const int m0 = (t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+  const int half = lane >> 5, l32 = lane & 31;
 
-  constexpr int CPR = BK / 8;  // 16-byte chunks per row
-  uint4 ra[T::A_PER_T], rb[T::B_PER_T];
-
+  uint4 ra[A_PER_T], rb[B_PER_T];
   auto load_global = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < T::A_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      int r = c / CPR, kc = (c % CPR) * 8;
-      int gr = m0 + r, gk = k0 + kc;
-      if (gr < p.M && gk < p.K)
-        ra[i] = *reinterpret_cast<const uint4*>(p.A + (long)gr * p.lda + gk);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int c = tid + i * kRegThreads;
+      const int gr = m0 + c / CPR, gk = k0 + (c % CPR) * 8;
+      ra[i] = (gr < p.M && gk < p.K) ? *reinterpret_cast<const uint4*>(p.A + (long)gr * p.lda + gk)
+                                     : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < T::B_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      int r = c / CPR, kc = (c % CPR) * 8;
-      int gr = n0 + r, gk = k0 + kc;
-      if (gr < p.N && gk < p.K)
-        rb[i] = *reinterpret_cast<const uint4*>(p.B + (long)gr * p.ldb + gk);
-      else
-        rb[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int c = tid + i * kRegThreads;
+      const int gr = n0 + c / CPR, gk = k0 + (c % CPR) * 8;
+      rb[i] = (gr < p.N && gk < p.K) ? *reinterpret_cast<const uint4*>(p.B + (long)gr * p.ldb + gk)
+                                     : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_lds = [&](int buf) {
-    uint16_t* sa = smem + buf * T::STAGE;
-    uint16_t* sb = sa + BM * T::LDS;
+    uint16_t* sa = smem + buf * STAGE;
+    uint16_t* sb = sa + BM * LDS;
 #pragma unroll
-    for (int i = 0; i < T::A_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      int r = c / CPR, kc = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(sa + r * T::LDS + kc) = ra[i];
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int c = tid + i * kRegThreads;
+      *reinterpret_cast<uint4*>(sa + (c / CPR) * LDS + (c % CPR) * 8) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < T::B_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      int r = c / CPR, kc = (c % CPR) * 8;
-      *reinterpret_cast<uint4*>(sb + r * T::LDS + kc) = rb[i];
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int c = tid + i * kRegThreads;
+      *reinterpret_cast<uint4*>(sb + (c / CPR) * LDS + (c % CPR) * 8) = rb[i];
     }
   };
 
-  // Accumulators, C layout of the 32x32 MFMA: lane holds column l32 and
-  // rows 8*(i/4) + 4*half + (i%4), i = 0..15.
-  f32x16 acc[T::TM][T::TN];
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  if (p.acc_in) {
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j) {
-        const int gn = n0 + wn * T::WN + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          if (gm < p.M && gn < p.N) acc[i][j][r] = p.acc_in[(long)gm * p.ld_acc_in + gn];
-        }
-      }
-  }
+  f32x16 acc[TM][TN];
+  init_acc<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 
   const int nk = (p.K + BK - 1) / BK;
   load_global(0);
   store_lds(0);
   __syncthreads();
-
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = STAGES == 2 ? (kt & 1) : 0;
+    const int cur = kt & 1;
     if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const uint16_t* sa = smem + cur * T::STAGE + (wm * T::WM) * T::LDS;
-    const uint16_t* sb = smem + cur * T::STAGE + BM * T::LDS + (wn * T::WN) * T::LDS;
+    const uint16_t* sa = smem + cur * STAGE + (wm * WM) * LDS;
+    const uint16_t* sb = smem + cur * STAGE + BM * LDS + (wn * WN) * LDS;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kofs = ks * 16 + half * 8;
-      bf16x8 af[T::TM], bfr[T::TN];
+      bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + (i * 32 + l32) * T::LDS + kofs);
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(sa + (i * 32 + l32) * LDS + kofs);
 #pragma unroll
-      for (int j = 0; j < T::TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (j * 32 + l32) * T::LDS + kofs);
+      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (j * 32 + l32) * LDS + kofs);
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
+        for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (STAGES == 1) __syncthreads();
-    if (kt + 1 < nk) store_lds(STAGES == 2 ? (cur ^ 1) : 0);
+    if (kt + 1 < nk) store_lds(cur ^ 1);
     __syncthreads();
   }
-
-  // Epilogue.
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-      const int gn = n0 + wn * T::WN + j * 32 + l32;
-      if (gn >= p.N) continue;
-      const float bn = (p.bias && !p.bias_on_m) ? bf2f(p.bias[gn]) : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-        if (gm >= p.M) continue;
-        const float v = acc[i][j][r];
-        if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
-        if (p.out) {
-          float t;
-          if (p.bias) {
-            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
-            t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
-          } else {
-            t = v;
-          }
-          uint16_t y = f2bf(t);
-          if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
-          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
-          p.out[(long)gm * p.ldo + gn] = y;
-        }
-      }
-    }
+  epilogue<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 }
 
-// Deep-prefetch variant: K tiles are fetched two iterations ahead into two
-// register stages (the loop is unrolled by two so stage indices are
-// compile-time), loads are branch-free (rows past M or N are clamped to
-// the last row: they only feed outputs that are never stored; the K tail
-// is zeroed with a select), and LDS is double-buffered.
-template <int BM, int BN, int BK>
-__global__ __launch_bounds__(kThreads) void gemm_kernel_pf(GemmArgs p, int tiles_m, int tiles_n) {
-  using T = Tile<BM, BN, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
-
-  const int nt = tiles_m * tiles_n;
-  int t = blockIdx.x;
-  if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
-  const int tm = t / tiles_n;
-  const int tn = t % tiles_n;
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-
-  constexpr int CPR = BK / 8;
-  // per-thread chunk coordinates (row within the tile, k offset)
-  const uint16_t* pa[T::A_PER_T];
-  const uint16_t* pb[T::B_PER_T];
-  int ka[T::A_PER_T], kb[T::B_PER_T];
-#pragma unroll
-  for (int i = 0; i < T::A_PER_T; ++i) {
-    int c = tid + i * kThreads;
-    int r = m0 + c / CPR;
-    r = r < p.M ? r : p.M - 1;
-    ka[i] = (c % CPR) * 8;
-    pa[i] = p.A + (long)r * p.lda;
-  }
-#pragma unroll
-  for (int i = 0; i < T::B_PER_T; ++i) {
-    int c = tid + i * kThreads;
-    int r = n0 + c / CPR;
-    r = r < p.N ? r : p.N - 1;
-    kb[i] = (c % CPR) * 8;
-    pb[i] = p.B + (long)r * p.ldb;
-  }
-  uint4 ra[2][T::A_PER_T], rb[2][T::B_PER_T];
-
-  auto load = [&](int k0, uint4* xa, uint4* xb) {
-#pragma unroll
-    for (int i = 0; i < T::A_PER_T; ++i) {
-      const int gk = k0 + ka[i];
-      const bool ok = gk < p.K;
-      uint4 v = *reinterpret_cast<const uint4*>(pa[i] + (ok ? gk : 0));
-      xa[i] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_PER_T; ++i) {
-      const int gk = k0 + kb[i];
-      const bool ok = gk < p.K;
-      uint4 v = *reinterpret_cast<const uint4*>(pb[i] + (ok ? gk : 0));
-      xb[i] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf, const uint4* xa, const uint4* xb) {
-    uint16_t* sa = smem + buf * T::STAGE;
-    uint16_t* sb = sa + BM * T::LDS;
-#pragma unroll
-    for (int i = 0; i < T::A_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(sa + (c / CPR) * T::LDS + (c % CPR) * 8) = xa[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_PER_T; ++i) {
-      int c = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(sb + (c / CPR) * T::LDS + (c % CPR) * 8) = xb[i];
-    }
-  };
-
-  f32x16 acc[T::TM][T::TN];
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  if (p.acc_in) {
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j) {
-        const int gn = n0 + wn * T::WN + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          if (gm < p.M && gn < p.N) acc[i][j][r] = p.acc_in[(long)gm * p.ld_acc_in + gn];
-        }
-      }
-  }
-
-  auto compute = [&](int buf) {
-    const uint16_t* sa = smem + buf * T::STAGE + (wm * T::WM) * T::LDS;
-    const uint16_t* sb = smem + buf * T::STAGE + BM * T::LDS + (wn * T::WN) * T::LDS;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kofs = ks * 16 + half * 8;
-      bf16x8 af[T::TM], bfr[T::TN];
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + (i * 32 + l32) * T::LDS + kofs);
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (j * 32 + l32) * T::LDS + kofs);
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int nk = (p.K + BK - 1) / BK;
-  // prologue: tile 0 in LDS buffer 0, tile 1 in register stage 1
-  load(0, ra[0], rb[0]);
-  store(0, ra[0], rb[0]);
-  if (nk > 1) load(BK, ra[1], rb[1]);
-  __syncthreads();
-
-  // iteration kt: issue tile kt+2 into register stage kt&1, compute tile kt
-  // from LDS buffer kt&1, then move tile kt+1 (register stage (kt+1)&1) into
-  // LDS buffer (kt+1)&1.
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) load((kt + 2) * BK, ra[0], rb[0]);
-    compute(0);
-    if (kt + 1 < nk) store(1, ra[1], rb[1]);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) load((kt + 3) * BK, ra[1], rb[1]);
-    compute(1);
-    if (kt + 2 < nk) store(0, ra[0], rb[0]);
-    __syncthreads();
-  }
-
-  // Epilogue.
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-      const int gn = n0 + wn * T::WN + j * 32 + l32;
-      if (gn >= p.N) continue;
-      const float bn = (p.bias && !p.bias_on_m) ? bf2f(p.bias[gn]) : 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gm = m0 + wm * T::WM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-        if (gm >= p.M) continue;
-        const float v = acc[i][j][r];
-        if (p.acc_out) p.acc_out[(long)gm * p.ld_acc_out + gn] = v;
-        if (p.out) {
-          float t;
-          if (p.bias) {
-            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
-            t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
-          } else {
-            t = v;
-          }
-          uint16_t y = f2bf(t);
-          if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
-          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
-          p.out[(long)gm * p.ldo + gn] = y;
-        }
-      }
-    }
-}
-
-template <int BM, int BN, int BK>
-hipError_t launch_pf(const GemmArgs& a, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, int S>
+hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel_pf<BM, BN, BK>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
-                     tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_kernel_dma<BM, BN, WGM, WGN, S>), dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, s,
+                     a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int STAGES>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, STAGES>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
-                     tiles_m, tiles_n);
+hipError_t launch_reg(const GemmArgs& a, hipStream_t s) {
+  const int tiles_m = (a.M + 127) / 128;
+  const int tiles_n = (a.N + 127) / 128;
+  hipLaunchKernelGGL(gemm_kernel_reg, dim3(tiles_m * tiles_n), dim3(kRegThreads), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+bool dma_ok(const GemmArgs& a) {
+  const uintptr_t al = (uintptr_t)a.A | (uintptr_t)a.B;
+  return a.K > 0 && a.K % 64 == 0 && (al & 15) == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0;
 }
 
 }  // namespace
 
-// Tile configurations (every one gives the same bits: each output sees the
-// same ascending sequence of k16 MFMA steps whatever the tile).
-//   1: 256x256, 2: 256x128, 3: 128x256, 4: 128x128 (double-buffered LDS)
-//   5: 256x128, 6: 128x256 with one LDS stage (two workgroups per CU)
-//   7: 128x128 (BK 64), 8: 128x128 (BK 32), 9: 256x128 (BK 32), 10: 128x256
-//      (BK 32): two register stages, tiles fetched two iterations ahead
-// Measured on MI355X: the 128x128 tile, at two waves per SIMD (two
-// workgroups per CU), is the fastest on every page shape of this path;
-// the single-wave large tiles are latency-bound.
-int gemm_auto_config(int M, int N) {
-  (void)M;
-  (void)N;
-  return 4;
+// Tile configurations (all give identical bits):
+//   1: direct-to-LDS 256 x 128, 8 waves of 64 x 64, 3 LDS stages (144 KiB,
+//      one workgroup per CU);
+//   2: direct-to-LDS 128 x 128, 4 waves of 64 x 64, 2 LDS stages (64 KiB,
+//      two workgroups per CU);
+//   3: register-staged 128 x 128 (any K, 8-element-aligned rows).
+// Configurations 1 and 2 need K % 64 == 0 and 16-byte aligned rows; other
+// operands take configuration 3 whatever is asked.  Measured on MI355X on the
+// page shapes of this path: 1 is fastest where it still yields >= 256 tiles
+// and no fp32 accumulator streams through the epilogue; 2 overlaps one
+// workgroup's accumulator traffic with the other's MFMAs (K-split pages)
+// and fills more CUs on small outputs.
+int gemm_auto_config(const GemmArgs& a) {
+  if (!dma_ok(a)) return 3;
+  if (a.acc_in || a.acc_out) return 2;
+  const long tiles1 = (long)((a.M + 255) / 256) * ((a.N + 127) / 128);
+  return tiles1 >= 256 ? 1 : 2;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  int cfg = a.config > 0 ? a.config : gemm_auto_config(a.M, a.N);
+  int cfg = a.config > 0 ? a.config : gemm_auto_config(a);
+  if (cfg != 3 && !dma_ok(a)) cfg = 3;
   switch (cfg) {
-    case 1: return launch_cfg<256, 256, 64, 2>(a, s);
-    case 2: return launch_cfg<256, 128, 64, 2>(a, s);
-    case 3: return launch_cfg<128, 256, 64, 2>(a, s);
-    case 5: return launch_cfg<256, 128, 64, 1>(a, s);
-    case 6: return launch_cfg<128, 256, 64, 1>(a, s);
-    case 7: return launch_pf<128, 128, 64>(a, s);
-    case 8: return launch_pf<128, 128, 32>(a, s);
-    case 9: return launch_pf<256, 128, 32>(a, s);
-    case 10: return launch_pf<128, 256, 32>(a, s);
-    default: return launch_cfg<128, 128, 64, 2>(a, s);
+    case 1: return launch_dma<256, 128, 4, 2, 3>(a, s);
+    case 2: return launch_dma<128, 128, 2, 2, 2>(a, s);
+    default: return launch_reg(a, s);
   }
 }
 

@@ -60,7 +60,7 @@ struct GemmArgs {
   int config;           // tile configuration; 0 = chosen from the shape
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
-int gemm_auto_config(int M, int N);
+int gemm_auto_config(const GemmArgs& a);
 
 struct AttnArgs {
   uint16_t* q;         // [Mq, ldq]; head h occupies columns h*128..h*128+127; O overwrites it
@@ -92,11 +92,9 @@ int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COL
 struct psi_page_slot {
   enum State { FREE = 0, FILLING = 1, CONSUMING = 2 };
   State state = FREE;
-  hipEvent_t ready = nullptr;    // recorded on copy stream 0 after its half of the copy
-  hipEvent_t ready1 = nullptr;   // recorded on copy stream 1 after the other half
+  hipEvent_t ready = nullptr;    // recorded on the copy stream after the copy
   hipEvent_t release = nullptr;  // recorded on the compute stream after the last consumer
   bool released_once = false;
-  bool split = false;            // the last copy used both copy streams
   void* dev = nullptr;
 };
 
@@ -112,8 +110,9 @@ struct psi_arena {
   bool dry = false;
   char* base = nullptr;
   hipStream_t compute = nullptr;
-  hipStream_t copy = nullptr;   // page copies (first half) and bias copies
-  hipStream_t copy1 = nullptr;  // second half of each page copy (a second DMA engine)
+  hipStream_t copy = nullptr;   // even page copies and bias copies
+  hipStream_t copy1 = nullptr;  // odd page copies (a second DMA engine)
+  int next_copy = 0;            // copy stream of the next page
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
   psi_page_slot bias_slots[2];  // same lifecycle as pages, one per operator, alternating
@@ -128,6 +127,10 @@ struct psi_arena {
   std::vector<psi_timed> pending;
   std::vector<hipEvent_t> event_pool;
   double copy_ms_stream[2] = {0.0, 0.0};
+  // device timeline (psi_arena_trace_start / _read)
+  hipEvent_t trace_base = nullptr;
+  size_t trace_cap = 0;
+  std::vector<psi_trace_event> trace;
   int device = 0;
 };
 

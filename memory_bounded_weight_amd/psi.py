@@ -96,6 +96,11 @@ class psi_stats(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class psi_trace_event(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("start_ms", ctypes.c_double),
+                ("dur_ms", ctypes.c_double), ("work", ctypes.c_double)]
+
+
 class psi_matrix(ctypes.Structure):
     _fields_ = [("pages_host", _vp), ("bias_host", _vp), ("rows", _i), ("cols", _i),
                 ("split", _i), ("block", _i), ("resident", _i)]
@@ -140,6 +145,8 @@ _sig("psi_arena_destroy", [_vp])
 _sig("psi_arena_sync", [_vp])
 _sig("psi_arena_stats", [_vp, _P(psi_stats)])
 _sig("psi_arena_reset_stats", [_vp])
+_sig("psi_arena_trace_start", [_vp, _sz])
+_sig("psi_arena_trace_read", [_vp, _P(psi_trace_event), _sz, _P(_sz)])
 _sig("psi_arena_device_base", [_vp, _P(_vp), _P(_sz)])
 _sig("psi_arena_set_probe", [_vp, _vp, ctypes.c_int32, ctypes.c_int32])
 _sig("psi_page_submit", [_vp, _vp, _sz, _P(_i)])
@@ -163,7 +170,8 @@ _sig("psi_journal_counters", [_vp, _P(ctypes.c_uint64), _P(ctypes.c_uint64), _P(
 EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_arena_plan",
            "psi_linear_plan", "psi_ffn_plan", "psi_attn_plan", "psi_last_error", "psi_version",
            "psi_arena_create", "psi_arena_destroy", "psi_arena_sync", "psi_arena_stats",
-           "psi_arena_reset_stats", "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
+           "psi_arena_reset_stats", "psi_arena_trace_start", "psi_arena_trace_read",
+           "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
            "psi_attn_paged", "psi_block_paged", "psi_journal_create", "psi_journal_destroy",
            "psi_journal_commit", "psi_journal_reload", "psi_journal_fence", "psi_journal_sync",
@@ -284,6 +292,19 @@ def psi_arena_stats(arena: int) -> psi_stats:
 
 def psi_arena_reset_stats(arena: int):
     return _check(_lib.psi_arena_reset_stats(arena), "psi_arena_reset_stats")
+
+
+def psi_arena_trace_start(arena: int, capacity: int = 1 << 16):
+    return _check(_lib.psi_arena_trace_start(arena, capacity), "psi_arena_trace_start")
+
+
+def psi_arena_trace_read(arena: int, capacity: int = 1 << 16):
+    """Timeline since psi_arena_trace_start as a list of (kind, start_ms,
+    dur_ms, work); kind 0 GEMM, 1 attention, 2 / 3 page copy stream 0 / 1."""
+    buf = (psi_trace_event * capacity)()
+    n = _sz()
+    _check(_lib.psi_arena_trace_read(arena, buf, capacity, ctypes.byref(n)), "psi_arena_trace_read")
+    return [(e.kind, e.start_ms, e.dur_ms, e.work) for e in buf[:min(n.value, capacity)]]
 
 
 def psi_arena_device_base(arena: int):
