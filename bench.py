@@ -59,6 +59,8 @@ def build_workload(args, torch, psi, synth):
     """Returns a dict with the step callable, its FLOPs and H2D bytes."""
     stream = torch.cuda.current_stream().cuda_stream
     flags = 0 if args.no_profile else psi.PSI_ARENA_PROFILE
+    if args.profile_copies and not args.no_profile:
+        flags |= psi.PSI_ARENA_PROFILE_COPIES
     if args.sync_copy:
         flags |= psi.PSI_ARENA_SYNC_COPY
     W = {}
@@ -223,6 +225,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--resident", action="store_true", help="weights pre-loaded in HBM (no H2D)")
     ap.add_argument("--no-profile", action="store_true", help="no per-launch event timing")
+    ap.add_argument("--profile-copies", action="store_true",
+                    help="also time every page copy with HIP events (adds two events per copy on the "
+                         "copy streams, which are the binding resource: slower)")
     ap.add_argument("--no-journal", action="store_true")
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -57,9 +57,12 @@ typedef int psi_status;
 
 /* ------------------------------------------------------------ arena flags */
 #define PSI_ARENA_SYNC_COPY 0x1u /* page copies on the compute stream (transport control) */
-#define PSI_ARENA_PROFILE 0x2u   /* time every kernel launch and page copy with HIP events */
+#define PSI_ARENA_PROFILE 0x2u   /* time every kernel launch with HIP events */
 #define PSI_ARENA_DRY_RUN 0x4u   /* no device memory and no HIP calls: plans, lifecycle and
                                     byte accounting only (host-side tests) */
+#define PSI_ARENA_PROFILE_COPIES 0x8u /* with PSI_ARENA_PROFILE: time page copies too (two more
+                                         events per copy on the copy streams); also on while a
+                                         device timeline is being kept */
 
 /* --------------------------------------------------------- operator flags */
 #define PSI_OP_BASELINE_BIAS 0x1u /* [PSI] sec. III-A baseline: round the product to BF16,
@@ -124,7 +127,8 @@ typedef struct psi_stats {
   double attn_ms;
   uint64_t attn_launches;
   double attn_flops;        /* algorithmic 4*Mq*Mk*dh per head of the timed launches */
-  double copy_ms;           /* busy time of the busier of the two page-copy streams */
+  double copy_ms;           /* busy time of the busier of the two page-copy streams
+                               (PSI_ARENA_PROFILE_COPIES or while tracing) */
   uint64_t copy_bytes_timed;
 } psi_stats;
 
@@ -208,7 +212,8 @@ psi_status psi_arena_reset_stats(psi_arena* a);
  * to a base event.
  *   psi_arena_trace_start synchronises the arena's streams, records the base
  *   event on the compute stream and starts keeping up to `capacity` events
- *   (older ones are not overwritten: later events are dropped once full).
+ *   (older ones are not overwritten: later events are dropped once full);
+ *   page copies are timed from then on, as with PSI_ARENA_PROFILE_COPIES.
  *   psi_arena_trace_read synchronises (to read the timers), copies up to
  *   `capacity` events into `out` (caller-owned host array) and stores the
  *   number recorded in *count.

@@ -99,7 +99,8 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
         a->stats.event_waits++;
       }
       hipEvent_t t0 = nullptr, t1 = nullptr;
-      if (a->desc.flags & PSI_ARENA_PROFILE) {
+      if ((a->desc.flags & PSI_ARENA_PROFILE) &&
+          ((a->desc.flags & PSI_ARENA_PROFILE_COPIES) || a->trace_base)) {
         t0 = pool_event(a);
         t1 = pool_event(a);
         if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");

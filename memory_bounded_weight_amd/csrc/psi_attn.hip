@@ -260,6 +260,258 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
   }
 }
 
+// Software-pipelined variant.  The scores of key tile t+1 (S^T = K Q^T,
+// 16 MFMAs) are issued before the softmax of tile t (fp32 VALU and exp2),
+// so every wave always has independent matrix-core and vector work in
+// flight and the two waves of a SIMD no longer alternate between an
+// MFMA-only and a VALU-only phase.  K and V^T tiles are triple-buffered in
+// LDS: iteration t reads K of tile t+1 and V^T of tile t while tile t+2 is
+// stored.  Same arithmetic, in the same order per query, as attn_kernel.
+template <int QB, bool BF16P>
+__global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
+  constexpr int NT = QB * 2;
+  constexpr int KCH = KT * DH / 8 / NT;
+  constexpr int VCH = DH * KT / 8 / NT;
+  constexpr int NB = 3;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NB][KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NB][DH * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int h = blockIdx.y;
+  const int qrow = blockIdx.x * QB + wave * 32 + l32;
+  const bool qvalid = qrow < p.Mq;
+  const float c = p.alpha * 1.4426950408889634f;
+
+  bf16x8 qf[DH / 16];
+  {
+    const int qr = qvalid ? qrow : p.Mq - 1;
+    const uint16_t* qp = p.q + (long)qr * p.ldq + h * DH + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + kk * 16));
+  }
+
+  uint4 rk[KCH], rv[VCH];
+  const uint16_t* kbase = p.k + h * DH;
+  const uint16_t* vbase = p.vt + (long)h * DH * p.ldvt;
+  // Tile loads: K rows past Mk are clamped (their scores are masked), V^T
+  // entries past Mk are zeroed (their weights are 0; the padding of V^T is
+  // not initialised).
+  auto load_tile = [&](int key0) {
+    const bool ragged = key0 + KT > p.Mk;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = tid + i * NT;
+      int key = key0 + (c2 >> 4);
+      if (ragged) key = key < p.Mk ? key : p.Mk - 1;
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 & 15) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = tid + i * NT;
+      int vr = c2 >> 3, vkey = key0 + (c2 & 7) * 8;
+      if (!ragged) {
+        rv[i] = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+      } else {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (vkey < p.Mk) {
+          v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+          const int keep = p.Mk - vkey;  // elements of this chunk in range (>= 1)
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t mlo = (2 * q < keep) ? 0x0000FFFFu : 0u;
+            const uint32_t mhi = (2 * q + 1 < keep) ? 0xFFFF0000u : 0u;
+            w[q] &= (mlo | mhi);
+          }
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        rv[i] = v;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = tid + i * NT;
+      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 >> 4) * KS + (c2 & 15) * 8]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = tid + i * NT;
+      uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][(c2 >> 3) * VS + (c2 & 7) * 8]);
+      dst[0] = make_uint2(rv[i].x, rv[i].y);
+      dst[1] = make_uint2(rv[i].z, rv[i].w);
+    }
+  };
+  // S^T of one tile: the two 32-key accumulator chains alternate, and the
+  // K fragments of step kk+1 are read while the MFMAs of step kk run.
+  auto scores = [&](int buf, f32x16 (&s)[2]) {
+    const uint16_t* kr0 = &k_lds[buf][l32 * KS + half * 8];
+    const uint16_t* kr1 = kr0 + 32 * KS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[0][r] = 0.0f;
+      s[1][r] = 0.0f;
+    }
+    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr0);
+    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr1);
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      bf16x8 n0 = a0, n1 = a1;
+      if (kk + 1 < DH / 16) {
+        n0 = *reinterpret_cast<const bf16x8*>(kr0 + (kk + 1) * 16);
+        n1 = *reinterpret_cast<const bf16x8*>(kr1 + (kk + 1) * 16);
+      }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s[1], 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+
+  // softmax of tile scores s (key0: first key of the tile) and O^T += V^T P^T
+  auto softmax_pv = [&](f32x16 (&s)[2], int buf, int key0) {
+    if (key0 + KT > p.Mk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= p.Mk) s[kb][r] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float mc = m_new * c;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+        s[kb][r] = e;
+        lsum += e;
+      }
+    lsum += __shfl_xor(lsum, 32);
+    if (__any(m_new != m_run)) {
+      const float eta = __builtin_amdgcn_exp2f(m_run * c - mc);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= eta;
+      l_run *= eta;
+    }
+    l_run += lsum;
+    m_run = m_new;
+    // P^T as B operands for the 4 groups of 16 keys
+    bf16x8 bhi[4], blo[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
+        bf16x2 hi = __builtin_convertvector(pv, bf16x2);
+        bhi[g][j] = hi[0];
+        bhi[g][j + 1] = hi[1];
+        if (!BF16P) {
+          f32x2 hf = __builtin_convertvector(hi, f32x2);
+          f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};
+          bf16x2 lo = __builtin_convertvector(rem, bf16x2);
+          blo[g][j] = lo[0];
+          blo[g][j + 1] = lo[1];
+        }
+      }
+    }
+    // O^T += V^T P^T: per group the four channel tiles' hi MFMAs, then their
+    // lo MFMAs (each accumulator still sees hi then lo of every group in
+    // order); the V^T fragments of group g+1 are read during group g.
+    auto vfrag = [&](int g, int dt) {
+      const uint16_t* vr = &v_lds[buf][(dt * 32 + l32) * VS + 16 * g + 4 * half];
+      uint2 x0 = *reinterpret_cast<const uint2*>(vr);
+      uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
+      return __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+    };
+    bf16x8 va[DH / 32];
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt) va[dt] = vfrag(0, dt);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x8 vn[DH / 32];
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) vn[dt] = g + 1 < 4 ? vfrag(g + 1, dt) : va[dt];
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], bhi[g], o[dt], 0, 0, 0);
+      if (!BF16P) {
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], blo[g], o[dt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) va[dt] = vn[dt];
+    }
+  };
+
+  const int ntiles = (p.Mk + KT - 1) / KT;
+  load_tile(0);
+  store_tile(0);
+  if (ntiles > 1) {
+    load_tile(KT);
+    store_tile(1);
+  }
+  __syncthreads();
+  f32x16 s_cur[2], s_nxt[2];
+  scores(0, s_cur);
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t % NB;
+    if (t + 2 < ntiles) load_tile((t + 2) * KT);
+    if (t + 1 < ntiles) scores((t + 1) % NB, s_nxt);
+    softmax_pv(s_cur, b, t * KT);
+    if (t + 2 < ntiles) store_tile((t + 2) % NB);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  }
+
+  if (qvalid) {
+    uint16_t* op = p.q + (long)qrow * p.ldq + h * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = dt * 32 + 8 * rg + 4 * half;
+        uint16_t b0 = f2bf(o[dt][rg * 4 + 0] / l_run);
+        uint16_t b1 = f2bf(o[dt][rg * 4 + 1] / l_run);
+        uint16_t b2 = f2bf(o[dt][rg * 4 + 2] / l_run);
+        uint16_t b3 = f2bf(o[dt][rg * 4 + 3] / l_run);
+        uint2 w = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16));
+        *reinterpret_cast<uint2*>(op + c0) = w;
+      }
+  }
+}
+
+template <int QB, bool BF16P>
+hipError_t launch_pipe(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.Mq + QB - 1) / QB, a.heads);
+  hipLaunchKernelGGL((attn_kernel_pipe<QB, BF16P>), grid, dim3(QB * 2), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int QB, bool BF16P>
 hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
@@ -271,11 +523,17 @@ hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Mq <= 0) return hipSuccess;
-  // 256-query workgroups (8 waves sharing each K/V tile) when they still
-  // give every CU a workgroup, else 128-query ones
-  const bool big = a.config == 2 || (a.config == 0 && ((a.Mq + 255) / 256) * a.heads >= 256);
-  if (big) return a.bf16_p ? launch_q<256, true>(a, s) : launch_q<256, false>(a, s);
-  return a.bf16_p ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
+  // 256-query workgroups (8 waves sharing each K/V tile, software-pipelined)
+  // when they still give every CU a workgroup, else 128-query ones.
+  // Configurations: 1 = 128-query, 2 = 256-query, 3 = 256-query pipelined;
+  // all give identical bits.
+  int cfg = a.config;
+  if (cfg == 0) cfg = ((a.Mq + 255) / 256) * a.heads >= 256 ? 3 : 1;
+  switch (cfg) {
+    case 2: return a.bf16_p ? launch_q<256, true>(a, s) : launch_q<256, false>(a, s);
+    case 3: return a.bf16_p ? launch_pipe<256, true>(a, s) : launch_pipe<256, false>(a, s);
+    default: return a.bf16_p ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
+  }
 }
 
 }  // namespace psi

@@ -117,14 +117,23 @@ __device__ __forceinline__ void init_acc(const GemmArgs& p, f32x16 (&acc)[TM][TN
     }
 }
 
-// Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).
-// Remap so that every XCD owns a contiguous range of logical tiles, walked
-// with N fastest: concurrently running tiles of an XCD then share their A
-// row bands (and the page's B bands) in its L2.
-__device__ __forceinline__ int xcd_tile(int nt) {
+// Tile order.  Workgroup ids are dealt round-robin to the 8 XCDs (each
+// with its own L2); remap them so that every XCD owns a contiguous range of
+// logical tiles.  Within that range tiles are walked in groups of gm tile
+// rows: consecutive tiles go down the gm rows of a group, then to the next
+// column.  The tiles an XCD runs at the same time then cover about gm rows
+// x (concurrent / gm) columns, and share both operands' K slices in its L2
+// (gm = 1 walks whole rows, N fastest).
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  const int nt = tiles_m * tiles_n;
   int t = blockIdx.x;
   if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
-  return t;
+  const int per_group = gm * tiles_n;
+  const int first_m = (t / per_group) * gm;
+  const int rows = min(tiles_m - first_m, gm);
+  const int r = t % per_group;
+  tm = first_m + r % rows;
+  tn = r / rows;
 }
 
 // s_waitcnt immediate for gfx9: vmcnt = n (6 bits), expcnt and lgkmcnt not
@@ -148,7 +157,7 @@ __device__ __forceinline__ int xcd_tile(int nt) {
 // have landed (vmcnt) and the workgroup meets at a barrier, after which the
 // first fragments of tile kt+1 are read while the last MFMAs of kt run.
 template <int BM, int BN, int WGM, int WGN, int S>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, int tiles_m, int tiles_n, int gm) {
   constexpr int BK = 64, NW = WGM * WGN;
   constexpr int CPR = BK / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;        // rows per load instruction
@@ -159,9 +168,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, in
   static_assert(S >= 2 && S <= 4, "stages");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
 
-  const int t = xcd_tile(tiles_m * tiles_n);
-  const int m0 = (t / tiles_n) * BM;
-  const int n0 = (t % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, gm, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -259,15 +269,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, in
 // loaded into registers while the current one is multiplied, K tail zeroed.
 constexpr int kRegThreads = 256;
 
-__global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int tiles_m, int tiles_n, int gm) {
   constexpr int BM = 128, BN = 128, BK = 64, LDS = BK + 8, CPR = BK / 8;
   constexpr int A_PER_T = BM * BK / 8 / kRegThreads, B_PER_T = BN * BK / 8 / kRegThreads;
   constexpr int WM = 64, WN = 64, TM = 2, TN = 2, STAGE = (BM + BN) * LDS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
-  const int t = xcd_tile(tiles_m * tiles_n);
-  const int m0 = (t / tiles_n) * BM;
-  const int n0 = (t % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, gm, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
@@ -336,19 +347,34 @@ __global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int t
   epilogue<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 }
 
+// Group height of the tile order: with C tiles of one XCD in flight, a
+// window of g rows x C/g columns reads about g*BM + (C/g)*BN operand rows
+// per K slice, least near g = sqrt(C * BN / BM); a power of two, at most
+// the number of tile rows.
+int group_rows(int tiles_m, int concurrent, int bm, int bn) {
+  int g = 1;
+  while (g * 2 <= tiles_m && (double)(g * 2) * (g * 2) <= (double)concurrent * bn / bm) g *= 2;
+  return g;
+}
+
+constexpr int kXcdCUs = 32;  // CUs per XCD on MI355X
+
 template <int BM, int BN, int WGM, int WGN, int S>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
+  constexpr int per_cu = (160 * 1024) / (S * (BM + BN) * 64 * 2);  // workgroups per CU by LDS
+  const int gm = group_rows(tiles_m, kXcdCUs * per_cu, BM, BN);
   hipLaunchKernelGGL((gemm_kernel_dma<BM, BN, WGM, WGN, S>), dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, s,
-                     a, tiles_m, tiles_n);
+                     a, tiles_m, tiles_n, gm);
   return hipGetLastError();
 }
 
 hipError_t launch_reg(const GemmArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + 127) / 128;
   const int tiles_n = (a.N + 127) / 128;
-  hipLaunchKernelGGL(gemm_kernel_reg, dim3(tiles_m * tiles_n), dim3(kRegThreads), 0, s, a, tiles_m, tiles_n);
+  const int gm = group_rows(tiles_m, kXcdCUs * 2, 128, 128);
+  hipLaunchKernelGGL(gemm_kernel_reg, dim3(tiles_m * tiles_n), dim3(kRegThreads), 0, s, a, tiles_m, tiles_n, gm);
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ struct AttnArgs {
   int Mq, Mk, heads;
   float alpha;         // 1/sqrt(128) rounded to fp32
   int bf16_p;          // 1: softmax weights rounded to BF16 before P*V
-  int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query workgroups
+  int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query, 3: 256-query pipelined
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

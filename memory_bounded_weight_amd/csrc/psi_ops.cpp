@@ -226,9 +226,12 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
   return bias.release();
 }
 
-psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
-                         const psi_matrix* V, int token_chunks, float* acc_dev, uint16_t* y,
-                         unsigned flags) {
+// The FFN; with out_fence, the compute stream first waits for every journal
+// copy enqueued so far right before the first launch that writes y (the
+// journal's reads of y's previous contents are earlier consumers).
+static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
+                            const psi_matrix* V, int token_chunks, float* acc_dev, uint16_t* y,
+                            unsigned flags, psi_journal* out_fence) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
   size_t need = 0;
   psi_status st = psi_ffn_plan(&a->desc, M, d, U, V, token_chunks, acc_dev != nullptr, &need);
@@ -293,6 +296,7 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
     // down-projection: carried fp32 accumulator, bias once after the last tile
     if ((st = feeder.take(2 * J + 1, &page))) return st;
     if (last && (st = bias.get(1, &bb))) return st;
+    if (last && out_fence && !a->dry && (st = psi_journal_fence(out_fence, a->compute))) return st;
     for (int r0 = 0; r0 < M; r0 += rows_per) {
       const int mr = M - r0 < rows_per ? M - r0 : rows_per;
       GemmArgs g = gemm_args();
@@ -314,6 +318,12 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
     if ((st = feeder.give_back(2 * J + 1))) return st;
   }
   return bias.release();
+}
+
+psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
+                         const psi_matrix* V, int token_chunks, float* acc_dev, uint16_t* y,
+                         unsigned flags) {
+  return ffn_paged(a, x, M, d, U, V, token_chunks, acc_dev, y, flags, nullptr);
 }
 
 psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
@@ -446,8 +456,6 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   return bias.release();
 }
 
-psi_status psi_journal_fence(psi_journal* j, void* stream);
-
 psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int heads, int head_dim,
                            const psi_block_weights* w, int token_chunks, float* acc_dev,
                            psi_journal* fence, unsigned flags) {
@@ -464,8 +472,7 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
   if ((st = psi_attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo,
                            acc_dev, xt, f)))
     return st;
-  if (fence && !a->dry && (st = psi_journal_fence(fence, a->compute))) return st;
-  return psi_ffn_paged(a, xt, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f);
+  return ffn_paged(a, xt, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, fence);
 }
 
 }  // extern "C"

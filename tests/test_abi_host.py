@@ -268,3 +268,22 @@ def test_single_hip_runtime_in_process():
     hsa = {l.split()[-1] for l in maps if "libhsa-runtime64" in l}
     assert len(hip) == 1, hip
     assert len(hsa) <= 1, hsa
+
+
+def test_trace_needs_profiling_arena():
+    """psi_arena_trace_start / _read reject an arena created without
+    PSI_ARENA_PROFILE, and accept a profiling one (dry run: no events)."""
+    a = psi.psi_arena_create(desc(8, 1, 2))
+    try:
+        with pytest.raises(psi.PsiError):
+            psi.psi_arena_trace_start(a, 16)
+        with pytest.raises(psi.PsiError):
+            psi.psi_arena_trace_read(a, 16)
+    finally:
+        psi.psi_arena_destroy(a)
+    a = psi.psi_arena_create(desc(8, 1, 2, flags=psi.PSI_ARENA_DRY_RUN | psi.PSI_ARENA_PROFILE))
+    try:
+        psi.psi_arena_trace_start(a, 16)
+        assert psi.psi_arena_trace_read(a, 16) == []
+    finally:
+        psi.psi_arena_destroy(a)
