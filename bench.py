@@ -29,7 +29,7 @@ MiB = 1 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 HBM_PEAK_GBPS = 8000.0
 
-WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096")
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched")
 
 
 def log(*a):
@@ -57,6 +57,8 @@ def measure_h2d_gbps(torch, nbytes=256 * MiB, reps=5):
 
 def build_workload(args, torch, psi, synth):
     """Returns a dict with the step callable, its FLOPs and H2D bytes."""
+    import numpy as np
+
     stream = torch.cuda.current_stream().cuda_stream
     flags = 0 if args.no_profile else psi.PSI_ARENA_PROFILE
     if args.profile_copies and not args.no_profile:
@@ -86,7 +88,7 @@ def build_workload(args, torch, psi, synth):
         live += [x0, x, xt, acc]
         journal = None
         if not args.no_journal:
-            store = (args.steps + args.warmup + (1 if args.trace else 0)) * nblk * M * d * 2
+            store = (args.steps + args.warmup) * nblk * M * d * 2
             journal = psi.psi_journal_create(8 * MiB, 4, store)
         flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
         h2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2
@@ -137,6 +139,61 @@ def build_workload(args, torch, psi, synth):
                     config={"workload": f"paged FFN d={d} hidden={hid}", "tokens": M,
                             "token_chunks": chunks, "ffn_tile": tile, "arena_MiB": arena_mib,
                             "page_MiB": 8, "resident_weights": args.resident})
+    if args.workload == "ffnsched":
+        # FFN schedules over down-projection output tiles ([PSI] sec. III-B FFN
+        # reuse, Table IV): the timed step is the resident K-split schedule;
+        # after it, the reuse (journal) and recompute schedules are timed on
+        # the same input and compared bit for bit
+        M, d, hid, th, to = 1024, 2048, 8192, 2048, 512
+        c = synth.ffn_case(args.seed, M, d, hid)
+        U = psi.pinned_matrix(c["U"], c["a"], psi.PSI_SPLIT_ROWS, th)
+        V = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_COLS, th)
+        Vo = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_ROWS, to)
+        arena = psi.psi_arena_create(psi.arena_desc(32 * MiB, 8 * MiB, 2, 0, 0, stream, flags))
+        x = torch.from_numpy(c["x"].view("int16")).cuda()
+        y = torch.empty_like(x)
+        live += [x, y]
+        runs = args.warmup + args.steps
+        journal = psi.psi_journal_create(8 * MiB, 2, runs * hid * M * 2)
+
+        def step():
+            psi.psi_ffn_paged(arena, x, M, d, U, V, 1, None, y, 0)
+
+        def schedules():
+            torch.cuda.synchronize()
+            psi.psi_arena_sync(arena)
+            ref = y.cpu().numpy()
+            res = {}
+            for name, sched in (("reuse", psi.PSI_FFN_REUSE), ("recompute", psi.PSI_FFN_RECOMPUTE)):
+                yt = torch.empty_like(x)
+                s0 = psi.psi_arena_stats(arena)
+                j0 = psi.psi_journal_counters(journal)
+                times = []
+                for r in range(runs):
+                    torch.cuda.synchronize()
+                    t = time.perf_counter()
+                    psi.psi_ffn_tiled(arena, x, M, d, U, Vo, sched, journal, r, 0 if name == "reuse" else 1,
+                                      yt, 0)
+                    psi.psi_arena_sync(arena)
+                    psi.psi_journal_sync(journal)
+                    torch.cuda.synchronize()
+                    times.append(time.perf_counter() - t)
+                s1 = psi.psi_arena_stats(arena)
+                j1 = psi.psi_journal_counters(journal)
+                ms = 1e3 * sum(times[args.warmup:]) / max(1, len(times) - args.warmup)
+                res[name] = {"ms": round(ms, 3),
+                             "weight_bytes_h2d": (s1.bytes_h2d - s0.bytes_h2d) // runs,
+                             "journal_bytes_d2h": (j1[0] - j0[0]) // runs,
+                             "journal_bytes_h2d": (j1[1] - j0[1]) // runs,
+                             "bitwise_equal_to_resident": bool(np.array_equal(yt.cpu().numpy(), ref))}
+            return res
+
+        return dict(step=step, arena=arena, journal=None, flops=2 * 2.0 * M * d * hid,
+                    h2d=2 * d * hid * 2 + (hid + d) * 2, live=live, keep=(U, V, Vo, journal),
+                    after=schedules, after_name="schedules", close=lambda: psi.psi_journal_destroy(journal),
+                    config={"workload": f"FFN schedules d={d} hidden={hid}", "tokens": M,
+                            "ffn_tile": th, "output_tile": to, "arena_MiB": 32, "page_MiB": 8,
+                            "pages": 2, "resident_weights": False})
     if args.workload == "attn4096":
         M, Mc, d, heads = 6144, 1024, 4096, 32
         c = synth.attn_case(args.seed, M, Mc, d, cross=True)
@@ -234,8 +291,8 @@ def main():
     ap.add_argument("--pages", type=int, default=3,
                     help="page slots in the 80 MiB arena: 2 (+8 MiB workspace) or 3 (no workspace)")
     ap.add_argument("--trace", metavar="FILE",
-                    help="after the timed steps, run one more step with the device timeline on and write "
-                         "it to FILE as JSON (kind 0 GEMM, 1 attention, 2/3 page copy stream 0/1)")
+                    help="keep the device timeline of the timed steps (page copies timed too) and write it "
+                         "to FILE as JSON (kind 0 GEMM, 1 attention, 2/3 page copy stream 0/1)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -277,6 +334,8 @@ def main():
         step()
     sync_all()
     psi.psi_arena_reset_stats(arena)
+    if args.trace and not args.no_profile:
+        psi.psi_arena_trace_start(arena, 1 << 18)  # times page copies too from here on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     sync_all()
     t0 = time.perf_counter()
@@ -290,11 +349,8 @@ def main():
     ev_ms = ev0.elapsed_time(ev1)
     st = psi.psi_arena_stats(arena)
     if args.trace and not args.no_profile:
-        psi.psi_arena_trace_start(arena, 1 << 16)
-        step()
-        sync_all()
         with open(args.trace, "w") as f:
-            json.dump(psi.psi_arena_trace_read(arena, 1 << 16), f)
+            json.dump(psi.psi_arena_trace_read(arena, 1 << 18), f)
 
     total_flops = wl["flops"] * args.steps
     value = total_flops / wall / 1e12
@@ -358,6 +414,9 @@ def main():
             extra["output_finite"] = bool(np.isfinite((a.view(np.uint16).astype(np.uint32) << 16)
                                                       .view(np.float32)).all())
 
+    if wl.get("after"):
+        extra[wl["after_name"]] = wl["after"]()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.seed)
@@ -386,6 +445,8 @@ def main():
     print(json.dumps(out), flush=True)
     if journal:
         psi.psi_journal_destroy(journal)
+    if wl.get("close"):
+        wl["close"]()
     psi.psi_arena_destroy(arena)
 
 

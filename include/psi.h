@@ -243,15 +243,20 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
  * NULL to detach.  Errors: PSI_E_INVALID. */
 #define PSI_ROLE_ATTN_O 16
 #define PSI_ROLE_FFN_H 17
+#define PSI_ROLE_FFN_HSTATE 18  /* hidden tiles journaled by PSI_FFN_REUSE */
 psi_status psi_arena_set_probe(psi_arena* a, psi_journal* j, int32_t step, int32_t block);
 
 /* ------------------------------------------------------------ page API */
 
-/* Slice request ([PSI] sec. II-D): take the next page slot in round-robin
- * order and enqueue an H2D copy of `bytes` from pinned host memory into it
- * (free -> filling).  The copy waits for the slot's previous release event.
- * Errors: PSI_E_PAGE_TOO_SMALL (bytes > P), PSI_E_PAGE_BUSY (the slot still
- * has an unreleased request), PSI_E_NOT_PINNED, PSI_E_ALIGN. */
+/* Slice request ([PSI] sec. II-D): take the first free page slot from the
+ * round-robin position on (the next slot after the last one taken) and
+ * enqueue an H2D copy of `bytes` from pinned host memory into it (free ->
+ * filling).  The copy follows the slot's previous release event: if that
+ * has not completed yet, the host waits for it before enqueueing (counted
+ * in host_syncs), so the host never runs more than one round of slots
+ * ahead of the consumers.
+ * Errors: PSI_E_PAGE_TOO_SMALL (bytes > P), PSI_E_PAGE_BUSY (every slot
+ * still has an unreleased request), PSI_E_NOT_PINNED, PSI_E_ALIGN. */
 psi_status psi_page_submit(psi_arena* a, const void* host_pinned, size_t bytes, int* page_out);
 
 /* Makes the compute stream wait for the page's copy (filling -> consuming)
@@ -287,11 +292,42 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x_dev, int M, int K,
  *   V: [d, h] PSI_SPLIT_COLS with the same block t_h; bias b [d].
  *   Each U_J page, then each V_J page, serves all token_chunks chunks of x
  *   before release (page reuse across token chunks); the hidden tile H_J
- *   lives in arena scratch, the fp32 accumulator in acc_dev or scratch.
+ *   holds every token and lives in arena scratch, so all chunks of a page
+ *   go into one launch (per row the same arithmetic); the fp32 accumulator
+ *   lives in acc_dev or scratch.
  *   y_dev may alias x_dev (with PSI_OP_RESIDUAL: y = B(x + F(x))). */
 psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x_dev, int M, int d,
                          const psi_matrix* U, const psi_matrix* V, int token_chunks,
                          float* acc_dev, uint16_t* y_dev, unsigned flags);
+
+/* FFN over output tiles of the down-projection ([PSI] sec. III-B "FFN
+ * reuse"): V is split by rows into output tiles V_o = V[o t_o:(o+1) t_o, :]
+ * (PSI_SPLIT_ROWS, block t_o; one page holds t_o x h), U as in
+ * psi_ffn_paged (PSI_SPLIT_ROWS, block t_h).  Per output tile o:
+ * ACC_o = sum over J ascending of H_J V_o[:, J]^T (fp32, carried across J),
+ * y[:, o] = B(ACC_o + b_o) (+ residual), with H_J = B(phi(B(x U_J^T + a_J))).
+ *   PSI_FFN_REUSE      each H_J is computed once for all tokens, committed to
+ *                      the journal `j` under key (step, block, J,
+ *                      PSI_ROLE_FFN_HSTATE) and reloaded for every output
+ *                      tile (the paper's FFN reuse)
+ *   PSI_FFN_RECOMPUTE  scheduling baseline: for every output tile each U_J
+ *                      page is streamed again and H_J recomputed; `j` unused
+ * Per output the accumulation is the one of psi_ffn_paged (same hidden
+ * tiles in the same order), so both schedules give its bits.
+ *   x_dev [M, d], y_dev [M, d] (may alias x_dev with PSI_OP_RESIDUAL only
+ *   when t_o == d).  Scratch: H_J [M, t_h] bf16 and ACC_o [M, t_o] fp32.
+ *   flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL.  The journal store must
+ *   hold h x M x 2 bytes more than it holds (PSI_FFN_REUSE).
+ * Errors: PSI_E_INVALID (shapes, unknown schedule, missing journal, y
+ * aliasing x over more than one output tile), PSI_E_SCRATCH_EXHAUSTED,
+ * PSI_E_PAGE_TOO_SMALL, PSI_E_JOURNAL_KEY / PSI_E_JOURNAL_FULL. */
+#define PSI_FFN_REUSE 1
+#define PSI_FFN_RECOMPUTE 2
+psi_status psi_ffn_tiled_plan(const psi_arena_desc* d, int M, int dmodel, const psi_matrix* U,
+                              const psi_matrix* Vo, int schedule, size_t* scratch_needed);
+psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x_dev, int M, int d, const psi_matrix* U,
+                         const psi_matrix* Vo, int schedule, psi_journal* j, int32_t step,
+                         int32_t block, uint16_t* y_dev, unsigned flags);
 
 /* Paged attention sub-block ([PSI] sec. II-B eqs. (3)-(4)): per head group
  * g (heads_per_group = Wq->block / head_dim): Q_g = x Wq_g^T + bq_g,

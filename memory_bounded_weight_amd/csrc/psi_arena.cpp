@@ -67,16 +67,42 @@ static hipEvent_t pool_event(psi_arena* a) {
   return e;
 }
 
+// Before a copy into a slot, the host waits until the slot's previous
+// consumers have finished (the release event).  Ordering the copy after them
+// on the GPU instead (a copy-stream wait on the compute stream's event) lets
+// the host run ahead, and the runtime then blocks an H2D enqueue for
+// milliseconds at a time while the DMA engines idle (measured: 22 vs 43 GB/s
+// for 8 MiB pages in a slot/event pipeline).  With the wait on the host the
+// host stays at most one slot round ahead of the consumers, which keeps the
+// compute stream fed.
+static psi_status wait_release(psi_arena* a, psi_page_slot& slot) {
+  hipError_t q = hipEventQuery(slot.release);
+  if (q == hipSuccess) return PSI_OK;
+  if (q != hipErrorNotReady) return hip_fail(q, "hipEventQuery(release)");
+  PSI_HIP(hipEventSynchronize(slot.release));
+  a->stats.host_syncs++;
+  return PSI_OK;
+}
+
+int first_free_slot(const psi_arena* a) {
+  for (int i = 0; i < a->desc.n_pages; ++i) {
+    const int c = (a->next_slot + i) % a->desc.n_pages;
+    if (a->slots[c].state == psi_page_slot::FREE) return c;
+  }
+  return -1;
+}
+
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool pinned_check) {
   if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
   if (bytes > a->desc.page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
                                           " B > " + std::to_string(a->desc.page_bytes) + " B");
-  const int s = a->next_slot;
+  // the first free slot from the round-robin position on (a page held
+  // across many requests does not stall the others)
+  const int s = first_free_slot(a);
+  if (s < 0) return fail(PSI_E_PAGE_BUSY, "every page slot still has an unreleased request");
   psi_page_slot& slot = a->slots[s];
-  if (slot.state != psi_page_slot::FREE)
-    return fail(PSI_E_PAGE_BUSY, "page " + std::to_string(s) + " still has an unreleased request");
   if (!a->dry && pinned_check) {
     psi_status st = check_pinned(host, "page slice");
     if (st) return st;
@@ -88,15 +114,15 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
       PSI_HIP(hipEventRecord(slot.ready, a->compute));
     } else {
       // Whole pages, alternating between the two copy streams (two DMA
-      // engines): while one engine pays the start-up of its next copy (the
-      // release wait and the command set-up), the other one is streaming,
-      // so back-to-back 8 MiB pages keep the host link near its bulk rate.
+      // engines): while one engine pays the start-up of its next copy, the
+      // other one is streaming, so back-to-back 8 MiB pages keep the host
+      // link near its bulk rate.
       const int ci = a->next_copy;
       hipStream_t cs = ci ? a->copy1 : a->copy;
       a->next_copy = ci ^ 1;
       if (slot.released_once) {
-        PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
-        a->stats.event_waits++;
+        psi_status st = wait_release(a, slot);
+        if (st) return st;
       }
       hipEvent_t t0 = nullptr, t1 = nullptr;
       if ((a->desc.flags & PSI_ARENA_PROFILE) &&
@@ -139,8 +165,8 @@ psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_
   const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
   hipStream_t cs = sync ? a->compute : a->copy;
   if (!a->dry && !sync && slot.released_once) {
-    PSI_HIP(hipStreamWaitEvent(cs, slot.release, 0));
-    a->stats.event_waits++;
+    psi_status st = wait_release(a, slot);
+    if (st) return st;
   }
   size_t off = 0;
   for (int i = 0; i < n; ++i) {

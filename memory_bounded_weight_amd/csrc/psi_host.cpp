@@ -214,6 +214,30 @@ psi_status psi_ffn_plan(const psi_arena_desc* d, int M, int dmodel, const psi_ma
   return PSI_OK;
 }
 
+psi_status psi_ffn_tiled_plan(const psi_arena_desc* d, int M, int dmodel, const psi_matrix* U,
+                              const psi_matrix* Vo, int schedule, size_t* scratch_needed) {
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  if (schedule != PSI_FFN_REUSE && schedule != PSI_FFN_RECOMPUTE)
+    return fail(PSI_E_INVALID, "ffn tiled: unknown schedule");
+  if ((st = check_matrix(U, "U", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(Vo, "V", PSI_SPLIT_ROWS))) return st;
+  if (M < 0 || dmodel <= 0 || U->cols != dmodel || Vo->rows != dmodel || Vo->cols != U->rows)
+    return fail(PSI_E_INVALID, "ffn tiled: need U [h, d] and V [d, h]");
+  if (U->block % 8 != 0) return fail(PSI_E_ALIGN, "ffn tiled: hidden tile must be a multiple of 8");
+  if ((st = page_fit(d, U, "U")) || (st = page_fit(d, Vo, "V"))) return st;
+  if (schedule == PSI_FFN_RECOMPUTE && d->n_pages < 2 && !(U->resident && Vo->resident))
+    return fail(PSI_E_INVALID, "ffn tiled: the recompute schedule holds an output tile while U streams: "
+                               "needs two page slots");
+  const psi_matrix* uv[2] = {U, Vo};
+  if ((st = bias_fit(L, uv, 2))) return st;
+  size_t need = align_up((size_t)M * U->block * 2, kAlign) + align_up((size_t)M * Vo->block * 4, kAlign);
+  if ((st = scratch_fit(L, need, "FFN hidden tile and output-tile accumulator"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
 psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
                          const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
                          const psi_matrix* Wo, int acc_external, size_t* scratch_needed) {

@@ -140,6 +140,7 @@ void* scratch_alloc(psi_arena* a, size_t bytes, psi_status* st);
 void scratch_reset(psi_arena* a, size_t mark);
 
 // Page request (slice copy into the next round-robin page slot).
+int first_free_slot(const psi_arena* a);  // -1 when every slot is taken
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool check_pinned);
 psi_status page_acquire(psi_arena* a, int page);

@@ -75,7 +75,7 @@ class PageFeeder {
         ++submitted_;
         continue;
       }
-      if (a_->slots[a_->next_slot].state != psi_page_slot::FREE) break;
+      if (first_free_slot(a_) < 0) break;
       int s = -1;
       psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false);
       if (st) return st;
@@ -267,8 +267,12 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
     reqs.push_back(ru[J]);
     reqs.push_back(rv[J]);
   }
-  const int chunks = token_chunks > M ? M : token_chunks;
-  const int rows_per = (M + chunks - 1) / chunks;
+  // The hidden tile holds every token, so each page serves all token chunks
+  // (contiguous row ranges of x and H) in one launch: per row the
+  // arithmetic is that of a chunk-by-chunk loop, and the page is streamed
+  // once whatever the number of chunks ([PSI] sec. III-B page reuse).
+  (void)token_chunks;
+  const int rows_per = M;
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t *ba = nullptr, *bb = nullptr;
@@ -324,6 +328,131 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const ps
                          const psi_matrix* V, int token_chunks, float* acc_dev, uint16_t* y,
                          unsigned flags) {
   return ffn_paged(a, x, M, d, U, V, token_chunks, acc_dev, y, flags, nullptr);
+}
+
+psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
+                         const psi_matrix* Vo, int schedule, psi_journal* j, int32_t step, int32_t block,
+                         uint16_t* y, unsigned flags) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  psi_status st = psi_ffn_tiled_plan(&a->desc, M, d, U, Vo, schedule, nullptr);
+  if (st) return st;
+  if (schedule == PSI_FFN_REUSE && !j) return fail(PSI_E_INVALID, "ffn tiled: FFN reuse needs a journal");
+  if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "ffn tiled: no full accumulator to store");
+  const int nO = psi_matrix_pages(Vo);
+  if (x == y && nO > 1)
+    return fail(PSI_E_INVALID, "ffn tiled: y may alias x only with a single output tile");
+  if (!a->dry) {
+    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y"))) return st;
+    if (d % 8 != 0) return fail(PSI_E_ALIGN, "d must be a multiple of 8");
+    if ((st = check_matrix_pinned(a, U, "U")) || (st = check_matrix_pinned(a, Vo, "V"))) return st;
+  }
+  if (M == 0) return PSI_OK;
+  const bool resid = flags & PSI_OP_RESIDUAL;
+  const int th = U->block, to = Vo->block, h = U->rows;
+  const int nJ = psi_matrix_pages(U);
+  ScratchMark mark(a);
+  uint16_t* H = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
+  if (st) return st;
+  float* acc = static_cast<float*>(scratch_alloc(a, (size_t)M * to * 4, &st));
+  if (st) return st;
+  const psi_matrix* ms[2] = {U, Vo};
+  OpBiases bias;
+  if ((st = bias.stage(a, ms, 2))) return st;
+  std::vector<PageReq> ru, rv, reqs;
+  matrix_requests(U, ru);
+  matrix_requests(Vo, rv);
+  if (schedule == PSI_FFN_REUSE) {
+    reqs = ru;
+    reqs.insert(reqs.end(), rv.begin(), rv.end());
+  } else {
+    for (int o = 0; o < nO; ++o) {
+      reqs.push_back(rv[o]);
+      reqs.insert(reqs.end(), ru.begin(), ru.end());
+    }
+  }
+  PageFeeder feeder(a, reqs);
+  if ((st = feeder.feed())) return st;
+  const uint16_t *ba = nullptr, *bb = nullptr;
+  const unsigned baseline = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  // H_J = B(phi(B(x U_J^T + a_J))) for all tokens, stored compactly
+  // ([M, e_J], row stride e_J) so that a ragged last tile is also one
+  // contiguous journal entry
+  auto up = [&](int J, const uint16_t* page) -> psi_status {
+    psi_status s2 = bias.get(0, &ba);
+    if (s2) return s2;
+    const int ej = matrix_page_extent(U, J);
+    GemmArgs g = gemm_args();
+    g.A = x; g.lda = d;
+    g.B = page; g.ldb = d;
+    g.M = M; g.N = ej; g.K = d;
+    g.bias = ba ? ba + (size_t)J * th : nullptr;
+    g.out = H; g.ldo = ej;
+    g.epi = EPI_GELU;
+    g.baseline_bias = baseline;
+    return run_gemm(a, g);
+  };
+  // ACC_o (+)= H_J V_o[:, J]^T; the last hidden tile writes y[:, o]
+  auto down = [&](int o, int J, const uint16_t* vpage) -> psi_status {
+    const int eo = matrix_page_extent(Vo, o), ej = matrix_page_extent(U, J);
+    const bool last = J == nJ - 1;
+    GemmArgs g = gemm_args();
+    g.A = H; g.lda = ej;
+    g.B = vpage + (size_t)J * th; g.ldb = h;
+    g.M = M; g.N = eo; g.K = ej;
+    if (J > 0) { g.acc_in = acc; g.ld_acc_in = eo; }
+    if (last) {
+      psi_status s2 = bias.get(1, &bb);
+      if (s2) return s2;
+      const size_t c0 = (size_t)o * to;
+      g.bias = bb ? bb + c0 : nullptr;
+      g.out = y + c0; g.ldo = d;
+      if (resid) { g.resid = x + c0; g.ldr = d; }
+      g.baseline_bias = baseline;
+    } else {
+      g.epi = EPI_ACC;
+      g.acc_out = acc; g.ld_acc_out = eo;
+    }
+    return run_gemm(a, g);
+  };
+  const uint16_t* page;
+  if (schedule == PSI_FFN_REUSE) {
+    for (int J = 0; J < nJ; ++J) {
+      if ((st = feeder.take(J, &page)) || (st = up(J, page)) || (st = feeder.give_back(J))) return st;
+      const size_t hb = (size_t)M * matrix_page_extent(U, J) * 2;
+      if (!a->dry) {
+        // H_J to the journal; the next hidden tile overwrites H after the copy
+        if ((st = psi_journal_commit(j, psi_key{step, block, J, PSI_ROLE_FFN_HSTATE}, H, hb, a->compute)) ||
+            (st = psi_journal_fence(j, a->compute)))
+          return st;
+      }
+    }
+    for (int o = 0; o < nO; ++o) {
+      const uint16_t* vpage;
+      if ((st = feeder.take(nJ + o, &vpage))) return st;
+      for (int J = 0; J < nJ; ++J) {
+        const size_t hb = (size_t)M * matrix_page_extent(U, J) * 2;
+        if (!a->dry &&
+            (st = psi_journal_reload(j, psi_key{step, block, J, PSI_ROLE_FFN_HSTATE}, H, hb, a->compute)))
+          return st;
+        if ((st = down(o, J, vpage))) return st;
+      }
+      if ((st = feeder.give_back(nJ + o))) return st;
+    }
+  } else {
+    size_t r = 0;
+    for (int o = 0; o < nO; ++o) {
+      const size_t vi = r++;
+      const uint16_t* vpage;
+      if ((st = feeder.take(vi, &vpage))) return st;
+      for (int J = 0; J < nJ; ++J) {
+        const size_t ui = r++;
+        if ((st = feeder.take(ui, &page)) || (st = up(J, page)) || (st = feeder.give_back(ui))) return st;
+        if ((st = down(o, J, vpage))) return st;
+      }
+      if ((st = feeder.give_back(vi))) return st;
+    }
+  }
+  return bias.release();
 }
 
 psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,

@@ -56,6 +56,9 @@ PSI_OP_BF16_SOFTMAX = 0x8
 
 PSI_ROLE_ATTN_O = 16
 PSI_ROLE_FFN_H = 17
+PSI_ROLE_FFN_HSTATE = 18
+PSI_FFN_REUSE = 1
+PSI_FFN_RECOMPUTE = 2
 
 PSI_SPLIT_ROWS = 0
 PSI_SPLIT_COLS = 1
@@ -155,6 +158,9 @@ _sig("psi_page_acquire", [_vp, _i, _P(_vp)])
 _sig("psi_page_release", [_vp, _i])
 _sig("psi_linear_paged", [_vp, _vp, _i, _i, _P(psi_matrix), _vp, _vp, _u])
 _sig("psi_ffn_paged", [_vp, _vp, _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _vp, _vp, _u])
+_sig("psi_ffn_tiled_plan", [_P(psi_arena_desc), _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _P(_sz)])
+_sig("psi_ffn_tiled", [_vp, _vp, _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _vp, ctypes.c_int32,
+                       ctypes.c_int32, _vp, _u])
 _sig("psi_attn_paged", [_vp, _vp, _i, _vp, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
                         _P(psi_matrix), _P(psi_matrix), _vp, _vp, _u])
 _sig("psi_block_paged", [_vp, _vp, _vp, _i, _i, _i, _P(psi_block_weights), _i, _vp, _vp, _u])
@@ -174,7 +180,8 @@ EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_
            "psi_arena_reset_stats", "psi_arena_trace_start", "psi_arena_trace_read",
            "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
-           "psi_attn_paged", "psi_block_paged", "psi_journal_create", "psi_journal_destroy",
+           "psi_attn_paged", "psi_block_paged", "psi_ffn_tiled_plan", "psi_ffn_tiled",
+           "psi_journal_create", "psi_journal_destroy",
            "psi_journal_commit", "psi_journal_reload", "psi_journal_fence", "psi_journal_sync",
            "psi_journal_read", "psi_journal_counters"]
 
@@ -344,6 +351,18 @@ def psi_linear_paged(arena, x, M, K, W: psi_matrix, acc, y, flags=0):
 def psi_ffn_paged(arena, x, M, d, U: psi_matrix, V: psi_matrix, token_chunks, acc, y, flags=0):
     return _check(_lib.psi_ffn_paged(arena, _ptr(x), M, d, ctypes.byref(U), ctypes.byref(V),
                                      token_chunks, _ptr(acc), _ptr(y), flags), "psi_ffn_paged")
+
+
+def psi_ffn_tiled_plan(desc, M, d, U: psi_matrix, Vo: psi_matrix, schedule):
+    need = _sz(0)
+    st = _lib.psi_ffn_tiled_plan(ctypes.byref(desc), M, d, ctypes.byref(U), ctypes.byref(Vo), schedule,
+                                 ctypes.byref(need))
+    return _plan_status(st, need)
+
+
+def psi_ffn_tiled(arena, x, M, d, U: psi_matrix, Vo: psi_matrix, schedule, journal, step, block, y, flags=0):
+    return _check(_lib.psi_ffn_tiled(arena, _ptr(x), M, d, ctypes.byref(U), ctypes.byref(Vo), schedule,
+                                     journal, step, block, _ptr(y), flags), "psi_ffn_tiled")
 
 
 def psi_attn_paged(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc, y, flags=0):

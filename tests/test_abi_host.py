@@ -202,7 +202,8 @@ def test_page_lifecycle_dry_run():
 def test_ffn_streams_every_page_once_dry_run():
     """Page reuse across token chunks: with 4 chunks of 1,024 tokens each
     U_J and V_J page is copied exactly once (32 pages = 256 MiB of weights,
-    plus the bias slices), never once per chunk."""
+    plus the bias slices), never once per chunk; the hidden tile holds every
+    token, so one launch per page serves all four chunks."""
     a = psi.psi_arena_create(desc(80, 8, 2, 8))
     try:
         U, V = cfg5_ffn()
@@ -211,7 +212,7 @@ def test_ffn_streams_every_page_once_dry_run():
         s = psi.psi_arena_stats(a)
         assert s.page_copies == 32
         assert s.bytes_h2d == 256 * MiB + 16384 * 2 + 4096 * 2
-        assert s.kernel_launches == 32 * 4
+        assert s.kernel_launches == 32
         assert s.scratch_high_water == 4096 * 1024 * 2
     finally:
         psi.psi_arena_destroy(a)
@@ -285,5 +286,40 @@ def test_trace_needs_profiling_arena():
     try:
         psi.psi_arena_trace_start(a, 16)
         assert psi.psi_arena_trace_read(a, 16) == []
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_ffn_tiled_plans_and_recompute_stream_dry_run():
+    """FFN over down-projection output tiles ([PSI] sec. III-B): plan checks,
+    and the recompute baseline streams every U_J page again for every output
+    tile while the output-tile page of V stays held (two page slots)."""
+    d = desc(80, 8, 2, 8)
+    U, _ = cfg5_ffn()                                            # [16384, 4096], 1,024-row pages
+    Vo = fake_matrix(4096, 16384, psi.PSI_SPLIT_ROWS, 256)       # 256 x 16,384 = 8 MiB pages
+    st, need = psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vo, psi.PSI_FFN_REUSE)
+    assert st == psi.PSI_OK and need == 2048 * 1024 * 2 + 2048 * 256 * 4
+    assert psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vo, 3)[0] == psi.PSI_E_INVALID
+    Vk = fake_matrix(4096, 16384, psi.PSI_SPLIT_COLS, 1024)
+    assert psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vk, psi.PSI_FFN_REUSE)[0] == psi.PSI_E_INVALID
+    Vbig = fake_matrix(4096, 16384, psi.PSI_SPLIT_ROWS, 512)     # 16 MiB pages
+    assert psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vbig, psi.PSI_FFN_REUSE)[0] == psi.PSI_E_PAGE_TOO_SMALL
+    one = desc(80, 8, 1, 8)
+    assert psi.psi_ffn_tiled_plan(one, 2048, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE)[0] == psi.PSI_E_INVALID
+    assert psi.psi_ffn_tiled_plan(one, 2048, 4096, U, Vo, psi.PSI_FFN_REUSE)[0] == psi.PSI_OK
+    a = psi.psi_arena_create(desc(80, 8, 3, 0))
+    try:
+        fake = 0x10000
+        with pytest.raises(psi.PsiError) as e:  # FFN reuse without a journal
+            psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_REUSE, None, 0, 0, fake)
+        assert e.value.status == psi.PSI_E_INVALID
+        with pytest.raises(psi.PsiError) as e:  # y aliasing x over 16 output tiles
+            psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE, None, 0, 0, fake)
+        assert e.value.status == psi.PSI_E_INVALID
+        psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE, None, 0, 0, 2 * fake)
+        s = psi.psi_arena_stats(a)
+        n_o, n_j = 4096 // 256, 16384 // 1024
+        assert s.page_copies == n_o * (1 + n_j)
+        assert s.kernel_launches == n_o * n_j * 2  # up + down per (output tile, hidden tile)
     finally:
         psi.psi_arena_destroy(a)

@@ -420,8 +420,9 @@ def test_operators_back_to_back_share_arena(P):
 
 def test_device_timeline_structure(P):
     """The profiled arena's device timeline ([PSI] sec. II-D page lifecycle):
-    one copy per page on the two copy streams, one GEMM per page and token
-    chunk, ordered events with positive durations; kernel-only profiling
+    one copy per page on the two copy streams, one GEMM per page (both
+    token chunks in one launch), ordered events with positive durations;
+    kernel-only profiling
     keeps copy events off the copy streams until a trace is started."""
     c = synth.ffn_case(seed=4, M=192, d=256, hidden=1024)
     mu = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, 256)
@@ -433,12 +434,12 @@ def test_device_timeline_structure(P):
         P.psi_ffn_paged(ar, xd, 192, 256, mu, mv, 2, None, y, 0)
         P.psi_arena_sync(ar)
         st = P.psi_arena_stats(ar)
-        assert st.gemm_launches == 16 and st.copy_ms == 0.0  # 8 pages x 2 chunks; copies untimed
+        assert st.gemm_launches == 8 and st.copy_ms == 0.0  # one launch per page; copies untimed
         P.psi_arena_trace_start(ar, 1024)
         P.psi_ffn_paged(ar, xd, 192, 256, mu, mv, 2, None, y, 0)
         ev = P.psi_arena_trace_read(ar, 1024)
         kinds = [e[0] for e in ev]
-        assert kinds.count(0) == 16 and kinds.count(1) == 0
+        assert kinds.count(0) == 8 and kinds.count(1) == 0
         assert kinds.count(2) + kinds.count(3) == 8 and kinds.count(2) >= 1 and kinds.count(3) >= 1
         assert all(e[1] >= 0.0 and e[2] > 0.0 for e in ev)
         gemm_starts = [e[1] for e in ev if e[0] == 0]
