@@ -29,7 +29,7 @@ MiB = 1 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 HBM_PEAK_GBPS = 8000.0
 
-WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched")
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity")
 
 
 def log(*a):
@@ -139,6 +139,87 @@ def build_workload(args, torch, psi, synth):
                     config={"workload": f"paged FFN d={d} hidden={hid}", "tokens": M,
                             "token_chunks": chunks, "ffn_tile": tile, "arena_MiB": arena_mib,
                             "page_MiB": 8, "resident_weights": args.resident})
+    if args.workload == "capacity":
+        # [PSI] Table V analogue: one block of the 8-block stack (8,192 tokens)
+        # with the tiles fixed (8-head groups, 1,024-channel FFN tiles) under
+        # arenas 48/64/80/96 MiB x pages 4/8/16 MiB (two pages + 8 MiB
+        # workspace, the paper's layout); the timed step is the 80/8 setting.
+        # Afterwards every setting runs once: outcome, time, bitwise equality
+        # of the successes; and the device footprint of 2-, 4- and 8-block
+        # stacks at 80/8 (checkpoint-size independence, [PSI] sec. II-A).
+        M, d, heads, hid, nblk = 8192, 4096, 32, 16384, 8
+        blocks = [psi.block_weights(synth.block_weights(args.seed, b, d, hid), 1024, 1024) for b in range(nblk)]
+        x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
+        x = torch.empty_like(x0)
+        xt = torch.empty_like(x0)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        live += [x0, x, xt, acc]
+
+        def new_arena(arena_mib, page_mib, fl=flags):
+            return psi.psi_arena_create(psi.arena_desc(arena_mib * MiB, page_mib * MiB, 2, 8 * MiB, 0, stream, fl))
+
+        arena = new_arena(80, 8)
+
+        def step():
+            x.copy_(x0)
+            psi.psi_block_paged(arena, x, xt, M, heads, 128, blocks[0], 1, acc, None, 0)
+
+        def sweep():
+            torch.cuda.synchronize()
+            res, ref = [], None
+            for am in (48, 64, 80, 96):
+                for pm in (4, 8, 16):
+                    row = {"arena_MiB": am, "page_MiB": pm}
+                    try:
+                        a = new_arena(am, pm, 0)
+                    except psi.PsiError as e:
+                        row["outcome"] = e.name
+                        res.append(row)
+                        continue
+                    try:
+                        x.copy_(x0)
+                        torch.cuda.synchronize()
+                        t = time.perf_counter()
+                        psi.psi_block_paged(a, x, xt, M, heads, 128, blocks[0], 1, acc, None, 0)
+                        psi.psi_arena_sync(a)
+                        torch.cuda.synchronize()
+                        row["ms"] = round((time.perf_counter() - t) * 1e3, 3)
+                        row["outcome"] = "ok"
+                        out = x.cpu().numpy()
+                        if ref is None:
+                            ref = out
+                        row["bitwise_equal"] = bool(np.array_equal(out, ref))
+                    except psi.PsiError as e:
+                        row["outcome"] = e.name
+                    finally:
+                        psi.psi_arena_destroy(a)
+                    res.append(row)
+            # device footprint of stacks of 2, 4, 8 blocks at 80/8
+            foot = {}
+            for nb in (2, 4, 8):
+                torch.cuda.synchronize()
+                torch.cuda.reset_peak_memory_stats()
+                a = new_arena(80, 8, 0)
+                x.copy_(x0)
+                for b in range(nb):
+                    psi.psi_block_paged(a, x, xt, M, heads, 128, blocks[b], 1, acc, None, 0)
+                psi.psi_arena_sync(a)
+                torch.cuda.synchronize()
+                st2 = psi.psi_arena_stats(a)
+                foot[str(nb)] = {"arena_bytes": st2.arena_bytes, "scratch_high_water": st2.scratch_high_water,
+                                 "torch_peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+                                 "page_copies": st2.page_copies}
+                psi.psi_arena_destroy(a)
+            return {"settings": res, "footprint_by_blocks": foot}
+
+        flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
+        h2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2
+        return dict(step=step, arena=arena, journal=None, flops=flops_block, h2d=h2d_block, live=live,
+                    keep=blocks, after=sweep, after_name="capacity",
+                    config={"workload": "one block, capacity settings (Table V analogue)", "tokens": M,
+                            "d_model": d, "heads": heads, "head_dim": 128, "ffn_hidden": hid,
+                            "arena_MiB": 80, "page_MiB": 8, "pages": 2, "workspace_MiB": 8,
+                            "head_group": 8, "ffn_tile": 1024, "resident_weights": False})
     if args.workload == "ffnsched":
         # FFN schedules over down-projection output tiles ([PSI] sec. III-B FFN
         # reuse, Table IV): the timed step is the resident K-split schedule;

@@ -189,6 +189,7 @@ EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_
 class PsiError(RuntimeError):
     def __init__(self, status, func):
         self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
         msg = _lib.psi_last_error().decode(errors="replace")
         super().__init__(f"{func} -> {STATUS_NAMES.get(status, status)}: {msg}")
 

@@ -113,3 +113,44 @@ def test_stack_invocations_and_controls_bitwise(P, stack):
         got = run_stack(P, blocks, x0, **kw)[0]
         for b in range(3):
             assert np.array_equal(got[b], ref[0][b]), f"{name}: block {b} differs"
+
+
+def test_capacity_settings_outcomes_and_bitwise(P, stack):
+    """[PSI] Table V analogue at small size: one block with its tiles fixed
+    (1-head groups, 256-channel FFN tiles) under several arena/page
+    settings.  Too little scratch and too small pages fail at plan time
+    with their error, before anything is enqueued; every setting that runs
+    gives the same bits."""
+    blocks, x0 = stack
+    bw = P.block_weights(blocks[0], 128, 256)
+    page = 256 * D * 2  # the largest tile: 128 KiB
+    scratch = 3 * M * 128 * 2 + M * D * 4  # Q, K, V^T of one group + the fp32 ACC in scratch
+    outcomes, ref = {}, None
+    settings = [("fits", 2 * (page + 64 * 1024) + 2 * 64 * 1024 + scratch + 64 * 1024, page),
+                ("roomy", 4 * MiB, page),
+                ("big pages", 8 * MiB, 2 * page),
+                ("small scratch", 2 * page + 2 * 64 * 1024 + scratch // 2, page),
+                ("small pages", 4 * MiB, page // 2)]
+    for name, arena_bytes, page_bytes in settings:
+        try:
+            ar = make_arena(arena_bytes, page_bytes)
+        except P.PsiError as e:
+            outcomes[name] = e.name
+            continue
+        try:
+            x = dev(x0)
+            xt = torch.empty_like(x)
+            P.psi_block_paged(ar, x, xt, M, HEADS, 128, bw, 1, None, None, 0)
+            P.psi_arena_sync(ar)
+            out = host(x)
+            outcomes[name] = "ok"
+            if ref is None:
+                ref = out
+            assert np.array_equal(out, ref), name
+        except P.PsiError as e:
+            outcomes[name] = e.name
+            assert e.status in (P.PSI_E_SCRATCH_EXHAUSTED, P.PSI_E_PAGE_TOO_SMALL), name
+        finally:
+            P.psi_arena_destroy(ar)
+    assert outcomes == {"fits": "ok", "roomy": "ok", "big pages": "ok",
+                        "small scratch": "PSI_E_SCRATCH_EXHAUSTED", "small pages": "PSI_E_PAGE_TOO_SMALL"}, outcomes
