@@ -87,6 +87,21 @@ def _configure(lib):
     lib.orc_block.restype = ctypes.c_int
     lib.orc_block.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                               ctypes.c_int] + [_u16p] * 12 + [ctypes.c_int]
+    lib.orc_attention_ex.restype = ctypes.c_int
+    lib.orc_attention_ex.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _u16p, _u16p, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     _u16p, ctypes.c_int]
+    lib.orc_rmsnorm.restype = None
+    lib.orc_rmsnorm.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u16p, ctypes.c_double,
+                                ctypes.c_int, _u16p, ctypes.c_int]
+    lib.orc_rope_split.restype = None
+    lib.orc_rope_split.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p,
+                                   _f32p, _u16p, ctypes.c_int]
+    lib.orc_attn_sublayer_ext.restype = ctypes.c_int
+    lib.orc_attn_sublayer_ext.argtypes = [_u16p, ctypes.c_int, _u16p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int] + [_u16p] * 10 + \
+        [ctypes.c_double, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+         ctypes.c_int, _u16p]
     lib.orc_residual.restype = None
     lib.orc_residual.argtypes = [_u16p, _u16p, ctypes.c_size_t]
     return lib
@@ -241,3 +256,52 @@ def residual(x, y):
     out = np.array(x, dtype=np.uint16, copy=True, order="C")
     _load().orc_residual(_u16(out), _u16(np.ascontiguousarray(y, dtype=np.uint16)), out.size)
     return out
+
+
+def attention_ex(q, k, v, heads, dh, *, bf16_p=False):
+    """orc_attention with the baseline BF16-numerator choice (bf16_p)."""
+    Mq, dq = q.shape
+    Mk, dk = k.shape
+    assert v.shape == (Mk, dk) and dq == dk == heads * dh
+    o = np.empty((Mq, dq), dtype=np.uint16)
+    rc = _load().orc_attention_ex(_u16(q), Mq, dq, _u16(k), _u16(v), Mk, dk, dk, heads, dh,
+                                  int(bool(bf16_p)), _u16(o), dq)
+    if rc != 0:
+        raise RuntimeError(f"orc_attention_ex failed: {rc}")
+    return o
+
+
+def rmsnorm(x, g, eps=1e-6, tile=0):
+    """Full-row RMS normalisation with a tile-partitioned sum of squares."""
+    M, d = x.shape
+    y = np.empty((M, d), dtype=np.uint16)
+    _load().orc_rmsnorm(_u16(x), M, d, d, _u16(g), float(eps), int(tile), _u16(y), d)
+    return y
+
+
+def rope_split(x, heads, dh, cos, sin):
+    """Split rotary embedding per head with fp32 tables [M, dh/2]."""
+    M, d = x.shape
+    assert d == heads * dh and cos.shape == sin.shape == (M, dh // 2)
+    y = np.empty((M, d), dtype=np.uint16)
+    _load().orc_rope_split(_u16(x), M, heads, dh, d, _f32(cos), _f32(sin), _u16(y), d)
+    return y
+
+
+def attn_sublayer_ext(x, w, heads, dh, *, ctx=None, gq=None, gk=None, eps=1e-6, norm_tile=0,
+                      cos_q=None, sin_q=None, cos_k=None, sin_k=None, variant=0, bf16_p=False,
+                      residual=True):
+    """Attention sub-block with optional q/k RMS normalisation and split
+    rotary positions; ``w`` maps Wq,bq,Wk,bk,Wv,bv,Wo,bo to arrays."""
+    M, d = x.shape
+    Mc = 0 if ctx is None else ctx.shape[0]
+    y = np.empty((M, d), dtype=np.uint16)
+    names = ["Wq", "bq", "Wk", "bk", "Wv", "bv", "Wo", "bo"]
+    rc = _load().orc_attn_sublayer_ext(_u16(x), M, _u16(ctx), Mc, d, heads, dh,
+                                       *[_u16(w[n], n) for n in names], _u16(gq), _u16(gk),
+                                       float(eps), int(norm_tile), _f32(cos_q), _f32(sin_q),
+                                       _f32(cos_k), _f32(sin_k), int(variant), int(bool(bf16_p)),
+                                       int(bool(residual)), _u16(y))
+    if rc != 0:
+        raise RuntimeError(f"orc_attn_sublayer_ext failed: {rc}")
+    return y

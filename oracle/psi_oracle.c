@@ -271,6 +271,161 @@ int orc_attention(const uint16_t* q, int Mq, int ldq, const uint16_t* k,
   return err;
 }
 
+/* Attention with the BF16-numerator choice of the baseline/modified
+ * comparison ([PSI] sec. III-A, sec. IV-B).  bf16_p == 0 is orc_attention.
+ * bf16_p != 0 (baseline PSI): the weights multiplying V are rounded to
+ * BF16, z = sum_j fl32(f(B(p_j)) * f(v_j)); the normaliser l keeps the fp32
+ * weights, as in orc_attention. */
+int orc_attention_ex(const uint16_t* q, int Mq, int ldq, const uint16_t* k,
+                     const uint16_t* v, int Mk, int ldk, int ldv, int heads,
+                     int dh, int bf16_p, uint16_t* o, int ldo) {
+  if (!bf16_p) return orc_attention(q, Mq, ldq, k, v, Mk, ldk, ldv, heads, dh, o, ldo);
+  if (Mk < 1 || dh < 1 || heads < 1) return -1;
+  const float alpha = (float)(1.0 / sqrt((double)dh));
+  int err = 0;
+#pragma omp parallel
+  {
+    float* s = (float*)malloc((size_t)Mk * sizeof(float));
+    float* z = (float*)malloc((size_t)dh * sizeof(float));
+    if (!s || !z) {
+#pragma omp atomic write
+      err = -2;
+    } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+      for (int hd = 0; hd < heads; ++hd) {
+        for (int i = 0; i < Mq; ++i) {
+          const uint16_t* qi = q + (size_t)i * ldq + (size_t)hd * dh;
+          float m = -INFINITY;
+          for (int j = 0; j < Mk; ++j) {
+            const uint16_t* kj = k + (size_t)j * ldk + (size_t)hd * dh;
+            s[j] = alpha * dot_chain(0.0f, qi, kj, dh);
+            if (s[j] > m) m = s[j];
+          }
+          float l = 0.0f;
+          for (int c = 0; c < dh; ++c) z[c] = 0.0f;
+          for (int j = 0; j < Mk; ++j) {
+            float p = (float)exp((double)(s[j] - m));
+            l = l + p;
+            float pb = orc_f(orc_bf16_from_float(p));
+            const uint16_t* vj = v + (size_t)j * ldv + (size_t)hd * dh;
+            for (int c = 0; c < dh; ++c) z[c] = z[c] + pb * orc_f(vj[c]);
+          }
+          uint16_t* oi = o + (size_t)i * ldo + (size_t)hd * dh;
+          for (int c = 0; c < dh; ++c) oi[c] = orc_bf16_from_float(z[c] / l);
+        }
+      }
+    }
+    free(s);
+    free(z);
+  }
+  return err;
+}
+
+/* Full-row RMS normalisation with a tile-partitioned sum of squares
+ * ([PSI] sec. II-B): for each row, s = sum over column tiles J (ascending)
+ * of s_J = sum_{i in J} f(x_i)^2, then y_i = B(f(g_i) f(x_i) / sqrt(s/d +
+ * eps)): one denominator for every tile of the row.  Evaluated in double
+ * and rounded once per output.  tile <= 0 means one tile of width d.
+ * x and y may alias. */
+void orc_rmsnorm(const uint16_t* x, int M, int d, int ldx, const uint16_t* g,
+                 double eps, int tile, uint16_t* y, int ldy) {
+  if (tile <= 0 || tile > d) tile = d;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < M; ++r) {
+    const uint16_t* xr = x + (size_t)r * ldx;
+    double s = 0.0;
+    for (int j0 = 0; j0 < d; j0 += tile) {
+      const int j1 = j0 + tile < d ? j0 + tile : d;
+      double sj = 0.0;
+      for (int i = j0; i < j1; ++i) sj += (double)orc_f(xr[i]) * (double)orc_f(xr[i]);
+      s += sj;
+    }
+    const double den = sqrt(s / d + eps);
+    uint16_t* yr = y + (size_t)r * ldy;
+    for (int i = 0; i < d; ++i) yr[i] = orc_bf16_from_double((double)orc_f(g[i]) * (double)orc_f(xr[i]) / den);
+  }
+}
+
+/* Split rotary embedding ([PSI] sec. II-B): inside each head of width dh,
+ * the pair (a, b) = (x_j, x_{j+dh/2}), j < dh/2, becomes
+ * (c a - s b, s a + c b) with c = cos[t][j], s = sin[t][j] from the
+ * caller's fp32 tables [M, dh/2] (row t = token); evaluated in double,
+ * rounded once per output; in place allowed (x == y). */
+void orc_rope_split(const uint16_t* x, int M, int heads, int dh, int ldx,
+                    const float* cs, const float* sn, uint16_t* y, int ldy) {
+  const int hh = dh / 2;
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < M; ++t) {
+    for (int h = 0; h < heads; ++h) {
+      const uint16_t* xr = x + (size_t)t * ldx + (size_t)h * dh;
+      uint16_t* yr = y + (size_t)t * ldy + (size_t)h * dh;
+      for (int j = 0; j < hh; ++j) {
+        const double a = orc_f(xr[j]), b = orc_f(xr[j + hh]);
+        const double c = cs[(size_t)t * hh + j], sv = sn[(size_t)t * hh + j];
+        const uint16_t u = orc_bf16_from_double(c * a - sv * b);
+        const uint16_t w = orc_bf16_from_double(sv * a + c * b);
+        yr[j] = u;
+        yr[j + hh] = w;
+      }
+    }
+  }
+}
+
+/* Attention sub-block with q/k normalisation and rotary positions, each a
+ * declared BF16 write:
+ *   Q = B(x Wq^T + bq); if gq: Q = rmsnorm(Q, gq, eps, norm_tile); if
+ *   cos_q: Q = rope(Q, cos_q, sin_q); K likewise from src with gk and
+ *   cos_k/sin_k (NULL cos_k: the query tables, self-attention);
+ *   V = B(src Wv^T + bv); O = attention (bf16_p as orc_attention_ex);
+ *   Y = B(O Wo^T + bo); residual: y = B(f(x) + f(Y)). */
+int orc_attn_sublayer_ext(const uint16_t* x, int M, const uint16_t* ctx, int Mc,
+                          int d, int heads, int dh, const uint16_t* Wq,
+                          const uint16_t* bq, const uint16_t* Wk,
+                          const uint16_t* bk, const uint16_t* Wv,
+                          const uint16_t* bv, const uint16_t* Wo,
+                          const uint16_t* bo, const uint16_t* gq,
+                          const uint16_t* gk, double eps, int norm_tile,
+                          const float* cos_q, const float* sin_q,
+                          const float* cos_k, const float* sin_k, int variant,
+                          int bf16_p, int residual, uint16_t* y) {
+  if (heads * dh != d || dh % 2) return -1;
+  const uint16_t* src = ctx ? ctx : x;
+  const int Ms = ctx ? Mc : M;
+  if (!cos_k) { cos_k = cos_q; sin_k = sin_q; }
+  if (cos_q && cos_k == cos_q && Ms != M) return -1;
+  uint16_t* Q = (uint16_t*)malloc((size_t)M * d * 2);
+  uint16_t* Kb = (uint16_t*)malloc((size_t)Ms * d * 2);
+  uint16_t* Vb = (uint16_t*)malloc((size_t)Ms * d * 2);
+  uint16_t* O = (uint16_t*)malloc((size_t)M * d * 2);
+  uint16_t* Y = (uint16_t*)malloc((size_t)M * d * 2);
+  int rc = 0;
+  if (!Q || !Kb || !Vb || !O || !Y) {
+    rc = -2;
+  } else {
+    orc_linear(x, M, d, Wq, d, bq, variant, NULL, NULL, Q);
+    orc_linear(src, Ms, d, Wk, d, bk, variant, NULL, NULL, Kb);
+    orc_linear(src, Ms, d, Wv, d, bv, variant, NULL, NULL, Vb);
+    if (gq) orc_rmsnorm(Q, M, d, d, gq, eps, norm_tile, Q, d);
+    if (gk) orc_rmsnorm(Kb, Ms, d, d, gk, eps, norm_tile, Kb, d);
+    if (cos_q) {
+      orc_rope_split(Q, M, heads, dh, d, cos_q, sin_q, Q, d);
+      orc_rope_split(Kb, Ms, heads, dh, d, cos_k, sin_k, Kb, d);
+    }
+    rc = orc_attention_ex(Q, M, d, Kb, Vb, Ms, d, d, heads, dh, bf16_p, O, d);
+    if (rc == 0) {
+      orc_linear(O, M, d, Wo, d, bo, variant, NULL, NULL, Y);
+      for (size_t i = 0; i < (size_t)M * d; ++i)
+        y[i] = residual ? orc_bf16_from_float(orc_f(x[i]) + orc_f(Y[i])) : Y[i];
+    }
+  }
+  free(Q);
+  free(Kb);
+  free(Vb);
+  free(O);
+  free(Y);
+  return rc;
+}
+
 /* Attention sub-block: projections, attention, output projection, residual.
  *   x [M,d]; ctx [Mc,d] or NULL for self-attention (keys/values from x).
  *   Q = x Wq^T + bq, K = src Wk^T + bk, V = src Wv^T + bv   (bf16 writes)

@@ -42,6 +42,52 @@ MUTANTS["double_rounding_via_float"] = (
     "uint16_t orc_bf16_from_double(double v) {\n  return orc_bf16_from_float((float)v);\n  if (isnan(v))")
 
 
+# Mistakes in the q/k normalisation, rotary and BF16-numerator parts; their
+# pins are selected by keyword so the case stays short.
+EXT_PINS = "rmsnorm or rope or bf16_numerator or sublayer_ext"
+EXT_MUTANTS = {
+    "rms_drops_eps": ("const double den = sqrt(s / d + eps);", "const double den = sqrt(s / d);"),
+    "rms_mean_over_tile": ("const double den = sqrt(s / d + eps);", "const double den = sqrt(s / tile + eps);"),
+    "rms_no_square": ("sj += (double)orc_f(xr[i]) * (double)orc_f(xr[i]);", "sj += fabs((double)orc_f(xr[i]));"),
+    "rms_drops_gain": ("orc_bf16_from_double((double)orc_f(g[i]) * (double)orc_f(xr[i]) / den)",
+                       "orc_bf16_from_double((double)orc_f(xr[i]) / den)"),
+    "rms_last_tile_only": ("      s += sj;", "      s = sj;"),
+    "rope_sign": ("orc_bf16_from_double(c * a - sv * b)", "orc_bf16_from_double(c * a + sv * b)"),
+    "rope_ignores_head": ("const uint16_t* xr = x + (size_t)t * ldx + (size_t)h * dh;",
+                          "const uint16_t* xr = x + (size_t)t * ldx;"),
+    "rope_table_row": ("const double c = cs[(size_t)t * hh + j], sv = sn[(size_t)t * hh + j];",
+                       "const double c = cs[j], sv = sn[j];"),
+    "bf16p_not_rounded": ("float pb = orc_f(orc_bf16_from_float(p));", "float pb = p;"),
+    "bf16p_rounds_normaliser": ("float p = (float)exp((double)(s[j] - m));\n            l = l + p;",
+                                "float p = (float)exp((double)(s[j] - m));\n            l = l + orc_f(orc_bf16_from_float(p));"),
+    "ext_k_uses_q_gain": ("if (gk) orc_rmsnorm(Kb, Ms, d, d, gk,", "if (gk) orc_rmsnorm(Kb, Ms, d, d, gq,"),
+}
+
+
+def _run_mutant(old, new, tmp_path, select=None):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation pattern not found"
+    mut = src.replace(old, new)
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(mut)
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                    "-shared", "-w", "-o", str(lib), str(csrc), "-lm"], check=True)
+    env = dict(os.environ, PSI_ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
+    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+           os.path.join(ROOT, "tests", "test_oracle_pins.py")]
+    if select:
+        cmd += ["-k", select]
+    return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name", sorted(EXT_MUTANTS))
+def test_pins_reject_ext_mutant(name, tmp_path):
+    old, new = EXT_MUTANTS[name]
+    r = _run_mutant(old, new, tmp_path, EXT_PINS)
+    assert r.returncode != 0, f"pins accepted mutant {name}:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_reject_mutant(name, tmp_path):
     old, new = MUTANTS[name]

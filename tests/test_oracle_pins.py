@@ -496,3 +496,163 @@ def test_block_is_composition_of_sublayers():
                              w["Wo"], w["bo"], heads, dh)
     y2 = oracle.ffn(t, w["U"], w["a"], w["V"], w["b"], residual=True)
     assert np.array_equal(y, y2)
+
+
+# --------------------------------------------- RMS normalisation and RoPE
+
+def _bits(vals) -> np.ndarray:
+    return synth.f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def _rms_exact(xrow, grow, eps, digits=60):
+    """y_i = B(g_i x_i / sqrt(s/d + eps)) with s = sum x^2 exact (rationals) and
+    the square root in 60-digit decimal arithmetic."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = digits
+    xs = [frac_of_bits(u) for u in xrow]
+    gs = [frac_of_bits(u) for u in grow]
+    d = len(xs)
+    s = sum(v * v for v in xs)
+    q = s / d + Fraction(eps)
+    den = (Decimal(q.numerator) / Decimal(q.denominator)).sqrt()
+    out = []
+    for xv, gv in zip(xs, gs):
+        y = Decimal((gv * xv).numerator) / Decimal((gv * xv).denominator) / den
+        out.append(exact_bf16_round(Fraction(y)))
+    return out
+
+
+def test_rmsnorm_hand_example_and_brute_force():
+    """[PSI] sec. II-B full-row RMS: y = g x / sqrt(s/d + eps), s = sum x^2.
+    [3, 4] gives 3/sqrt(12.5), 4/sqrt(12.5); random 8-wide rows agree with an
+    exact-rational / 60-digit evaluation rounded to nearest-even BF16."""
+    y = oracle.rmsnorm(_bits([[3.0, 4.0]]), _bits([1.0, 1.0]), eps=0.0)
+    assert [frac_of_bits(u) for u in y[0]] == _rms_exact(_bits([3.0, 4.0]), _bits([1.0, 1.0]), 0.0)
+    assert f(y[0]).tolist() == [0.84765625, 1.1328125]
+    rng = np.random.default_rng(11)
+    x = _bits(rng.standard_normal((6, 8)) * 3)
+    g = _bits(1 + 0.3 * rng.standard_normal(8))
+    for eps in (0.0, 1e-6, 0.25):
+        y = oracle.rmsnorm(x, g, eps=eps, tile=3)
+        for r in range(6):
+            assert [frac_of_bits(u) for u in y[r]] == _rms_exact(x[r], g, eps), (eps, r)
+
+
+def test_rmsnorm_closed_forms_and_invariants():
+    """Constant rows normalise to +-g; scaling x by 2^k leaves y unchanged
+    (eps = 0); scaling g by 2^k scales y by 2^k; a zero row with eps > 0 is
+    zero; when every partial sum is exact, the tile width does not matter."""
+    one = _bits(np.ones(16))
+    c = _bits(np.full((2, 16), [[2.5], [-0.75]]))
+    y = oracle.rmsnorm(c, one, eps=0.0)
+    assert np.array_equal(f(y[0]), np.ones(16)) and np.array_equal(f(y[1]), -np.ones(16))
+    rng = np.random.default_rng(12)
+    x = _bits(rng.standard_normal((5, 64)))
+    g = _bits(rng.standard_normal(64))
+    y0 = oracle.rmsnorm(x, g, eps=0.0, tile=16)
+    assert np.array_equal(oracle.rmsnorm(_bits(f(x) * 8.0), g, eps=0.0, tile=16), y0)
+    assert np.array_equal(f(oracle.rmsnorm(x, _bits(f(g) * 0.25), eps=0.0, tile=16)), f(y0) * 0.25)
+    z = oracle.rmsnorm(_bits(np.zeros((1, 8))), one[:8], eps=1e-6)
+    assert np.array_equal(f(z), np.zeros((1, 8)))
+    xi = _bits(rng.integers(-3, 4, size=(4, 48)).astype(np.float32))  # squares and sums exact
+    gi = _bits(rng.standard_normal(48))
+    ref = oracle.rmsnorm(xi, gi, eps=1e-6, tile=0)
+    for tile in (1, 5, 16, 47):
+        assert np.array_equal(oracle.rmsnorm(xi, gi, eps=1e-6, tile=tile), ref), tile
+
+
+def test_rope_split_pairs_and_exact_angles():
+    """[PSI] sec. II-B split RoPE: inside each head the pair (x_j, x_{j+dh/2})
+    becomes (c a - s b, s a + c b).  cos 0 / sin 0 is the identity; a
+    quarter turn maps (a, b) to (-b, a) exactly; a single nonzero element
+    only touches its own pair in its own head; a rational rotation agrees
+    with exact arithmetic."""
+    heads, dh, M = 3, 8, 4
+    rng = np.random.default_rng(13)
+    x = _bits(rng.standard_normal((M, heads * dh)))
+    z = np.zeros((M, dh // 2), np.float32)
+    o = np.ones((M, dh // 2), np.float32)
+    assert np.array_equal(oracle.rope_split(x, heads, dh, o, z), x)
+    q = oracle.rope_split(x, heads, dh, z, o)
+    fx, fq = f(x).reshape(M, heads, dh), f(q).reshape(M, heads, dh)
+    assert np.array_equal(fq[..., :dh // 2], -fx[..., dh // 2:])
+    assert np.array_equal(fq[..., dh // 2:], fx[..., :dh // 2])
+    e = np.zeros((1, heads * dh), np.float32)
+    e[0, 1 * dh + 1] = 1.0  # head 1, j = 1
+    cs = np.full((1, dh // 2), 0.6, np.float32)
+    sn = np.full((1, dh // 2), 0.8, np.float32)
+    r = f(oracle.rope_split(_bits(e), heads, dh, cs, sn))[0]
+    nz = np.nonzero(r)[0].tolist()
+    assert nz == [1 * dh + 1, 1 * dh + 1 + dh // 2]
+    # per-token, per-pair tables (rows and pair indices taken from the table)
+    tab_c = rng.choice(np.array([1.0, 0.0, 0.6, -0.8, 0.28], np.float32), size=(M, dh // 2))
+    tab_s = rng.choice(np.array([0.0, 1.0, 0.8, 0.6, -0.96], np.float32), size=(M, dh // 2))
+    got = oracle.rope_split(x, heads, dh, tab_c, tab_s)
+    for t in range(M):
+        for h in range(heads):
+            for j in range(dh // 2):
+                cj, sj = Fraction(float(tab_c[t, j])), Fraction(float(tab_s[t, j]))
+                a, b = frac_of_bits(x[t, h * dh + j]), frac_of_bits(x[t, h * dh + j + dh // 2])
+                assert frac_of_bits(got[t, h * dh + j]) == exact_bf16_round(cj * a - sj * b)
+                assert frac_of_bits(got[t, h * dh + j + dh // 2]) == exact_bf16_round(sj * a + cj * b)
+
+
+def test_attention_bf16_numerator_two_keys():
+    """Baseline PSI's BF16 numerator: with two keys whose scores differ by a
+    gap g and one-hot values, the outputs are B(1 / l) and B(B(p) / l), with
+    p = exp(-g) and l = 1 + p in fp32 (the normaliser keeps the fp32
+    weight) -- versus B(p / l) for the fp32 weights of modified PSI.  A gap
+    is chosen where rounding the numerator, or the normaliser, would change
+    the BF16 output.  Equal scores give identical results."""
+    dh = 4
+    alpha = np.float32(0.5)  # 1 / sqrt(4)
+    B = lambda v: f(synth.f32_to_bf16_bits(np.array([v], np.float32)))[0]  # noqa: E731
+    chosen = None
+    for kb in synth.f32_to_bf16_bits(-np.linspace(0.2, 4.0, 400, dtype=np.float32)):
+        g = -np.float32(alpha * f(kb))
+        p = np.float32(np.exp(np.float64(-g)))
+        pb = np.float32(B(p))
+        l, lb = np.float32(np.float32(1.0) + p), np.float32(np.float32(1.0) + pb)
+        if B(pb / l) != B(p / l) and (B(np.float32(1.0) / lb) != B(np.float32(1.0) / l) or B(pb / lb) != B(pb / l)):
+            chosen = (kb, p, pb, l)
+            break
+    assert chosen is not None
+    kb, p, pb, l = chosen
+    q = _bits([[1.0, 0.0, 0.0, 0.0]])
+    k = np.array([_bits([0.0, 0, 0, 0]), np.array([kb, 0, 0, 0], np.uint16)])
+    v = _bits([[1.0, 0, 0, 0], [0.0, 1.0, 0, 0]])
+    o_b = f(oracle.attention_ex(q, k, v, 1, dh, bf16_p=True))[0]
+    o_f = f(oracle.attention_ex(q, k, v, 1, dh, bf16_p=False))[0]
+    assert o_b[1] == B(pb / l) and o_f[1] == B(p / l) and o_b[1] != o_f[1]
+    assert o_b[0] == o_f[0] == B(np.float32(1.0) / l)
+    qz = _bits(np.zeros((3, 8)))
+    kz = _bits(np.random.default_rng(14).standard_normal((5, 8)))
+    vz = _bits(np.random.default_rng(15).standard_normal((5, 8)))
+    assert np.array_equal(oracle.attention_ex(qz, kz, vz, 2, 4, bf16_p=True), oracle.attention(qz, kz, vz, 2, 4))
+
+
+def test_attn_sublayer_ext_reduces_to_plain_and_composes():
+    """Without normalisation or rotary tables the extended sub-block is the
+    pinned plain one; with them it is the plain sub-block on the projections
+    normalised and rotated by the pinned pieces (checked through the
+    attention core on those pieces)."""
+    rng = np.random.default_rng(16)
+    M, d, heads, dh = 12, 32, 2, 16
+    x = _bits(rng.standard_normal((M, d)))
+    w = {}
+    for n in ("q", "k", "v", "o"):
+        w["W" + n] = _bits(rng.standard_normal((d, d)) / np.sqrt(d))
+        w["b" + n] = _bits(0.1 * rng.standard_normal(d))
+    plain = oracle.attn_sublayer(x, w["Wq"], w["bq"], w["Wk"], w["bk"], w["Wv"], w["bv"], w["Wo"], w["bo"],
+                                 heads, dh)
+    assert np.array_equal(oracle.attn_sublayer_ext(x, w, heads, dh), plain)
+    gq, gk = _bits(1 + 0.2 * rng.standard_normal(d)), _bits(1 + 0.2 * rng.standard_normal(d))
+    ang = rng.uniform(0, 6.3, size=(M, dh // 2))
+    cs, sn = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    y = oracle.attn_sublayer_ext(x, w, heads, dh, gq=gq, gk=gk, eps=1e-6, norm_tile=8, cos_q=cs, sin_q=sn,
+                                 residual=False)
+    Q = oracle.rope_split(oracle.rmsnorm(oracle.linear(x, w["Wq"], w["bq"]), gq, 1e-6, 8), heads, dh, cs, sn)
+    K = oracle.rope_split(oracle.rmsnorm(oracle.linear(x, w["Wk"], w["bk"]), gk, 1e-6, 8), heads, dh, cs, sn)
+    V = oracle.linear(x, w["Wv"], w["bv"])
+    ref = oracle.linear(oracle.attention(Q, K, V, heads, dh), w["Wo"], w["bo"])
+    assert np.array_equal(y, ref)
