@@ -220,7 +220,8 @@ psi_status psi_arena_reset_stats(psi_arena* a);
  * Errors: PSI_E_INVALID without PSI_ARENA_PROFILE or for a null arena;
  * PSI_E_HIP if an event cannot be created or read. */
 typedef struct psi_trace_event {
-  int32_t kind;     /* 0 GEMM, 1 attention, 2 / 3 page copy on copy stream 0 / 1 */
+  int32_t kind;     /* 0 GEMM, 1 attention, 2 / 3 page copy on copy stream 0 / 1,
+                       4 query/key normalisation-rotary kernel */
   int32_t reserved;
   double start_ms;  /* from the base event */
   double dur_ms;
@@ -335,13 +336,63 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x_dev, int M, int d, cons
  * attention per head (unmasked, noncausal, dropout-free), then
  * ACC += O_g Wo[:, g]^T in group order, y = B(ACC + bo) (+ residual).
  *   Wq, Wk, Wv: [d, d] PSI_SPLIT_ROWS, block = heads_per_group*head_dim;
- *   Wo: [d, d] PSI_SPLIT_COLS with the same block.  head_dim must be 128.
+ *   Wo: [d, d] PSI_SPLIT_COLS with the same block.  head_dim is 128 or 64.
  *   ctx_dev nullable [Mc, d]; y_dev may alias x_dev. */
 psi_status psi_attn_paged(psi_arena* a, const uint16_t* x_dev, int M,
                           const uint16_t* ctx_dev, int Mc, int heads, int head_dim,
                           const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
                           const psi_matrix* Wo, float* acc_dev, uint16_t* y_dev,
                           unsigned flags);
+
+/* Query/key normalisation and rotary positions of the attention sub-block
+ * ([PSI] sec. II-B, full-row RMS and split RoPE), each a declared BF16 write:
+ *   Q = B(x Wq^T + bq); if gamma_q: Q = B(gamma_q * Q / sqrt(s/d + eps)),
+ *   s = sum over column tiles J (width norm_tile, ascending) of the tile's
+ *   sum of squares, ONE denominator per row for all tiles; if cos_q:
+ *   per head the pair (Q_j, Q_{j+dh/2}), j < dh/2, becomes
+ *   B(c Q_j - s Q_{j+dh/2}), B(s Q_j + c Q_{j+dh/2}) with c = cos[t][j],
+ *   s = sin[t][j] of the row's token t.  K likewise with gamma_k and the
+ *   key tables (NULL cos_k: the query tables, which needs Mk == M).
+ * Fields:
+ *   gamma_q, gamma_k  BF16 [d] or NULL (no normalisation of that operand);
+ *                     pinned host memory staged with the biases, or device
+ *                     memory when the projection matrices are resident
+ *   eps               > 0 when a gamma is given (fp32)
+ *   norm_tile         width of the partial sums, a multiple of 8;
+ *                     0 = the head-group block (one tile per weight page)
+ *   cos_q, sin_q      device fp32 [M, head_dim/2], 16-byte aligned, or NULL
+ *                     (no rotary embedding)
+ *   cos_k, sin_k      device fp32 [Mk, head_dim/2] or NULL */
+typedef struct psi_qk_norm_rope {
+  const uint16_t* gamma_q;
+  const uint16_t* gamma_k;
+  float eps;
+  int norm_tile;
+  const float* cos_q;
+  const float* sin_q;
+  const float* cos_k;
+  const float* sin_k;
+} psi_qk_norm_rope;
+
+/* psi_attn_paged with the normalisation/rotary stage above between the
+ * Q/K projections and attention.  Because the row statistic spans every
+ * head group, the Q and K projections of all groups are computed first
+ * (pages Wq_g, Wk_g for g ascending), then normalised/rotated in place,
+ * then per group V_g, attention and the O-projection (pages Wv_g, Wo_g).
+ * Scratch: Q [M, d] and K [Mk, d] BF16, V_g^T, and ACC unless acc_dev.
+ * nr == NULL (or nothing enabled in it) gives psi_attn_paged's bits.
+ * Errors: as psi_attn_paged, plus PSI_E_INVALID for eps <= 0 with a gamma,
+ * a bad norm_tile, a missing sin table, or NULL cos_k with Mk != M;
+ * PSI_E_ALIGN for misaligned tables. */
+psi_status psi_attn_ext_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                             const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                             const psi_matrix* Wo, const psi_qk_norm_rope* nr, int acc_external,
+                             size_t* scratch_needed);
+psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x_dev, int M,
+                              const uint16_t* ctx_dev, int Mc, int heads, int head_dim,
+                              const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                              const psi_matrix* Wo, const psi_qk_norm_rope* nr, float* acc_dev,
+                              uint16_t* y_dev, unsigned flags);
 
 /* One synthetic transformer block in place: x_tmp = x + Attn(x) (self),
  * then x = x_tmp + FFN(x_tmp), both with the residual write.  If `fence`

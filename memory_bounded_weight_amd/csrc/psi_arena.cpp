@@ -252,7 +252,8 @@ static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (
     PSI_HIP(hipEventRecord(t0, a->compute));
   }
   hipError_t e = fn(args, a->compute);
-  if (e != hipSuccess) return hip_fail(e, kind == 0 ? "gemm launch" : "attention launch");
+  if (e != hipSuccess)
+    return hip_fail(e, kind == 0 ? "gemm launch" : kind == 1 ? "attention launch" : "norm/rope launch");
   if (t0) {
     PSI_HIP(hipEventRecord(t1, a->compute));
     a->pending.push_back({t0, t1, kind, work});
@@ -273,8 +274,18 @@ psi_status run_gemm(psi_arena* a, const GemmArgs& g) {
 }
 
 psi_status run_attention(psi_arena* a, const AttnArgs& g) {
-  double flops = 4.0 * g.Mq * (double)g.Mk * 128.0 * g.heads;
+  double flops = 4.0 * g.Mq * (double)g.Mk * g.dh * g.heads;
   return timed_launch(a, 1, flops, attn_thunk, &g);
+}
+
+static hipError_t norm_thunk(const void* p, hipStream_t s) {
+  return launch_qk_norm_rope(*static_cast<const NormRopeArgs*>(p), s);
+}
+
+psi_status run_norm_rope(psi_arena* a, const NormRopeArgs& g) {
+  if (g.M <= 0) return PSI_OK;
+  double bytes = 4.0 * g.M * (double)g.d;  // one read and one write of each BF16 row
+  return timed_launch(a, 4, bytes, norm_thunk, &g);
 }
 
 static psi_status harvest(psi_arena* a) {
@@ -294,6 +305,8 @@ static psi_status harvest(psi_arena* a) {
       a->stats.attn_ms += ms;
       a->stats.attn_launches++;
       a->stats.attn_flops += t.work;
+    } else if (t.kind == 4) {
+      // normalisation / rotary kernels: device timeline only
     } else {
       // copy_ms = busy time of the busier copy stream
       a->copy_ms_stream[t.kind - 2] += ms;

@@ -9,7 +9,7 @@
 // After the last tile z / l is dense softmax attention (unmasked,
 // noncausal, no dropout, at least one key).
 //
-// Layout of the work (head_dim 128, 64 keys per tile):
+// Layout of the work (head_dim 128 or 64, 64 keys per tile):
 //   * one workgroup = 4 or 8 waves = 128 or 256 queries of one head; each
 //     wave owns 32 queries;
 //   * scores are computed transposed, S^T = K Q^T, with the 32x32x16 BF16
@@ -43,17 +43,17 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
   return (uint16_t)(w >> 16);
 }
 
-constexpr int DH = 128;       // head dimension
 constexpr int KT = 64;        // keys per tile
-constexpr int KS = DH + 8;    // K tile row stride in LDS (elements): 272 B
 constexpr int VS = KT + 4;    // V^T tile row stride in LDS (elements): 136 B
 
 // One workgroup = QB/32 waves = QB queries of one head.  Two waves per SIMD
 // (<= 256 registers each): while one wave runs its softmax arithmetic the
 // other keeps the matrix cores busy.  BF16P selects the BF16-numerator
 // variant (one MFMA per P.V step instead of hi + lo).
-template <int QB, bool BF16P>
+template <int QB, bool BF16P, int DH>
 __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
+  constexpr int KS = DH + 8;     // K tile row stride in LDS (elements)
+  constexpr int CPRK = DH / 8;   // 16-byte chunks per K row
   constexpr int NT = QB * 2;  // threads
   constexpr int KCH = KT * DH / 8 / NT;  // 16-byte K chunks per thread and tile
   constexpr int VCH = DH * KT / 8 / NT;  // 16-byte V^T chunks per thread and tile
@@ -94,9 +94,9 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       int c2 = tid + i * NT;
-      int key = key0 + (c2 >> 4);
+      int key = key0 + c2 / CPRK;
       if (ragged) key = key < p.Mk ? key : p.Mk - 1;
-      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 & 15) * 8);
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 % CPRK) * 8);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       int c2 = tid + i * NT;
-      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 >> 4) * KS + (c2 & 15) * 8]) = rk[i];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 / CPRK) * KS + (c2 % CPRK) * 8]) = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -267,8 +267,10 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
 // MFMA-only and a VALU-only phase.  K and V^T tiles are triple-buffered in
 // LDS: iteration t reads K of tile t+1 and V^T of tile t while tile t+2 is
 // stored.  Same arithmetic, in the same order per query, as attn_kernel.
-template <int QB, bool BF16P>
+template <int QB, bool BF16P, int DH>
 __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
+  constexpr int KS = DH + 8;
+  constexpr int CPRK = DH / 8;
   constexpr int NT = QB * 2;
   constexpr int KCH = KT * DH / 8 / NT;
   constexpr int VCH = DH * KT / 8 / NT;
@@ -306,9 +308,9 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       int c2 = tid + i * NT;
-      int key = key0 + (c2 >> 4);
+      int key = key0 + c2 / CPRK;
       if (ragged) key = key < p.Mk ? key : p.Mk - 1;
-      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 & 15) * 8);
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 % CPRK) * 8);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       int c2 = tid + i * NT;
-      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 >> 4) * KS + (c2 & 15) * 8]) = rk[i];
+      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 / CPRK) * KS + (c2 % CPRK) * 8]) = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -505,18 +507,27 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
   }
 }
 
-template <int QB, bool BF16P>
+template <int QB, bool BF16P, int DH>
 hipError_t launch_pipe(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel_pipe<QB, BF16P>), grid, dim3(QB * 2), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel_pipe<QB, BF16P, DH>), grid, dim3(QB * 2), 0, s, a);
   return hipGetLastError();
 }
 
-template <int QB, bool BF16P>
+template <int QB, bool BF16P, int DH>
 hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel<QB, BF16P>), grid, dim3(QB * 2), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<QB, BF16P, DH>), grid, dim3(QB * 2), 0, s, a);
   return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_dh(const AttnArgs& a, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case 2: return a.bf16_p ? launch_q<256, true, DH>(a, s) : launch_q<256, false, DH>(a, s);
+    case 3: return a.bf16_p ? launch_pipe<256, true, DH>(a, s) : launch_pipe<256, false, DH>(a, s);
+    default: return a.bf16_p ? launch_q<128, true, DH>(a, s) : launch_q<128, false, DH>(a, s);
+  }
 }
 
 }  // namespace
@@ -526,14 +537,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // 256-query workgroups (8 waves sharing each K/V tile, software-pipelined)
   // when they still give every CU a workgroup, else 128-query ones.
   // Configurations: 1 = 128-query, 2 = 256-query, 3 = 256-query pipelined;
-  // all give identical bits.
+  // all give identical bits.  Head dimension 128 or 64.
   int cfg = a.config;
   if (cfg == 0) cfg = ((a.Mq + 255) / 256) * a.heads >= 256 ? 3 : 1;
-  switch (cfg) {
-    case 2: return a.bf16_p ? launch_q<256, true>(a, s) : launch_q<256, false>(a, s);
-    case 3: return a.bf16_p ? launch_pipe<256, true>(a, s) : launch_pipe<256, false>(a, s);
-    default: return a.bf16_p ? launch_q<128, true>(a, s) : launch_q<128, false>(a, s);
-  }
+  if (a.dh == 64) return launch_dh<64>(a, cfg, s);
+  if (a.dh != 128) return hipErrorInvalidValue;
+  return launch_dh<128>(a, cfg, s);
 }
 
 }  // namespace psi

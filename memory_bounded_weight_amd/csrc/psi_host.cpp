@@ -244,7 +244,8 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
   psi_arena_layout L;
   psi_status st = psi_arena_plan(d, &L);
   if (st) return st;
-  if (head_dim != 128) return fail(PSI_E_INVALID, "attention: head_dim must be 128");
+  if (head_dim != 128 && head_dim != 64)
+    return fail(PSI_E_INVALID, "attention: head_dim must be 128 or 64");
   if (heads <= 0 || M < 0 || Mc < 0) return fail(PSI_E_INVALID, "attention: bad sizes");
   const int dm = heads * head_dim;
   if ((st = check_matrix(Wq, "Wq", PSI_SPLIT_ROWS))) return st;
@@ -270,6 +271,50 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
                 align_up((size_t)gw * ldvt * 2, kAlign);
   if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
   if ((st = scratch_fit(L, need, "attention Q/K/V head-group tiles"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
+psi_status psi_attn_ext_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                             const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                             const psi_matrix* Wo, const psi_qk_norm_rope* nr, int acc_external,
+                             size_t* scratch_needed) {
+  psi_status st = psi_attn_plan(d, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_external, scratch_needed);
+  if (st || !qk_stage_active(nr)) return st;
+  psi_arena_layout L;
+  if ((st = psi_arena_plan(d, &L))) return st;
+  if ((nr->gamma_q || nr->gamma_k) && !(nr->eps > 0.0f))
+    return fail(PSI_E_INVALID, "attention: eps must be > 0 with a normalisation gamma");
+  if (nr->norm_tile < 0 || nr->norm_tile % 8 != 0)
+    return fail(PSI_E_INVALID, "attention: norm_tile must be 0 or a positive multiple of 8");
+  if (!nr->cos_q && (nr->sin_q || nr->cos_k || nr->sin_k))
+    return fail(PSI_E_INVALID, "attention: rotary tables given without the query cosine table");
+  if (nr->cos_q && !nr->sin_q) return fail(PSI_E_INVALID, "attention: sin_q is missing");
+  if (nr->cos_k && !nr->sin_k) return fail(PSI_E_INVALID, "attention: sin_k is missing");
+  const int Ms = Mc > 0 ? Mc : M;
+  if (nr->cos_q && !nr->cos_k && Ms != M)
+    return fail(PSI_E_INVALID, "attention: keys need their own rotary tables when Mk != M");
+  const void* tabs[4] = {nr->cos_q, nr->sin_q, nr->cos_k, nr->sin_k};
+  for (const void* t : tabs)
+    if (reinterpret_cast<uintptr_t>(t) % 16 != 0)
+      return fail(PSI_E_ALIGN, "attention: rotary tables must be 16-byte aligned");
+  const int dm = heads * head_dim;
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  size_t bias = 0;
+  for (const psi_matrix* m : ms)
+    if (m->bias_host && !m->resident) bias += align_up((size_t)m->rows * 2, kAlign);
+  if (!Wq->resident) {
+    if (nr->gamma_q) bias += align_up((size_t)dm * 2, kAlign);
+    if (nr->gamma_k) bias += align_up((size_t)dm * 2, kAlign);
+  }
+  if (bias > L.bias_slot_bytes)
+    return fail(PSI_E_PAGE_TOO_SMALL, "the operator's biases and gammas (" + std::to_string(bias) +
+                                          " B) exceed a bias slot (" + std::to_string(L.bias_slot_bytes) + " B)");
+  const size_t ldvt = align_up((size_t)Ms, 64);
+  size_t need = align_up((size_t)M * dm * 2, kAlign) + align_up((size_t)Ms * dm * 2, kAlign) +
+                align_up((size_t)Wq->block * ldvt * 2, kAlign);
+  if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
+  if ((st = scratch_fit(L, need, "attention Q/K (all head groups) and V^T tiles"))) return st;
   if (scratch_needed) *scratch_needed = need;
   return PSI_OK;
 }

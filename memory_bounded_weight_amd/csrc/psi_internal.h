@@ -63,18 +63,36 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 int gemm_auto_config(const GemmArgs& a);
 
 struct AttnArgs {
-  uint16_t* q;         // [Mq, ldq]; head h occupies columns h*128..h*128+127; O overwrites it
+  uint16_t* q;         // [Mq, ldq]; head h occupies columns h*dh..(h+1)*dh-1; O overwrites it
   long ldq;
   const uint16_t* k;   // [Mk, ldk]
   long ldk;
-  const uint16_t* vt;  // [heads*128, ldvt]: V transposed (row = channel, column = key)
+  const uint16_t* vt;  // [heads*dh, ldvt]: V transposed (row = channel, column = key)
   long ldvt;
   int Mq, Mk, heads;
-  float alpha;         // 1/sqrt(128) rounded to fp32
+  int dh;              // head dimension: 128 or 64
+  float alpha;         // 1/sqrt(dh) rounded to fp32
   int bf16_p;          // 1: softmax weights rounded to BF16 before P*V
   int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query, 3: 256-query pipelined
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// In place on rows of x: optional full-row RMS normalisation (gamma
+// non-null; sum of squares as ascending partial sums over column tiles of
+// width `tile`), then optional split RoPE per head (cs/sn non-null, fp32
+// tables [M, dh/2]); each a BF16 write.  x, gamma, cs, sn 16-byte aligned,
+// ldx % 8 == 0, d % 16 == 0, tile % 8 == 0.
+struct NormRopeArgs {
+  uint16_t* x;
+  long ldx;
+  int M, d, dh;
+  const uint16_t* gamma;  // nullable, [d]
+  float eps;
+  int tile;
+  const float* cs;        // nullable, [M, dh/2]
+  const float* sn;
+};
+hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------- planning
 struct MatrixInfo {
@@ -82,6 +100,10 @@ struct MatrixInfo {
   size_t max_page_bytes;
 };
 psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split);
+// True when the query/key normalisation-rotary stage does any work.
+inline bool qk_stage_active(const psi_qk_norm_rope* nr) {
+  return nr && (nr->gamma_q || nr->gamma_k || nr->cos_q || nr->sin_q || nr->cos_k || nr->sin_k);
+}
 MatrixInfo matrix_info(const psi_matrix* m);
 const void* matrix_page_ptr(const psi_matrix* m, int p);
 int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COLS) in page p
@@ -100,7 +122,7 @@ struct psi_page_slot {
 
 struct psi_timed {
   hipEvent_t start, stop;
-  int kind;      // 0 gemm, 1 attention, 2 copy on stream 0, 3 copy on stream 1
+  int kind;      // 0 gemm, 1 attention, 2 copy on stream 0, 3 copy on stream 1, 4 norm/rope
   double work;   // flops (kernels) or bytes (copies)
 };
 
@@ -161,6 +183,7 @@ psi_status bias_release(psi_arena* a, int slot);
 // Kernel launch through the arena (profiling, counters).
 psi_status run_gemm(psi_arena* a, const GemmArgs& g);
 psi_status run_attention(psi_arena* a, const AttnArgs& g);
+psi_status run_norm_rope(psi_arena* a, const NormRopeArgs& g);
 
 psi_status check_pinned(const void* p, const char* what);
 

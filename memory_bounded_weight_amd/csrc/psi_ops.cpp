@@ -31,21 +31,30 @@ void matrix_requests(const psi_matrix* m, std::vector<PageReq>& out) {
 // after the last partial sum ([PSI] sec. II-B).
 class OpBiases {
  public:
-  psi_status stage(psi_arena* a, const psi_matrix* const* ms, int n) {
+  // Stages the biases of matrices ms[0..n) and then n_extra further BF16
+  // parameter vectors (pinned host, or device when `extra_resident`) in
+  // one bias-slot request; get(i) for i >= n returns extra vector i - n.
+  psi_status stage(psi_arena* a, const psi_matrix* const* ms, int n, const BiasPart* extra = nullptr,
+                   int n_extra = 0, bool extra_resident = false) {
     a_ = a;
-    BiasPart parts[4];
-    const uint16_t* dev[4];
+    BiasPart parts[kMax];
+    const uint16_t* dev[kMax];
+    if (n + n_extra > kMax) return fail(PSI_E_INVALID, "too many bias parts");
     for (int i = 0; i < n; ++i) {
       const bool copy = ms[i]->bias_host && !ms[i]->resident;
       parts[i] = BiasPart{copy ? ms[i]->bias_host : nullptr, copy ? (size_t)ms[i]->rows * 2 : 0};
     }
-    psi_status st = bias_submit(a, parts, n, dev, &slot_);
+    for (int i = 0; i < n_extra; ++i)
+      parts[n + i] = extra_resident ? BiasPart{nullptr, 0} : extra[i];
+    psi_status st = bias_submit(a, parts, n + n_extra, dev, &slot_);
     if (st) return st;
     for (int i = 0; i < n; ++i) ptr_[i] = ms[i]->resident ? ms[i]->bias_host : dev[i];
+    for (int i = 0; i < n_extra; ++i)
+      ptr_[n + i] = extra_resident ? static_cast<const uint16_t*>(extra[i].host) : dev[n + i];
     return PSI_OK;
   }
-  // Device address of matrix i's bias (nullable); the compute stream
-  // first waits for the bias copy.
+  // Device address of part i (nullable); the compute stream first waits
+  // for the bias copy.
   psi_status get(int i, const uint16_t** out) {
     psi_status st = bias_acquire(a_, slot_);
     if (st) return st;
@@ -55,9 +64,10 @@ class OpBiases {
   psi_status release() { return bias_release(a_, slot_); }
 
  private:
+  static constexpr int kMax = 6;
   psi_arena* a_ = nullptr;
   int slot_ = -1;
-  const uint16_t* ptr_[4] = {nullptr, nullptr, nullptr, nullptr};
+  const uint16_t* ptr_[kMax] = {};
 };
 
 // Streams a list of page requests through the arena's slots: requests are
@@ -557,7 +567,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
       A.q = Q; A.ldq = gw;
       A.k = Kb; A.ldk = gw;
       A.vt = Vt; A.ldvt = ldvt;
-      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim;
+      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
       A.alpha = alpha;
       A.bf16_p = (flags & PSI_OP_BF16_SOFTMAX) ? 1 : 0;
       if ((st = run_attention(a, A))) return st;
@@ -581,6 +591,161 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
       if ((st = run_gemm(a, G))) return st;
     }
     if ((st = feeder.give_back(4 * g + 3))) return st;
+  }
+  return bias.release();
+}
+
+psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
+                              int heads, int head_dim, const psi_matrix* Wq, const psi_matrix* Wk,
+                              const psi_matrix* Wv, const psi_matrix* Wo, const psi_qk_norm_rope* nr,
+                              float* acc_dev, uint16_t* y, unsigned flags) {
+  if (!qk_stage_active(nr))
+    return psi_attn_paged(a, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_dev, y, flags);
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
+  if (!ctx) Mc = 0;
+  psi_status st = psi_attn_ext_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr,
+                                    acc_dev != nullptr, nullptr);
+  if (st) return st;
+  if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  if (!a->dry) {
+    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true)) ||
+        (st = check_ptr(acc_dev, "acc", true)))
+      return st;
+    if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
+        (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
+      return st;
+    for (const uint16_t* g : {nr->gamma_q, nr->gamma_k}) {
+      if (!g) continue;
+      if ((st = Wq->resident ? check_ptr(g, "gamma") : check_pinned(g, "gamma"))) return st;
+    }
+  }
+  if (M == 0) return PSI_OK;
+  const int dm = heads * head_dim;
+  const int gw = Wq->block;
+  const uint16_t* src = ctx ? ctx : x;
+  const int Ms = ctx ? Mc : M;
+  const long ldvt = (long)align_up((size_t)Ms, 64);
+  const int bbase = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  ScratchMark mark(a);
+  uint16_t* Q = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * dm * 2, &st));
+  if (st) return st;
+  uint16_t* Kb = static_cast<uint16_t*>(scratch_alloc(a, (size_t)Ms * dm * 2, &st));
+  if (st) return st;
+  uint16_t* Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
+  if (st) return st;
+  float* acc = acc_dev;
+  if (!acc) {
+    acc = static_cast<float*>(scratch_alloc(a, (size_t)M * dm * 4, &st));
+    if (st) return st;
+  }
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  const BiasPart gam[2] = {{nr->gamma_q, nr->gamma_q ? (size_t)dm * 2 : 0},
+                           {nr->gamma_k, nr->gamma_k ? (size_t)dm * 2 : 0}};
+  OpBiases bias;
+  if ((st = bias.stage(a, ms, 4, gam, 2, Wq->resident != 0))) return st;
+  // pages: Wq_g, Wk_g for every group, then Wv_g, Wo_g for every group
+  std::vector<PageReq> rq, rk, rv, ro, reqs;
+  matrix_requests(Wq, rq);
+  matrix_requests(Wk, rk);
+  matrix_requests(Wv, rv);
+  matrix_requests(Wo, ro);
+  const int nG = (int)rq.size();
+  for (int g = 0; g < nG; ++g) {
+    reqs.push_back(rq[g]);
+    reqs.push_back(rk[g]);
+  }
+  for (int g = 0; g < nG; ++g) {
+    reqs.push_back(rv[g]);
+    reqs.push_back(ro[g]);
+  }
+  const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
+  PageFeeder feeder(a, reqs);
+  if ((st = feeder.feed())) return st;
+  const uint16_t* bq[6];
+  for (int i = 0; i < 6; ++i)
+    if ((st = bias.get(i, &bq[i]))) return st;
+  const uint16_t* page;
+  // Q[:, g] = x Wq_g^T + bq_g and K[:, g] = src Wk_g^T + bk_g for all groups
+  for (int g = 0; g < nG; ++g) {
+    const int ext = matrix_page_extent(Wq, g);
+    const size_t c0 = (size_t)g * gw;
+    if ((st = feeder.take(2 * g, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
+      G.M = M; G.N = ext; G.K = dm;
+      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q + c0; G.ldo = dm; G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(2 * g))) return st;
+    if ((st = feeder.take(2 * g + 1, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
+      G.M = Ms; G.N = ext; G.K = dm;
+      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb + c0; G.ldo = dm; G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(2 * g + 1))) return st;
+  }
+  // full-row RMS and split RoPE, in place
+  {
+    NormRopeArgs N{};
+    N.x = Q; N.ldx = dm; N.M = M; N.d = dm; N.dh = head_dim;
+    N.gamma = bq[4]; N.eps = nr->eps; N.tile = nr->norm_tile > 0 ? nr->norm_tile : gw;
+    N.cs = nr->cos_q; N.sn = nr->sin_q;
+    if ((nr->gamma_q || nr->cos_q) && (st = run_norm_rope(a, N))) return st;
+    N.x = Kb; N.M = Ms; N.gamma = bq[5];
+    N.cs = nr->cos_k ? nr->cos_k : nr->cos_q;
+    N.sn = nr->cos_k ? nr->sin_k : nr->sin_q;
+    if ((nr->gamma_k || nr->cos_q) && (st = run_norm_rope(a, N))) return st;
+  }
+  const size_t base = 2 * (size_t)nG;
+  for (int g = 0; g < nG; ++g) {
+    const int ext = matrix_page_extent(Wq, g);
+    const bool last = g == nG - 1;
+    const size_t c0 = (size_t)g * gw;
+    // V_g^T = Wv_g src^T + bv_g (bias along rows)
+    if ((st = feeder.take(base + 2 * g, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
+      G.M = ext; G.N = Ms; G.K = dm;
+      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
+      G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(base + 2 * g))) return st;
+    // O_g over Q[:, g] in place
+    {
+      AttnArgs A{};
+      A.q = Q + c0; A.ldq = dm;
+      A.k = Kb + c0; A.ldk = dm;
+      A.vt = Vt; A.ldvt = ldvt;
+      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
+      A.alpha = alpha;
+      A.bf16_p = (flags & PSI_OP_BF16_SOFTMAX) ? 1 : 0;
+      if ((st = run_attention(a, A))) return st;
+    }
+    // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
+    if ((st = feeder.take(base + 2 * g + 1, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = Q + c0; G.lda = dm; G.B = page; G.ldb = ext;
+      G.M = M; G.N = dm; G.K = ext;
+      G.baseline_bias = bbase;
+      if (g > 0) { G.acc_in = acc; G.ld_acc_in = dm; }
+      if (last) {
+        G.bias = bq[3]; G.out = y; G.ldo = dm;
+        if (flags & PSI_OP_RESIDUAL) { G.resid = x; G.ldr = dm; }
+        if (flags & PSI_OP_STORE_ACC) { G.acc_out = acc; G.ld_acc_out = dm; }
+      } else {
+        G.epi = EPI_ACC; G.acc_out = acc; G.ld_acc_out = dm;
+      }
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(base + 2 * g + 1))) return st;
   }
   return bias.release();
 }

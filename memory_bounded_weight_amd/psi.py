@@ -115,6 +115,18 @@ class psi_block_weights(ctypes.Structure):
                 ("U", psi_matrix), ("V", psi_matrix)]
 
 
+class psi_qk_norm_rope(ctypes.Structure):
+    _fields_ = [("gamma_q", _vp), ("gamma_k", _vp), ("eps", ctypes.c_float), ("norm_tile", _i),
+                ("cos_q", _vp), ("sin_q", _vp), ("cos_k", _vp), ("sin_k", _vp)]
+
+
+def qk_norm_rope(gamma_q=None, gamma_k=None, eps=1e-6, norm_tile=0, cos_q=None, sin_q=None,
+                 cos_k=None, sin_k=None) -> psi_qk_norm_rope:
+    """psi_qk_norm_rope from tensors/arrays/ints (None -> NULL)."""
+    return psi_qk_norm_rope(_ptr(gamma_q), _ptr(gamma_k), eps, norm_tile, _ptr(cos_q), _ptr(sin_q),
+                            _ptr(cos_k), _ptr(sin_k))
+
+
 class psi_key(ctypes.Structure):
     _fields_ = [("step", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("branch", ctypes.c_int32), ("role", ctypes.c_int32)]
@@ -163,6 +175,10 @@ _sig("psi_ffn_tiled", [_vp, _vp, _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _vp
                        ctypes.c_int32, _vp, _u])
 _sig("psi_attn_paged", [_vp, _vp, _i, _vp, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
                         _P(psi_matrix), _P(psi_matrix), _vp, _vp, _u])
+_sig("psi_attn_ext_plan", [_P(psi_arena_desc), _i, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
+                           _P(psi_matrix), _P(psi_matrix), _P(psi_qk_norm_rope), _i, _P(_sz)])
+_sig("psi_attn_paged_ext", [_vp, _vp, _i, _vp, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
+                            _P(psi_matrix), _P(psi_matrix), _P(psi_qk_norm_rope), _vp, _vp, _u])
 _sig("psi_block_paged", [_vp, _vp, _vp, _i, _i, _i, _P(psi_block_weights), _i, _vp, _vp, _u])
 _sig("psi_journal_create", [_P(psi_journal_desc), _P(_vp)])
 _sig("psi_journal_destroy", [_vp])
@@ -181,6 +197,7 @@ EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_
            "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
            "psi_attn_paged", "psi_block_paged", "psi_ffn_tiled_plan", "psi_ffn_tiled",
+           "psi_attn_ext_plan", "psi_attn_paged_ext",
            "psi_journal_create", "psi_journal_destroy",
            "psi_journal_commit", "psi_journal_reload", "psi_journal_fence", "psi_journal_sync",
            "psi_journal_read", "psi_journal_counters"]
@@ -277,6 +294,15 @@ def psi_attn_plan(desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_external=Tru
     return _plan_status(st, need)
 
 
+def psi_attn_ext_plan(desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr, acc_external=True):
+    need = _sz(0)
+    st = _lib.psi_attn_ext_plan(ctypes.byref(desc), M, Mc, heads, head_dim, ctypes.byref(Wq),
+                                ctypes.byref(Wk), ctypes.byref(Wv), ctypes.byref(Wo),
+                                ctypes.byref(nr) if nr is not None else None, int(acc_external),
+                                ctypes.byref(need))
+    return _plan_status(st, need)
+
+
 # -------------------------------------------------------------------- arena
 
 def psi_arena_create(desc: psi_arena_desc) -> int:
@@ -370,6 +396,13 @@ def psi_attn_paged(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc, y
     return _check(_lib.psi_attn_paged(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
                                       ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
                                       ctypes.byref(Wo), _ptr(acc), _ptr(y), flags), "psi_attn_paged")
+
+
+def psi_attn_paged_ext(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr, acc, y, flags=0):
+    return _check(_lib.psi_attn_paged_ext(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
+                                          ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
+                                          ctypes.byref(Wo), ctypes.byref(nr) if nr is not None else None,
+                                          _ptr(acc), _ptr(y), flags), "psi_attn_paged_ext")
 
 
 def psi_block_paged(arena, x, x_tmp, M, heads, head_dim, w: psi_block_weights, token_chunks,

@@ -14,7 +14,12 @@ not available; random weights of the same shapes stand in):
     even);
   * activations N(0, 1); weights N(0, 1/fan_in); biases N(0, 0.02);
   * a stack of blocks draws block ``i``'s weights from
-    ``default_rng([seed, i])`` so one block can be regenerated alone.
+    ``default_rng([seed, i])`` so one block can be regenerated alone;
+  * normalisation gains gamma ~ 1 + N(0, 0.01) (the float32 sum, rounded
+    to bfloat16);
+  * rotary tables are the caller's inputs: for token position t and pair
+    index j < dh/2, the angle t * base^(-2j/dh) (base 10000) in float64,
+    cos and sin rounded to float32.
 """
 from __future__ import annotations
 
@@ -105,3 +110,30 @@ def block_weights(seed: int, index: int, d: int = 4096, hidden: int = 16384):
 def stack_input(seed: int = 0, M: int = 8192, d: int = 4096):
     rng = np.random.default_rng(seed)
     return normal_bf16(rng, (M, d), 1.0)
+
+
+def norm_gamma(rng, d: int) -> np.ndarray:
+    z = rng.standard_normal(size=(d,), dtype=np.float32)
+    return f32_to_bf16_bits(np.float32(1.0) + z * np.float32(0.1))
+
+
+def rope_tables(M: int, dh: int, offset: int = 0, base: float = 10000.0):
+    """cos/sin tables [M, dh/2] (float32) for positions offset .. offset+M-1."""
+    t = np.arange(offset, offset + M, dtype=np.float64)[:, None]
+    j = np.arange(dh // 2, dtype=np.float64)[None, :]
+    ang = t * base ** (-2.0 * j / dh)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def attn_ext_case(seed: int = 0, M: int = 126, d: int = 2048, Mc: int = 0):
+    """Attention sub-block with q/k normalisation and rotary positions; the
+    defaults are the audio self-attention shape (126 tokens, d 2,048, which
+    is 32 heads of 64).  x [M,d] ~ N(0,1), ctx [Mc,d] ~ N(0,1) when Mc > 0,
+    the eight projection arrays as attn_weights, then gamma_q, gamma_k."""
+    rng = np.random.default_rng(seed)
+    x = normal_bf16(rng, (M, d), 1.0)
+    ctx = normal_bf16(rng, (Mc, d), 1.0) if Mc > 0 else None
+    w = attn_weights(rng, d)
+    gq = norm_gamma(rng, d)
+    gk = norm_gamma(rng, d)
+    return {"x": x, "ctx": ctx, "w": w, "gq": gq, "gk": gk}

@@ -323,3 +323,48 @@ def test_ffn_tiled_plans_and_recompute_stream_dry_run():
         assert s.kernel_launches == n_o * n_j * 2  # up + down per (output tile, hidden tile)
     finally:
         psi.psi_arena_destroy(a)
+
+
+def test_attn_ext_plan_errors():
+    """Query/key normalisation-rotary settings are checked by the plan."""
+    ms = [fake_matrix(256, 256, psi.PSI_SPLIT_ROWS, 128) for _ in range(3)] + \
+         [fake_matrix(256, 256, psi.PSI_SPLIT_COLS, 128)]
+    d = desc(8, 1)
+    ok = psi.qk_norm_rope(0x1000, None, 1e-6)
+    st, need = psi.psi_attn_ext_plan(d, 64, 0, 4, 64, *ms, ok)
+    assert st == psi.PSI_OK and need >= (64 + 64) * 256 * 2
+    assert psi.psi_attn_plan(d, 64, 0, 4, 64, *ms)[0] == psi.PSI_OK  # 64-dim heads
+    assert psi.psi_attn_plan(d, 64, 0, 8, 32, *ms)[0] == psi.PSI_E_INVALID
+    bad = [psi.qk_norm_rope(0x1000, None, 0.0),                  # eps <= 0 with a gamma
+           psi.qk_norm_rope(0x1000, None, 1e-6, norm_tile=12),   # not a multiple of 8
+           psi.qk_norm_rope(None, None, 1e-6, cos_q=0x1000),     # sin_q missing
+           psi.qk_norm_rope(None, None, 1e-6, cos_k=0x1000, sin_k=0x1000)]  # key tables alone
+    for s in bad:
+        assert psi.psi_attn_ext_plan(d, 64, 0, 4, 64, *ms, s)[0] == psi.PSI_E_INVALID
+    s = psi.qk_norm_rope(None, None, 1e-6, cos_q=0x1000, sin_q=0x1000)
+    assert psi.psi_attn_ext_plan(d, 64, 32, 4, 64, *ms, s)[0] == psi.PSI_E_INVALID  # Mk != M
+    s = psi.qk_norm_rope(None, None, 1e-6, cos_q=0x1008, sin_q=0x1000)
+    assert psi.psi_attn_ext_plan(d, 64, 0, 4, 64, *ms, s)[0] == psi.PSI_E_ALIGN
+
+
+def test_attn_ext_audio_shape_dry_run():
+    """Audio self-attention (126 tokens, 32 heads of 64) with 8-head pages:
+    16 pages, 4 GEMMs and one attention per group plus one
+    normalisation-rotary launch each for Q and K; biases and both gammas
+    share the operator's bias request."""
+    d, M, gw = 2048, 126, 512
+    ms = [fake_matrix(d, d, psi.PSI_SPLIT_ROWS, gw) for _ in range(3)] + \
+         [fake_matrix(d, d, psi.PSI_SPLIT_COLS, gw)]
+    a = psi.psi_arena_create(desc(16, 2))
+    try:
+        nr = psi.qk_norm_rope(0x1000, 0x2000, 1e-6, 0, 0x3000, 0x4000)
+        fake = 0x10000
+        psi.psi_attn_paged_ext(a, fake, M, None, 0, 32, 64, *ms, nr, fake, fake, psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 16
+        assert s.bytes_h2d == 16 * gw * d * 2 + 6 * d * 2
+        assert s.kernel_launches == 4 * 5 + 2
+        ldvt = 128
+        assert s.scratch_high_water == 2 * M * d * 2 + gw * ldvt * 2
+    finally:
+        psi.psi_arena_destroy(a)

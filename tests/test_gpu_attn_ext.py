@@ -1,0 +1,182 @@
+"""Attention sub-block with 64-dim heads, full-row RMS normalisation of the
+query/key projections and split RoPE ([PSI] sec. II-B, sec. III-A) on the
+GPU, against the oracle.
+
+* head_dim 64 through psi_attn_paged (the audio attention shape: 126
+  tokens, d 2,048 = 32 heads of 64);
+* psi_attn_paged_ext with gamma_q/gamma_k and rotary tables, self- and
+  cross-attention, with every stage alone and together;
+* with nothing enabled, or with identity rotations (cos 1, sin 0), the
+  extended path gives psi_attn_paged's bits (same GEMMs, same attention,
+  only the page order changes);
+* resident projections with device gammas give the paged bits.
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bounded_weight_amd import synth
+from tests.gpu_util import assert_bf16_close, dev, empty_bf16, f, host, make_arena
+
+pytestmark = pytest.mark.gpu
+
+KiB = 1024
+
+
+@pytest.fixture(scope="module")
+def P(psi_lib):
+    return psi_lib
+
+
+def mats(P, w, gw, resident=False):
+    ms = (P.pinned_matrix(w["Wq"], w["bq"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wk"], w["bk"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wv"], w["bv"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, gw))
+    return tuple(P.resident_matrix(m) for m in ms) if resident else ms
+
+
+def pinned_vec(a):
+    t = torch.empty(a.size, dtype=torch.int16, pin_memory=True)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)))
+    return t
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def arena_for(M, Ms, d, gw, group_pages=2):
+    pb = gw * d * 2
+    ldvt = (Ms + 63) // 64 * 64
+    scratch = (M + Ms) * d * 2 + gw * ldvt * 2 + M * d * 4 + 16 * KiB
+    return make_arena(group_pages * pb + 2 * 64 * KiB + scratch, pb, group_pages)
+
+
+def run(P, x, w, heads, dh, gh, *, ctx=None, nr=None, ext=True, flags=0, residual=True,
+        resident=False):
+    """One sub-block call; ``nr`` is a dict of numpy inputs for
+    psi_qk_norm_rope (gq, gk, eps, norm_tile, cos_q, sin_q, cos_k, sin_k)."""
+    M, d = x.shape
+    Mc = 0 if ctx is None else ctx.shape[0]
+    gw = gh * dh
+    ms = mats(P, w, gw, resident)
+    ar = arena_for(M, Mc or M, d, gw)
+    keep = []
+    try:
+        xd = dev(x)
+        cd = dev(ctx) if ctx is not None else None
+        y = empty_bf16(M, d)
+        fl = flags | (P.PSI_OP_RESIDUAL if residual else 0)
+        if not ext:
+            P.psi_attn_paged(ar, xd, M, cd, Mc, heads, dh, *ms, None, y, fl)
+        else:
+            s = None
+            if nr is not None:
+                vec = (lambda a: dev(a)) if resident else pinned_vec
+                g = {k: (vec(nr[k]) if nr.get(k) is not None else None) for k in ("gq", "gk")}
+                t = {k: (dev_f32(nr[k]) if nr.get(k) is not None else None)
+                     for k in ("cos_q", "sin_q", "cos_k", "sin_k")}
+                keep += list(g.values()) + list(t.values())
+                s = P.qk_norm_rope(g["gq"], g["gk"], nr.get("eps", 1e-6), nr.get("norm_tile", 0),
+                                   t["cos_q"], t["sin_q"], t["cos_k"], t["sin_k"])
+            P.psi_attn_paged_ext(ar, xd, M, cd, Mc, heads, dh, *ms, s, None, y, fl)
+        P.psi_arena_sync(ar)
+        return host(y)
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def ref(x, w, heads, dh, *, ctx=None, nr=None, bf16_p=False, residual=True):
+    nr = nr or {}
+    return oracle.attn_sublayer_ext(x, w, heads, dh, ctx=ctx, gq=nr.get("gq"), gk=nr.get("gk"),
+                                    eps=nr.get("eps", 1e-6), norm_tile=nr.get("norm_tile", 0),
+                                    cos_q=nr.get("cos_q"), sin_q=nr.get("sin_q"),
+                                    cos_k=nr.get("cos_k"), sin_k=nr.get("sin_k"),
+                                    bf16_p=bf16_p, residual=residual)
+
+
+def test_head_dim_64_audio_shape_parity(P):
+    """psi_attn_paged with 64-dim heads at the audio self-attention shape
+    (126 tokens, 32 heads of 64, 8 heads per page)."""
+    c = synth.attn_ext_case(seed=21)
+    x, w = c["x"], c["w"]
+    y = run(P, x, w, 32, 64, 8, ext=False)
+    assert_bf16_close(y, ref(x, w, 32, 64), what="dh 64 self")
+    # ragged cross-attention, one and two heads per group
+    rng = np.random.default_rng(22)
+    x2 = synth.normal_bf16(rng, (200, 256), 1.0)
+    ctx = synth.normal_bf16(rng, (77, 256), 1.0)
+    w2 = synth.attn_weights(rng, 256)
+    for gh in (1, 2):
+        yc = run(P, x2, w2, 4, 64, gh, ctx=ctx, ext=False)
+        assert_bf16_close(yc, ref(x2, w2, 4, 64, ctx=ctx), what=f"dh 64 cross gh={gh}")
+
+
+@pytest.mark.parametrize("norm,rope", [(True, True), (True, False), (False, True)])
+def test_ext_audio_self_attention_parity(P, norm, rope):
+    """Full-row RMS of Q and K (tiles = one page's head group) and split
+    RoPE at the audio shape, against the oracle's sub-block."""
+    c = synth.attn_ext_case(seed=23)
+    x, w = c["x"], c["w"]
+    cq, sq = synth.rope_tables(126, 64)
+    nr = {}
+    if norm:
+        nr.update(gq=c["gq"], gk=c["gk"], eps=1e-6)
+    if rope:
+        nr.update(cos_q=cq, sin_q=sq)
+    y = run(P, x, w, 32, 64, 8, nr=nr)
+    r = ref(x, w, 32, 64, nr=dict(nr, norm_tile=512))
+    assert_bf16_close(y, r, what=f"norm={norm} rope={rope}")
+    assert not np.array_equal(y, ref(x, w, 32, 64)), "the stage must change the result"
+
+
+@pytest.mark.parametrize("dh,tile", [(128, 0), (64, 96)])
+def test_ext_cross_attention_key_tables_and_tiles(P, dh, tile):
+    """Cross-attention with the keys' own rotary tables (other positions),
+    ragged token counts, and a norm tile that does not divide the row."""
+    rng = np.random.default_rng(24 + dh)
+    d = 512
+    heads = d // dh
+    x = synth.normal_bf16(rng, (150, d), 1.0)
+    ctx = synth.normal_bf16(rng, (77, d), 1.0)
+    w = synth.attn_weights(rng, d)
+    gq, gk = synth.norm_gamma(rng, d), synth.norm_gamma(rng, d)
+    cq, sq = synth.rope_tables(150, dh)
+    ck, sk = synth.rope_tables(77, dh, offset=1000)
+    nr = dict(gq=gq, gk=gk, eps=1e-5, norm_tile=tile, cos_q=cq, sin_q=sq, cos_k=ck, sin_k=sk)
+    gh = 256 // dh
+    y = run(P, x, w, heads, dh, gh, ctx=ctx, nr=nr)
+    r = ref(x, w, heads, dh, ctx=ctx, nr=dict(nr, norm_tile=tile or gh * dh))
+    assert_bf16_close(y, r, what=f"cross dh={dh} tile={tile}")
+
+
+def test_ext_disabled_and_identity_rotation_bitwise(P):
+    """Nothing enabled, or cos = 1 and sin = 0, gives psi_attn_paged's bits
+    (the rotation of rounded values by the identity is exact)."""
+    c = synth.attn_ext_case(seed=25, M=100, d=512)
+    x, w = c["x"], c["w"]
+    base = run(P, x, w, 8, 64, 4, ext=False)
+    assert np.array_equal(run(P, x, w, 8, 64, 4, nr=None), base)
+    assert np.array_equal(run(P, x, w, 8, 64, 4, nr={}), base)
+    one = np.ones((100, 32), np.float32)
+    zero = np.zeros((100, 32), np.float32)
+    assert np.array_equal(run(P, x, w, 8, 64, 4, nr=dict(cos_q=one, sin_q=zero)), base)
+
+
+def test_ext_resident_matches_paged_and_bf16_numerator(P):
+    """Resident projections with device gammas give the paged bits; the
+    BF16-numerator variant stays within tolerance of the oracle's own
+    BF16-numerator reference."""
+    c = synth.attn_ext_case(seed=26, M=130, d=512)
+    x, w = c["x"], c["w"]
+    cq, sq = synth.rope_tables(130, 64)
+    nr = dict(gq=c["gq"], gk=c["gk"], eps=1e-6, cos_q=cq, sin_q=sq)
+    paged = run(P, x, w, 8, 64, 2, nr=nr)
+    assert np.array_equal(run(P, x, w, 8, 64, 2, nr=nr, resident=True), paged)
+    y16 = run(P, x, w, 8, 64, 2, nr=nr, flags=P.PSI_OP_BF16_SOFTMAX)
+    assert_bf16_close(y16, ref(x, w, 8, 64, nr=dict(nr, norm_tile=128), bf16_p=True))
