@@ -70,7 +70,12 @@ typedef int psi_status;
 #define PSI_OP_RESIDUAL 0x2u      /* y = B(f(x) + f(B(acc + b))) */
 #define PSI_OP_STORE_ACC 0x4u     /* also store the final fp32 accumulator to acc_dev */
 #define PSI_OP_BF16_SOFTMAX 0x8u  /* attention: BF16 softmax numerator weights (the
-                                     [PSI] sec. III-A baseline); default fp32-faithful */
+                                     [PSI] sec. III-A baseline); default: fp32 weights
+                                     (modified PSI), fed to the BF16 matrix cores as
+                                     three BF16 terms */
+#define PSI_OP_ATTN_P2 0x10u      /* attention: fp32 weights carried as two BF16 terms
+                                     (about 17 significant bits; one MFMA fewer per
+                                     step); ignored with PSI_OP_BF16_SOFTMAX */
 
 /* -------------------------------------------------------- matrix layouts */
 #define PSI_SPLIT_ROWS 0 /* page p = rows [p*block, (p+1)*block) of W: an output-column

@@ -20,10 +20,13 @@
 //   * the output is also accumulated transposed, O^T = V^T P^T: V^T comes
 //     from the value projection, which writes V transposed, and P^T is fed
 //     straight from the score registers as the B operand;
-//   * the softmax weights stay fp32-faithful on the BF16 matrix cores by
-//     splitting p = hi + lo into two BF16 numbers and issuing two MFMAs
-//     (the FP32 accumulation of modified PSI, sec. III-A); with bf16_p set
-//     only hi is used (the BF16-numerator baseline).
+//   * the softmax weights stay fp32 on the BF16 matrix cores by splitting
+//     p = hi + lo + lo2 into three BF16 numbers (each the rounding of what
+//     the previous ones leave, so the three hold p's 24-bit significand)
+//     and issuing one MFMA per term: the FP32 online accumulation of
+//     modified PSI (sec. III-A).  With two terms (hi + lo) the weights keep
+//     about 17 significant bits; with one (hi) they are the BF16 numerator
+//     weights of baseline PSI.
 #include "psi_internal.h"
 
 namespace psi {
@@ -46,11 +49,27 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
 constexpr int KT = 64;        // keys per tile
 constexpr int VS = KT + 4;    // V^T tile row stride in LDS (elements): 136 B
 
+// Splits fp32 weights (two at a time) into NP BF16 terms, each the
+// round-to-nearest of the exact remainder left by the previous terms.
+template <int NP>
+__device__ __forceinline__ void split_p(f32x2 pv, bf16x2 (&t)[3]) {
+  t[0] = __builtin_convertvector(pv, bf16x2);  // round to nearest even
+  if (NP >= 2) {
+    const f32x2 h = __builtin_convertvector(t[0], f32x2);
+    const f32x2 r = {pv[0] - h[0], pv[1] - h[1]};  // exact
+    t[1] = __builtin_convertvector(r, bf16x2);
+    if (NP >= 3) {
+      const f32x2 l = __builtin_convertvector(t[1], f32x2);
+      const f32x2 r2 = {r[0] - l[0], r[1] - l[1]};  // exact
+      t[2] = __builtin_convertvector(r2, bf16x2);
+    }
+  }
+}
+
 // One workgroup = QB/32 waves = QB queries of one head.  Two waves per SIMD
 // (<= 256 registers each): while one wave runs its softmax arithmetic the
-// other keeps the matrix cores busy.  BF16P selects the BF16-numerator
-// variant (one MFMA per P.V step instead of hi + lo).
-template <int QB, bool BF16P, int DH>
+// other keeps the matrix cores busy.  NP = BF16 terms per weight (1, 2, 3).
+template <int QB, int NP, int DH>
 __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
   constexpr int KS = DH + 8;     // K tile row stride in LDS (elements)
   constexpr int CPRK = DH / 8;   // 16-byte chunks per K row
@@ -200,19 +219,16 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
     // operand (V^T) uses the same key for the same slot.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x8 bhi, blo;
+      bf16x8 bt[NP];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
-        bf16x2 hi = __builtin_convertvector(pv, bf16x2);  // round to nearest even
-        bhi[j] = hi[0];
-        bhi[j + 1] = hi[1];
-        if (!BF16P) {
-          f32x2 hf = __builtin_convertvector(hi, f32x2);
-          f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};  // exact
-          bf16x2 lo = __builtin_convertvector(rem, bf16x2);
-          blo[j] = lo[0];
-          blo[j + 1] = lo[1];
+        bf16x2 t[3];
+        split_p<NP>(pv, t);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          bt[n][j] = t[n][0];
+          bt[n][j + 1] = t[n][1];
         }
       }
 #pragma unroll
@@ -221,8 +237,8 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
         uint2 x0 = *reinterpret_cast<const uint2*>(vr);
         uint2 x1 = *reinterpret_cast<const uint2*>(vr + 8);
         bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, o[dt], 0, 0, 0);
-        if (!BF16P) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, o[dt], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bt[n], o[dt], 0, 0, 0);
       }
     }
   };
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(QB * 2, 2) void attn_kernel(AttnArgs p) {
 // MFMA-only and a VALU-only phase.  K and V^T tiles are triple-buffered in
 // LDS: iteration t reads K of tile t+1 and V^T of tile t while tile t+2 is
 // stored.  Same arithmetic, in the same order per query, as attn_kernel.
-template <int QB, bool BF16P, int DH>
+template <int QB, int NP, int DH>
 __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
   constexpr int KS = DH + 8;
   constexpr int CPRK = DH / 8;
@@ -420,27 +436,24 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
     }
     l_run += lsum;
     m_run = m_new;
-    // P^T as B operands for the 4 groups of 16 keys
-    bf16x8 bhi[4], blo[4];
+    // P^T as B operands for the 4 groups of 16 keys, NP terms each
+    bf16x8 bt[NP][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
-        bf16x2 hi = __builtin_convertvector(pv, bf16x2);
-        bhi[g][j] = hi[0];
-        bhi[g][j + 1] = hi[1];
-        if (!BF16P) {
-          f32x2 hf = __builtin_convertvector(hi, f32x2);
-          f32x2 rem = {pv[0] - hf[0], pv[1] - hf[1]};
-          bf16x2 lo = __builtin_convertvector(rem, bf16x2);
-          blo[g][j] = lo[0];
-          blo[g][j + 1] = lo[1];
+        bf16x2 t[3];
+        split_p<NP>(pv, t);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          bt[n][g][j] = t[n][0];
+          bt[n][g][j + 1] = t[n][1];
         }
       }
     }
-    // O^T += V^T P^T: per group the four channel tiles' hi MFMAs, then their
-    // lo MFMAs (each accumulator still sees hi then lo of every group in
+    // O^T += V^T P^T: per group the channel tiles' MFMAs of term 0, then of
+    // term 1, ... (each accumulator still sees the terms of every group in
     // order); the V^T fragments of group g+1 are read during group g.
     auto vfrag = [&](int g, int dt) {
       const uint16_t* vr = &v_lds[buf][(dt * 32 + l32) * VS + 16 * g + 4 * half];
@@ -457,13 +470,10 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) vn[dt] = g + 1 < 4 ? vfrag(g + 1, dt) : va[dt];
 #pragma unroll
-      for (int dt = 0; dt < DH / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], bhi[g], o[dt], 0, 0, 0);
-      if (!BF16P) {
+      for (int n = 0; n < NP; ++n)
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], blo[g], o[dt], 0, 0, 0);
-      }
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], bt[n][g], o[dt], 0, 0, 0);
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) va[dt] = vn[dt];
     }
@@ -507,26 +517,36 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
   }
 }
 
-template <int QB, bool BF16P, int DH>
+template <int QB, int NP, int DH>
 hipError_t launch_pipe(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel_pipe<QB, BF16P, DH>), grid, dim3(QB * 2), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel_pipe<QB, NP, DH>), grid, dim3(QB * 2), 0, s, a);
   return hipGetLastError();
 }
 
-template <int QB, bool BF16P, int DH>
+template <int QB, int NP, int DH>
 hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel<QB, BF16P, DH>), grid, dim3(QB * 2), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<QB, NP, DH>), grid, dim3(QB * 2), 0, s, a);
   return hipGetLastError();
+}
+
+template <int NP, int DH>
+hipError_t launch_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case 2: return launch_q<256, NP, DH>(a, s);
+    case 3: return launch_pipe<256, NP, DH>(a, s);
+    default: return launch_q<128, NP, DH>(a, s);
+  }
 }
 
 template <int DH>
 hipError_t launch_dh(const AttnArgs& a, int cfg, hipStream_t s) {
-  switch (cfg) {
-    case 2: return a.bf16_p ? launch_q<256, true, DH>(a, s) : launch_q<256, false, DH>(a, s);
-    case 3: return a.bf16_p ? launch_pipe<256, true, DH>(a, s) : launch_pipe<256, false, DH>(a, s);
-    default: return a.bf16_p ? launch_q<128, true, DH>(a, s) : launch_q<128, false, DH>(a, s);
+  switch (a.p_terms) {
+    case 1: return launch_cfg<1, DH>(a, cfg, s);
+    case 2: return launch_cfg<2, DH>(a, cfg, s);
+    case 3: return launch_cfg<3, DH>(a, cfg, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

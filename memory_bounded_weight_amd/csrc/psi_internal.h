@@ -72,7 +72,8 @@ struct AttnArgs {
   int Mq, Mk, heads;
   int dh;              // head dimension: 128 or 64
   float alpha;         // 1/sqrt(dh) rounded to fp32
-  int bf16_p;          // 1: softmax weights rounded to BF16 before P*V
+  int p_terms;         // BF16 terms per softmax weight in P*V: 3 = fp32 weights,
+                       // 2 = hi + lo (about 17 bits), 1 = BF16 numerator weights
   int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query, 3: 256-query pipelined
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

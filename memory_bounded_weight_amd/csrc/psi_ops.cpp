@@ -151,6 +151,11 @@ struct ScratchMark {
   ~ScratchMark() { scratch_reset(a, mark); }
 };
 
+int attn_p_terms(unsigned flags) {
+  if (flags & PSI_OP_BF16_SOFTMAX) return 1;
+  return (flags & PSI_OP_ATTN_P2) ? 2 : 3;
+}
+
 GemmArgs gemm_args() {
   GemmArgs g{};
   g.epi = EPI_BIAS;
@@ -569,7 +574,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
       A.vt = Vt; A.ldvt = ldvt;
       A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
       A.alpha = alpha;
-      A.bf16_p = (flags & PSI_OP_BF16_SOFTMAX) ? 1 : 0;
+      A.p_terms = attn_p_terms(flags);
       if ((st = run_attention(a, A))) return st;
     }
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, (size_t)M * gw * 2))) return st;
@@ -725,7 +730,7 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
       A.vt = Vt; A.ldvt = ldvt;
       A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
       A.alpha = alpha;
-      A.bf16_p = (flags & PSI_OP_BF16_SOFTMAX) ? 1 : 0;
+      A.p_terms = attn_p_terms(flags);
       if ((st = run_attention(a, A))) return st;
     }
     // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
@@ -755,7 +760,7 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
                            psi_journal* fence, unsigned flags) {
   if (!a || !w) return fail(PSI_E_INVALID, "null argument");
   if (x == xt && M > 0) return fail(PSI_E_INVALID, "block: x_tmp must be a separate buffer");
-  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX)) | PSI_OP_RESIDUAL;
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2)) | PSI_OP_RESIDUAL;
   // validate both halves before enqueueing anything
   const int dm = heads * head_dim;
   psi_status st = psi_attn_plan(&a->desc, M, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo,

@@ -137,3 +137,20 @@ def attn_ext_case(seed: int = 0, M: int = 126, d: int = 2048, Mc: int = 0):
     gq = norm_gamma(rng, d)
     gk = norm_gamma(rng, d)
     return {"x": x, "ctx": ctx, "w": w, "gq": gq, "gk": gk}
+
+
+def lattice_attn_case(seed: int = 0, M: int = 126, d: int = 2048):
+    """Attention inputs on an integer lattice: x in {-2..2}, W in
+    {-1, 0, 1}/64, biases in {-2..2}/64 (uniform draws).  Every product and
+    partial sum of a projection is a multiple of 1/64 below 2^24/64 in
+    magnitude, so the fp32 sum is exact in any order and the GPU and the
+    oracle project to the same BF16 Q, K, V."""
+    rng = np.random.default_rng(seed)
+    lat = lambda shape, lo, hi, s: f32_to_bf16_bits(
+        rng.integers(lo, hi + 1, size=shape).astype(np.float32) * np.float32(s))
+    x = lat((M, d), -2, 2, 1.0)
+    w = {}
+    for n in ("q", "k", "v", "o"):
+        w["W" + n] = lat((d, d), -1, 1, 1.0 / 64)
+        w["b" + n] = lat((d,), -2, 2, 1.0 / 64)
+    return {"x": x, "w": w}
