@@ -29,7 +29,7 @@ MiB = 1 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 HBM_PEAK_GBPS = 8000.0
 
-WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity")
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity", "lowlive")
 
 
 def log(*a):
@@ -275,6 +275,76 @@ def build_workload(args, torch, psi, synth):
                     config={"workload": f"FFN schedules d={d} hidden={hid}", "tokens": M,
                             "ffn_tile": th, "output_tile": to, "arena_MiB": 32, "page_MiB": 8,
                             "pages": 2, "resident_weights": False})
+    if args.workload == "lowlive":
+        # Low-live-state mode ([PSI] sec. III-B: intermediate state retained on
+        # device or stored in the host journal): x is the only device state;
+        # head-group outputs and FFN hidden tiles live in the journal and are
+        # reloaded for every output tile.  4,991 tokens: one [4991, 16384] BF16
+        # hidden state is 163,545,088 B, the per-block journal figure the paper
+        # reports (sec. IV).  Two blocks per step; afterwards the same blocks
+        # run as psi_block_paged (device-resident intermediates) for the
+        # footprint, time and bitwise comparison.
+        M, d, heads, hid, nblk = 4991, 4096, 32, 16384, 2
+        gw, th, to_a, to_f = 1024, 1024, 512, 256
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, flags))
+        ws = [synth.block_weights(args.seed, b, d, hid) for b in range(nblk)]
+        low = [psi.block_weights(w, gw, th, attn_out_tile=to_a, ffn_out_tile=to_f) for w in ws]
+        reg = [psi.block_weights(w, gw, th) for w in ws]
+        del ws
+        x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
+        x = torch.empty_like(x0)
+        live += [x0, x]
+        journal = psi.psi_journal_create(8 * MiB, 4, M * (d + hid) * 2 + MiB)
+        n_oa, n_of = -(-d // to_a), -(-d // to_f)
+        jh2d_block = (n_oa * M * d + n_of * M * hid) * 2
+        jd2h_block = M * (d + hid) * 2
+        wh2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2
+
+        def step():
+            x.copy_(x0)
+            for b in range(nblk):
+                psi.psi_block_lowlive(arena, x, M, heads, 128, low[b], journal, 0)
+
+        def compare():
+            torch.cuda.synchronize()
+            psi.psi_arena_sync(arena)
+            psi.psi_journal_sync(journal)
+            out_low = x.cpu().numpy()
+            xr = torch.empty_like(x0)
+            xt = torch.empty_like(x0)
+            acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+            a2 = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, 0))
+            times = []
+            for r in range(1 + args.steps):
+                xr.copy_(x0)
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                for b in range(nblk):
+                    psi.psi_block_paged(a2, xr, xt, M, heads, 128, reg[b], 1, acc, None, 0)
+                psi.psi_arena_sync(a2)
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t)
+            psi.psi_arena_destroy(a2)
+            same = bool(np.array_equal(out_low, xr.cpu().numpy()))
+            act = M * d * 2
+            return {"regular_ms_per_step": round(1e3 * sum(times[1:]) / args.steps, 3),
+                    "bitwise_equal_to_regular": same,
+                    "device_state_bytes": {"lowlive": {"x": act},
+                                           "regular": {"x": act, "x_tmp": act, "fp32_acc": 2 * act}},
+                    "journal_per_block": {"d2h_bytes": jd2h_block, "h2d_bytes": jh2d_block,
+                                          "hidden_state_bytes": M * hid * 2,
+                                          "attn_output_tiles": n_oa, "ffn_output_tiles": n_of},
+                    "weight_h2d_per_block": wh2d_block}
+
+        flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
+        return dict(step=step, arena=arena, journal=journal, flops=flops_block * nblk,
+                    h2d=(wh2d_block + jh2d_block) * nblk, live=live, keep=(low, reg), after=compare,
+                    after_name="lowlive",
+                    config={"workload": "low-live-state blocks (x the only device state)", "tokens": M,
+                            "d_model": d, "heads": heads, "head_dim": 128, "ffn_hidden": hid,
+                            "blocks_per_step": nblk, "arena_MiB": 80, "page_MiB": 8, "pages": 2,
+                            "head_group": 8, "ffn_tile": th, "attn_output_tile": to_a,
+                            "ffn_output_tile": to_f, "resident_weights": False})
     if args.workload == "attn4096":
         M, Mc, d, heads = 6144, 1024, 4096, 32
         c = synth.attn_case(args.seed, M, Mc, d, cross=True)
@@ -402,6 +472,7 @@ def main():
         return
     h2d_gbps = measure_h2d_gbps(torch)
     log(f"bench: pinned H2D {h2d_gbps:.1f} GB/s")
+    torch.cuda.reset_peak_memory_stats()  # the probe's 256 MiB buffer is not the workload's
     wl = build_workload(args, torch, psi, synth)
     arena, journal, step = wl["arena"], wl["journal"], wl["step"]
 

@@ -250,6 +250,7 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
 #define PSI_ROLE_ATTN_O 16
 #define PSI_ROLE_FFN_H 17
 #define PSI_ROLE_FFN_HSTATE 18  /* hidden tiles journaled by PSI_FFN_REUSE */
+#define PSI_ROLE_ATTN_OSTATE 19 /* head-group outputs journaled by psi_attn_tiled */
 psi_status psi_arena_set_probe(psi_arena* a, psi_journal* j, int32_t step, int32_t block);
 
 /* ------------------------------------------------------------ page API */
@@ -320,13 +321,18 @@ psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x_dev, int M, int d,
  *                      page is streamed again and H_J recomputed; `j` unused
  * Per output the accumulation is the one of psi_ffn_paged (same hidden
  * tiles in the same order), so both schedules give its bits.
- *   x_dev [M, d], y_dev [M, d] (may alias x_dev with PSI_OP_RESIDUAL only
- *   when t_o == d).  Scratch: H_J [M, t_h] bf16 and ACC_o [M, t_o] fp32.
- *   flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL.  The journal store must
- *   hold h x M x 2 bytes more than it holds (PSI_FFN_REUSE).
+ *   x_dev [M, d], y_dev [M, d].  y_dev may alias x_dev with PSI_FFN_REUSE
+ *   (every read of x precedes the output tiles, and tile o reads and writes
+ *   only its own columns), with PSI_FFN_RECOMPUTE only when t_o == d.
+ *   Scratch: H_J [M, t_h] bf16 (two such buffers with PSI_FFN_REUSE, so
+ *   that journal copies of one overlap the GEMMs on the other) and ACC_o
+ *   [M, t_o] fp32.  flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL.  The
+ *   journal store must hold h x M x 2 bytes more than it holds
+ *   (PSI_FFN_REUSE).
  * Errors: PSI_E_INVALID (shapes, unknown schedule, missing journal, y
- * aliasing x over more than one output tile), PSI_E_SCRATCH_EXHAUSTED,
- * PSI_E_PAGE_TOO_SMALL, PSI_E_JOURNAL_KEY / PSI_E_JOURNAL_FULL. */
+ * aliasing x under recomputation over more than one output tile),
+ * PSI_E_SCRATCH_EXHAUSTED, PSI_E_PAGE_TOO_SMALL, PSI_E_JOURNAL_KEY /
+ * PSI_E_JOURNAL_FULL. */
 #define PSI_FFN_REUSE 1
 #define PSI_FFN_RECOMPUTE 2
 psi_status psi_ffn_tiled_plan(const psi_arena_desc* d, int M, int dmodel, const psi_matrix* U,
@@ -399,6 +405,33 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x_dev, int M,
                               const psi_matrix* Wo, const psi_qk_norm_rope* nr, float* acc_dev,
                               uint16_t* y_dev, unsigned flags);
 
+/* Attention sub-block with the O-projection over output tiles and the
+ * head-group outputs held in the journal instead of device memory ([PSI]
+ * sec. III-B: intermediate state is retained on device or stored in the
+ * host journal for later use).  Per head group g (pages Wq_g, Wk_g, Wv_g):
+ * Q_g, K_g, V_g^T and attention as psi_attn_paged, then O_g [M, e_g] is
+ * committed under key (step, block, g, PSI_ROLE_ATTN_OSTATE).  Then per
+ * output tile o (Wo split by ROWS, block t_o; one page holds t_o x d):
+ * ACC_o = sum over g ascending of O_g Wo[o rows, g cols]^T (fp32, carried),
+ * y[:, o] = B(ACC_o + bo_o) (+ x[:, o]), with every O_g reloaded from the
+ * journal (two device buffers: the reload of the next group overlaps the
+ * GEMM of the current one).  Each output element sums over the same
+ * channels in the same order as psi_attn_paged, so the result is its bits.
+ * The device holds no [M, d] intermediate: scratch is two [M, gw] buffers
+ * plus max(K_g and V_g^T, ACC_o [M, t_o] fp32).
+ *   y_dev may alias x_dev.  flags as psi_attn_paged except PSI_OP_STORE_ACC.
+ *   Journal traffic: M x d x 2 bytes D2H, (d / t_o) x M x d x 2 bytes H2D.
+ * Errors: as psi_attn_paged, plus PSI_E_INVALID for a missing journal and
+ * PSI_E_JOURNAL_KEY / PSI_E_JOURNAL_FULL. */
+psi_status psi_attn_tiled_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                               const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                               const psi_matrix* Wo, size_t* scratch_needed);
+psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x_dev, int M, const uint16_t* ctx_dev,
+                          int Mc, int heads, int head_dim, const psi_matrix* Wq,
+                          const psi_matrix* Wk, const psi_matrix* Wv, const psi_matrix* Wo,
+                          psi_journal* j, int32_t step, int32_t block, uint16_t* y_dev,
+                          unsigned flags);
+
 /* One synthetic transformer block in place: x_tmp = x + Attn(x) (self),
  * then x = x_tmp + FFN(x_tmp), both with the residual write.  If `fence`
  * is non-NULL, the FFN's output write first waits for every journal copy
@@ -412,6 +445,16 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x_dev, uint16_t* x_tmp_dev, i
                            int heads, int head_dim, const psi_block_weights* w,
                            int token_chunks, float* acc_dev, psi_journal* fence,
                            unsigned flags);
+
+/* One synthetic block in place with only x as device state (low-live-state
+ * mode): psi_journal_reset(j), then psi_attn_tiled (x -> x, residual) and
+ * psi_ffn_tiled with PSI_FFN_REUSE (x -> x, residual); the head-group
+ * outputs and hidden tiles live in the journal `j` (its store needs
+ * M x (d + h) x 2 bytes; it is reused by every call).  w->Wo and w->V are
+ * split by ROWS (output tiles).  Same bits as psi_block_paged.
+ * flags: PSI_OP_BASELINE_BIAS, PSI_OP_BF16_SOFTMAX, PSI_OP_ATTN_P2. */
+psi_status psi_block_lowlive(psi_arena* a, uint16_t* x_dev, int M, int heads, int head_dim,
+                             const psi_block_weights* w, psi_journal* j, unsigned flags);
 
 /* --------------------------------------------------------------- journal */
 
@@ -446,6 +489,11 @@ typedef struct psi_journal_desc {
 
 psi_status psi_journal_create(const psi_journal_desc* d, psi_journal** out);
 psi_status psi_journal_destroy(psi_journal* j);
+
+/* Drop every entry and reuse the store from its start.  GPU-ordered: all
+ * journal copies enqueued before the reset precede those enqueued after
+ * it, so the host need not wait.  Counters are kept. */
+psi_status psi_journal_reset(psi_journal* j);
 
 /* Enqueue a byte copy of dev[0, bytes) into the store under key k, ordered
  * after all work enqueued so far on `producer`.  Errors: PSI_E_JOURNAL_KEY

@@ -360,6 +360,8 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->bias_slots[i].release, hipEventDisableTiming);
       a->bias_slots[i].dev = a->base + L.bias_off[i];
     }
+    for (int i = 0; e == hipSuccess && i < 4; ++i)
+      e = hipEventCreateWithFlags(&a->pipe_ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       psi_status r = hip_fail(e, "psi_arena_create");
       psi_arena_destroy(a);
@@ -391,6 +393,8 @@ psi_status psi_arena_destroy(psi_arena* a) {
       if (a->bias_slots[i].ready) (void)hipEventDestroy(a->bias_slots[i].ready);
       if (a->bias_slots[i].release) (void)hipEventDestroy(a->bias_slots[i].release);
     }
+    for (hipEvent_t e : a->pipe_ev)
+      if (e) (void)hipEventDestroy(e);
     if (a->copy) (void)hipStreamDestroy(a->copy);
     if (a->copy1) (void)hipStreamDestroy(a->copy1);
     if (a->base) {

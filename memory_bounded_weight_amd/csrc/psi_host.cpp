@@ -232,7 +232,8 @@ psi_status psi_ffn_tiled_plan(const psi_arena_desc* d, int M, int dmodel, const 
                                "needs two page slots");
   const psi_matrix* uv[2] = {U, Vo};
   if ((st = bias_fit(L, uv, 2))) return st;
-  size_t need = align_up((size_t)M * U->block * 2, kAlign) + align_up((size_t)M * Vo->block * 4, kAlign);
+  const size_t hbuf = align_up((size_t)M * U->block * 2, kAlign);
+  size_t need = (schedule == PSI_FFN_REUSE ? 2 : 1) * hbuf + align_up((size_t)M * Vo->block * 4, kAlign);
   if ((st = scratch_fit(L, need, "FFN hidden tile and output-tile accumulator"))) return st;
   if (scratch_needed) *scratch_needed = need;
   return PSI_OK;
@@ -271,6 +272,45 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
                 align_up((size_t)gw * ldvt * 2, kAlign);
   if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
   if ((st = scratch_fit(L, need, "attention Q/K/V head-group tiles"))) return st;
+  if (scratch_needed) *scratch_needed = need;
+  return PSI_OK;
+}
+
+psi_status psi_attn_tiled_plan(const psi_arena_desc* d, int M, int Mc, int heads, int head_dim,
+                               const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                               const psi_matrix* Wo, size_t* scratch_needed) {
+  psi_arena_layout L;
+  psi_status st = psi_arena_plan(d, &L);
+  if (st) return st;
+  if (head_dim != 128 && head_dim != 64)
+    return fail(PSI_E_INVALID, "attention: head_dim must be 128 or 64");
+  if (heads <= 0 || M < 0 || Mc < 0) return fail(PSI_E_INVALID, "attention: bad sizes");
+  const int dm = heads * head_dim;
+  if ((st = check_matrix(Wq, "Wq", PSI_SPLIT_ROWS)) || (st = check_matrix(Wk, "Wk", PSI_SPLIT_ROWS)) ||
+      (st = check_matrix(Wv, "Wv", PSI_SPLIT_ROWS)))
+    return st;
+  if ((st = check_matrix(Wo, "Wo", PSI_SPLIT_ROWS))) return st;  // output tiles of the O-projection
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  for (const psi_matrix* m : ms)
+    if (m->rows != dm || m->cols != dm)
+      return fail(PSI_E_INVALID, "attention: projections must be [heads*head_dim, heads*head_dim]");
+  const int gw = Wq->block;
+  if (gw % head_dim != 0 || Wk->block != gw || Wv->block != gw)
+    return fail(PSI_E_INVALID, "attention: Wq, Wk, Wv need the same head-group block (a multiple of head_dim)");
+  if (gw % 8 != 0 || Wo->block % 8 != 0)
+    return fail(PSI_E_ALIGN, "attention: head-group and output tiles must be multiples of 8");
+  const char* names[4] = {"Wq", "Wk", "Wv", "Wo"};
+  for (int i = 0; i < 4; ++i)
+    if ((st = page_fit(d, ms[i], names[i]))) return st;
+  if ((st = bias_fit(L, ms, 4))) return st;
+  const int Ms = Mc > 0 ? Mc : M;
+  if (Ms < 1 && M > 0) return fail(PSI_E_INVALID, "attention: at least one key per row is required");
+  const size_t ldvt = align_up((size_t)Ms, 64);
+  const size_t obuf = align_up((size_t)M * gw * 2, kAlign);
+  const size_t kv = align_up((size_t)Ms * gw * 2, kAlign) + align_up((size_t)gw * ldvt * 2, kAlign);
+  const size_t acc = align_up((size_t)M * Wo->block * 4, kAlign);
+  const size_t need = 2 * obuf + (kv > acc ? kv : acc);
+  if ((st = scratch_fit(L, need, "attention Q/O buffers, K/V^T tiles, output-tile accumulator"))) return st;
   if (scratch_needed) *scratch_needed = need;
   return PSI_OK;
 }

@@ -154,6 +154,9 @@ struct psi_arena {
   hipEvent_t trace_base = nullptr;
   size_t trace_cap = 0;
   std::vector<psi_trace_event> trace;
+  // double-buffered journal transport inside operators (commit-read and
+  // reload-done events of two buffers)
+  hipEvent_t pipe_ev[4] = {nullptr, nullptr, nullptr, nullptr};
   int device = 0;
 };
 
@@ -192,4 +195,15 @@ psi_status check_pinned(const void* p, const char* what);
 // no probe journal is attached) and make the compute stream wait for the
 // copy before the buffer is reused.
 psi_status probe_commit(psi_arena* a, int32_t branch, int32_t role, const void* dev, size_t bytes);
+
+// Journal transport with caller events, so that an operator can keep two
+// buffers in flight: a commit records `read_ev` once the device bytes have
+// been read (the buffer may then be overwritten); a reload records `done`
+// once the bytes are in place and does NOT make the consumer wait (the
+// caller waits on `done` right before the reading kernel).  Null events
+// give psi_journal_commit / psi_journal_reload.
+psi_status journal_commit_ev(psi_journal* j, psi_key k, const void* dev, size_t bytes, hipStream_t prod,
+                             hipEvent_t read_ev);
+psi_status journal_reload_ev(psi_journal* j, psi_key k, void* dev, size_t bytes, hipStream_t cons,
+                             hipEvent_t done);
 }  // namespace psi

@@ -69,6 +69,155 @@ struct psi_journal {
   uint64_t bytes_d2h = 0, bytes_h2d = 0;
 };
 
+namespace psi {
+
+// Records `ev` on journal stream 1 once the work enqueued so far on the
+// streams marked in `touched` has completed.
+static psi_status join_record(psi_journal* j, hipEvent_t ev, const bool touched[2]) {
+  if (touched[0]) {
+    PSI_HIP(hipEventRecord(j->cross[0], j->stream[0]));
+    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->cross[0], 0));
+  }
+  return hipEventRecord(ev, j->stream[1]) == hipSuccess ? PSI_OK : fail(PSI_E_HIP, "journal event");
+}
+
+psi_status journal_commit_ev(psi_journal* j, psi_key k, const void* dev, size_t bytes, hipStream_t prod,
+                             hipEvent_t read_ev) {
+  if (!j || !dev || bytes == 0) return fail(PSI_E_INVALID, "journal commit: bad arguments");
+  if (j->index.count(k)) return fail(PSI_E_JOURNAL_KEY, "journal commit: duplicate key");
+  const size_t need = align_up(bytes, 64);
+  if (j->store_top + need > j->desc.store_bytes)
+    return fail(PSI_E_JOURNAL_FULL, "journal store full: " + std::to_string(j->store_top + need) +
+                                        " B > " + std::to_string(j->desc.store_bytes) + " B");
+  const Entry ent{j->store_top, bytes};
+  const size_t S = j->desc.ring_slot_bytes;
+  const char* src = static_cast<const char*>(dev);
+  if (j->desc.flags & PSI_JOURNAL_SYNC) {
+    // transport control: copies on the producer's stream, host blocks per slot
+    for (size_t off = 0; off < bytes; off += S) {
+      size_t n = bytes - off < S ? bytes - off : S;
+      PSI_HIP(hipMemcpyAsync(j->ring, src + off, n, hipMemcpyDeviceToHost, prod));
+      PSI_HIP(hipStreamSynchronize(prod));
+      std::memcpy(j->store + ent.off + off, j->ring, n);
+    }
+    if (read_ev) PSI_HIP(hipEventRecord(read_ev, prod));
+  } else if (!j->ring_mode) {
+    // one DMA copy straight into the pinned entry, after the producer's work
+    PSI_HIP(hipEventRecord(j->dep, prod));
+    PSI_HIP(hipStreamWaitEvent(j->stream[0], j->dep, 0));
+    PSI_HIP(hipMemcpyAsync(j->store + ent.off, src, bytes, hipMemcpyDeviceToHost, j->stream[0]));
+    PSI_HIP(hipEventRecord(j->read_done[0], j->stream[0]));
+    if (read_ev) PSI_HIP(hipEventRecord(read_ev, j->stream[0]));
+    j->used[0] = true;
+  } else {
+    PSI_HIP(hipEventRecord(j->dep, prod));
+    for (int i = 0; i < 2; ++i) PSI_HIP(hipStreamWaitEvent(j->stream[i], j->dep, 0));
+    bool touched[2] = {false, false};
+    for (size_t off = 0; off < bytes; off += S) {
+      size_t n = bytes - off < S ? bytes - off : S;
+      const int slot = j->next_slot;
+      j->next_slot = (slot + 1) % j->desc.ring_slots;
+      const int si = slot % 2;
+      char* stage = j->ring + (size_t)slot * S;
+      PSI_HIP(hipMemcpyAsync(stage, src + off, n, hipMemcpyDeviceToHost, j->stream[si]));
+      PSI_HIP(hipEventRecord(j->read_done[si], j->stream[si]));
+      j->used[si] = true;
+      touched[si] = true;
+      HostCopy* c = new HostCopy{j->store + ent.off + off, stage, n};
+      hipError_t e = hipLaunchHostFunc(j->stream[si], host_copy_cb, c);
+      if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "hipLaunchHostFunc(journal commit)");
+      }
+    }
+    if (read_ev) {
+      psi_status st = join_record(j, read_ev, touched);
+      if (st) return st;
+    }
+  }
+  j->index[k] = ent;
+  j->store_top += need;
+  j->bytes_d2h += bytes;
+  return PSI_OK;
+}
+
+psi_status journal_reload_ev(psi_journal* j, psi_key k, void* dev, size_t bytes, hipStream_t cons,
+                             hipEvent_t done) {
+  if (!j || !dev) return fail(PSI_E_INVALID, "journal reload: bad arguments");
+  auto it = j->index.find(k);
+  if (it == j->index.end()) return fail(PSI_E_JOURNAL_KEY, "journal reload: key not found");
+  if (it->second.bytes != bytes) return fail(PSI_E_JOURNAL_KEY, "journal reload: size mismatch");
+  const size_t S = j->desc.ring_slot_bytes;
+  char* dst = static_cast<char*>(dev);
+  const Entry ent = it->second;
+  if (j->desc.flags & PSI_JOURNAL_SYNC) {
+    PSI_HIP(hipStreamSynchronize(j->stream[0]));
+    PSI_HIP(hipStreamSynchronize(j->stream[1]));
+    for (size_t off = 0; off < bytes; off += S) {
+      size_t n = bytes - off < S ? bytes - off : S;
+      PSI_HIP(hipStreamSynchronize(cons));
+      std::memcpy(j->ring, j->store + ent.off + off, n);
+      PSI_HIP(hipMemcpyAsync(dst + off, j->ring, n, hipMemcpyHostToDevice, cons));
+    }
+    PSI_HIP(hipStreamSynchronize(cons));
+    if (done) PSI_HIP(hipEventRecord(done, cons));
+  } else if (!j->ring_mode) {
+    // the overwrite of dev follows its previous consumers on `cons`, and the
+    // entry's commit (both on the journal's streams) precedes the read
+    PSI_HIP(hipEventRecord(j->dep, cons));
+    PSI_HIP(hipEventRecord(j->cross[0], j->stream[0]));
+    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->dep, 0));
+    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->cross[0], 0));
+    PSI_HIP(hipMemcpyAsync(dst, j->store + ent.off, bytes, hipMemcpyHostToDevice, j->stream[1]));
+    if (done) {
+      PSI_HIP(hipEventRecord(done, j->stream[1]));
+    } else {
+      PSI_HIP(hipEventRecord(j->write_done[1], j->stream[1]));
+      PSI_HIP(hipStreamWaitEvent(cons, j->write_done[1], 0));
+    }
+  } else {
+    // the overwrite of dev follows its previous consumers on `cons`, and
+    // every earlier host commit (on either stream) precedes the reads of
+    // the store
+    PSI_HIP(hipEventRecord(j->dep, cons));
+    for (int i = 0; i < 2; ++i) PSI_HIP(hipEventRecord(j->cross[i], j->stream[i]));
+    for (int i = 0; i < 2; ++i) {
+      PSI_HIP(hipStreamWaitEvent(j->stream[i], j->dep, 0));
+      PSI_HIP(hipStreamWaitEvent(j->stream[i], j->cross[1 - i], 0));
+    }
+    bool touched[2] = {false, false};
+    for (size_t off = 0; off < bytes; off += S) {
+      size_t n = bytes - off < S ? bytes - off : S;
+      const int slot = j->next_slot;
+      j->next_slot = (slot + 1) % j->desc.ring_slots;
+      const int si = slot % 2;
+      char* stage = j->ring + (size_t)slot * S;
+      HostCopy* c = new HostCopy{stage, j->store + ent.off + off, n};
+      hipError_t e = hipLaunchHostFunc(j->stream[si], host_copy_cb, c);
+      if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "hipLaunchHostFunc(journal reload)");
+      }
+      PSI_HIP(hipMemcpyAsync(dst + off, stage, n, hipMemcpyHostToDevice, j->stream[si]));
+      touched[si] = true;
+    }
+    if (done) {
+      psi_status st = join_record(j, done, touched);
+      if (st) return st;
+    } else {
+      for (int i = 0; i < 2; ++i)
+        if (touched[i]) {
+          PSI_HIP(hipEventRecord(j->write_done[i], j->stream[i]));
+          PSI_HIP(hipStreamWaitEvent(cons, j->write_done[i], 0));
+        }
+    }
+  }
+  j->bytes_h2d += bytes;
+  return PSI_OK;
+}
+
+}  // namespace psi
+
 using namespace psi;
 
 extern "C" {
@@ -149,119 +298,21 @@ psi_status psi_journal_destroy(psi_journal* j) {
 
 psi_status psi_journal_commit(psi_journal* j, psi_key k, const void* dev, size_t bytes,
                               void* producer_stream) {
-  if (!j || !dev || bytes == 0) return fail(PSI_E_INVALID, "journal commit: bad arguments");
-  if (j->index.count(k)) return fail(PSI_E_JOURNAL_KEY, "journal commit: duplicate key");
-  const size_t need = align_up(bytes, 64);
-  if (j->store_top + need > j->desc.store_bytes)
-    return fail(PSI_E_JOURNAL_FULL, "journal store full: " + std::to_string(j->store_top + need) +
-                                        " B > " + std::to_string(j->desc.store_bytes) + " B");
-  hipStream_t prod = static_cast<hipStream_t>(producer_stream);
-  const Entry ent{j->store_top, bytes};
-  const size_t S = j->desc.ring_slot_bytes;
-  const char* src = static_cast<const char*>(dev);
-  if (j->desc.flags & PSI_JOURNAL_SYNC) {
-    // transport control: copies on the producer's stream, host blocks per slot
-    for (size_t off = 0; off < bytes; off += S) {
-      size_t n = bytes - off < S ? bytes - off : S;
-      PSI_HIP(hipMemcpyAsync(j->ring, src + off, n, hipMemcpyDeviceToHost, prod));
-      PSI_HIP(hipStreamSynchronize(prod));
-      std::memcpy(j->store + ent.off + off, j->ring, n);
-    }
-  } else if (!j->ring_mode) {
-    // one DMA copy straight into the pinned entry, after the producer's work
-    PSI_HIP(hipEventRecord(j->dep, prod));
-    PSI_HIP(hipStreamWaitEvent(j->stream[0], j->dep, 0));
-    PSI_HIP(hipMemcpyAsync(j->store + ent.off, src, bytes, hipMemcpyDeviceToHost, j->stream[0]));
-    PSI_HIP(hipEventRecord(j->read_done[0], j->stream[0]));
-    j->used[0] = true;
-  } else {
-    PSI_HIP(hipEventRecord(j->dep, prod));
-    for (int i = 0; i < 2; ++i) PSI_HIP(hipStreamWaitEvent(j->stream[i], j->dep, 0));
-    for (size_t off = 0; off < bytes; off += S) {
-      size_t n = bytes - off < S ? bytes - off : S;
-      const int slot = j->next_slot;
-      j->next_slot = (slot + 1) % j->desc.ring_slots;
-      const int si = slot % 2;
-      char* stage = j->ring + (size_t)slot * S;
-      PSI_HIP(hipMemcpyAsync(stage, src + off, n, hipMemcpyDeviceToHost, j->stream[si]));
-      PSI_HIP(hipEventRecord(j->read_done[si], j->stream[si]));
-      j->used[si] = true;
-      HostCopy* c = new HostCopy{j->store + ent.off + off, stage, n};
-      hipError_t e = hipLaunchHostFunc(j->stream[si], host_copy_cb, c);
-      if (e != hipSuccess) {
-        delete c;
-        return hip_fail(e, "hipLaunchHostFunc(journal commit)");
-      }
-    }
-  }
-  j->index[k] = ent;
-  j->store_top += need;
-  j->bytes_d2h += bytes;
-  return PSI_OK;
+  return journal_commit_ev(j, k, dev, bytes, static_cast<hipStream_t>(producer_stream), nullptr);
 }
 
 psi_status psi_journal_reload(psi_journal* j, psi_key k, void* dev, size_t bytes, void* consumer_stream) {
-  if (!j || !dev) return fail(PSI_E_INVALID, "journal reload: bad arguments");
-  auto it = j->index.find(k);
-  if (it == j->index.end()) return fail(PSI_E_JOURNAL_KEY, "journal reload: key not found");
-  if (it->second.bytes != bytes) return fail(PSI_E_JOURNAL_KEY, "journal reload: size mismatch");
-  hipStream_t cons = static_cast<hipStream_t>(consumer_stream);
-  const size_t S = j->desc.ring_slot_bytes;
-  char* dst = static_cast<char*>(dev);
-  const Entry ent = it->second;
-  if (j->desc.flags & PSI_JOURNAL_SYNC) {
-    PSI_HIP(hipStreamSynchronize(j->stream[0]));
-    PSI_HIP(hipStreamSynchronize(j->stream[1]));
-    for (size_t off = 0; off < bytes; off += S) {
-      size_t n = bytes - off < S ? bytes - off : S;
-      PSI_HIP(hipStreamSynchronize(cons));
-      std::memcpy(j->ring, j->store + ent.off + off, n);
-      PSI_HIP(hipMemcpyAsync(dst + off, j->ring, n, hipMemcpyHostToDevice, cons));
-    }
-    PSI_HIP(hipStreamSynchronize(cons));
-  } else if (!j->ring_mode) {
-    // the overwrite of dev follows its previous consumers on `cons`, and the
-    // entry's commit (both on the journal's streams) precedes the read
-    PSI_HIP(hipEventRecord(j->dep, cons));
-    PSI_HIP(hipEventRecord(j->cross[0], j->stream[0]));
-    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->dep, 0));
-    PSI_HIP(hipStreamWaitEvent(j->stream[1], j->cross[0], 0));
-    PSI_HIP(hipMemcpyAsync(dst, j->store + ent.off, bytes, hipMemcpyHostToDevice, j->stream[1]));
-    PSI_HIP(hipEventRecord(j->write_done[1], j->stream[1]));
-    PSI_HIP(hipStreamWaitEvent(cons, j->write_done[1], 0));
-  } else {
-    // the overwrite of dev follows its previous consumers on `cons`, and
-    // every earlier host commit (on either stream) precedes the reads of
-    // the store
-    PSI_HIP(hipEventRecord(j->dep, cons));
-    for (int i = 0; i < 2; ++i) PSI_HIP(hipEventRecord(j->cross[i], j->stream[i]));
-    for (int i = 0; i < 2; ++i) {
-      PSI_HIP(hipStreamWaitEvent(j->stream[i], j->dep, 0));
-      PSI_HIP(hipStreamWaitEvent(j->stream[i], j->cross[1 - i], 0));
-    }
-    bool touched[2] = {false, false};
-    for (size_t off = 0; off < bytes; off += S) {
-      size_t n = bytes - off < S ? bytes - off : S;
-      const int slot = j->next_slot;
-      j->next_slot = (slot + 1) % j->desc.ring_slots;
-      const int si = slot % 2;
-      char* stage = j->ring + (size_t)slot * S;
-      HostCopy* c = new HostCopy{stage, j->store + ent.off + off, n};
-      hipError_t e = hipLaunchHostFunc(j->stream[si], host_copy_cb, c);
-      if (e != hipSuccess) {
-        delete c;
-        return hip_fail(e, "hipLaunchHostFunc(journal reload)");
-      }
-      PSI_HIP(hipMemcpyAsync(dst + off, stage, n, hipMemcpyHostToDevice, j->stream[si]));
-      touched[si] = true;
-    }
-    for (int i = 0; i < 2; ++i)
-      if (touched[i]) {
-        PSI_HIP(hipEventRecord(j->write_done[i], j->stream[i]));
-        PSI_HIP(hipStreamWaitEvent(cons, j->write_done[i], 0));
-      }
-  }
-  j->bytes_h2d += bytes;
+  return journal_reload_ev(j, k, dev, bytes, static_cast<hipStream_t>(consumer_stream), nullptr);
+}
+
+psi_status psi_journal_reset(psi_journal* j) {
+  if (!j) return fail(PSI_E_INVALID, "null journal");
+  // everything enqueued so far on either journal stream (reloads reading
+  // the store, host commits writing it) precedes everything enqueued later
+  for (int i = 0; i < 2; ++i) PSI_HIP(hipEventRecord(j->cross[i], j->stream[i]));
+  for (int i = 0; i < 2; ++i) PSI_HIP(hipStreamWaitEvent(j->stream[i], j->cross[1 - i], 0));
+  j->index.clear();
+  j->store_top = 0;
   return PSI_OK;
 }
 

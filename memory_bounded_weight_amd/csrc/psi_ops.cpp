@@ -354,8 +354,8 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   if (schedule == PSI_FFN_REUSE && !j) return fail(PSI_E_INVALID, "ffn tiled: FFN reuse needs a journal");
   if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "ffn tiled: no full accumulator to store");
   const int nO = psi_matrix_pages(Vo);
-  if (x == y && nO > 1)
-    return fail(PSI_E_INVALID, "ffn tiled: y may alias x only with a single output tile");
+  if (x == y && nO > 1 && schedule != PSI_FFN_REUSE)
+    return fail(PSI_E_INVALID, "ffn tiled: with recomputation y may alias x only with a single output tile");
   if (!a->dry) {
     if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y"))) return st;
     if (d % 8 != 0) return fail(PSI_E_ALIGN, "d must be a multiple of 8");
@@ -365,9 +365,16 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   const bool resid = flags & PSI_OP_RESIDUAL;
   const int th = U->block, to = Vo->block, h = U->rows;
   const int nJ = psi_matrix_pages(U);
+  const bool reuse = schedule == PSI_FFN_REUSE;
   ScratchMark mark(a);
-  uint16_t* H = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
+  uint16_t* Hb[2];
+  Hb[0] = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
   if (st) return st;
+  Hb[1] = Hb[0];
+  if (reuse) {  // two hidden-tile buffers: journal copies overlap the GEMMs
+    Hb[1] = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
+    if (st) return st;
+  }
   float* acc = static_cast<float*>(scratch_alloc(a, (size_t)M * to * 4, &st));
   if (st) return st;
   const psi_matrix* ms[2] = {U, Vo};
@@ -392,7 +399,7 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   // H_J = B(phi(B(x U_J^T + a_J))) for all tokens, stored compactly
   // ([M, e_J], row stride e_J) so that a ragged last tile is also one
   // contiguous journal entry
-  auto up = [&](int J, const uint16_t* page) -> psi_status {
+  auto up = [&](int J, const uint16_t* page, uint16_t* H) -> psi_status {
     psi_status s2 = bias.get(0, &ba);
     if (s2) return s2;
     const int ej = matrix_page_extent(U, J);
@@ -407,7 +414,7 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
     return run_gemm(a, g);
   };
   // ACC_o (+)= H_J V_o[:, J]^T; the last hidden tile writes y[:, o]
-  auto down = [&](int o, int J, const uint16_t* vpage) -> psi_status {
+  auto down = [&](int o, int J, const uint16_t* vpage, const uint16_t* H) -> psi_status {
     const int eo = matrix_page_extent(Vo, o), ej = matrix_page_extent(U, J);
     const bool last = J == nJ - 1;
     GemmArgs g = gemm_args();
@@ -430,26 +437,38 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
     return run_gemm(a, g);
   };
   const uint16_t* page;
-  if (schedule == PSI_FFN_REUSE) {
+  if (reuse) {
+    // H_J in buffer J % 2: the commit of H_J records rd[b] once the journal
+    // has read it, and up(J + 2) overwrites the buffer only after that
+    hipEvent_t* rd = a->pipe_ev;
+    hipEvent_t* ld = a->pipe_ev + 2;
+    auto hkey = [&](int J) { return psi_key{step, block, J, PSI_ROLE_FFN_HSTATE}; };
+    auto hbytes = [&](int J) { return (size_t)M * matrix_page_extent(U, J) * 2; };
     for (int J = 0; J < nJ; ++J) {
-      if ((st = feeder.take(J, &page)) || (st = up(J, page)) || (st = feeder.give_back(J))) return st;
-      const size_t hb = (size_t)M * matrix_page_extent(U, J) * 2;
-      if (!a->dry) {
-        // H_J to the journal; the next hidden tile overwrites H after the copy
-        if ((st = psi_journal_commit(j, psi_key{step, block, J, PSI_ROLE_FFN_HSTATE}, H, hb, a->compute)) ||
-            (st = psi_journal_fence(j, a->compute)))
-          return st;
-      }
+      const int b = J % 2;
+      if (!a->dry && J >= 2) PSI_HIP(hipStreamWaitEvent(a->compute, rd[b], 0));
+      if ((st = feeder.take(J, &page)) || (st = up(J, page, Hb[b])) || (st = feeder.give_back(J))) return st;
+      if (!a->dry && (st = journal_commit_ev(j, hkey(J), Hb[b], hbytes(J), a->compute, rd[b]))) return st;
     }
+    // down-projection steps t = o * nJ + J read buffer t % 2; the reload of
+    // step t + 1 is issued before the GEMM of step t (after the GEMM of
+    // step t - 1, the buffer's previous reader), so copies overlap GEMMs
+    const int T = nO * nJ;
+    auto issue = [&](int t) -> psi_status {
+      const int J = t % nJ;
+      return journal_reload_ev(j, hkey(J), Hb[t % 2], hbytes(J), a->compute, ld[t % 2]);
+    };
+    if (!a->dry && (st = issue(0))) return st;
     for (int o = 0; o < nO; ++o) {
       const uint16_t* vpage;
       if ((st = feeder.take(nJ + o, &vpage))) return st;
       for (int J = 0; J < nJ; ++J) {
-        const size_t hb = (size_t)M * matrix_page_extent(U, J) * 2;
-        if (!a->dry &&
-            (st = psi_journal_reload(j, psi_key{step, block, J, PSI_ROLE_FFN_HSTATE}, H, hb, a->compute)))
-          return st;
-        if ((st = down(o, J, vpage))) return st;
+        const int t = o * nJ + J;
+        if (!a->dry) {
+          if (t + 1 < T && (st = issue(t + 1))) return st;
+          PSI_HIP(hipStreamWaitEvent(a->compute, ld[t % 2], 0));
+        }
+        if ((st = down(o, J, vpage, Hb[t % 2]))) return st;
       }
       if ((st = feeder.give_back(nJ + o))) return st;
     }
@@ -461,8 +480,8 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
       if ((st = feeder.take(vi, &vpage))) return st;
       for (int J = 0; J < nJ; ++J) {
         const size_t ui = r++;
-        if ((st = feeder.take(ui, &page)) || (st = up(J, page)) || (st = feeder.give_back(ui))) return st;
-        if ((st = down(o, J, vpage))) return st;
+        if ((st = feeder.take(ui, &page)) || (st = up(J, page, Hb[0])) || (st = feeder.give_back(ui))) return st;
+        if ((st = down(o, J, vpage, Hb[0]))) return st;
       }
       if ((st = feeder.give_back(vi))) return st;
     }
@@ -753,6 +772,168 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
     if ((st = feeder.give_back(base + 2 * g + 1))) return st;
   }
   return bias.release();
+}
+
+psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc, int heads,
+                          int head_dim, const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                          const psi_matrix* Wo, psi_journal* j, int32_t step, int32_t block, uint16_t* y,
+                          unsigned flags) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
+  if (!ctx) Mc = 0;
+  psi_status st = psi_attn_tiled_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nullptr);
+  if (st) return st;
+  if (!j) return fail(PSI_E_INVALID, "attention tiled: needs a journal for the head-group outputs");
+  if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "attention tiled: no full accumulator to store");
+  if (!a->dry) {
+    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true))) return st;
+    if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
+        (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
+      return st;
+  }
+  if (M == 0) return PSI_OK;
+  const int dm = heads * head_dim;
+  const int gw = Wq->block, to = Wo->block;
+  const uint16_t* src = ctx ? ctx : x;
+  const int Ms = ctx ? Mc : M;
+  const long ldvt = (long)align_up((size_t)Ms, 64);
+  const int bbase = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  ScratchMark mark(a);
+  uint16_t* Ob[2];  // Q_g, then O_g in place; later the reloaded O_g
+  for (int i = 0; i < 2; ++i) {
+    Ob[i] = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * gw * 2, &st));
+    if (st) return st;
+  }
+  const size_t phase_mark = a->scratch_top;
+  uint16_t* Kb = static_cast<uint16_t*>(scratch_alloc(a, (size_t)Ms * gw * 2, &st));
+  if (st) return st;
+  uint16_t* Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
+  if (st) return st;
+  const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
+  OpBiases bias;
+  if ((st = bias.stage(a, ms, 4))) return st;
+  std::vector<PageReq> rq, rk, rv, ro, reqs;
+  matrix_requests(Wq, rq);
+  matrix_requests(Wk, rk);
+  matrix_requests(Wv, rv);
+  matrix_requests(Wo, ro);
+  const int nG = (int)rq.size(), nO = (int)ro.size();
+  for (int g = 0; g < nG; ++g) {
+    reqs.push_back(rq[g]);
+    reqs.push_back(rk[g]);
+    reqs.push_back(rv[g]);
+  }
+  reqs.insert(reqs.end(), ro.begin(), ro.end());
+  const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
+  PageFeeder feeder(a, reqs);
+  if ((st = feeder.feed())) return st;
+  const uint16_t* bq[4];
+  for (int i = 0; i < 4; ++i)
+    if ((st = bias.get(i, &bq[i]))) return st;
+  hipEvent_t* rd = a->pipe_ev;
+  hipEvent_t* ld = a->pipe_ev + 2;
+  auto okey = [&](int g) { return psi_key{step, block, g, PSI_ROLE_ATTN_OSTATE}; };
+  auto obytes = [&](int g) { return (size_t)M * matrix_page_extent(Wq, g) * 2; };
+  const uint16_t* page;
+  // per head group: Q_g, K_g, V_g^T, attention; O_g (compact [M, e_g]) to the journal
+  for (int g = 0; g < nG; ++g) {
+    const int ext = matrix_page_extent(Wq, g);
+    const size_t c0 = (size_t)g * gw;
+    uint16_t* Q = Ob[g % 2];
+    if (!a->dry && g >= 2) PSI_HIP(hipStreamWaitEvent(a->compute, rd[g % 2], 0));
+    if ((st = feeder.take(3 * g, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
+      G.M = M; G.N = ext; G.K = dm;
+      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q; G.ldo = ext; G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(3 * g))) return st;
+    if ((st = feeder.take(3 * g + 1, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
+      G.M = Ms; G.N = ext; G.K = dm;
+      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb; G.ldo = ext; G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(3 * g + 1))) return st;
+    if ((st = feeder.take(3 * g + 2, &page))) return st;
+    {
+      GemmArgs G = gemm_args();
+      G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
+      G.M = ext; G.N = Ms; G.K = dm;
+      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
+      G.baseline_bias = bbase;
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(3 * g + 2))) return st;
+    {
+      AttnArgs A{};
+      A.q = Q; A.ldq = ext;
+      A.k = Kb; A.ldk = ext;
+      A.vt = Vt; A.ldvt = ldvt;
+      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
+      A.alpha = alpha;
+      A.p_terms = attn_p_terms(flags);
+      if ((st = run_attention(a, A))) return st;
+    }
+    if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, obytes(g)))) return st;
+    if (!a->dry && (st = journal_commit_ev(j, okey(g), Q, obytes(g), a->compute, rd[g % 2]))) return st;
+  }
+  // per output tile o: ACC_o = sum over g ascending of O_g Wo[o, g]^T, then
+  // y[:, o] = B(ACC_o + bo_o) (+ x[:, o]); O_g reloads alternate buffers
+  scratch_reset(a, phase_mark);
+  float* acc = static_cast<float*>(scratch_alloc(a, (size_t)M * to * 4, &st));
+  if (st) return st;
+  const int T = nO * nG;
+  auto issue = [&](int t) -> psi_status {
+    const int g = t % nG;
+    return journal_reload_ev(j, okey(g), Ob[t % 2], obytes(g), a->compute, ld[t % 2]);
+  };
+  if (!a->dry && (st = issue(0))) return st;
+  for (int o = 0; o < nO; ++o) {
+    const int eo = matrix_page_extent(Wo, o);
+    const size_t c0 = (size_t)o * to;
+    if ((st = feeder.take(3 * nG + o, &page))) return st;
+    for (int g = 0; g < nG; ++g) {
+      const int t = o * nG + g;
+      const int ext = matrix_page_extent(Wq, g);
+      if (!a->dry) {
+        if (t + 1 < T && (st = issue(t + 1))) return st;
+        PSI_HIP(hipStreamWaitEvent(a->compute, ld[t % 2], 0));
+      }
+      GemmArgs G = gemm_args();
+      G.A = Ob[t % 2]; G.lda = ext; G.B = page + (size_t)g * gw; G.ldb = dm;
+      G.M = M; G.N = eo; G.K = ext;
+      G.baseline_bias = bbase;
+      if (g > 0) { G.acc_in = acc; G.ld_acc_in = eo; }
+      if (g == nG - 1) {
+        G.bias = bq[3] ? bq[3] + c0 : nullptr; G.out = y + c0; G.ldo = dm;
+        if (flags & PSI_OP_RESIDUAL) { G.resid = x + c0; G.ldr = dm; }
+      } else {
+        G.epi = EPI_ACC; G.acc_out = acc; G.ld_acc_out = eo;
+      }
+      if ((st = run_gemm(a, G))) return st;
+    }
+    if ((st = feeder.give_back(3 * nG + o))) return st;
+  }
+  return bias.release();
+}
+
+psi_status psi_block_lowlive(psi_arena* a, uint16_t* x, int M, int heads, int head_dim,
+                             const psi_block_weights* w, psi_journal* j, unsigned flags) {
+  if (!a || !w || !j) return fail(PSI_E_INVALID, "null argument");
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2)) | PSI_OP_RESIDUAL;
+  const int dm = heads * head_dim;
+  psi_status st = psi_attn_tiled_plan(&a->desc, M, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, nullptr);
+  if (st) return st;
+  if ((st = psi_ffn_tiled_plan(&a->desc, M, dm, &w->U, &w->V, PSI_FFN_REUSE, nullptr))) return st;
+  if (!a->dry && (st = psi_journal_reset(j))) return st;
+  if ((st = psi_attn_tiled(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, j, 0, 0, x, f)))
+    return st;
+  return psi_ffn_tiled(a, x, M, dm, &w->U, &w->V, PSI_FFN_REUSE, j, 0, 1, x, f & ~PSI_OP_BF16_SOFTMAX);
 }
 
 psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int heads, int head_dim,

@@ -58,6 +58,7 @@ PSI_OP_ATTN_P2 = 0x10
 PSI_ROLE_ATTN_O = 16
 PSI_ROLE_FFN_H = 17
 PSI_ROLE_FFN_HSTATE = 18
+PSI_ROLE_ATTN_OSTATE = 19
 PSI_FFN_REUSE = 1
 PSI_FFN_RECOMPUTE = 2
 
@@ -180,6 +181,12 @@ _sig("psi_attn_ext_plan", [_P(psi_arena_desc), _i, _i, _i, _i, _P(psi_matrix), _
                            _P(psi_matrix), _P(psi_matrix), _P(psi_qk_norm_rope), _i, _P(_sz)])
 _sig("psi_attn_paged_ext", [_vp, _vp, _i, _vp, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
                             _P(psi_matrix), _P(psi_matrix), _P(psi_qk_norm_rope), _vp, _vp, _u])
+_sig("psi_attn_tiled_plan", [_P(psi_arena_desc), _i, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
+                             _P(psi_matrix), _P(psi_matrix), _P(_sz)])
+_sig("psi_attn_tiled", [_vp, _vp, _i, _vp, _i, _i, _i, _P(psi_matrix), _P(psi_matrix),
+                        _P(psi_matrix), _P(psi_matrix), _vp, ctypes.c_int32, ctypes.c_int32, _vp, _u])
+_sig("psi_block_lowlive", [_vp, _vp, _i, _i, _i, _P(psi_block_weights), _vp, _u])
+_sig("psi_journal_reset", [_vp])
 _sig("psi_block_paged", [_vp, _vp, _vp, _i, _i, _i, _P(psi_block_weights), _i, _vp, _vp, _u])
 _sig("psi_journal_create", [_P(psi_journal_desc), _P(_vp)])
 _sig("psi_journal_destroy", [_vp])
@@ -198,7 +205,8 @@ EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_
            "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
            "psi_attn_paged", "psi_block_paged", "psi_ffn_tiled_plan", "psi_ffn_tiled",
-           "psi_attn_ext_plan", "psi_attn_paged_ext",
+           "psi_attn_ext_plan", "psi_attn_paged_ext", "psi_attn_tiled_plan", "psi_attn_tiled",
+           "psi_block_lowlive", "psi_journal_reset",
            "psi_journal_create", "psi_journal_destroy",
            "psi_journal_commit", "psi_journal_reload", "psi_journal_fence", "psi_journal_sync",
            "psi_journal_read", "psi_journal_counters"]
@@ -406,6 +414,29 @@ def psi_attn_paged_ext(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr
                                           _ptr(acc), _ptr(y), flags), "psi_attn_paged_ext")
 
 
+def psi_attn_tiled_plan(desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo):
+    need = _sz(0)
+    st = _lib.psi_attn_tiled_plan(ctypes.byref(desc), M, Mc, heads, head_dim, ctypes.byref(Wq),
+                                  ctypes.byref(Wk), ctypes.byref(Wv), ctypes.byref(Wo), ctypes.byref(need))
+    return _plan_status(st, need)
+
+
+def psi_attn_tiled(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, journal, step, block, y, flags=0):
+    return _check(_lib.psi_attn_tiled(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
+                                      ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
+                                      ctypes.byref(Wo), journal, step, block, _ptr(y), flags),
+                  "psi_attn_tiled")
+
+
+def psi_block_lowlive(arena, x, M, heads, head_dim, w: psi_block_weights, journal, flags=0):
+    return _check(_lib.psi_block_lowlive(arena, _ptr(x), M, heads, head_dim, ctypes.byref(w), journal,
+                                         flags), "psi_block_lowlive")
+
+
+def psi_journal_reset(j):
+    return _check(_lib.psi_journal_reset(j), "psi_journal_reset")
+
+
 def psi_block_paged(arena, x, x_tmp, M, heads, head_dim, w: psi_block_weights, token_chunks,
                     acc, journal=None, flags=0):
     return _check(_lib.psi_block_paged(arena, _ptr(x), _ptr(x_tmp), M, heads, head_dim,
@@ -494,15 +525,21 @@ def resident_matrix(m: psi_matrix) -> psi_matrix:
     return r
 
 
-def block_weights(w: dict, group_cols: int, hidden_tile: int, resident: bool = False) -> psi_block_weights:
+def block_weights(w: dict, group_cols: int, hidden_tile: int, resident: bool = False,
+                  attn_out_tile: int = 0, ffn_out_tile: int = 0) -> psi_block_weights:
     """psi_block_weights from a dict of host bf16 arrays (Wq..bo, U, a, V, b);
-    ``resident`` places the page images in device memory instead.  The
-    returned structure holds (copies of) the six psi_matrix values and keeps
-    the Python objects that own their buffers alive."""
+    ``resident`` places the page images in device memory instead.  With
+    ``attn_out_tile`` / ``ffn_out_tile`` set, Wo / V are split by rows into
+    output tiles of that many rows (the layout psi_block_lowlive takes);
+    otherwise by columns (psi_block_paged).  The returned structure holds
+    (copies of) the six psi_matrix values and keeps the Python objects that
+    own their buffers alive."""
     mats = {n: pinned_matrix(w[n], w["b" + n[1]], PSI_SPLIT_ROWS, group_cols) for n in ("Wq", "Wk", "Wv")}
-    mats["Wo"] = pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_COLS, group_cols)
+    mats["Wo"] = (pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_ROWS, attn_out_tile) if attn_out_tile else
+                  pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_COLS, group_cols))
     mats["U"] = pinned_matrix(w["U"], w["a"], PSI_SPLIT_ROWS, hidden_tile)
-    mats["V"] = pinned_matrix(w["V"], w["b"], PSI_SPLIT_COLS, hidden_tile)
+    mats["V"] = (pinned_matrix(w["V"], w["b"], PSI_SPLIT_ROWS, ffn_out_tile) if ffn_out_tile else
+                 pinned_matrix(w["V"], w["b"], PSI_SPLIT_COLS, hidden_tile))
     if resident:
         mats = {n: resident_matrix(m) for n, m in mats.items()}
     bw = psi_block_weights(mats["Wq"], mats["Wk"], mats["Wv"], mats["Wo"], mats["U"], mats["V"])

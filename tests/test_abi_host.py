@@ -298,6 +298,8 @@ def test_ffn_tiled_plans_and_recompute_stream_dry_run():
     U, _ = cfg5_ffn()                                            # [16384, 4096], 1,024-row pages
     Vo = fake_matrix(4096, 16384, psi.PSI_SPLIT_ROWS, 256)       # 256 x 16,384 = 8 MiB pages
     st, need = psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vo, psi.PSI_FFN_REUSE)
+    assert st == psi.PSI_OK and need == 2 * 2048 * 1024 * 2 + 2048 * 256 * 4  # two hidden-tile buffers
+    st, need = psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE)
     assert st == psi.PSI_OK and need == 2048 * 1024 * 2 + 2048 * 256 * 4
     assert psi.psi_ffn_tiled_plan(d, 2048, 4096, U, Vo, 3)[0] == psi.PSI_E_INVALID
     Vk = fake_matrix(4096, 16384, psi.PSI_SPLIT_COLS, 1024)
@@ -366,5 +368,36 @@ def test_attn_ext_audio_shape_dry_run():
         assert s.kernel_launches == 4 * 5 + 2
         ldvt = 128
         assert s.scratch_high_water == 2 * M * d * 2 + gw * ldvt * 2
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_attn_tiled_plan_and_lowlive_block_dry_run():
+    """Low-live-state block ([PSI] sec. III-B: state retained on device or in
+    the host journal): Wo and V split by rows into output tiles; the arena
+    holds two [M, gw] buffers plus max(K/V^T, ACC_o) for attention and two
+    hidden tiles plus ACC_o for the FFN; pages stream once per block."""
+    d, h, M, gw, to_a, to_f, th = 4096, 16384, 2048, 1024, 512, 256, 1024
+    q, k, v = [fake_matrix(d, d, psi.PSI_SPLIT_ROWS, gw) for _ in range(3)]
+    wo = fake_matrix(d, d, psi.PSI_SPLIT_ROWS, to_a)
+    st, need = psi.psi_attn_tiled_plan(desc(80, 8, 2), M, 0, 32, 128, q, k, v, wo)
+    ldvt = M
+    kv = M * gw * 2 + gw * ldvt * 2
+    assert st == psi.PSI_OK and need == 2 * M * gw * 2 + max(kv, M * to_a * 4)
+    wo_cols = fake_matrix(d, d, psi.PSI_SPLIT_COLS, gw)
+    assert psi.psi_attn_tiled_plan(desc(80, 8, 2), M, 0, 32, 128, q, k, v, wo_cols)[0] == psi.PSI_E_INVALID
+    U = fake_matrix(h, d, psi.PSI_SPLIT_ROWS, th)
+    V = fake_matrix(d, h, psi.PSI_SPLIT_ROWS, to_f)
+    bw = psi.psi_block_weights(q, k, v, wo, U, V)
+    a = psi.psi_arena_create(desc(80, 8, 2))
+    try:
+        fake, fake_journal = 0x10000, 0x20000
+        psi.psi_block_lowlive(a, fake, M, 32, 128, bw, fake_journal, 0)
+        s = psi.psi_arena_stats(a)
+        nG, nOa, nJ, nOf = d // gw, d // to_a, h // th, d // to_f
+        assert s.page_copies == 3 * nG + nOa + nJ + nOf
+        assert s.kernel_launches == 4 * nG + nOa * nG + nJ + nOf * nJ
+        assert s.bytes_h2d == 4 * d * d * 2 + 2 * d * h * 2 + (4 * d + h + d) * 2
+        assert s.scratch_high_water == max(need, 2 * M * th * 2 + M * to_f * 4)
     finally:
         psi.psi_arena_destroy(a)

@@ -94,3 +94,36 @@ def test_journal_commit_follows_producer(P):
             assert (out == expect).all()
     finally:
         P.psi_journal_destroy(j)
+
+
+@pytest.mark.parametrize("flags", [0, "ring"])
+def test_journal_reset_reuses_store_in_stream_order(P, flags):
+    """psi_journal_reset drops every key and reuses the store from its
+    start without a host wait: a reload enqueued before the reset still
+    reads the old bytes, a commit after it writes the same store bytes."""
+    fl = {0: 0, "ring": P.PSI_JOURNAL_RING}[flags]
+    n = 3 * MiB
+    j = P.psi_journal_create(1 * MiB, 4, n + MiB, fl)  # room for one entry only
+    try:
+        s = torch.cuda.current_stream().cuda_stream
+        a = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        b = torch.full((n,), 9, dtype=torch.uint8, device="cuda")
+        out_a = torch.empty_like(a)
+        out_b = torch.empty_like(b)
+        P.psi_journal_commit(j, P.key(0, 0, 0, 1), a, n, s)
+        P.psi_journal_reload(j, P.key(0, 0, 0, 1), out_a, n, s)
+        with pytest.raises(P.PsiError) as e:  # the store is full
+            P.psi_journal_commit(j, P.key(0, 0, 1, 1), b, n, s)
+        assert e.value.status == P.PSI_E_JOURNAL_FULL
+        P.psi_journal_reset(j)
+        with pytest.raises(P.PsiError) as e:
+            P.psi_journal_reload(j, P.key(0, 0, 0, 1), out_b, n, s)
+        assert e.value.status == P.PSI_E_JOURNAL_KEY
+        P.psi_journal_commit(j, P.key(0, 0, 0, 1), b, n, s)  # same key, same store bytes
+        P.psi_journal_reload(j, P.key(0, 0, 0, 1), out_b, n, s)
+        torch.cuda.synchronize()
+        P.psi_journal_sync(j)
+        assert torch.equal(out_a, a) and torch.equal(out_b, b)
+        assert P.psi_journal_counters(j) == (2 * n, 2 * n, 1)
+    finally:
+        P.psi_journal_destroy(j)
