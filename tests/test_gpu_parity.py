@@ -378,7 +378,7 @@ def test_attention_uniform_weights_bitwise(P, Mc):
 
 def test_attention_bf16_softmax_variant(P):
     """The BF16-numerator variant (baseline) is within tolerance of the
-    oracle but further from it than the default fp32-faithful weights."""
+    oracle but further from it than the default fp32 weights."""
     rng = np.random.default_rng(11)
     d, heads = 256, 2
     x = synth.normal_bf16(rng, (128, d), 1.0)
