@@ -29,7 +29,7 @@ MiB = 1 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 HBM_PEAK_GBPS = 8000.0
 
-WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity", "lowlive")
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity", "lowlive", "audio8")
 
 
 def log(*a):
@@ -345,6 +345,53 @@ def build_workload(args, torch, psi, synth):
                             "blocks_per_step": nblk, "arena_MiB": 80, "page_MiB": 8, "pages": 2,
                             "head_group": 8, "ffn_tile": th, "attn_output_tile": to_a,
                             "ffn_output_tile": to_f, "resident_weights": False})
+    if args.workload == "audio8":
+        # Audio-branch shape ([PSI] sec. II-B, sec. III-A): 8 blocks of 126
+        # tokens at d 2,048 (32 heads of 64) with RMS-normalised, rotated Q/K
+        # (psi_attn_paged_ext, 8-head pages) and an FFN of 8,192 (1,024-channel
+        # tiles), each sub-block with its residual.  Tiny token count: every
+        # step is bound by streaming the 8 blocks' weights.
+        M, d, heads, dh, hid, nblk = 126, 2048, 32, 64, 8192, 8
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 3, 0, 0, stream, flags))
+        blocks, gammas = [], []
+        for b in range(nblk):
+            w = synth.block_weights(args.seed, b, d, hid)
+            blocks.append(psi.block_weights(w, 8 * dh, 1024, resident=args.resident))
+            rng = np.random.default_rng([args.seed, b, 1])
+            g = [synth.norm_gamma(rng, d) for _ in range(2)]
+            if args.resident:
+                gammas.append([torch.from_numpy(v.view("int16")).cuda() for v in g])
+            else:
+                pv = [torch.empty(d, dtype=torch.int16, pin_memory=True) for _ in g]
+                for t, v in zip(pv, g):
+                    t.copy_(torch.from_numpy(v.view("int16")))
+                gammas.append(pv)
+        cq, sq = synth.rope_tables(M, dh)
+        cos_t = torch.from_numpy(cq).cuda()
+        sin_t = torch.from_numpy(sq).cuda()
+        nrs = [psi.qk_norm_rope(g[0], g[1], 1e-6, 0, cos_t, sin_t) for g in gammas]
+        x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
+        x = torch.empty_like(x0)
+        xt = torch.empty_like(x0)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        live += [x0, x, xt, acc, cos_t, sin_t]
+
+        def step():
+            x.copy_(x0)
+            for b in range(nblk):
+                w = blocks[b]
+                psi.psi_attn_paged_ext(arena, x, M, None, 0, heads, dh, w.Wq, w.Wk, w.Wv, w.Wo, nrs[b], acc, xt,
+                                       psi.PSI_OP_RESIDUAL)
+                psi.psi_ffn_paged(arena, xt, M, d, w.U, w.V, 1, acc, x, psi.PSI_OP_RESIDUAL)
+
+        flops_block = 4 * 2.0 * M * d * d + 4.0 * M * M * dh * heads + 2 * 2.0 * M * d * hid
+        h2d_block = (4 * d * d + 2 * d * hid) * 2 + (4 * d + hid + d) * 2 + 2 * d * 2
+        return dict(step=step, arena=arena, journal=None, flops=flops_block * nblk, h2d=h2d_block * nblk,
+                    live=live, keep=(blocks, gammas, nrs),
+                    config={"workload": "8 audio-shape blocks (Q/K RMS + RoPE attention, FFN)", "tokens": M,
+                            "d_model": d, "heads": heads, "head_dim": dh, "ffn_hidden": hid, "blocks": nblk,
+                            "arena_MiB": 80, "page_MiB": 8, "pages": 3, "head_group": 8, "ffn_tile": 1024,
+                            "resident_weights": args.resident})
     if args.workload == "attn4096":
         M, Mc, d, heads = 6144, 1024, 4096, 32
         c = synth.attn_case(args.seed, M, Mc, d, cross=True)
