@@ -399,7 +399,6 @@ bool dma_ok(const GemmArgs& a) {
 // and fills more CUs on small outputs.
 int gemm_auto_config(const GemmArgs& a) {
   if (!dma_ok(a)) return 3;
-  if (a.acc_in || a.acc_out) return 2;
   const long tiles1 = (long)((a.M + 255) / 256) * ((a.N + 127) / 128);
   return tiles1 >= 256 ? 1 : 2;
 }
