@@ -401,3 +401,39 @@ def test_attn_tiled_plan_and_lowlive_block_dry_run():
         assert s.scratch_high_water == max(need, 2 * M * th * 2 + M * to_f * 4)
     finally:
         psi.psi_arena_destroy(a)
+
+
+def test_new_entry_points_empty_inputs_and_layout_errors_dry_run():
+    """Zero tokens enqueue nothing; a low-live block needs Wo and V split by
+    rows (output tiles), and the extended attention rejects a gain block that
+    does not fit the bias slot together with the biases."""
+    d, h, gw = 512, 2048, 128
+    q, k, v = [fake_matrix(d, d, psi.PSI_SPLIT_ROWS, gw) for _ in range(3)]
+    wo_rows = fake_matrix(d, d, psi.PSI_SPLIT_ROWS, 128)
+    wo_cols = fake_matrix(d, d, psi.PSI_SPLIT_COLS, gw)
+    U = fake_matrix(h, d, psi.PSI_SPLIT_ROWS, 256)
+    V_rows = fake_matrix(d, h, psi.PSI_SPLIT_ROWS, 128)
+    a = psi.psi_arena_create(desc(16, 1))
+    try:
+        fake, fj = 0x10000, 0x20000
+        nr = psi.qk_norm_rope(0x1000, 0x2000, 1e-6)
+        psi.psi_attn_paged_ext(a, fake, 0, None, 0, 4, 128, q, k, v, wo_cols, nr, None, fake, 0)
+        psi.psi_attn_tiled(a, fake, 0, None, 0, 4, 128, q, k, v, wo_rows, fj, 0, 0, fake, 0)
+        psi.psi_block_lowlive(a, fake, 0, 4, 128, psi.psi_block_weights(q, k, v, wo_rows, U, V_rows), fj, 0)
+        s = psi.psi_arena_stats(a)
+        assert s.kernel_launches == 0 and s.page_copies == 0
+        for bad in (psi.psi_block_weights(q, k, v, wo_cols, U, V_rows),
+                    psi.psi_block_weights(q, k, v, wo_rows, U, fake_matrix(d, h, psi.PSI_SPLIT_COLS, 256))):
+            with pytest.raises(psi.PsiError) as e:
+                psi.psi_block_lowlive(a, fake, 64, 4, 128, bad, fj, 0)
+            assert e.value.status == psi.PSI_E_INVALID
+        with pytest.raises(psi.PsiError) as e:  # the head-group outputs need a journal
+            psi.psi_attn_tiled(a, fake, 64, None, 0, 4, 128, q, k, v, wo_rows, None, 0, 0, fake, 0)
+        assert e.value.status == psi.PSI_E_INVALID
+    finally:
+        psi.psi_arena_destroy(a)
+    # biases (4 x 1 KiB) and two 1 KiB gains in a 4 KiB bias slot
+    small = psi.arena_desc(16 * MiB, 1 * MiB, 2, 0, 4096, None, psi.PSI_ARENA_DRY_RUN)
+    st, _ = psi.psi_attn_ext_plan(small, 64, 0, 4, 128, q, k, v, wo_cols, psi.qk_norm_rope(0x1000, 0x2000, 1e-6))
+    assert st == psi.PSI_E_PAGE_TOO_SMALL
+    assert psi.psi_attn_ext_plan(small, 64, 0, 4, 128, q, k, v, wo_cols, None)[0] == psi.PSI_OK
