@@ -156,3 +156,32 @@ def test_lowlive_stack_matches_paged_stack_bitwise(P, ring):
     finally:
         P.psi_journal_destroy(j)
         P.psi_arena_destroy(ar)
+
+
+def test_lowlive_block_ragged_medium_size_matches_paged(P):
+    """One low-live block at a size spanning many tiles with ragged token
+    count, output tiles and hidden tiles (777 tokens, d 1,024, 8 heads of
+    128, FFN 4,096 in 768-channel tiles; attention output tiles of 384, FFN
+    output tiles of 320) gives psi_block_paged's bits and is within the
+    tolerance of the oracle's block."""
+    M, d, heads, h, gw = 777, 1024, 8, 4096, 256
+    x0 = synth.stack_input(48, M, d)
+    w = synth.block_weights(48, 0, d, h)
+    ar = make_arena(32 * MiB, 4 * MiB, 3)
+    j = P.psi_journal_create(MiB, 2, M * (d + h) * 2 + MiB)
+    try:
+        xr = dev(x0)
+        xt = torch.empty_like(xr)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        P.psi_block_paged(ar, xr, xt, M, heads, 128, P.block_weights(w, gw, 768), 1, acc, None, 0)
+        xl = dev(x0)
+        P.psi_block_lowlive(ar, xl, M, heads, 128, P.block_weights(w, gw, 768, attn_out_tile=384,
+                                                                    ffn_out_tile=320), j, 0)
+        P.psi_arena_sync(ar)
+        P.psi_journal_sync(j)
+        got = host(xl)
+        assert np.array_equal(got, host(xr))
+        assert_bf16_close(got, oracle.block(x0, w, heads, 128))
+    finally:
+        P.psi_journal_destroy(j)
+        P.psi_arena_destroy(ar)
