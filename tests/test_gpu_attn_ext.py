@@ -180,3 +180,41 @@ def test_ext_resident_matches_paged_and_bf16_numerator(P):
     assert np.array_equal(run(P, x, w, 8, 64, 2, nr=nr, resident=True), paged)
     y16 = run(P, x, w, 8, 64, 2, nr=nr, flags=P.PSI_OP_BF16_SOFTMAX)
     assert_bf16_close(y16, ref(x, w, 8, 64, nr=dict(nr, norm_tile=128), bf16_p=True))
+
+
+def test_audio_blocks_full_shape_against_oracle(P):
+    """Two blocks of the audio workload in the configuration the benchmark
+    times (126 tokens, d 2,048, 32 heads of 64 with RMS-normalised and
+    rotated Q/K on 8-head pages, FFN 8,192 in 1,024-channel tiles, 80 MiB
+    arena with three 8 MiB pages), against the oracle's extended attention
+    sub-block and FFN on each block's GPU input."""
+    from tests.gpu_util import MiB
+    M, d, heads, dh, hid = 126, 2048, 32, 64, 8192
+    ar = make_arena(80 * MiB, 8 * MiB, 3)
+    cq, sq = synth.rope_tables(M, dh)
+    ct, st = dev_f32(cq), dev_f32(sq)
+    try:
+        x = dev(synth.stack_input(5, M, d))
+        xt = torch.empty_like(x)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        for b in range(2):
+            w = synth.block_weights(5, b, d, hid)
+            rng = np.random.default_rng([5, b, 1])
+            gq, gk = synth.norm_gamma(rng, d), synth.norm_gamma(rng, d)
+            bw = P.block_weights(w, 8 * dh, 1024)
+            g = [pinned_vec(gq), pinned_vec(gk)]
+            nr = P.qk_norm_rope(g[0], g[1], 1e-6, 0, ct, st)
+            x_in = host(x)
+            P.psi_attn_paged_ext(ar, x, M, None, 0, heads, dh, bw.Wq, bw.Wk, bw.Wv, bw.Wo, nr, acc, xt,
+                                 P.PSI_OP_RESIDUAL)
+            P.psi_arena_sync(ar)
+            y_attn = host(xt)
+            ref_attn = oracle.attn_sublayer_ext(x_in, w, heads, dh, gq=gq, gk=gk, eps=1e-6, norm_tile=8 * dh,
+                                                cos_q=cq, sin_q=sq)
+            assert_bf16_close(y_attn, ref_attn, what=f"block {b} attention")
+            P.psi_ffn_paged(ar, xt, M, d, bw.U, bw.V, 1, acc, x, P.PSI_OP_RESIDUAL)
+            P.psi_arena_sync(ar)
+            ref_ffn = oracle.ffn(y_attn, w["U"], w["a"], w["V"], w["b"], residual=True)
+            assert_bf16_close(host(x), ref_ffn, what=f"block {b} FFN")
+    finally:
+        P.psi_arena_destroy(ar)
