@@ -63,6 +63,10 @@ typedef int psi_status;
 #define PSI_ARENA_PROFILE_COPIES 0x8u /* with PSI_ARENA_PROFILE: time page copies too (two more
                                          events per copy on the copy streams); also on while a
                                          device timeline is being kept */
+#define PSI_ARENA_JITTER 0x10u /* transport control ([PSI] sec. II-D): delay every page or
+                                  bias copy and every kernel launch by a deterministic
+                                  pseudo-random 0-63 us (a one-wave wait kernel on the copy
+                                  or compute stream); results must not change */
 
 /* --------------------------------------------------------- operator flags */
 #define PSI_OP_BASELINE_BIAS 0x1u /* [PSI] sec. III-A baseline: round the product to BF16,

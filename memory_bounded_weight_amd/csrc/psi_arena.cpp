@@ -25,6 +25,17 @@ psi_status probe_commit(psi_arena* a, int32_t branch, int32_t role, const void* 
   return psi_journal_fence(a->probe, a->compute);
 }
 
+psi_status jitter(psi_arena* a, hipStream_t s) {
+  if (a->dry || !(a->desc.flags & PSI_ARENA_JITTER)) return PSI_OK;
+  uint32_t x = a->jitter_state;  // xorshift32
+  x ^= x << 13;
+  x ^= x >> 17;
+  x ^= x << 5;
+  a->jitter_state = x;
+  PSI_HIP(launch_delay(x % 64u, s));
+  return PSI_OK;
+}
+
 psi_status check_pinned(const void* p, const char* what) {
   if (!p) return PSI_OK;
   hipPointerAttribute_t attr;
@@ -110,6 +121,8 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
   if (!a->dry) {
     const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
     if (sync) {
+      psi_status st = jitter(a, a->compute);
+      if (st) return st;
       PSI_HIP(hipMemcpyAsync(slot.dev, host, bytes, hipMemcpyHostToDevice, a->compute));
       PSI_HIP(hipEventRecord(slot.ready, a->compute));
     } else {
@@ -124,6 +137,7 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
         psi_status st = wait_release(a, slot);
         if (st) return st;
       }
+      if (psi_status st = jitter(a, cs)) return st;
       hipEvent_t t0 = nullptr, t1 = nullptr;
       if ((a->desc.flags & PSI_ARENA_PROFILE) &&
           ((a->desc.flags & PSI_ARENA_PROFILE_COPIES) || a->trace_base)) {
@@ -168,6 +182,7 @@ psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_
     psi_status st = wait_release(a, slot);
     if (st) return st;
   }
+  if (psi_status st = jitter(a, cs)) return st;
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
     if (!parts[i].host || !parts[i].bytes) continue;
@@ -244,6 +259,7 @@ static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (
                                const void* args) {
   a->stats.kernel_launches++;
   if (a->dry) return PSI_OK;
+  if (psi_status st = jitter(a, a->compute)) return st;  // delays the consumer, not the copies
   hipEvent_t t0 = nullptr, t1 = nullptr;
   if (a->desc.flags & PSI_ARENA_PROFILE) {
     t0 = pool_event(a);

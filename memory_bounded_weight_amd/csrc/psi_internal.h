@@ -95,6 +95,10 @@ struct NormRopeArgs {
 };
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t s);
 
+// One-wave kernel that waits the given time (bounded spin on the real-time
+// counter); PSI_ARENA_JITTER transport control.
+hipError_t launch_delay(uint32_t microseconds, hipStream_t s);
+
 // ------------------------------------------------------------- planning
 struct MatrixInfo {
   int pages;
@@ -157,6 +161,7 @@ struct psi_arena {
   // double-buffered journal transport inside operators (commit-read and
   // reload-done events of two buffers)
   hipEvent_t pipe_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  uint32_t jitter_state = 0x9E3779B9u;  // PSI_ARENA_JITTER sequence
   int device = 0;
 };
 
@@ -190,6 +195,9 @@ psi_status run_attention(psi_arena* a, const AttnArgs& g);
 psi_status run_norm_rope(psi_arena* a, const NormRopeArgs& g);
 
 psi_status check_pinned(const void* p, const char* what);
+
+// PSI_ARENA_JITTER: enqueue a delay of 0-63 us (deterministic sequence) on s.
+psi_status jitter(psi_arena* a, hipStream_t s);
 
 // Stage probe: journal a device tensor of the current operator (no-op when
 // no probe journal is attached) and make the compute stream wait for the

@@ -48,6 +48,7 @@ PSI_ARENA_SYNC_COPY = 0x1
 PSI_ARENA_PROFILE = 0x2
 PSI_ARENA_DRY_RUN = 0x4
 PSI_ARENA_PROFILE_COPIES = 0x8
+PSI_ARENA_JITTER = 0x10
 
 PSI_OP_BASELINE_BIAS = 0x1
 PSI_OP_RESIDUAL = 0x2

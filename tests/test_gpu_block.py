@@ -17,9 +17,11 @@ import torch
 
 import oracle
 from memory_bounded_weight_amd import synth
-from tests.gpu_util import MiB, assert_bf16_close, dev, host, make_arena
+from tests.gpu_util import MiB, assert_bf16_close, dev, empty_bf16, host, make_arena
 
 pytestmark = pytest.mark.gpu
+
+KiB = 1024
 
 D, HEADS, HID, M = 256, 2, 512, 160
 
@@ -154,3 +156,55 @@ def test_capacity_settings_outcomes_and_bitwise(P, stack):
             P.psi_arena_destroy(ar)
     assert outcomes == {"fits": "ok", "roomy": "ok", "big pages": "ok",
                         "small scratch": "PSI_E_SCRATCH_EXHAUSTED", "small pages": "PSI_E_PAGE_TOO_SMALL"}, outcomes
+
+
+@pytest.mark.parametrize("n_pages", [2, 3])
+def test_transport_jitter_keeps_bits(P, n_pages):
+    """[PSI] sec. II-D transport control: with every page/bias copy and every
+    kernel launch delayed by a pseudo-random 0-63 us (PSI_ARENA_JITTER), a
+    block, the FFN reuse schedule and the extended attention give the same
+    bits as without; a missing copy or consumer wait would change them."""
+    from tests.gpu_util import make_arena as _mk
+    M, d, heads, h = 200, 256, 2, 1024
+    x0 = synth.stack_input(61, M, d)
+    w = synth.block_weights(61, 0, d, h)
+    c = synth.attn_ext_case(seed=62, M=M, d=d)
+    cq, sq = synth.rope_tables(M, 64)
+
+    def run(flags):
+        ar = _mk(8 * MiB, 256 * KiB, n_pages, flags=flags)
+        j = P.psi_journal_create(MiB, 2, 4 * MiB)
+        try:
+            x = dev(x0)
+            xt = torch.empty_like(x)
+            acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            P.psi_block_paged(ar, x, xt, M, heads, 128, P.block_weights(w, 128, 256), 2, acc, None, 0)
+            y2 = torch.empty_like(x)
+            Vo = P.pinned_matrix(w["V"], w["b"], P.PSI_SPLIT_ROWS, 128)
+            U = P.pinned_matrix(w["U"], w["a"], P.PSI_SPLIT_ROWS, 256)
+            P.psi_ffn_tiled(ar, x, M, d, U, Vo, P.PSI_FFN_REUSE, j, 0, 0, y2, P.PSI_OP_RESIDUAL)
+            ms = [P.pinned_matrix(c["w"]["W" + n], c["w"]["b" + n], P.PSI_SPLIT_ROWS, 128) for n in "qkv"]
+            ms.append(P.pinned_matrix(c["w"]["Wo"], c["w"]["bo"], P.PSI_SPLIT_COLS, 128))
+            g = [torch.from_numpy(c[k].view(np.int16)).pin_memory() for k in ("gq", "gk")]
+            ct = torch.from_numpy(cq).cuda()
+            st = torch.from_numpy(sq).cuda()
+            nr = P.qk_norm_rope(g[0], g[1], 1e-6, 0, ct, st)
+            y3 = empty_bf16(M, d)
+            P.psi_attn_paged_ext(ar, dev(c["x"]), M, None, 0, 4, 64, *ms, nr, None, y3, P.PSI_OP_RESIDUAL)
+            e1.record()
+            P.psi_arena_sync(ar)
+            P.psi_journal_sync(j)
+            return (host(x), host(y2), host(y3)), e0.elapsed_time(e1)
+        finally:
+            P.psi_journal_destroy(j)
+            P.psi_arena_destroy(ar)
+
+    ref, t_a = run(0)
+    got, t_j = run(P.PSI_ARENA_JITTER)
+    ref2, t_b = run(0)
+    for r, r2, g_ in zip(ref, ref2, got):
+        assert np.array_equal(r, g_) and np.array_equal(r2, g_)
+    # the delays are real: ~60 launches and copies at 31.5 us on average
+    assert t_j > min(t_a, t_b) + 0.5, (t_j, t_a, t_b)
