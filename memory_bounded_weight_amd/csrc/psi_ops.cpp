@@ -162,6 +162,58 @@ GemmArgs gemm_args() {
   return g;
 }
 
+const uint16_t* offset(const uint16_t* v, size_t off) { return v ? v + off : nullptr; }
+
+// Projection of one head group from a page of rows (Wq_g or Wk_g):
+// out[Ms, ext] (row stride ldo) = B(src page^T + bias).
+psi_status project(psi_arena* a, const uint16_t* src, int Ms, int dm, const uint16_t* page, int ext,
+                   const uint16_t* bias, uint16_t* out, long ldo, int bbase) {
+  GemmArgs G = gemm_args();
+  G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
+  G.M = Ms; G.N = ext; G.K = dm;
+  G.bias = bias; G.out = out; G.ldo = ldo; G.baseline_bias = bbase;
+  return run_gemm(a, G);
+}
+
+// V_g^T [ext, Ms] (row stride ldvt) = B(page src^T + bias), the bias along
+// rows: V written transposed, so that P.V reads keys contiguously.
+psi_status project_vt(psi_arena* a, const uint16_t* src, int Ms, int dm, const uint16_t* page, int ext,
+                      const uint16_t* bias, uint16_t* vt, long ldvt, int bbase) {
+  GemmArgs G = gemm_args();
+  G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
+  G.M = ext; G.N = Ms; G.K = dm;
+  G.bias = bias; G.bias_on_m = 1; G.out = vt; G.ldo = ldvt; G.baseline_bias = bbase;
+  return run_gemm(a, G);
+}
+
+// Online-softmax attention of the heads of one group; O overwrites Q.
+psi_status attend(psi_arena* a, uint16_t* q, long ldq, const uint16_t* k, long ldk, const uint16_t* vt,
+                  long ldvt, int Mq, int Mk, int heads, int dh, unsigned flags) {
+  AttnArgs A{};
+  A.q = q; A.ldq = ldq;
+  A.k = k; A.ldk = ldk;
+  A.vt = vt; A.ldvt = ldvt;
+  A.Mq = Mq; A.Mk = Mk; A.heads = heads; A.dh = dh;
+  A.alpha = (float)(1.0 / std::sqrt((double)dh));
+  A.p_terms = attn_p_terms(flags);
+  return run_attention(a, A);
+}
+
+// Device pointers and pinned page images of an attention operator.
+psi_status check_attn_args(psi_arena* a, const uint16_t* x, const uint16_t* y, const uint16_t* ctx,
+                           const float* acc, const psi_matrix* Wq, const psi_matrix* Wk,
+                           const psi_matrix* Wv, const psi_matrix* Wo) {
+  if (a->dry) return PSI_OK;
+  psi_status st;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true)) ||
+      (st = check_ptr(acc, "acc", true)))
+    return st;
+  if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
+      (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
+    return st;
+  return PSI_OK;
+}
+
 }  // namespace
 }  // namespace psi
 
@@ -500,14 +552,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   psi_status st = psi_attn_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_dev != nullptr, &need);
   if (st) return st;
   if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
-  if (!a->dry) {
-    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true)) ||
-        (st = check_ptr(acc_dev, "acc", true)))
-      return st;
-    if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
-        (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
-      return st;
-  }
+  if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
   if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
   const int gw = Wq->block;
@@ -542,7 +587,6 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     reqs.push_back(rv[g]);
     reqs.push_back(ro[g]);
   }
-  const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[4];
@@ -554,48 +598,21 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     if (g == 0)
       for (int i = 0; i < 4; ++i)
         if ((st = bias.get(i, &bq[i]))) return st;
-    // Q_g = x Wq_g^T + bq_g
-    if ((st = feeder.take(4 * g, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = M; G.N = ext; G.K = dm;
-      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q; G.ldo = gw; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(4 * g))) return st;
-    // K_g = src Wk_g^T + bk_g
-    if ((st = feeder.take(4 * g + 1, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = Ms; G.N = ext; G.K = dm;
-      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb; G.ldo = gw; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(4 * g + 1))) return st;
-    // V_g^T = Wv_g src^T + bv_g (bias along rows): written transposed
-    if ((st = feeder.take(4 * g + 2, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
-      G.M = ext; G.N = Ms; G.K = dm;
-      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
-      G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(4 * g + 2))) return st;
+    // Q_g = x Wq_g^T + bq_g, K_g = src Wk_g^T + bk_g, V_g^T = Wv_g src^T + bv_g
+    if ((st = feeder.take(4 * g, &page)) ||
+        (st = project(a, x, M, dm, page, ext, offset(bq[0], c0), Q, gw, bbase)) ||
+        (st = feeder.give_back(4 * g)))
+      return st;
+    if ((st = feeder.take(4 * g + 1, &page)) ||
+        (st = project(a, src, Ms, dm, page, ext, offset(bq[1], c0), Kb, gw, bbase)) ||
+        (st = feeder.give_back(4 * g + 1)))
+      return st;
+    if ((st = feeder.take(4 * g + 2, &page)) ||
+        (st = project_vt(a, src, Ms, dm, page, ext, offset(bq[2], c0), Vt, ldvt, bbase)) ||
+        (st = feeder.give_back(4 * g + 2)))
+      return st;
     // O_g over Q_g (online softmax, fp32 state)
-    {
-      AttnArgs A{};
-      A.q = Q; A.ldq = gw;
-      A.k = Kb; A.ldk = gw;
-      A.vt = Vt; A.ldvt = ldvt;
-      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
-      A.alpha = alpha;
-      A.p_terms = attn_p_terms(flags);
-      if ((st = run_attention(a, A))) return st;
-    }
+    if ((st = attend(a, Q, gw, Kb, gw, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, (size_t)M * gw * 2))) return st;
     // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
     if ((st = feeder.take(4 * g + 3, &page))) return st;
@@ -632,13 +649,8 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
                                     acc_dev != nullptr, nullptr);
   if (st) return st;
   if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
   if (!a->dry) {
-    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true)) ||
-        (st = check_ptr(acc_dev, "acc", true)))
-      return st;
-    if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
-        (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
-      return st;
     for (const uint16_t* g : {nr->gamma_q, nr->gamma_k}) {
       if (!g) continue;
       if ((st = Wq->resident ? check_ptr(g, "gamma") : check_pinned(g, "gamma"))) return st;
@@ -683,7 +695,6 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
     reqs.push_back(rv[g]);
     reqs.push_back(ro[g]);
   }
-  const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[6];
@@ -694,24 +705,14 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
   for (int g = 0; g < nG; ++g) {
     const int ext = matrix_page_extent(Wq, g);
     const size_t c0 = (size_t)g * gw;
-    if ((st = feeder.take(2 * g, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = M; G.N = ext; G.K = dm;
-      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q + c0; G.ldo = dm; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(2 * g))) return st;
-    if ((st = feeder.take(2 * g + 1, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = Ms; G.N = ext; G.K = dm;
-      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb + c0; G.ldo = dm; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(2 * g + 1))) return st;
+    if ((st = feeder.take(2 * g, &page)) ||
+        (st = project(a, x, M, dm, page, ext, offset(bq[0], c0), Q + c0, dm, bbase)) ||
+        (st = feeder.give_back(2 * g)))
+      return st;
+    if ((st = feeder.take(2 * g + 1, &page)) ||
+        (st = project(a, src, Ms, dm, page, ext, offset(bq[1], c0), Kb + c0, dm, bbase)) ||
+        (st = feeder.give_back(2 * g + 1)))
+      return st;
   }
   // full-row RMS and split RoPE, in place
   {
@@ -730,28 +731,12 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
     const int ext = matrix_page_extent(Wq, g);
     const bool last = g == nG - 1;
     const size_t c0 = (size_t)g * gw;
-    // V_g^T = Wv_g src^T + bv_g (bias along rows)
-    if ((st = feeder.take(base + 2 * g, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
-      G.M = ext; G.N = Ms; G.K = dm;
-      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
-      G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(base + 2 * g))) return st;
-    // O_g over Q[:, g] in place
-    {
-      AttnArgs A{};
-      A.q = Q + c0; A.ldq = dm;
-      A.k = Kb + c0; A.ldk = dm;
-      A.vt = Vt; A.ldvt = ldvt;
-      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
-      A.alpha = alpha;
-      A.p_terms = attn_p_terms(flags);
-      if ((st = run_attention(a, A))) return st;
-    }
+    // V_g^T = Wv_g src^T + bv_g, then O_g over Q[:, g] in place
+    if ((st = feeder.take(base + 2 * g, &page)) ||
+        (st = project_vt(a, src, Ms, dm, page, ext, offset(bq[2], c0), Vt, ldvt, bbase)) ||
+        (st = feeder.give_back(base + 2 * g)))
+      return st;
+    if ((st = attend(a, Q + c0, dm, Kb + c0, dm, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
     // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
     if ((st = feeder.take(base + 2 * g + 1, &page))) return st;
     {
@@ -785,12 +770,7 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
   if (st) return st;
   if (!j) return fail(PSI_E_INVALID, "attention tiled: needs a journal for the head-group outputs");
   if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "attention tiled: no full accumulator to store");
-  if (!a->dry) {
-    if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(ctx, "ctx", true))) return st;
-    if ((st = check_matrix_pinned(a, Wq, "Wq")) || (st = check_matrix_pinned(a, Wk, "Wk")) ||
-        (st = check_matrix_pinned(a, Wv, "Wv")) || (st = check_matrix_pinned(a, Wo, "Wo")))
-      return st;
-  }
+  if ((st = check_attn_args(a, x, y, ctx, nullptr, Wq, Wk, Wv, Wo))) return st;
   if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
   const int gw = Wq->block, to = Wo->block;
@@ -824,7 +804,6 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
     reqs.push_back(rv[g]);
   }
   reqs.insert(reqs.end(), ro.begin(), ro.end());
-  const float alpha = (float)(1.0 / std::sqrt((double)head_dim));
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[4];
@@ -841,44 +820,19 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
     const size_t c0 = (size_t)g * gw;
     uint16_t* Q = Ob[g % 2];
     if (!a->dry && g >= 2) PSI_HIP(hipStreamWaitEvent(a->compute, rd[g % 2], 0));
-    if ((st = feeder.take(3 * g, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = x; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = M; G.N = ext; G.K = dm;
-      G.bias = bq[0] ? bq[0] + c0 : nullptr; G.out = Q; G.ldo = ext; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(3 * g))) return st;
-    if ((st = feeder.take(3 * g + 1, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = src; G.lda = dm; G.B = page; G.ldb = dm;
-      G.M = Ms; G.N = ext; G.K = dm;
-      G.bias = bq[1] ? bq[1] + c0 : nullptr; G.out = Kb; G.ldo = ext; G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(3 * g + 1))) return st;
-    if ((st = feeder.take(3 * g + 2, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = page; G.lda = dm; G.B = src; G.ldb = dm;
-      G.M = ext; G.N = Ms; G.K = dm;
-      G.bias = bq[2] ? bq[2] + c0 : nullptr; G.bias_on_m = 1; G.out = Vt; G.ldo = ldvt;
-      G.baseline_bias = bbase;
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(3 * g + 2))) return st;
-    {
-      AttnArgs A{};
-      A.q = Q; A.ldq = ext;
-      A.k = Kb; A.ldk = ext;
-      A.vt = Vt; A.ldvt = ldvt;
-      A.Mq = M; A.Mk = Ms; A.heads = ext / head_dim; A.dh = head_dim;
-      A.alpha = alpha;
-      A.p_terms = attn_p_terms(flags);
-      if ((st = run_attention(a, A))) return st;
-    }
+    if ((st = feeder.take(3 * g, &page)) ||
+        (st = project(a, x, M, dm, page, ext, offset(bq[0], c0), Q, ext, bbase)) ||
+        (st = feeder.give_back(3 * g)))
+      return st;
+    if ((st = feeder.take(3 * g + 1, &page)) ||
+        (st = project(a, src, Ms, dm, page, ext, offset(bq[1], c0), Kb, ext, bbase)) ||
+        (st = feeder.give_back(3 * g + 1)))
+      return st;
+    if ((st = feeder.take(3 * g + 2, &page)) ||
+        (st = project_vt(a, src, Ms, dm, page, ext, offset(bq[2], c0), Vt, ldvt, bbase)) ||
+        (st = feeder.give_back(3 * g + 2)))
+      return st;
+    if ((st = attend(a, Q, ext, Kb, ext, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, obytes(g)))) return st;
     if (!a->dry && (st = journal_commit_ev(j, okey(g), Q, obytes(g), a->compute, rd[g % 2]))) return st;
   }
