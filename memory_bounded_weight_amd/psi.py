@@ -125,9 +125,12 @@ class psi_qk_norm_rope(ctypes.Structure):
 
 def qk_norm_rope(gamma_q=None, gamma_k=None, eps=1e-6, norm_tile=0, cos_q=None, sin_q=None,
                  cos_k=None, sin_k=None) -> psi_qk_norm_rope:
-    """psi_qk_norm_rope from tensors/arrays/ints (None -> NULL)."""
-    return psi_qk_norm_rope(_ptr(gamma_q), _ptr(gamma_k), eps, norm_tile, _ptr(cos_q), _ptr(sin_q),
-                            _ptr(cos_k), _ptr(sin_k))
+    """psi_qk_norm_rope from tensors/arrays/ints (None -> NULL); the
+    structure keeps the buffers it points into alive."""
+    r = psi_qk_norm_rope(_ptr(gamma_q), _ptr(gamma_k), eps, norm_tile, _ptr(cos_q), _ptr(sin_q),
+                         _ptr(cos_k), _ptr(sin_k))
+    r._keepalive = (gamma_q, gamma_k, cos_q, sin_q, cos_k, sin_k)
+    return r
 
 
 class psi_key(ctypes.Structure):
@@ -321,12 +324,34 @@ def psi_arena_create(desc: psi_arena_desc) -> int:
     return h.value
 
 
+# Host weight objects (page images, biases, norm parameters) that an
+# arena's enqueued operators copy from: the operators return before their
+# copies run, and the C ABI requires the host memory to stay valid until
+# the compute stream has passed the operator.  The binding keeps the
+# Python owners alive until the next psi_arena_sync / psi_arena_destroy,
+# so a temporary argument is not freed (and its pinned block handed to
+# the next allocation) while a DMA still reads it.
+_held: dict = {}
+
+
+def _hold(arena, *objs):
+    h = _held.setdefault(arena, {})
+    for o in objs:
+        if o is not None:
+            h[id(o)] = o
+
+
 def psi_arena_destroy(arena: int):
-    return _check(_lib.psi_arena_destroy(arena), "psi_arena_destroy")
+    try:
+        return _check(_lib.psi_arena_destroy(arena), "psi_arena_destroy")
+    finally:
+        _held.pop(arena, None)
 
 
 def psi_arena_sync(arena: int):
-    return _check(_lib.psi_arena_sync(arena), "psi_arena_sync")
+    st = _check(_lib.psi_arena_sync(arena), "psi_arena_sync")
+    _held.pop(arena, None)
+    return st
 
 
 def psi_arena_stats(arena: int) -> psi_stats:
@@ -381,11 +406,13 @@ def psi_page_release(arena: int, page: int):
 # ---------------------------------------------------------------- operators
 
 def psi_linear_paged(arena, x, M, K, W: psi_matrix, acc, y, flags=0):
+    _hold(arena, W)
     return _check(_lib.psi_linear_paged(arena, _ptr(x), M, K, ctypes.byref(W), _ptr(acc), _ptr(y),
                                         flags), "psi_linear_paged")
 
 
 def psi_ffn_paged(arena, x, M, d, U: psi_matrix, V: psi_matrix, token_chunks, acc, y, flags=0):
+    _hold(arena, U, V)
     return _check(_lib.psi_ffn_paged(arena, _ptr(x), M, d, ctypes.byref(U), ctypes.byref(V),
                                      token_chunks, _ptr(acc), _ptr(y), flags), "psi_ffn_paged")
 
@@ -398,17 +425,20 @@ def psi_ffn_tiled_plan(desc, M, d, U: psi_matrix, Vo: psi_matrix, schedule):
 
 
 def psi_ffn_tiled(arena, x, M, d, U: psi_matrix, Vo: psi_matrix, schedule, journal, step, block, y, flags=0):
+    _hold(arena, U, Vo)
     return _check(_lib.psi_ffn_tiled(arena, _ptr(x), M, d, ctypes.byref(U), ctypes.byref(Vo), schedule,
                                      journal, step, block, _ptr(y), flags), "psi_ffn_tiled")
 
 
 def psi_attn_paged(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc, y, flags=0):
+    _hold(arena, Wq, Wk, Wv, Wo)
     return _check(_lib.psi_attn_paged(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
                                       ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
                                       ctypes.byref(Wo), _ptr(acc), _ptr(y), flags), "psi_attn_paged")
 
 
 def psi_attn_paged_ext(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr, acc, y, flags=0):
+    _hold(arena, Wq, Wk, Wv, Wo, nr)
     return _check(_lib.psi_attn_paged_ext(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
                                           ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
                                           ctypes.byref(Wo), ctypes.byref(nr) if nr is not None else None,
@@ -423,6 +453,7 @@ def psi_attn_tiled_plan(desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo):
 
 
 def psi_attn_tiled(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, journal, step, block, y, flags=0):
+    _hold(arena, Wq, Wk, Wv, Wo)
     return _check(_lib.psi_attn_tiled(arena, _ptr(x), M, _ptr(ctx), Mc, heads, head_dim,
                                       ctypes.byref(Wq), ctypes.byref(Wk), ctypes.byref(Wv),
                                       ctypes.byref(Wo), journal, step, block, _ptr(y), flags),
@@ -430,6 +461,7 @@ def psi_attn_tiled(arena, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, journa
 
 
 def psi_block_lowlive(arena, x, M, heads, head_dim, w: psi_block_weights, journal, flags=0):
+    _hold(arena, w)
     return _check(_lib.psi_block_lowlive(arena, _ptr(x), M, heads, head_dim, ctypes.byref(w), journal,
                                          flags), "psi_block_lowlive")
 
@@ -440,6 +472,7 @@ def psi_journal_reset(j):
 
 def psi_block_paged(arena, x, x_tmp, M, heads, head_dim, w: psi_block_weights, token_chunks,
                     acc, journal=None, flags=0):
+    _hold(arena, w)
     return _check(_lib.psi_block_paged(arena, _ptr(x), _ptr(x_tmp), M, heads, head_dim,
                                        ctypes.byref(w), token_chunks, _ptr(acc), journal or None,
                                        flags), "psi_block_paged")
