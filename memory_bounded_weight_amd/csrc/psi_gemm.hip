@@ -60,11 +60,32 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // Epilogue of one wave's TM x TN block of 32x32 accumulator tiles.  C layout
 // of the 32x32 MFMA: lane holds column l32 and rows
 // 8*(r/4) + 4*half + (r%4), r = 0..15.
+//
+// The residual (and a bias along rows) of each 32-row group is loaded
+// before the group's first store.  The output may alias the residual, so
+// the compiler cannot move a load above an earlier store: loaded element by
+// element, each of the 16 TN values of a group would wait a full memory
+// round trip.  Every element is still read by the lane that writes it,
+// before its write.
 template <int TM, int TN>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
                                          int l32) {
+  const bool resid = p.out && p.resid;
+  const bool row_bias = p.out && p.bias && p.bias_on_m;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    float rv[TN][16];
+    float bm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int gm = min(mb + i * 32 + 8 * (r / 4) + 4 * half + (r % 4), p.M - 1);
+      bm[r] = row_bias ? bf2f(p.bias[gm]) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int gn = min(nb + j * 32 + l32, p.N - 1);
+        rv[j][r] = resid ? bf2f(p.resid[(long)gm * p.ldr + gn]) : 0.0f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int gn = nb + j * 32 + l32;
@@ -79,18 +100,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN
         if (p.out) {
           float t;
           if (p.bias) {
-            const float bv = p.bias_on_m ? bf2f(p.bias[gm]) : bn;
+            const float bv = p.bias_on_m ? bm[r] : bn;
             t = p.baseline_bias ? bf2f(f2bf(v)) + bv : v + bv;
           } else {
             t = v;
           }
           uint16_t y = f2bf(t);
           if (p.epi == EPI_GELU) y = f2bf(gelu_tanh(bf2f(y)));
-          if (p.resid) y = f2bf(bf2f(p.resid[(long)gm * p.ldr + gn]) + bf2f(y));
+          if (resid) y = f2bf(rv[j][r] + bf2f(y));
           p.out[(long)gm * p.ldo + gn] = y;
         }
       }
     }
+  }
 }
 
 // Accumulators start from acc_in (carried K-split chain) or zero.
