@@ -69,16 +69,23 @@ def build_workload(args, torch, psi, synth):
     live = []
     if args.workload == "stack8":
         M, d, heads, hid, nblk = 8192, 4096, 32, 16384, 8
-        # 80 MiB = pages x 8 MiB + workspace + scratch: two pages leave the
-        # paper's 8 MiB workspace; three pages take its place (no kernel here
-        # uses a workspace), scratch keeps its 56 MiB
+        # 80 MiB = pages x 8 MiB + workspace + scratch.  O-projection over
+        # output tiles (default): the head-group outputs live in the fp32
+        # accumulator's memory, attention scratch is K and V^T of one group
+        # (32 MiB), and five pages fit.  K-split O-projection: Q, K, V^T
+        # (48 MiB); two pages leave the paper's 8 MiB workspace, three take
+        # its place (no kernel here uses a workspace), scratch keeps 56 MiB.
+        otiles = args.o_proj == "tiles"
+        if args.pages is None:
+            args.pages = 5 if otiles else 3
         ws = 8 * MiB if args.pages == 2 else max(0, 80 * MiB - 56 * MiB - args.pages * 8 * MiB)
         arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, ws, 0, stream, flags))
         t0 = time.time()
         blocks = []
         for b in range(nblk):
             w = synth.block_weights(args.seed, b, d, hid)
-            blocks.append(psi.block_weights(w, 1024, 1024, resident=args.resident))
+            blocks.append(psi.block_weights(w, 1024, 1024, resident=args.resident,
+                                            attn_out_tile=1024 if otiles else 0))
             del w
         log(f"bench: generated and pinned {nblk} blocks in {time.time() - t0:.1f}s")
         x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
@@ -113,7 +120,7 @@ def build_workload(args, torch, psi, synth):
                             "tokens": M, "d_model": d, "heads": heads, "head_dim": 128,
                             "ffn_hidden": hid, "blocks": nblk, "arena_MiB": 80, "page_MiB": 8,
                             "pages": args.pages, "workspace_MiB": ws // MiB, "head_group": 8,
-                            "ffn_tile": 1024,
+                            "ffn_tile": 1024, "o_projection": "output tiles" if otiles else "K-split",
                             "journal": not args.no_journal, "resident_weights": args.resident})
     if args.workload in ("ffn2048", "ffn4096"):
         if args.workload == "ffn2048":
@@ -486,8 +493,12 @@ def main():
     ap.add_argument("--no-journal", action="store_true")
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pages", type=int, default=3,
-                    help="page slots in the 80 MiB arena: 2 (+8 MiB workspace) or 3 (no workspace)")
+    ap.add_argument("--pages", type=int, default=None,
+                    help="page slots in the 80 MiB stack arena (default 5 with output-tile "
+                         "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
+    ap.add_argument("--o-proj", choices=("tiles", "ksplit"), default="tiles",
+                    help="stack: attention O-projection over output tiles of Wo rows from every head "
+                         "group's output (default), or K-split over head groups with the fp32 accumulator")
     ap.add_argument("--trace", metavar="FILE",
                     help="keep the device timeline of the timed steps (page copies timed too) and write it "
                          "to FILE as JSON (kind 0 GEMM, 1 attention, 2/3 page copy stream 0/1)")
@@ -533,6 +544,10 @@ def main():
         step()
     sync_all()
     psi.psi_arena_reset_stats(arena)
+    # per-launch HIP events (two around every kernel) cost the compute stream
+    # a few microseconds each: inside the timed region only the last step's
+    # launches are timed, unless the whole timeline is kept
+    sample_all = bool(args.trace or args.profile_copies)
     if args.trace and not args.no_profile:
         psi.psi_arena_trace_start(arena, 1 << 18)  # times page copies too from here on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -540,6 +555,8 @@ def main():
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
+        if not args.no_profile:
+            psi.psi_arena_set_timing(arena, sample_all or i == args.steps - 1)
         step()
     ev1.record()
     sync_all()
@@ -581,7 +598,8 @@ def main():
                         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": traffic,
                         "launches": n, "avg_launch_us": round(ms * 1e3 / n, 2),
-                        "flops_per_launch": fl / n}
+                        "flops_per_launch": fl / n,
+                        "timed_steps": "all" if sample_all else f"the last of {args.steps}"}
         other = [k for k in kinds if k[0] != name and k[2]]
         if other:
             o = other[0]

@@ -215,6 +215,14 @@ psi_status psi_arena_stats(psi_arena* a, psi_stats* out);
 /* Zeroes the counters and the scratch high-water mark. */
 psi_status psi_arena_reset_stats(psi_arena* a);
 
+/* Per-launch timing of a profiled arena (PSI_ARENA_PROFILE) on (on != 0,
+ * the initial state) or off for the launches and traced page copies
+ * enqueued from now on; timings already enqueued are kept.  The two events
+ * around each launch cost the compute stream a few microseconds, so a
+ * caller can time a sample of its launches (e.g. one invocation of many).
+ * Errors: PSI_E_INVALID for a null arena or one without PSI_ARENA_PROFILE. */
+psi_status psi_arena_set_timing(psi_arena* a, int on);
+
 /* Device timeline of a profiled arena (PSI_ARENA_PROFILE), for overlap
  * analysis of the page lifecycle of [PSI] sec. II-D: every timed GEMM and
  * attention launch and every timed half-page copy, with its start relative

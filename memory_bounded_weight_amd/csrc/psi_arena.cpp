@@ -95,6 +95,15 @@ static psi_status wait_release(psi_arena* a, psi_page_slot& slot) {
   return PSI_OK;
 }
 
+bool slot_released(psi_arena* a, int s) {
+  const psi_page_slot& slot = a->slots[s];
+  if (a->dry || !slot.released_once || (a->desc.flags & PSI_ARENA_SYNC_COPY)) return true;
+  const hipError_t q = hipEventQuery(slot.release);
+  if (q == hipSuccess) return true;
+  if (q != hipErrorNotReady) (void)hipGetLastError();  // reported by the blocking wait later
+  return false;
+}
+
 int first_free_slot(const psi_arena* a) {
   for (int i = 0; i < a->desc.n_pages; ++i) {
     const int c = (a->next_slot + i) % a->desc.n_pages;
@@ -139,7 +148,7 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
       }
       if (psi_status st = jitter(a, cs)) return st;
       hipEvent_t t0 = nullptr, t1 = nullptr;
-      if ((a->desc.flags & PSI_ARENA_PROFILE) &&
+      if ((a->desc.flags & PSI_ARENA_PROFILE) && !a->timing_off &&
           ((a->desc.flags & PSI_ARENA_PROFILE_COPIES) || a->trace_base)) {
         t0 = pool_event(a);
         t1 = pool_event(a);
@@ -261,7 +270,7 @@ static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (
   if (a->dry) return PSI_OK;
   if (psi_status st = jitter(a, a->compute)) return st;  // delays the consumer, not the copies
   hipEvent_t t0 = nullptr, t1 = nullptr;
-  if (a->desc.flags & PSI_ARENA_PROFILE) {
+  if ((a->desc.flags & PSI_ARENA_PROFILE) && !a->timing_off) {
     t0 = pool_event(a);
     t1 = pool_event(a);
     if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
@@ -484,6 +493,13 @@ psi_status psi_arena_trace_read(psi_arena* a, psi_trace_event* out, size_t capac
   const size_t n = a->trace.size() < capacity ? a->trace.size() : capacity;
   for (size_t i = 0; i < n; ++i) out[i] = a->trace[i];
   if (count) *count = a->trace.size();
+  return PSI_OK;
+}
+
+psi_status psi_arena_set_timing(psi_arena* a, int on) {
+  if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (!(a->desc.flags & PSI_ARENA_PROFILE)) return fail(PSI_E_INVALID, "timing needs PSI_ARENA_PROFILE");
+  a->timing_off = !on;
   return PSI_OK;
 }
 

@@ -252,15 +252,19 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
   if ((st = check_matrix(Wq, "Wq", PSI_SPLIT_ROWS))) return st;
   if ((st = check_matrix(Wk, "Wk", PSI_SPLIT_ROWS))) return st;
   if ((st = check_matrix(Wv, "Wv", PSI_SPLIT_ROWS))) return st;
-  if ((st = check_matrix(Wo, "Wo", PSI_SPLIT_COLS))) return st;
+  // Wo split by columns: K-split over the head groups with the fp32 ACC
+  // carried; split by rows: output tiles over the full K from every
+  // group's O (the same summation per output)
+  if ((st = check_matrix(Wo, "Wo", -1))) return st;
+  const bool otiles = Wo->split == PSI_SPLIT_ROWS;
   const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
   for (const psi_matrix* m : ms)
     if (m->rows != dm || m->cols != dm)
       return fail(PSI_E_INVALID, "attention: projections must be [heads*head_dim, heads*head_dim]");
   const int gw = Wq->block;
-  if (gw % head_dim != 0 || Wk->block != gw || Wv->block != gw || Wo->block != gw)
-    return fail(PSI_E_INVALID, "attention: all four matrices need the same head-group block "
-                               "(a multiple of head_dim)");
+  if (gw % head_dim != 0 || Wk->block != gw || Wv->block != gw || (!otiles && Wo->block != gw))
+    return fail(PSI_E_INVALID, "attention: Wq, Wk, Wv (and a column-split Wo) need the same head-group "
+                               "block (a multiple of head_dim)");
   const char* names[4] = {"Wq", "Wk", "Wv", "Wo"};
   for (int i = 0; i < 4; ++i)
     if ((st = page_fit(d, ms[i], names[i]))) return st;
@@ -268,9 +272,13 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
   const int Ms = Mc > 0 ? Mc : M;
   if (Ms < 1 && M > 0) return fail(PSI_E_INVALID, "attention: at least one key per row is required");
   size_t ldvt = align_up((size_t)Ms, 64);
-  size_t need = align_up((size_t)M * gw * 2, kAlign) + align_up((size_t)Ms * gw * 2, kAlign) +
-                align_up((size_t)gw * ldvt * 2, kAlign);
-  if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
+  size_t need = align_up((size_t)Ms * gw * 2, kAlign) + align_up((size_t)gw * ldvt * 2, kAlign);
+  if (otiles) {
+    if (!acc_external) need += align_up((size_t)M * dm * 2, kAlign);  // O of every group (else in acc_dev)
+  } else {
+    need += align_up((size_t)M * gw * 2, kAlign);
+    if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
+  }
   if ((st = scratch_fit(L, need, "attention Q/K/V head-group tiles"))) return st;
   if (scratch_needed) *scratch_needed = need;
   return PSI_OK;
@@ -353,7 +361,7 @@ psi_status psi_attn_ext_plan(const psi_arena_desc* d, int M, int Mc, int heads, 
   const size_t ldvt = align_up((size_t)Ms, 64);
   size_t need = align_up((size_t)M * dm * 2, kAlign) + align_up((size_t)Ms * dm * 2, kAlign) +
                 align_up((size_t)Wq->block * ldvt * 2, kAlign);
-  if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);
+  if (!acc_external && Wo->split == PSI_SPLIT_COLS) need += align_up((size_t)M * dm * 4, kAlign);
   if ((st = scratch_fit(L, need, "attention Q/K (all head groups) and V^T tiles"))) return st;
   if (scratch_needed) *scratch_needed = need;
   return PSI_OK;

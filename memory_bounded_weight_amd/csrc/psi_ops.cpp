@@ -70,32 +70,41 @@ class OpBiases {
   const uint16_t* ptr_[kMax] = {};
 };
 
-// Streams a list of page requests through the arena's slots: requests are
-// submitted as soon as their (round-robin) slot is free, so the copy of the
-// next pages overlaps the consumers of the current one; with two slots this
-// is the paper's two alternating pages ([PSI] sec. III-B weight prefetch).
+// Streams a list of page requests through the arena's slots: the copy of
+// the next pages overlaps the consumers of the current one; with two slots
+// this is the paper's two alternating pages ([PSI] sec. III-B weight
+// prefetch).  A request is submitted as soon as a slot is free on the host
+// AND the slot's last consumer has finished on the GPU (checked without
+// blocking), so that the host keeps enqueueing compute while the copies
+// wait for their slots.  Only take() blocks, when the request it needs has
+// not been submitted yet: the host then waits for that slot's release while
+// the compute stream still holds the kernels enqueued before it.
 class PageFeeder {
  public:
   PageFeeder(psi_arena* a, std::vector<PageReq> reqs) : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {}
 
-  psi_status feed() {
+  // Submits requests in order while their slot is ready; requests up to
+  // index `need` are submitted whatever it takes (waiting on the host).
+  psi_status feed(long need = -1) {
     while (submitted_ < reqs_.size()) {
       const PageReq& r = reqs_[submitted_];
       if (r.resident) {  // consumed in place: no copy, no slot
         ++submitted_;
         continue;
       }
-      if (first_free_slot(a_) < 0) break;
-      int s = -1;
-      psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false);
+      const int s = first_free_slot(a_);
+      if (s < 0) break;
+      if ((long)submitted_ > need && !slot_released(a_, s)) break;
+      int got = -1;
+      psi_status st = page_submit_ex(a_, r.host, r.bytes, &got, false);
       if (st) return st;
-      slot_[submitted_++] = s;
+      slot_[submitted_++] = got;
     }
     return PSI_OK;
   }
   // Waits (on the compute stream) for request i and returns its page.
   psi_status take(size_t i, const uint16_t** page) {
-    psi_status st = feed();
+    psi_status st = feed((long)i);
     if (st) return st;
     const PageReq& r = reqs_[i];
     if (r.resident) {
@@ -197,6 +206,39 @@ psi_status attend(psi_arena* a, uint16_t* q, long ldq, const uint16_t* k, long l
   A.alpha = (float)(1.0 / std::sqrt((double)dh));
   A.p_terms = attn_p_terms(flags);
   return run_attention(a, A);
+}
+
+// K-split O-projection step: ACC (+)= O_g Wo[:, g]^T over the group's K
+// extent; after the last group y = B(ACC + bo) (+ x).
+psi_status oproj_ksplit(psi_arena* a, const uint16_t* og, long ldog, int M, int dm, const uint16_t* page,
+                        int ext, bool first, bool last, float* acc, const uint16_t* bo, uint16_t* y,
+                        const uint16_t* x, unsigned flags, int bbase) {
+  GemmArgs G = gemm_args();
+  G.A = og; G.lda = ldog; G.B = page; G.ldb = ext;
+  G.M = M; G.N = dm; G.K = ext;
+  G.baseline_bias = bbase;
+  if (!first) { G.acc_in = acc; G.ld_acc_in = dm; }
+  if (last) {
+    G.bias = bo; G.out = y; G.ldo = dm;
+    if (flags & PSI_OP_RESIDUAL) { G.resid = x; G.ldr = dm; }
+    if (flags & PSI_OP_STORE_ACC) { G.acc_out = acc; G.ld_acc_out = dm; }
+  } else {
+    G.epi = EPI_ACC; G.acc_out = acc; G.ld_acc_out = dm;
+  }
+  return run_gemm(a, G);
+}
+
+// O-projection output tile: y[:, c0 : c0+eo] = B(O Wo[c0 : c0+eo, :]^T + bo)
+// (+ x) over the full K, O holding every head group's output ([M, dm]).
+// Each output sums the same products in the same order as the K-split.
+psi_status oproj_tile(psi_arena* a, const uint16_t* O, int M, int dm, const uint16_t* page, int eo, size_t c0,
+                      const uint16_t* bo, uint16_t* y, const uint16_t* x, unsigned flags, int bbase) {
+  GemmArgs G = gemm_args();
+  G.A = O; G.lda = dm; G.B = page; G.ldb = dm;
+  G.M = M; G.N = eo; G.K = dm;
+  G.bias = offset(bo, c0); G.out = y + c0; G.ldo = dm; G.baseline_bias = bbase;
+  if (flags & PSI_OP_RESIDUAL) { G.resid = x + c0; G.ldr = dm; }
+  return run_gemm(a, G);
 }
 
 // Device pointers and pinned page images of an attention operator.
@@ -551,7 +593,9 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   size_t need = 0;
   psi_status st = psi_attn_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_dev != nullptr, &need);
   if (st) return st;
-  if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  const bool otiles = Wo->split == PSI_SPLIT_ROWS;
+  if ((flags & PSI_OP_STORE_ACC) && (!acc_dev || otiles))
+    return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev and a column-split Wo");
   if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
   if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
@@ -561,77 +605,91 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   const long ldvt = (long)align_up((size_t)Ms, 64);
   const int bbase = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
   ScratchMark mark(a);
-  uint16_t* Q = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * gw * 2, &st));
+  // Q_g, overwritten by O_g: one group's tile [M, gw] for the K-split, or
+  // columns g of an [M, dm] buffer that keeps every group's O for the
+  // output tiles (in acc_dev's memory when given, which then holds no
+  // fp32 accumulator)
+  uint16_t* Q;
+  long ldq;
+  if (otiles) {
+    Q = acc_dev ? reinterpret_cast<uint16_t*>(acc_dev)
+                : static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * dm * 2, &st));
+    ldq = dm;
+  } else {
+    Q = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * gw * 2, &st));
+    ldq = gw;
+  }
   if (st) return st;
   uint16_t* Kb = static_cast<uint16_t*>(scratch_alloc(a, (size_t)Ms * gw * 2, &st));
   if (st) return st;
   uint16_t* Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
   if (st) return st;
   float* acc = acc_dev;
-  if (!acc) {
+  if (!acc && !otiles) {
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * dm * 4, &st));
     if (st) return st;
   }
   const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
   OpBiases bias;
   if ((st = bias.stage(a, ms, 4))) return st;
+  // pages: Wq_g, Wk_g, Wv_g (, Wo[:, g]) per group; output tiles Wo_o last
   std::vector<PageReq> rq, rk, rv, ro, reqs;
   matrix_requests(Wq, rq);
   matrix_requests(Wk, rk);
   matrix_requests(Wv, rv);
   matrix_requests(Wo, ro);
   const int nG = (int)rq.size();
+  const int per = otiles ? 3 : 4;
   for (int g = 0; g < nG; ++g) {
     reqs.push_back(rq[g]);
     reqs.push_back(rk[g]);
     reqs.push_back(rv[g]);
-    reqs.push_back(ro[g]);
+    if (!otiles) reqs.push_back(ro[g]);
   }
+  if (otiles) reqs.insert(reqs.end(), ro.begin(), ro.end());
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[4];
   for (int g = 0; g < nG; ++g) {
     const int ext = matrix_page_extent(Wq, g);
-    const bool last = g == nG - 1;
     const size_t c0 = (size_t)g * gw;
+    const size_t r0 = (size_t)per * g;
+    uint16_t* Qg = otiles ? Q + c0 : Q;
     const uint16_t* page;
     if (g == 0)
       for (int i = 0; i < 4; ++i)
         if ((st = bias.get(i, &bq[i]))) return st;
     // Q_g = x Wq_g^T + bq_g, K_g = src Wk_g^T + bk_g, V_g^T = Wv_g src^T + bv_g
-    if ((st = feeder.take(4 * g, &page)) ||
-        (st = project(a, x, M, dm, page, ext, offset(bq[0], c0), Q, gw, bbase)) ||
-        (st = feeder.give_back(4 * g)))
+    if ((st = feeder.take(r0, &page)) ||
+        (st = project(a, x, M, dm, page, ext, offset(bq[0], c0), Qg, ldq, bbase)) ||
+        (st = feeder.give_back(r0)))
       return st;
-    if ((st = feeder.take(4 * g + 1, &page)) ||
+    if ((st = feeder.take(r0 + 1, &page)) ||
         (st = project(a, src, Ms, dm, page, ext, offset(bq[1], c0), Kb, gw, bbase)) ||
-        (st = feeder.give_back(4 * g + 1)))
+        (st = feeder.give_back(r0 + 1)))
       return st;
-    if ((st = feeder.take(4 * g + 2, &page)) ||
+    if ((st = feeder.take(r0 + 2, &page)) ||
         (st = project_vt(a, src, Ms, dm, page, ext, offset(bq[2], c0), Vt, ldvt, bbase)) ||
-        (st = feeder.give_back(4 * g + 2)))
+        (st = feeder.give_back(r0 + 2)))
       return st;
     // O_g over Q_g (online softmax, fp32 state)
-    if ((st = attend(a, Q, gw, Kb, gw, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
+    if ((st = attend(a, Qg, ldq, Kb, gw, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
+    if (otiles) continue;
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, (size_t)M * gw * 2))) return st;
-    // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
-    if ((st = feeder.take(4 * g + 3, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = Q; G.lda = gw; G.B = page; G.ldb = ext;
-      G.M = M; G.N = dm; G.K = ext;
-      G.baseline_bias = bbase;
-      if (g > 0) { G.acc_in = acc; G.ld_acc_in = dm; }
-      if (last) {
-        G.bias = bq[3]; G.out = y; G.ldo = dm;
-        if (flags & PSI_OP_RESIDUAL) { G.resid = x; G.ldr = dm; }
-        if (flags & PSI_OP_STORE_ACC) { G.acc_out = acc; G.ld_acc_out = dm; }
-      } else {
-        G.epi = EPI_ACC; G.acc_out = acc; G.ld_acc_out = dm;
-      }
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(4 * g + 3))) return st;
+    if ((st = feeder.take(r0 + 3, &page)) ||
+        (st = oproj_ksplit(a, Q, gw, M, dm, page, ext, g == 0, g == nG - 1, acc, bq[3], y, x, flags, bbase)) ||
+        (st = feeder.give_back(r0 + 3)))
+      return st;
+  }
+  if (otiles) {
+    const size_t r0 = (size_t)per * nG;
+    const uint16_t* page;
+    for (int o = 0; o < (int)ro.size(); ++o)
+      if ((st = feeder.take(r0 + o, &page)) ||
+          (st = oproj_tile(a, Q, M, dm, page, matrix_page_extent(Wo, o), (size_t)o * Wo->block, bq[3], y, x,
+                           flags, bbase)) ||
+          (st = feeder.give_back(r0 + o)))
+        return st;
   }
   return bias.release();
 }
@@ -648,7 +706,9 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
   psi_status st = psi_attn_ext_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nr,
                                     acc_dev != nullptr, nullptr);
   if (st) return st;
-  if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  const bool otiles = Wo->split == PSI_SPLIT_ROWS;
+  if ((flags & PSI_OP_STORE_ACC) && (!acc_dev || otiles))
+    return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev and a column-split Wo");
   if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
   if (!a->dry) {
     for (const uint16_t* g : {nr->gamma_q, nr->gamma_k}) {
@@ -671,7 +731,7 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
   uint16_t* Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
   if (st) return st;
   float* acc = acc_dev;
-  if (!acc) {
+  if (!acc && !otiles) {
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * dm * 4, &st));
     if (st) return st;
   }
@@ -680,21 +740,24 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
                            {nr->gamma_k, nr->gamma_k ? (size_t)dm * 2 : 0}};
   OpBiases bias;
   if ((st = bias.stage(a, ms, 4, gam, 2, Wq->resident != 0))) return st;
-  // pages: Wq_g, Wk_g for every group, then Wv_g, Wo_g for every group
+  // pages: Wq_g, Wk_g for every group, then Wv_g (, Wo[:, g]) for every
+  // group; output tiles Wo_o last
   std::vector<PageReq> rq, rk, rv, ro, reqs;
   matrix_requests(Wq, rq);
   matrix_requests(Wk, rk);
   matrix_requests(Wv, rv);
   matrix_requests(Wo, ro);
   const int nG = (int)rq.size();
+  const int per = otiles ? 1 : 2;
   for (int g = 0; g < nG; ++g) {
     reqs.push_back(rq[g]);
     reqs.push_back(rk[g]);
   }
   for (int g = 0; g < nG; ++g) {
     reqs.push_back(rv[g]);
-    reqs.push_back(ro[g]);
+    if (!otiles) reqs.push_back(ro[g]);
   }
+  if (otiles) reqs.insert(reqs.end(), ro.begin(), ro.end());
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[6];
@@ -729,32 +792,29 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
   const size_t base = 2 * (size_t)nG;
   for (int g = 0; g < nG; ++g) {
     const int ext = matrix_page_extent(Wq, g);
-    const bool last = g == nG - 1;
     const size_t c0 = (size_t)g * gw;
+    const size_t r0 = base + (size_t)per * g;
     // V_g^T = Wv_g src^T + bv_g, then O_g over Q[:, g] in place
-    if ((st = feeder.take(base + 2 * g, &page)) ||
+    if ((st = feeder.take(r0, &page)) ||
         (st = project_vt(a, src, Ms, dm, page, ext, offset(bq[2], c0), Vt, ldvt, bbase)) ||
-        (st = feeder.give_back(base + 2 * g)))
+        (st = feeder.give_back(r0)))
       return st;
     if ((st = attend(a, Q + c0, dm, Kb + c0, dm, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
-    // ACC (+)= O_g Wo[:, g]^T; after the last group y = B(ACC + bo) (+ x)
-    if ((st = feeder.take(base + 2 * g + 1, &page))) return st;
-    {
-      GemmArgs G = gemm_args();
-      G.A = Q + c0; G.lda = dm; G.B = page; G.ldb = ext;
-      G.M = M; G.N = dm; G.K = ext;
-      G.baseline_bias = bbase;
-      if (g > 0) { G.acc_in = acc; G.ld_acc_in = dm; }
-      if (last) {
-        G.bias = bq[3]; G.out = y; G.ldo = dm;
-        if (flags & PSI_OP_RESIDUAL) { G.resid = x; G.ldr = dm; }
-        if (flags & PSI_OP_STORE_ACC) { G.acc_out = acc; G.ld_acc_out = dm; }
-      } else {
-        G.epi = EPI_ACC; G.acc_out = acc; G.ld_acc_out = dm;
-      }
-      if ((st = run_gemm(a, G))) return st;
-    }
-    if ((st = feeder.give_back(base + 2 * g + 1))) return st;
+    if (otiles) continue;
+    if ((st = feeder.take(r0 + 1, &page)) ||
+        (st = oproj_ksplit(a, Q + c0, dm, M, dm, page, ext, g == 0, g == nG - 1, acc, bq[3], y, x, flags,
+                           bbase)) ||
+        (st = feeder.give_back(r0 + 1)))
+      return st;
+  }
+  if (otiles) {
+    const size_t r0 = base + (size_t)per * nG;
+    for (int o = 0; o < (int)ro.size(); ++o)
+      if ((st = feeder.take(r0 + o, &page)) ||
+          (st = oproj_tile(a, Q, M, dm, page, matrix_page_extent(Wo, o), (size_t)o * Wo->block, bq[3], y, x,
+                           flags, bbase)) ||
+          (st = feeder.give_back(r0 + o)))
+        return st;
   }
   return bias.release();
 }

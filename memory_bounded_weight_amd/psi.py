@@ -165,6 +165,7 @@ _sig("psi_version", [], ctypes.c_char_p)
 _sig("psi_arena_create", [_P(psi_arena_desc), _P(_vp)])
 _sig("psi_arena_destroy", [_vp])
 _sig("psi_arena_sync", [_vp])
+_sig("psi_arena_set_timing", [_vp, _i])
 _sig("psi_arena_stats", [_vp, _P(psi_stats)])
 _sig("psi_arena_reset_stats", [_vp])
 _sig("psi_arena_trace_start", [_vp, _sz])
@@ -204,7 +205,8 @@ _sig("psi_journal_counters", [_vp, _P(ctypes.c_uint64), _P(ctypes.c_uint64), _P(
 #: every symbol the header declares (checked by the CPU test suite)
 EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_arena_plan",
            "psi_linear_plan", "psi_ffn_plan", "psi_attn_plan", "psi_last_error", "psi_version",
-           "psi_arena_create", "psi_arena_destroy", "psi_arena_sync", "psi_arena_stats",
+           "psi_arena_create", "psi_arena_destroy", "psi_arena_sync", "psi_arena_set_timing",
+           "psi_arena_stats",
            "psi_arena_reset_stats", "psi_arena_trace_start", "psi_arena_trace_read",
            "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
            "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
@@ -352,6 +354,10 @@ def psi_arena_sync(arena: int):
     st = _check(_lib.psi_arena_sync(arena), "psi_arena_sync")
     _held.pop(arena, None)
     return st
+
+
+def psi_arena_set_timing(arena: int, on: bool):
+    return _check(_lib.psi_arena_set_timing(arena, int(bool(on))), "psi_arena_set_timing")
 
 
 def psi_arena_stats(arena: int) -> psi_stats:

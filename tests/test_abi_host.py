@@ -280,12 +280,16 @@ def test_trace_needs_profiling_arena():
             psi.psi_arena_trace_start(a, 16)
         with pytest.raises(psi.PsiError):
             psi.psi_arena_trace_read(a, 16)
+        with pytest.raises(psi.PsiError):
+            psi.psi_arena_set_timing(a, False)
     finally:
         psi.psi_arena_destroy(a)
     a = psi.psi_arena_create(desc(8, 1, 2, flags=psi.PSI_ARENA_DRY_RUN | psi.PSI_ARENA_PROFILE))
     try:
         psi.psi_arena_trace_start(a, 16)
         assert psi.psi_arena_trace_read(a, 16) == []
+        psi.psi_arena_set_timing(a, False)
+        psi.psi_arena_set_timing(a, True)
     finally:
         psi.psi_arena_destroy(a)
 
@@ -437,3 +441,42 @@ def test_new_entry_points_empty_inputs_and_layout_errors_dry_run():
     st, _ = psi.psi_attn_ext_plan(small, 64, 0, 4, 128, q, k, v, wo_cols, psi.qk_norm_rope(0x1000, 0x2000, 1e-6))
     assert st == psi.PSI_E_PAGE_TOO_SMALL
     assert psi.psi_attn_ext_plan(small, 64, 0, 4, 128, q, k, v, wo_cols, None)[0] == psi.PSI_OK
+
+
+def test_attention_output_tiles_plan_and_page_order_dry_run():
+    """With Wo split by rows (output tiles) the O-projection runs once per
+    tile over the full K after every head group, from the groups' outputs
+    kept in acc_dev's memory: the arena needs only K and V^T of one group
+    (two 8 MiB pages more than with the K-split fit the 80 MiB arena), the
+    same 16 pages stream, Wo's last, and PSI_OP_STORE_ACC (no fp32
+    accumulator exists) is refused.  Without acc_dev the outputs take
+    M x d BF16 of scratch."""
+    Wq, Wk, Wv, _ = cfg5_attn()
+    Wo_t = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 768)  # ragged: 5 tiles of 768 + 256
+    d5 = desc(80, 8, 5, 0)
+    st, need = psi.psi_attn_plan(d5, 8192, 0, 32, 128, Wq, Wk, Wv, Wo_t, True)
+    assert st == psi.PSI_OK and need == 2 * 8192 * 1024 * 2
+    st, _ = psi.psi_attn_plan(d5, 8192, 0, 32, 128, *cfg5_attn(), True)
+    assert st == psi.PSI_E_SCRATCH_EXHAUSTED  # the K-split keeps Q_g too
+    st, need = psi.psi_attn_plan(desc(80, 8, 2, 0), 1024, 0, 32, 128, Wq, Wk, Wv, Wo_t, False)
+    assert st == psi.PSI_OK and need == 2 * 1024 * 1024 * 2 + 1024 * 4096 * 2
+    a = psi.psi_arena_create(d5)
+    try:
+        fake = 0x10000
+        psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, fake, fake,
+                           psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 12 + 6
+        assert s.bytes_h2d == 16 * 8 * MiB + 4 * 4096 * 2
+        assert s.kernel_launches == 4 * 4 + 6  # Q, K, V^T, attention per group; one GEMM per tile
+        assert s.scratch_high_water == 2 * 8192 * 1024 * 2
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, fake, fake,
+                               psi.PSI_OP_STORE_ACC)
+        assert e.value.status == psi.PSI_E_INVALID
+        Wo_bad = fake_matrix(4096, 4096, psi.PSI_SPLIT_COLS, 512)  # a K-split Wo needs the group block
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_bad, fake, fake, 0)
+        assert e.value.status == psi.PSI_E_INVALID
+    finally:
+        psi.psi_arena_destroy(a)

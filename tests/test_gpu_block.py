@@ -208,3 +208,28 @@ def test_transport_jitter_keeps_bits(P, n_pages):
         assert np.array_equal(r, g_) and np.array_equal(r2, g_)
     # the delays are real: ~60 launches and copies at 31.5 us on average
     assert t_j > min(t_a, t_b) + 0.5, (t_j, t_a, t_b)
+
+
+def test_launch_timing_sample(P):
+    """psi_arena_set_timing: launches enqueued with timing off are not timed
+    (no events), those enqueued after it is turned back on are, and the
+    output does not depend on it."""
+    from tests.gpu_util import make_arena as _mk
+    c = synth.ffn_case(seed=63, M=64, d=256, hidden=512)
+    U = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, 256)
+    V = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, 256)
+    ar = _mk(8 * MiB, 256 * KiB, 2, flags=P.PSI_ARENA_PROFILE)
+    try:
+        x = dev(c["x"])
+        ys = [torch.empty_like(x) for _ in range(2)]
+        P.psi_arena_set_timing(ar, False)
+        P.psi_ffn_paged(ar, x, 64, 256, U, V, 1, None, ys[0], 0)
+        s = P.psi_arena_stats(ar)
+        assert s.kernel_launches == 4 and s.gemm_launches == 0 and s.gemm_ms == 0.0
+        P.psi_arena_set_timing(ar, True)
+        P.psi_ffn_paged(ar, x, 64, 256, U, V, 1, None, ys[1], 0)
+        s = P.psi_arena_stats(ar)
+        assert s.kernel_launches == 8 and s.gemm_launches == 4 and s.gemm_ms > 0.0
+        assert np.array_equal(host(ys[0]), host(ys[1]))
+    finally:
+        P.psi_arena_destroy(ar)
