@@ -70,14 +70,15 @@ def build_workload(args, torch, psi, synth):
     if args.workload == "stack8":
         M, d, heads, hid, nblk = 8192, 4096, 32, 16384, 8
         # 80 MiB = pages x 8 MiB + workspace + scratch.  O-projection over
-        # output tiles (default): the head-group outputs live in the fp32
-        # accumulator's memory, attention scratch is K and V^T of one group
-        # (32 MiB), and five pages fit.  K-split O-projection: Q, K, V^T
-        # (48 MiB); two pages leave the paper's 8 MiB workspace, three take
-        # its place (no kernel here uses a workspace), scratch keeps 56 MiB.
+        # output tiles (default): the head-group outputs, K and V^T live in
+        # the fp32 accumulator's memory (declared live state), the arena's
+        # scratch serves the FFN's 16 MiB hidden tile, and seven pages fit.
+        # K-split O-projection: Q, K, V^T of a group in scratch (48 MiB); two
+        # pages leave the paper's 8 MiB workspace, three take its place (no
+        # kernel here uses a workspace), scratch keeps 56 MiB.
         otiles = args.o_proj == "tiles"
         if args.pages is None:
-            args.pages = 5 if otiles else 3
+            args.pages = 7 if otiles else 3
         ws = 8 * MiB if args.pages == 2 else max(0, 80 * MiB - 56 * MiB - args.pages * 8 * MiB)
         arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, ws, 0, stream, flags))
         t0 = time.time()
@@ -494,7 +495,7 @@ def main():
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages", type=int, default=None,
-                    help="page slots in the 80 MiB stack arena (default 5 with output-tile "
+                    help="page slots in the 80 MiB stack arena (default 7 with output-tile "
                          "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
     ap.add_argument("--o-proj", choices=("tiles", "ksplit"), default="tiles",
                     help="stack: attention O-projection over output tiles of Wo rows from every head "

@@ -274,7 +274,11 @@ psi_status psi_attn_plan(const psi_arena_desc* d, int M, int Mc, int heads, int 
   size_t ldvt = align_up((size_t)Ms, 64);
   size_t need = align_up((size_t)Ms * gw * 2, kAlign) + align_up((size_t)gw * ldvt * 2, kAlign);
   if (otiles) {
-    if (!acc_external) need += align_up((size_t)M * dm * 2, kAlign);  // O of every group (else in acc_dev)
+    // every group's O [M, dm] BF16, then one group's K and V^T: in acc_dev
+    // (M dm 4 bytes) when given, K and V^T only where they fit behind O
+    const size_t obytes = align_up((size_t)M * dm * 2, kAlign);
+    if (!acc_external) need += obytes;
+    else if (obytes + need <= (size_t)M * dm * 4) need = 0;
   } else {
     need += align_up((size_t)M * gw * 2, kAlign);
     if (!acc_external) need += align_up((size_t)M * dm * 4, kAlign);

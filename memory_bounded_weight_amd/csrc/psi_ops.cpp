@@ -596,6 +596,8 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   const bool otiles = Wo->split == PSI_SPLIT_ROWS;
   if ((flags & PSI_OP_STORE_ACC) && (!acc_dev || otiles))
     return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev and a column-split Wo");
+  if (otiles && (reinterpret_cast<uintptr_t>(acc_dev) & 15))
+    return fail(PSI_E_ALIGN, "attention: acc_dev must be 16-byte aligned when it holds the head-group outputs");
   if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
   if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
@@ -607,10 +609,17 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   ScratchMark mark(a);
   // Q_g, overwritten by O_g: one group's tile [M, gw] for the K-split, or
   // columns g of an [M, dm] buffer that keeps every group's O for the
-  // output tiles (in acc_dev's memory when given, which then holds no
-  // fp32 accumulator)
+  // output tiles.  With output tiles acc_dev holds no fp32 accumulator: its
+  // memory takes that buffer and, where they fit behind it, K_g and V_g^T
+  // (the plan's scratch figure follows the same rule).
   uint16_t* Q;
+  uint16_t* Kb;
+  uint16_t* Vt;
   long ldq;
+  const size_t kbytes = align_up((size_t)Ms * gw * 2, kAlign);
+  const size_t kvbytes = kbytes + align_up((size_t)gw * ldvt * 2, kAlign);
+  const size_t obytes = align_up((size_t)M * dm * 2, kAlign);
+  const bool kv_in_acc = otiles && acc_dev && obytes + kvbytes <= (size_t)M * dm * 4;
   if (otiles) {
     Q = acc_dev ? reinterpret_cast<uint16_t*>(acc_dev)
                 : static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * dm * 2, &st));
@@ -620,10 +629,16 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     ldq = gw;
   }
   if (st) return st;
-  uint16_t* Kb = static_cast<uint16_t*>(scratch_alloc(a, (size_t)Ms * gw * 2, &st));
-  if (st) return st;
-  uint16_t* Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
-  if (st) return st;
+  if (kv_in_acc) {
+    char* base = reinterpret_cast<char*>(acc_dev) + obytes;
+    Kb = reinterpret_cast<uint16_t*>(base);
+    Vt = reinterpret_cast<uint16_t*>(base + kbytes);
+  } else {
+    Kb = static_cast<uint16_t*>(scratch_alloc(a, (size_t)Ms * gw * 2, &st));
+    if (st) return st;
+    Vt = static_cast<uint16_t*>(scratch_alloc(a, (size_t)gw * ldvt * 2, &st));
+    if (st) return st;
+  }
   float* acc = acc_dev;
   if (!acc && !otiles) {
     acc = static_cast<float*>(scratch_alloc(a, (size_t)M * dm * 4, &st));

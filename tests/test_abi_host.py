@@ -446,18 +446,22 @@ def test_new_entry_points_empty_inputs_and_layout_errors_dry_run():
 def test_attention_output_tiles_plan_and_page_order_dry_run():
     """With Wo split by rows (output tiles) the O-projection runs once per
     tile over the full K after every head group, from the groups' outputs
-    kept in acc_dev's memory: the arena needs only K and V^T of one group
-    (two 8 MiB pages more than with the K-split fit the 80 MiB arena), the
+    kept in acc_dev's memory, which also takes K and V^T of one group where
+    they fit behind them: the stack's attention needs no arena scratch, the
     same 16 pages stream, Wo's last, and PSI_OP_STORE_ACC (no fp32
-    accumulator exists) is refused.  Without acc_dev the outputs take
-    M x d BF16 of scratch."""
+    accumulator exists) and a misaligned acc_dev are refused.  Without
+    acc_dev the outputs take M x d BF16 of scratch."""
     Wq, Wk, Wv, _ = cfg5_attn()
     Wo_t = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 768)  # ragged: 5 tiles of 768 + 256
     d5 = desc(80, 8, 5, 0)
-    st, need = psi.psi_attn_plan(d5, 8192, 0, 32, 128, Wq, Wk, Wv, Wo_t, True)
-    assert st == psi.PSI_OK and need == 2 * 8192 * 1024 * 2
+    # O (64 MiB), K and V^T (32 MiB) all sit in acc_dev's 128 MiB
+    st, need = psi.psi_attn_plan(desc(80, 8, 8, 0), 8192, 0, 32, 128, Wq, Wk, Wv, Wo_t, True)
+    assert st == psi.PSI_OK and need == 0
+    # cross-attention to 16,384 keys: K and V^T (64 MiB) do not fit behind O of 4,096 queries
+    st, need = psi.psi_attn_plan(desc(160, 8, 5, 0), 4096, 16384, 32, 128, Wq, Wk, Wv, Wo_t, True)
+    assert st == psi.PSI_OK and need == 2 * 16384 * 1024 * 2
     st, _ = psi.psi_attn_plan(d5, 8192, 0, 32, 128, *cfg5_attn(), True)
-    assert st == psi.PSI_E_SCRATCH_EXHAUSTED  # the K-split keeps Q_g too
+    assert st == psi.PSI_E_SCRATCH_EXHAUSTED  # the K-split keeps Q_g, K_g, V_g^T in the arena
     st, need = psi.psi_attn_plan(desc(80, 8, 2, 0), 1024, 0, 32, 128, Wq, Wk, Wv, Wo_t, False)
     assert st == psi.PSI_OK and need == 2 * 1024 * 1024 * 2 + 1024 * 4096 * 2
     a = psi.psi_arena_create(d5)
@@ -469,7 +473,10 @@ def test_attention_output_tiles_plan_and_page_order_dry_run():
         assert s.page_copies == 12 + 6
         assert s.bytes_h2d == 16 * 8 * MiB + 4 * 4096 * 2
         assert s.kernel_launches == 4 * 4 + 6  # Q, K, V^T, attention per group; one GEMM per tile
-        assert s.scratch_high_water == 2 * 8192 * 1024 * 2
+        assert s.scratch_high_water == 0       # O, K and V^T in acc_dev's memory
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, fake + 8, fake, 0)
+        assert e.value.status == psi.PSI_E_ALIGN
         with pytest.raises(psi.PsiError) as e:
             psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, fake, fake,
                                psi.PSI_OP_STORE_ACC)
