@@ -360,11 +360,17 @@ def build_workload(args, torch, psi, synth):
         # tiles), each sub-block with its residual.  Tiny token count: every
         # step is bound by streaming the 8 blocks' weights.
         M, d, heads, dh, hid, nblk = 126, 2048, 32, 64, 8192, 8
-        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 3, 0, 0, stream, flags))
+        # output tiles of Wo (default): attention scratch is a few MiB and the
+        # arena takes eight pages; K-split: three
+        otiles = args.o_proj == "tiles"
+        if args.pages is None:
+            args.pages = 8 if otiles else 3
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, 0, 0, stream, flags))
         blocks, gammas = [], []
         for b in range(nblk):
             w = synth.block_weights(args.seed, b, d, hid)
-            blocks.append(psi.block_weights(w, 8 * dh, 1024, resident=args.resident))
+            blocks.append(psi.block_weights(w, 8 * dh, 1024, resident=args.resident,
+                                            attn_out_tile=1024 if otiles else 0))
             rng = np.random.default_rng([args.seed, b, 1])
             g = [synth.norm_gamma(rng, d) for _ in range(2)]
             if args.resident:
@@ -398,20 +404,29 @@ def build_workload(args, torch, psi, synth):
                     live=live, keep=(blocks, gammas, nrs),
                     config={"workload": "8 audio-shape blocks (Q/K RMS + RoPE attention, FFN)", "tokens": M,
                             "d_model": d, "heads": heads, "head_dim": dh, "ffn_hidden": hid, "blocks": nblk,
-                            "arena_MiB": 80, "page_MiB": 8, "pages": 3, "head_group": 8, "ffn_tile": 1024,
+                            "arena_MiB": 80, "page_MiB": 8, "pages": args.pages, "head_group": 8, "ffn_tile": 1024,
+                            "o_projection": "output tiles" if otiles else "K-split",
                             "resident_weights": args.resident})
     if args.workload == "attn4096":
         M, Mc, d, heads = 6144, 1024, 4096, 32
         c = synth.attn_case(args.seed, M, Mc, d, cross=True)
+        # output tiles of Wo (default): O, K and V^T sit in the accumulator's
+        # memory and the arena takes eight pages; K-split: the paper's two
+        # pages and 8 MiB workspace
+        otiles = args.o_proj == "tiles"
+        if args.pages is None:
+            args.pages = 8 if otiles else 2
         mats = {}
         for part in ("self", "cross"):
             w = c[part]
             ms = [psi.pinned_matrix(w["W" + n], w["b" + n], psi.PSI_SPLIT_ROWS, 1024) for n in "qkv"]
-            ms.append(psi.pinned_matrix(w["Wo"], w["bo"], psi.PSI_SPLIT_COLS, 1024))
+            ms.append(psi.pinned_matrix(w["Wo"], w["bo"], psi.PSI_SPLIT_ROWS if otiles else psi.PSI_SPLIT_COLS,
+                                        1024))
             if args.resident:
                 ms = [psi.resident_matrix(m) for m in ms]
             mats[part] = ms
-        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 8 * MiB, 0, stream, flags))
+        ws = 8 * MiB if args.pages == 2 else 0
+        arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, ws, 0, stream, flags))
         x0 = torch.from_numpy(c["x"].view("int16")).cuda()
         ctx = torch.from_numpy(c["ctx"].view("int16")).cuda()
         x = torch.empty_like(x0)
@@ -429,7 +444,8 @@ def build_workload(args, torch, psi, synth):
                     live=live, keep=mats,
                     config={"workload": "paged attention sub-blocks (self + cross)", "tokens": M,
                             "context_tokens": Mc, "d_model": d, "heads": heads, "head_dim": 128,
-                            "head_group": 8, "arena_MiB": 80, "page_MiB": 8,
+                            "head_group": 8, "arena_MiB": 80, "page_MiB": 8, "pages": args.pages,
+                            "o_projection": "output tiles" if otiles else "K-split",
                             "resident_weights": args.resident})
     raise ValueError(args.workload)
 
@@ -498,7 +514,8 @@ def main():
                     help="page slots in the 80 MiB stack arena (default 7 with output-tile "
                          "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
     ap.add_argument("--o-proj", choices=("tiles", "ksplit"), default="tiles",
-                    help="stack: attention O-projection over output tiles of Wo rows from every head "
+                    help="stack, attn4096, audio8: attention O-projection over output tiles of Wo rows "
+                         "from every head "
                          "group's output (default), or K-split over head groups with the fp32 accumulator")
     ap.add_argument("--trace", metavar="FILE",
                     help="keep the device timeline of the timed steps (page copies timed too) and write it "

@@ -95,15 +95,6 @@ static psi_status wait_release(psi_arena* a, psi_page_slot& slot) {
   return PSI_OK;
 }
 
-bool slot_released(psi_arena* a, int s) {
-  const psi_page_slot& slot = a->slots[s];
-  if (a->dry || !slot.released_once || (a->desc.flags & PSI_ARENA_SYNC_COPY)) return true;
-  const hipError_t q = hipEventQuery(slot.release);
-  if (q == hipSuccess) return true;
-  if (q != hipErrorNotReady) (void)hipGetLastError();  // reported by the blocking wait later
-  return false;
-}
-
 int first_free_slot(const psi_arena* a) {
   for (int i = 0; i < a->desc.n_pages; ++i) {
     const int c = (a->next_slot + i) % a->desc.n_pages;

@@ -173,9 +173,6 @@ void scratch_reset(psi_arena* a, size_t mark);
 
 // Page request (slice copy into the next round-robin page slot).
 int first_free_slot(const psi_arena* a);  // -1 when every slot is taken
-// True when slot s may be refilled without a host wait: never released, or
-// its release event (the last consumer) has completed; no blocking.
-bool slot_released(psi_arena* a, int s);
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool check_pinned);
 psi_status page_acquire(psi_arena* a, int page);
