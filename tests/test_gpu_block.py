@@ -233,3 +233,38 @@ def test_launch_timing_sample(P):
         assert np.array_equal(host(ys[0]), host(ys[1]))
     finally:
         P.psi_arena_destroy(ar)
+
+
+def test_temporary_weights_survive_until_sync(P):
+    """Operators return before their page copies run; the binding keeps the
+    host weights of a temporary argument alive until psi_arena_sync.  With
+    copies delayed (PSI_ARENA_JITTER), same-size pinned buffers allocated and
+    overwritten right after the call do not change the block's bits (they
+    would, if the freed pinned blocks were handed out while a DMA still
+    read them)."""
+    from tests.gpu_util import make_arena as _mk
+    M, d, heads, h = 128, 256, 2, 1024
+    x0 = synth.stack_input(64, M, d)
+    w = synth.block_weights(64, 0, d, h)
+    outs = []
+    for temporary in (False, True):
+        ar = _mk(8 * MiB, 256 * KiB, 3, flags=P.PSI_ARENA_JITTER)
+        try:
+            x = dev(x0)
+            xt = torch.empty_like(x)
+            acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+            if temporary:
+                P.psi_block_paged(ar, x, xt, M, heads, 128, P.block_weights(w, 128, 256), 1, acc, None, 0)
+                assert P._held.get(ar), "the binding holds the temporary weights"
+                junk = [P.pinned_matrix(np.zeros_like(w[n]), None, P.PSI_SPLIT_ROWS, 128)
+                        for n in ("Wq", "Wk", "Wv", "Wo", "U", "V")]
+                del junk
+            else:
+                bw = P.block_weights(w, 128, 256)
+                P.psi_block_paged(ar, x, xt, M, heads, 128, bw, 1, acc, None, 0)
+            P.psi_arena_sync(ar)
+            assert not P._held.get(ar)
+            outs.append(host(x))
+        finally:
+            P.psi_arena_destroy(ar)
+    assert np.array_equal(outs[0], outs[1])
