@@ -568,7 +568,10 @@ def main():
     sample_all = bool(args.trace or args.profile_copies)
     if args.trace and not args.no_profile:
         psi.psi_arena_trace_start(arena, 1 << 18)  # times page copies too from here on
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps on the compute stream: per-step
+    # device times for the mean and sample SD
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev0, ev1 = evs[0], evs[-1]
     sync_all()
     t0 = time.perf_counter()
     ev0.record()
@@ -576,11 +579,14 @@ def main():
         if not args.no_profile:
             psi.psi_arena_set_timing(arena, sample_all or i == args.steps - 1)
         step()
-    ev1.record()
+        evs[i + 1].record()
     sync_all()
     t1 = time.perf_counter()
     wall = t1 - t0
     ev_ms = ev0.elapsed_time(ev1)
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    step_mean = sum(step_ms) / len(step_ms)
+    step_sd = (sum((v - step_mean) ** 2 for v in step_ms) / (len(step_ms) - 1)) ** 0.5 if len(step_ms) > 1 else 0.0
     st = psi.psi_arena_stats(arena)
     if args.trace and not args.no_profile:
         with open(args.trace, "w") as f:
@@ -665,6 +671,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "event_ms_per_step": round(ev_ms / args.steps, 3),
+        "step_ms_mean_sd": [round(step_mean, 3), round(step_sd, 3)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
