@@ -139,6 +139,7 @@ typedef struct psi_stats {
   double copy_ms;           /* busy time of the busier of the two page-copy streams
                                (PSI_ARENA_PROFILE_COPIES or while tracing) */
   uint64_t copy_bytes_timed;
+  uint64_t lent_page_copies; /* page copies into slots lent from an operator's idle scratch */
 } psi_stats;
 
 /* A weight matrix W[rows, cols] in pinned host memory, already packed into

@@ -103,17 +103,98 @@ int first_free_slot(const psi_arena* a) {
   return -1;
 }
 
+static psi_page_slot* slot_ptr(psi_arena* a, int s) {
+  if (s >= 0 && s < a->desc.n_pages) return &a->slots[s];
+  if (s >= a->desc.n_pages && s < a->desc.n_pages + a->n_lent) return &a->lent[s - a->desc.n_pages];
+  return nullptr;
+}
+
+static bool event_done(hipEvent_t e) {
+  const hipError_t q = hipEventQuery(e);
+  if (q == hipSuccess) return true;
+  if (q != hipErrorNotReady) (void)hipGetLastError();  // not ready for this purpose; the waits report it
+  return false;
+}
+
+// A lent slot that can be filled without a host wait, or -1.
+static int ready_lent_slot(psi_arena* a) {
+  for (int i = 0; i < a->n_lent; ++i) {
+    const psi_page_slot& l = a->lent[i];
+    if (l.state != psi_page_slot::FREE) continue;
+    if (a->dry) return a->desc.n_pages + i;
+    if (a->lent_fresh[i] ? event_done(a->scratch_free) : (!l.released_once || event_done(l.release)))
+      return a->desc.n_pages + i;
+  }
+  return -1;
+}
+
+// A free lent slot whose fill needs a host wait, or -1.
+static int free_lent_slot(const psi_arena* a) {
+  for (int i = 0; i < a->n_lent; ++i)
+    if (a->lent[i].state == psi_page_slot::FREE) return a->desc.n_pages + i;
+  return -1;
+}
+
+int submit_slot(psi_arena* a) {
+  int s = ready_lent_slot(a);
+  if (s < 0) s = first_free_slot(a);
+  if (s < 0) s = free_lent_slot(a);
+  return s;
+}
+
+void* slot_dev(psi_arena* a, int s) {
+  psi_page_slot* p = slot_ptr(a, s);
+  return p ? p->dev : nullptr;
+}
+
+int lend_scratch_slots(psi_arena* a) {
+  if (a->desc.flags & PSI_ARENA_SYNC_COPY) return 0;
+  const size_t start = align_up(a->scratch_top, kAlign);
+  const size_t stride = align_up(a->desc.page_bytes, kAlign);
+  if (stride == 0 || start >= a->layout.scratch_bytes) return 0;
+  size_t n = (a->layout.scratch_bytes - start) / stride;
+  if (n > (size_t)psi_arena::kMaxLent) n = psi_arena::kMaxLent;
+  for (size_t i = 0; i < n; ++i) {
+    psi_page_slot& l = a->lent[i];
+    l.state = psi_page_slot::FREE;
+    l.released_once = false;
+    l.dev = a->dry ? nullptr : a->base + a->layout.scratch_off + start + i * stride;
+    a->lent_fresh[i] = true;
+  }
+  a->n_lent = (int)n;
+  if (n) {
+    // the scratch's earlier users (previous operators) precede any copy into
+    // it; the scratch high-water mark stays the operators' own allocations
+    if (!a->dry && hipEventRecord(a->scratch_free, a->compute) != hipSuccess) {
+      a->n_lent = 0;
+      return 0;
+    }
+  }
+  return (int)n;
+}
+
+psi_status return_lent_slots(psi_arena* a) {
+  bool busy = false;
+  for (int i = 0; i < a->n_lent; ++i) busy |= a->lent[i].state != psi_page_slot::FREE;
+  a->n_lent = 0;
+  if (busy) return fail(PSI_E_STATE, "a lent page slot is still in use at the end of the operator");
+  return PSI_OK;
+}
+
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool pinned_check) {
   if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
   if (bytes > a->desc.page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
                                           " B > " + std::to_string(a->desc.page_bytes) + " B");
-  // the first free slot from the round-robin position on (a page held
-  // across many requests does not stall the others)
-  const int s = first_free_slot(a);
+  // a lent slot that needs no wait, else the first free slot from the
+  // round-robin position on (a page held across many requests does not
+  // stall the others)
+  // (a lent slot that is not ready comes last and then takes a host wait)
+  const int s = submit_slot(a);
   if (s < 0) return fail(PSI_E_PAGE_BUSY, "every page slot still has an unreleased request");
-  psi_page_slot& slot = a->slots[s];
+  const bool lent = s >= a->desc.n_pages;
+  psi_page_slot& slot = *slot_ptr(a, s);
   if (!a->dry && pinned_check) {
     psi_status st = check_pinned(host, "page slice");
     if (st) return st;
@@ -133,7 +214,14 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
       const int ci = a->next_copy;
       hipStream_t cs = ci ? a->copy1 : a->copy;
       a->next_copy = ci ^ 1;
-      if (slot.released_once) {
+      if (lent) {
+        const int li = s - a->desc.n_pages;
+        hipEvent_t w = a->lent_fresh[li] ? a->scratch_free : (slot.released_once ? slot.release : nullptr);
+        if (w && !event_done(w)) {
+          PSI_HIP(hipEventSynchronize(w));
+          a->stats.host_syncs++;
+        }
+      } else if (slot.released_once) {
         psi_status st = wait_release(a, slot);
         if (st) return st;
       }
@@ -157,7 +245,12 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
   slot.state = psi_page_slot::FILLING;
   a->stats.bytes_h2d += bytes;
   a->stats.page_copies++;
-  a->next_slot = (s + 1) % a->desc.n_pages;
+  if (lent) {
+    a->lent_fresh[s - a->desc.n_pages] = false;
+    a->stats.lent_page_copies++;
+  } else {
+    a->next_slot = (s + 1) % a->desc.n_pages;
+  }
   if (page_out) *page_out = s;
   return PSI_OK;
 }
@@ -227,8 +320,9 @@ psi_status bias_release(psi_arena* a, int s) {
 }
 
 psi_status page_acquire(psi_arena* a, int page) {
-  if (page < 0 || page >= a->desc.n_pages) return fail(PSI_E_INVALID, "bad page index");
-  psi_page_slot& slot = a->slots[page];
+  psi_page_slot* sp = slot_ptr(a, page);
+  if (!sp) return fail(PSI_E_INVALID, "bad page index");
+  psi_page_slot& slot = *sp;
   if (slot.state == psi_page_slot::FREE)
     return fail(PSI_E_STATE, "page " + std::to_string(page) + " has no outstanding request");
   if (slot.state == psi_page_slot::CONSUMING) return PSI_OK;
@@ -241,8 +335,9 @@ psi_status page_acquire(psi_arena* a, int page) {
 }
 
 psi_status page_release(psi_arena* a, int page) {
-  if (page < 0 || page >= a->desc.n_pages) return fail(PSI_E_INVALID, "bad page index");
-  psi_page_slot& slot = a->slots[page];
+  psi_page_slot* sp = slot_ptr(a, page);
+  if (!sp) return fail(PSI_E_INVALID, "bad page index");
+  psi_page_slot& slot = *sp;
   if (slot.state == psi_page_slot::FREE)
     return fail(PSI_E_STATE, "page " + std::to_string(page) + " released while free");
   if (slot.state == psi_page_slot::FILLING) {
@@ -378,6 +473,11 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
     }
     for (int i = 0; e == hipSuccess && i < 4; ++i)
       e = hipEventCreateWithFlags(&a->pipe_ev[i], hipEventDisableTiming);
+    for (int i = 0; e == hipSuccess && i < psi_arena::kMaxLent; ++i) {
+      e = hipEventCreateWithFlags(&a->lent[i].ready, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&a->lent[i].release, hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a->scratch_free, hipEventDisableTiming);
     if (e != hipSuccess) {
       psi_status r = hip_fail(e, "psi_arena_create");
       psi_arena_destroy(a);
@@ -411,6 +511,11 @@ psi_status psi_arena_destroy(psi_arena* a) {
     }
     for (hipEvent_t e : a->pipe_ev)
       if (e) (void)hipEventDestroy(e);
+    for (psi_page_slot& l : a->lent) {
+      if (l.ready) (void)hipEventDestroy(l.ready);
+      if (l.release) (void)hipEventDestroy(l.release);
+    }
+    if (a->scratch_free) (void)hipEventDestroy(a->scratch_free);
     if (a->copy) (void)hipStreamDestroy(a->copy);
     if (a->copy1) (void)hipStreamDestroy(a->copy1);
     if (a->base) {

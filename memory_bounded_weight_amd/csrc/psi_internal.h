@@ -142,6 +142,16 @@ struct psi_arena {
   int next_copy = 0;            // copy stream of the next page
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
+  // Page slots lent by the running operator from the whole pages of scratch
+  // above its own allocations (indices n_pages .. n_pages + n_lent - 1).
+  // A lent slot is filled only when no host wait is needed: on first use
+  // once `scratch_free` (the compute stream before the operator) has
+  // completed, later once its own release has.
+  static constexpr int kMaxLent = 4;
+  psi_page_slot lent[kMaxLent];
+  bool lent_fresh[kMaxLent] = {};
+  int n_lent = 0;
+  hipEvent_t scratch_free = nullptr;
   psi_page_slot bias_slots[2];  // same lifecycle as pages, one per operator, alternating
   int next_bias = 0;
   // scratch stack (offsets relative to layout.scratch_off)
@@ -171,8 +181,19 @@ namespace psi {
 void* scratch_alloc(psi_arena* a, size_t bytes, psi_status* st);
 void scratch_reset(psi_arena* a, size_t mark);
 
-// Page request (slice copy into the next round-robin page slot).
+// Page request (slice copy into a lent slot that is ready, else into the
+// next round-robin page slot).
 int first_free_slot(const psi_arena* a);  // -1 when every slot is taken
+// Lends the whole pages of scratch above scratch_top as page slots to the
+// running operator (none in a sync-copy arena); returns how many.  The
+// operator must not allocate scratch afterwards, and returns them with
+// return_lent_slots once every request is released.
+int lend_scratch_slots(psi_arena* a);
+psi_status return_lent_slots(psi_arena* a);
+// The slot the next page_submit_ex would fill (-1: none free), and the
+// device address of slot s (regular or lent).
+int submit_slot(psi_arena* a);
+void* slot_dev(psi_arena* a, int s);
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool check_pinned);
 psi_status page_acquire(psi_arena* a, int page);

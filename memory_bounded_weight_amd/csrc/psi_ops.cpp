@@ -90,7 +90,7 @@ class PageFeeder {
         ++submitted_;
         continue;
       }
-      if (first_free_slot(a_) < 0) break;
+      if (submit_slot(a_) < 0) break;
       int s = -1;
       psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false);
       if (st) return st;
@@ -110,7 +110,7 @@ class PageFeeder {
     if (i >= submitted_) return fail(PSI_E_STATE, "page request not submitted (slots exhausted)");
     st = page_acquire(a_, slot_[i]);
     if (st) return st;
-    *page = static_cast<const uint16_t*>(a_->dry ? nullptr : a_->slots[slot_[i]].dev);
+    *page = static_cast<const uint16_t*>(slot_dev(a_, slot_[i]));
     return PSI_OK;
   }
   psi_status give_back(size_t i) {
@@ -160,6 +160,22 @@ int attn_p_terms(unsigned flags) {
   if (flags & PSI_OP_BF16_SOFTMAX) return 1;
   return (flags & PSI_OP_ATTN_P2) ? 2 : 3;
 }
+
+// Lends the operator's idle scratch (the whole pages above its own
+// allocations) as page slots for its requests, and takes them back when
+// the operator returns; construct it after the last scratch allocation.
+// Those pages wait behind compute less often: a lent slot is filled only
+// when that needs no host wait.
+class LentSlots {
+ public:
+  explicit LentSlots(psi_arena* a) : a_(a) { lend_scratch_slots(a); }
+  ~LentSlots() { (void)return_lent_slots(a_); }
+  LentSlots(const LentSlots&) = delete;
+  LentSlots& operator=(const LentSlots&) = delete;
+
+ private:
+  psi_arena* a_;
+};
 
 GemmArgs gemm_args() {
   GemmArgs g{};
@@ -286,6 +302,7 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
   if ((st = bias.stage(a, &W, 1))) return st;
   std::vector<PageReq> reqs;
   matrix_requests(W, reqs);
+  LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* b = nullptr;
@@ -378,6 +395,7 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
   // once whatever the number of chunks ([PSI] sec. III-B page reuse).
   (void)token_chunks;
   const int rows_per = M;
+  LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t *ba = nullptr, *bb = nullptr;
@@ -482,6 +500,7 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
       reqs.insert(reqs.end(), ru.begin(), ru.end());
     }
   }
+  LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t *ba = nullptr, *bb = nullptr;
@@ -658,6 +677,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     if (!otiles) reqs.push_back(ro[g]);
   }
   if (otiles) reqs.insert(reqs.end(), ro.begin(), ro.end());
+  LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[4];
@@ -769,6 +789,7 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
     if (!otiles) reqs.push_back(ro[g]);
   }
   if (otiles) reqs.insert(reqs.end(), ro.begin(), ro.end());
+  LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[6];

@@ -487,3 +487,32 @@ def test_attention_output_tiles_plan_and_page_order_dry_run():
         assert e.value.status == psi.PSI_E_INVALID
     finally:
         psi.psi_arena_destroy(a)
+
+
+def test_scratch_lent_as_page_slots_dry_run():
+    """An operator lends the whole pages of scratch above its own allocations
+    as page slots for its requests: in the stack's 80 MiB arena (7 pages),
+    attention with output tiles (no arena scratch) lends two 8 MiB slots,
+    while the FFN, whose 16 MiB hidden tile leaves less than a page, lends
+    none; a sync-copy arena lends none.  Copies, launches and the scratch
+    high-water mark are unchanged."""
+    Wq, Wk, Wv, _ = cfg5_attn()
+    Wo_t = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 1024)
+    U, V = cfg5_ffn()
+    fake = 0x10000
+    for flags, lent_attn in ((psi.PSI_ARENA_DRY_RUN, True),
+                             (psi.PSI_ARENA_DRY_RUN | psi.PSI_ARENA_SYNC_COPY, False)):
+        a = psi.psi_arena_create(desc(80, 8, 7, 0, flags))
+        try:
+            psi.psi_attn_paged(a, fake, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, fake, fake,
+                               psi.PSI_OP_RESIDUAL)
+            s = psi.psi_arena_stats(a)
+            assert s.page_copies == 16 and s.kernel_launches == 20 and s.scratch_high_water == 0
+            assert (s.lent_page_copies > 0) == lent_attn
+            lent0 = s.lent_page_copies
+            psi.psi_ffn_paged(a, fake, 8192, 4096, U, V, 1, fake, fake, psi.PSI_OP_RESIDUAL)
+            s = psi.psi_arena_stats(a)
+            assert s.page_copies == 48 and s.lent_page_copies == lent0
+            assert s.scratch_high_water == 8192 * 1024 * 2
+        finally:
+            psi.psi_arena_destroy(a)

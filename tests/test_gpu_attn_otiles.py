@@ -130,3 +130,31 @@ def test_block_stack_output_tiles_match_ksplit(P):
         finally:
             P.psi_arena_destroy(ar)
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_lent_scratch_slots_keep_bits(P):
+    """Operators lend their idle scratch as extra page slots.  Two blocks
+    with output-tile attention (no arena scratch) and the FFN, with every
+    copy and launch delayed by a pseudo-random 0-63 us (PSI_ARENA_JITTER),
+    give the bits of the sync-copy transport control, which lends nothing;
+    pages did go through lent slots."""
+    M, d, heads, h, gw = 200, 256, 2, 1024, 128
+    x0 = synth.stack_input(78, M, d)
+    ws = [synth.block_weights(78, i, d, h) for i in range(2)]
+    bws = [P.block_weights(w, gw, 256, attn_out_tile=128) for w in ws]
+    outs, lent = [], []
+    for flags in (P.PSI_ARENA_SYNC_COPY, P.PSI_ARENA_JITTER):
+        ar = make_arena(4 * MiB, 128 * KiB, 3, flags=flags)
+        try:
+            x = dev(x0)
+            xt = torch.empty_like(x)
+            acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+            for bw in bws:
+                P.psi_block_paged(ar, x, xt, M, heads, 128, bw, 1, acc, None, 0)
+            P.psi_arena_sync(ar)
+            outs.append(host(x))
+            lent.append(P.psi_arena_stats(ar).lent_page_copies)
+        finally:
+            P.psi_arena_destroy(ar)
+    assert np.array_equal(outs[0], outs[1])
+    assert lent[0] == 0 and lent[1] > 0, lent
