@@ -357,11 +357,24 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x_dev, int M, int d, cons
 /* Paged attention sub-block ([PSI] sec. II-B eqs. (3)-(4)): per head group
  * g (heads_per_group = Wq->block / head_dim): Q_g = x Wq_g^T + bq_g,
  * K_g/V_g from ctx (cross-attention) or x (self), fp32 online-softmax
- * attention per head (unmasked, noncausal, dropout-free), then
- * ACC += O_g Wo[:, g]^T in group order, y = B(ACC + bo) (+ residual).
- *   Wq, Wk, Wv: [d, d] PSI_SPLIT_ROWS, block = heads_per_group*head_dim;
- *   Wo: [d, d] PSI_SPLIT_COLS with the same block.  head_dim is 128 or 64.
- *   ctx_dev nullable [Mc, d]; y_dev may alias x_dev. */
+ * attention per head (unmasked, noncausal, dropout-free), then the
+ * O-projection y = B(O Wo^T + bo) (+ residual), in one of two layouts of
+ * Wo with the same summation per output (same bits):
+ *   - Wo PSI_SPLIT_COLS with the head-group block: K-split over the groups,
+ *     ACC += O_g Wo[:, g]^T in group order with the fp32 ACC carried in
+ *     acc_dev (or scratch when it fits);
+ *   - Wo PSI_SPLIT_ROWS (output tiles of any block): every group's O is kept
+ *     in an [M, d] BF16 buffer and each tile y[:, o] is one GEMM over the
+ *     full K.  No fp32 accumulator exists: acc_dev (M x d x 4 bytes,
+ *     16-byte aligned) then serves as working memory, holding that buffer
+ *     and, behind it, K_g and V_g^T when they fit (else scratch); without
+ *     acc_dev the buffer takes scratch.  PSI_OP_STORE_ACC is refused.
+ *   Wq, Wk, Wv: [d, d] PSI_SPLIT_ROWS, block = heads_per_group*head_dim.
+ *   head_dim is 128 or 64.  ctx_dev nullable [Mc, d]; y_dev may alias x_dev.
+ * Errors: PSI_E_INVALID (shapes, blocks, PSI_OP_STORE_ACC without acc_dev
+ * or with output tiles), PSI_E_ALIGN (acc_dev holding the outputs not
+ * 16-byte aligned), PSI_E_SCRATCH_EXHAUSTED, PSI_E_PAGE_TOO_SMALL,
+ * PSI_E_NOT_PINNED. */
 psi_status psi_attn_paged(psi_arena* a, const uint16_t* x_dev, int M,
                           const uint16_t* ctx_dev, int Mc, int heads, int head_dim,
                           const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
@@ -402,8 +415,11 @@ typedef struct psi_qk_norm_rope {
  * Q/K projections and attention.  Because the row statistic spans every
  * head group, the Q and K projections of all groups are computed first
  * (pages Wq_g, Wk_g for g ascending), then normalised/rotated in place,
- * then per group V_g, attention and the O-projection (pages Wv_g, Wo_g).
- * Scratch: Q [M, d] and K [Mk, d] BF16, V_g^T, and ACC unless acc_dev.
+ * then per group V_g and attention (pages Wv_g), with the O-projection per
+ * group (Wo[:, g], column split) or over output tiles after every group
+ * (row split; the tiles read the Q buffer, which the attention overwrote
+ * with O).  Scratch: Q [M, d] and K [Mk, d] BF16, V_g^T, and, for the
+ * column split, ACC unless acc_dev.
  * nr == NULL (or nothing enabled in it) gives psi_attn_paged's bits.
  * Errors: as psi_attn_paged, plus PSI_E_INVALID for eps <= 0 with a gamma,
  * a bad norm_tile, a missing sin table, or NULL cos_k with Mk != M;
@@ -446,7 +462,9 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x_dev, int M, const uint
                           unsigned flags);
 
 /* One synthetic transformer block in place: x_tmp = x + Attn(x) (self),
- * then x = x_tmp + FFN(x_tmp), both with the residual write.  If `fence`
+ * then x = x_tmp + FFN(x_tmp), both with the residual write.  w->Wo may be
+ * split by columns or by rows (psi_attn_paged's two O-projection layouts);
+ * acc_dev serves both sub-blocks in turn.  If `fence`
  * is non-NULL, the FFN's output write first waits for every journal copy
  * enqueued so far (the journal's reads of x are previous consumers,
  * [PSI] sec. II-D). */
