@@ -199,7 +199,10 @@ const char* psi_version(void);
 /* [PSI] sec. II-A, Fig. 1: one device allocation of arena_bytes carved into
  * n_pages page slots, two bias slots (the bounded metadata term eps of
  * eq. (1)), the workspace and scratch.  Creates the copy stream and the
- * per-slot events.  *out is the caller's handle until psi_arena_destroy.
+ * per-slot events.  While an operator runs, the whole pages of scratch
+ * above its own allocations serve as extra page slots for its requests
+ * (psi_stats.lent_page_copies; not in a PSI_ARENA_SYNC_COPY arena).
+ * *out is the caller's handle until psi_arena_destroy.
  * Errors: PSI_E_INVALID, PSI_E_ARENA_TOO_SMALL, PSI_E_HIP. */
 psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out);
 
