@@ -259,6 +259,9 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
  * operator also commits its intermediate BF16 stage tensors under
  * key (step, block, branch = head group or hidden tile, role):
  *   PSI_ROLE_ATTN_O   attention output O_g of head group g, [M, group cols]
+ *                     (Wo split by columns); with Wo split into output
+ *                     tiles, every group's outputs at once, [M, d], under
+ *                     branch -1
  *   PSI_ROLE_FFN_H    FFN hidden tile H_J (after GELU), [M, tile]
  * and the compute stream waits for each copy before the scratch holding
  * the tensor is reused (probes cost time; they are a diagnostic).  Pass

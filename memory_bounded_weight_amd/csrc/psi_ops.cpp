@@ -713,6 +713,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
       return st;
   }
   if (otiles) {
+    if ((st = probe_commit(a, -1, PSI_ROLE_ATTN_O, Q, (size_t)M * dm * 2))) return st;
     const size_t r0 = (size_t)per * nG;
     const uint16_t* page;
     for (int o = 0; o < (int)ro.size(); ++o)

@@ -1,6 +1,8 @@
 """Parity at the full workload sizes, on sampled outputs the oracle computes
 one by one, in the launch configuration the benchmark times (80 MiB arena,
-8 MiB pages, 8-head groups, 1,024-channel FFN tiles).
+8 MiB pages, 8-head groups, 1,024-channel FFN tiles, the O-projection over
+output tiles with seven or eight pages), and in the paper's layout (two
+pages + 8 MiB workspace, K-split O-projection).
 
 Rows of an FFN are independent, so sampled rows of x go through the
 oracle directly.  Attention rows depend on every key; the paged operator's
@@ -40,12 +42,16 @@ def read_probe(P, j, role, branch, M, cols, step=0, block=0):
     return out
 
 
-def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0):
+def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0, otiles=False):
     """(a) head 0 on sampled rows against the oracle's own projections of
-    head 0; (b) output projection + residual on the journaled O."""
+    head 0; (b) output projection + residual on the journaled O (per head
+    group for the K-split, all groups at once for output tiles)."""
     M, d = x_in.shape
-    O = np.concatenate([read_probe(P, j, P.PSI_ROLE_ATTN_O, g, M, gw, step) for g in range(d // gw)],
-                       axis=1)
+    if otiles:
+        O = read_probe(P, j, P.PSI_ROLE_ATTN_O, -1, M, d, step)
+    else:
+        O = np.concatenate([read_probe(P, j, P.PSI_ROLE_ATTN_O, g, M, gw, step) for g in range(d // gw)],
+                           axis=1)
     src = x_in if ctx is None else ctx
     h0 = slice(0, 128)
     K0 = oracle.linear(src, np.ascontiguousarray(w["Wk"][h0]), w["bk"][h0].copy())
@@ -58,15 +64,18 @@ def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0):
     assert_bf16_close(y[rows], ref, what="output projection + residual")
 
 
-def test_fullsize_block_8192_tokens(P):
+@pytest.mark.parametrize("layout", ["tiles", "ksplit"])
+def test_fullsize_block_8192_tokens(P, layout):
     """One block of the 8-block stack at full size (8,192 tokens, d 4,096,
-    32 heads, FFN 16,384) in the benchmark's 80 MiB / 8 MiB arena."""
+    32 heads, FFN 16,384) in an 80 MiB arena of 8 MiB pages: the benchmark's
+    seven pages with output-tile O-projection, or the paper's two pages +
+    workspace with the K-split."""
     M, d, heads, hid = 8192, 4096, 32, 16384
+    otiles = layout == "tiles"
     w = synth.block_weights(0, 0, d, hid)
     x0 = synth.stack_input(0, M, d)
-    bw = P.block_weights(w, 1024, 1024)
-    s = torch.cuda.current_stream().cuda_stream
-    ar = make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
+    bw = P.block_weights(w, 1024, 1024, attn_out_tile=1024 if otiles else 0)
+    ar = make_arena(80 * MiB, 8 * MiB, 7, 0) if otiles else make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
     j = P.psi_journal_create(8 * MiB, 2, (4 + 16) * M * 1024 * 2 + MiB, 0)
     try:
         P.psi_arena_set_probe(ar, j, 0, 0)
@@ -78,7 +87,7 @@ def test_fullsize_block_8192_tokens(P):
         P.psi_journal_sync(j)
         y_attn, y = host(xt), host(x)
         rows = sample_rows(M, 12)
-        check_attention(P, j, x0, y_attn, w, heads, 1024, rows)
+        check_attention(P, j, x0, y_attn, w, heads, 1024, rows, otiles=otiles)
         # FFN on the GPU's own attention output (identical inputs), and its
         # first hidden tile from the stage probe
         xr = np.ascontiguousarray(y_attn[rows])
@@ -93,14 +102,16 @@ def test_fullsize_block_8192_tokens(P):
         P.psi_arena_destroy(ar)
 
 
-def test_fullsize_attention_self_and_cross(P):
+@pytest.mark.parametrize("layout", ["tiles", "ksplit"])
+def test_fullsize_attention_self_and_cross(P, layout):
     """Attention sub-blocks at full size: 6,144 tokens self-attention, then
     cross-attention to 1,024 conditioning tokens, 32 heads of 128, 8-head
-    groups, 80 MiB arena."""
+    groups, 80 MiB arena (eight pages with output tiles, as benchmarked; or
+    two pages + workspace with the K-split)."""
     M, Mc, d, heads = 6144, 1024, 4096, 32
+    otiles = layout == "tiles"
     c = synth.attn_case(0, M, Mc, d, cross=True)
-    s = torch.cuda.current_stream().cuda_stream
-    ar = make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
+    ar = make_arena(80 * MiB, 8 * MiB, 8, 0) if otiles else make_arena(80 * MiB, 8 * MiB, 2, 8 * MiB)
     j = P.psi_journal_create(8 * MiB, 2, 2 * 4 * M * 1024 * 2 + MiB, 0)
     try:
         x = dev(c["x"])
@@ -110,7 +121,8 @@ def test_fullsize_attention_self_and_cross(P):
         for part in ("self", "cross"):
             w = c[part]
             mats[part] = [P.pinned_matrix(w["W" + n], w["b" + n], P.PSI_SPLIT_ROWS, 1024) for n in "qkv"] + \
-                         [P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, 1024)]
+                         [P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_ROWS if otiles else P.PSI_SPLIT_COLS,
+                                          1024)]
         P.psi_arena_set_probe(ar, j, 0, 0)
         y1 = torch.empty_like(x)
         P.psi_attn_paged(ar, x, M, None, 0, heads, 128, *mats["self"], acc, y1, P.PSI_OP_RESIDUAL)
@@ -121,8 +133,8 @@ def test_fullsize_attention_self_and_cross(P):
         P.psi_journal_sync(j)
         rows = sample_rows(M, 12, seed=1)
         y1h, y2h = host(y1), host(y2)
-        check_attention(P, j, c["x"], y1h, c["self"], heads, 1024, rows, step=0)
-        check_attention(P, j, y1h, y2h, c["cross"], heads, 1024, rows, ctx=c["ctx"], step=1)
+        check_attention(P, j, c["x"], y1h, c["self"], heads, 1024, rows, step=0, otiles=otiles)
+        check_attention(P, j, y1h, y2h, c["cross"], heads, 1024, rows, ctx=c["ctx"], step=1, otiles=otiles)
     finally:
         P.psi_arena_set_probe(ar, None)
         P.psi_journal_destroy(j)
