@@ -6,11 +6,13 @@
 // reusable pages, a workspace and scratch.  [PSI] sec. II-D: a page has at
 // most one outstanding slice request; its lifecycle is free -> filling ->
 // ready -> consuming; copy completion permits consumption and completion of
-// the last consumer permits the next write.  Here the copy runs on a
-// library stream and records `ready`; consumers on the compute stream wait
-// on `ready`; release records `release` on the compute stream after every
-// enqueued use, and the next copy into the slot waits on it.  The host
-// never blocks to enforce this.
+// the last consumer permits the next write.  Here the copy runs on one of
+// two library streams and records `ready`; consumers on the compute stream
+// wait on `ready`; release records `release` on the compute stream after
+// every enqueued use, and the next copy into the slot is enqueued once the
+// host has seen `release` complete (a host wait when it has not: see
+// wait_release).  Inside an operator, whole pages of idle scratch serve as
+// extra (lent) slots, filled only when that needs no wait.
 #include <cstring>
 
 #include "psi_internal.h"

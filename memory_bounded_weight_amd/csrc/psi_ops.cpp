@@ -71,14 +71,14 @@ class OpBiases {
 };
 
 // Streams a list of page requests through the arena's slots: requests are
-// submitted as soon as their (round-robin) slot is free, so the copy of the
-// next pages overlaps the consumers of the current one; with two slots this
-// is the paper's two alternating pages ([PSI] sec. III-B weight prefetch).
-// Refilling a slot waits on the host for its last consumer (see
-// page_submit_ex); submitting only slots whose consumer had already
-// finished, to keep the host further ahead of the compute stream, started
-// each copy later after its slot's release and cost the copy-bound
-// workloads 2-6%.
+// submitted as soon as a slot is free (a lent slot that needs no wait, else
+// the round-robin slot), so the copy of the next pages overlaps the
+// consumers of the current one; with two slots this is the paper's two
+// alternating pages ([PSI] sec. III-B weight prefetch).  Refilling a slot
+// waits on the host for its last consumer (see page_submit_ex); submitting
+// only slots whose consumer had already finished, to keep the host further
+// ahead of the compute stream, started each copy later after its slot's
+// release and cost the copy-bound workloads 2-6%.
 class PageFeeder {
  public:
   PageFeeder(psi_arena* a, std::vector<PageReq> reqs) : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {}
