@@ -1,4 +1,6 @@
 """Helpers shared by the GPU tests: device buffers, comparisons."""
+import os
+
 import numpy as np
 import torch
 
@@ -46,5 +48,11 @@ def stream_handle():
 
 
 def make_arena(arena_bytes, page_bytes, n_pages=2, workspace=0, flags=0):
+    """A test arena on torch's current stream.  PSI_TEST_JITTER=1 in the
+    environment adds PSI_ARENA_JITTER to every arena (the whole suite then
+    runs with pseudo-random delays before each copy and launch; results
+    must not change)."""
+    if os.environ.get("PSI_TEST_JITTER") == "1" and not flags & psi.PSI_ARENA_SYNC_COPY:
+        flags |= psi.PSI_ARENA_JITTER
     d = psi.arena_desc(arena_bytes, page_bytes, n_pages, workspace, 0, stream_handle(), flags)
     return psi.psi_arena_create(d)

@@ -11,6 +11,8 @@ bitwise identical.
 [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
 Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -207,7 +209,9 @@ def test_transport_jitter_keeps_bits(P, n_pages):
     for r, r2, g_ in zip(ref, ref2, got):
         assert np.array_equal(r, g_) and np.array_equal(r2, g_)
     # the delays are real: ~60 launches and copies at 31.5 us on average
-    assert t_j > min(t_a, t_b) + 0.5, (t_j, t_a, t_b)
+    # (unless every arena of the suite already runs with them)
+    if os.environ.get("PSI_TEST_JITTER") != "1":
+        assert t_j > min(t_a, t_b) + 0.5, (t_j, t_a, t_b)
 
 
 def test_launch_timing_sample(P):
