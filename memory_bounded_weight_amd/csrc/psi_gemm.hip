@@ -34,6 +34,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 
@@ -44,6 +46,22 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
   w += 0x7FFFu + ((w >> 16) & 1u);
   return (uint16_t)(w >> 16);
 }
+
+// Round a pair to bfloat16 with the packed conversion instruction (a in
+// the low half).  It rounds to nearest with ties to even and gives f2bf's
+// bits for every input but NaN, whose sign and payload it keeps; a value
+// that is stored canonicalises NaN first (nan_canon), so NaN still gives
+// 0x7FC0.  An intermediate rounding needs no canonical NaN: only NaN-ness
+// reaches the stored value, and both conversions keep it.
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float nan_canon(float v) {
+  return __uint_as_float(v != v ? 0x7FC00000u : __float_as_uint(v));
+}
+__device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 // tanh-GELU, phi(v) = v/2 (1 + tanh(z)), z = sqrt(2/pi) (v + 0.044715 v^3),
 // through 1 + tanh(z) = 2 / (1 + e^(-2z)) = 2 e^(2z) / (1 + e^(2z)); the
@@ -115,6 +133,109 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN
   }
 }
 
+// Wave blocks wholly inside the output, on the epilogues of the hot path.
+// A row's address is the same for every lane of the wave (a scalar base)
+// plus a per-lane 32-bit byte offset (rows 4*half, column l32) and the
+// tile's column offset as an immediate, so an element costs no address
+// arithmetic and no bounds test; rows 2k and 2k+1 of a column are rounded
+// by one conversion.  The arithmetic is epilogue()'s, in the same order,
+// so both give the same bits.  Row offsets in bytes must fit 32 bits:
+// leading dimensions below 2^26 (checked by finish()).
+__device__ __forceinline__ int block_row(int mb, int i, int r) { return mb + i * 32 + 8 * (r / 4) + (r % 4); }
+
+// BF16 output = B(acc + bias along columns), then optionally GELU and a
+// residual; no fp32 store.
+template <int TM, int TN, bool GELU, bool RESID>
+__device__ __forceinline__ void epilogue_full(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
+                                              int l32) {
+  const uint32_t lane_out = (uint32_t)(4 * half * (int)p.ldo + l32) * 2u;
+  const uint32_t lane_res = RESID ? (uint32_t)(4 * half * (int)p.ldr + l32) * 2u : 0u;
+  float bn[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bn[j] = bf2f(p.bias[nb + j * 32 + l32]);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    // the residual of the 32-row group, read before its first store (the
+    // output may alias it; each element is read by the lane that writes it)
+    float rv[TN][16];
+    if (RESID) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const char* rb = (const char*)(p.resid + (long)block_row(mb, i, r) * p.ldr + nb) + lane_res;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) rv[j][r] = bf2f(*(const uint16_t*)(rb + j * 64));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      char* o0 = (char*)(p.out + (long)block_row(mb, i, r) * p.ldo + nb) + lane_out;
+      char* o1 = (char*)(p.out + (long)block_row(mb, i, r + 1) * p.ldo + nb) + lane_out;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const float t0 = acc[i][j][r] + bn[j], t1 = acc[i][j][r + 1] + bn[j];
+        uint32_t y;
+        if (!GELU && !RESID) {
+          y = cvt_pair(nan_canon(t0), nan_canon(t1));
+        } else {
+          y = cvt_pair(t0, t1);
+          if (GELU) {
+            const float g0 = gelu_tanh(lo_f(y)), g1 = gelu_tanh(hi_f(y));
+            y = RESID ? cvt_pair(g0, g1) : cvt_pair(nan_canon(g0), nan_canon(g1));
+          }
+          if (RESID) y = cvt_pair(nan_canon(rv[j][r] + lo_f(y)), nan_canon(rv[j][r + 1] + hi_f(y)));
+        }
+        *(uint16_t*)(o0 + j * 64) = (uint16_t)y;
+        *(uint16_t*)(o1 + j * 64) = (uint16_t)(y >> 16);
+      }
+    }
+  }
+}
+
+// fp32 accumulator store only (a step of a carried K-split chain).
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc_full(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
+                                               int l32) {
+  const uint32_t lane = (uint32_t)(4 * half * (int)p.ld_acc_out + l32) * 4u;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      char* ob = (char*)(p.acc_out + (long)block_row(mb, i, r) * p.ld_acc_out + nb) + lane;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) *(float*)(ob + j * 128) = acc[i][j][r];
+    }
+}
+
+__device__ __forceinline__ bool ld_ok(long ld) { return ld >= 0 && ld < (1L << 26); }
+
+// The epilogue of a wave block: the whole-block paths above where they
+// apply, epilogue() otherwise (ragged blocks, fp32 store beside the BF16
+// output, bias along rows, the baseline bias rounding, no bias).
+template <int TM, int TN>
+__device__ __forceinline__ void finish(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
+                                       int l32) {
+  mb = __builtin_amdgcn_readfirstlane(mb);
+  nb = __builtin_amdgcn_readfirstlane(nb);
+  const bool full = mb + TM * 32 <= p.M && nb + TN * 32 <= p.N;
+  if (full && !p.out && p.acc_out && ld_ok(p.ld_acc_out)) {
+    store_acc_full<TM, TN>(p, acc, mb, nb, half, l32);
+    return;
+  }
+  if (full && p.out && !p.acc_out && p.bias && !p.bias_on_m && !p.baseline_bias && ld_ok(p.ldo) &&
+      (!p.resid || ld_ok(p.ldr))) {
+    const bool gelu = p.epi == EPI_GELU;
+    if (p.resid) {
+      if (gelu) epilogue_full<TM, TN, true, true>(p, acc, mb, nb, half, l32);
+      else epilogue_full<TM, TN, false, true>(p, acc, mb, nb, half, l32);
+    } else {
+      if (gelu) epilogue_full<TM, TN, true, false>(p, acc, mb, nb, half, l32);
+      else epilogue_full<TM, TN, false, false>(p, acc, mb, nb, half, l32);
+    }
+    return;
+  }
+  epilogue<TM, TN>(p, acc, mb, nb, half, l32);
+}
+
 // Accumulators start from acc_in (carried K-split chain) or zero.
 template <int TM, int TN>
 __device__ __forceinline__ void init_acc(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
@@ -126,6 +247,21 @@ __device__ __forceinline__ void init_acc(const GemmArgs& p, f32x16 (&acc)[TM][TN
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (!p.acc_in) return;
+  // whole block inside the output: scalar row bases, as in epilogue_full
+  mb = __builtin_amdgcn_readfirstlane(mb);
+  nb = __builtin_amdgcn_readfirstlane(nb);
+  if (mb + TM * 32 <= p.M && nb + TN * 32 <= p.N && p.ld_acc_in >= 0 && p.ld_acc_in < (1L << 26)) {
+    const uint32_t lane = (uint32_t)(4 * half * (int)p.ld_acc_in + l32) * 4u;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const char* ib = (const char*)(p.acc_in + (long)(mb + i * 32 + 8 * (r / 4) + (r % 4)) * p.ld_acc_in + nb) + lane;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j][r] = *(const float*)(ib + j * 128);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -178,8 +314,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, in
 // last k16 step of tile kt each wave waits until its own loads of stage kt+1
 // have landed (vmcnt) and the workgroup meets at a barrier, after which the
 // first fragments of tile kt+1 are read while the last MFMAs of kt run.
+//
+// Launch bound: at least two waves per SIMD (at most 256 registers per
+// lane), so that two 4-wave workgroups share a CU where LDS allows it.
 template <int BM, int BN, int WGM, int WGN, int S>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, int tiles_m, int tiles_n, int gm) {
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_kernel_dma(GemmArgs p, int tiles_m, int tiles_n, int gm) {
   constexpr int BK = 64, NW = WGM * WGN;
   constexpr int CPR = BK / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;        // rows per load instruction
@@ -282,7 +421,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, in
     }
   }
   __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0));
-  epilogue<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
+  finish<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,7 +430,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel_dma(GemmArgs p, in
 // loaded into registers while the current one is multiplied, K tail zeroed.
 constexpr int kRegThreads = 256;
 
-__global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int tiles_m, int tiles_n, int gm) {
+__global__ __launch_bounds__(kRegThreads, 2) void gemm_kernel_reg(GemmArgs p, int tiles_m, int tiles_n, int gm) {
   constexpr int BM = 128, BN = 128, BK = 64, LDS = BK + 8, CPR = BK / 8;
   constexpr int A_PER_T = BM * BK / 8 / kRegThreads, B_PER_T = BN * BK / 8 / kRegThreads;
   constexpr int WM = 64, WN = 64, TM = 2, TN = 2, STAGE = (BM + BN) * LDS;
@@ -366,7 +505,7 @@ __global__ __launch_bounds__(kRegThreads) void gemm_kernel_reg(GemmArgs p, int t
     if (kt + 1 < nk) store_lds(cur ^ 1);
     __syncthreads();
   }
-  epilogue<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
+  finish<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 }
 
 // Group height of the tile order: with C tiles of one XCD in flight, a
