@@ -143,18 +143,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, f32x16 (&acc)[TM][TN
 // leading dimensions below 2^26 (checked by finish()).
 __device__ __forceinline__ int block_row(int mb, int i, int r) { return mb + i * 32 + 8 * (r / 4) + (r % 4); }
 
-// BF16 output = B(acc + bias along columns), then optionally GELU and a
-// residual; no fp32 store.
-template <int TM, int TN, bool GELU, bool RESID>
+// BF16 output = B(acc + bias), then optionally GELU and a residual; no
+// fp32 store.  The bias runs along columns, or along rows (BIAS_M: the
+// transposed V projection).
+template <int TM, int TN, bool GELU, bool RESID, bool BIAS_M>
 __device__ __forceinline__ void epilogue_full(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
                                               int l32) {
   const uint32_t lane_out = (uint32_t)(4 * half * (int)p.ldo + l32) * 2u;
   const uint32_t lane_res = RESID ? (uint32_t)(4 * half * (int)p.ldr + l32) * 2u : 0u;
   float bn[TN];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) bn[j] = bf2f(p.bias[nb + j * 32 + l32]);
+  for (int j = 0; j < TN; ++j) bn[j] = BIAS_M ? 0.0f : bf2f(p.bias[nb + j * 32 + l32]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    float bm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bm[r] = BIAS_M ? bf2f(p.bias[block_row(mb, i, r) + 4 * half]) : 0.0f;
     // the residual of the 32-row group, read before its first store (the
     // output may alias it; each element is read by the lane that writes it)
     float rv[TN][16];
@@ -172,7 +176,8 @@ __device__ __forceinline__ void epilogue_full(const GemmArgs& p, f32x16 (&acc)[T
       char* o1 = (char*)(p.out + (long)block_row(mb, i, r + 1) * p.ldo + nb) + lane_out;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const float t0 = acc[i][j][r] + bn[j], t1 = acc[i][j][r + 1] + bn[j];
+        const float t0 = acc[i][j][r] + (BIAS_M ? bm[r] : bn[j]);
+        const float t1 = acc[i][j][r + 1] + (BIAS_M ? bm[r + 1] : bn[j]);
         uint32_t y;
         if (!GELU && !RESID) {
           y = cvt_pair(nan_canon(t0), nan_canon(t1));
@@ -210,7 +215,8 @@ __device__ __forceinline__ bool ld_ok(long ld) { return ld >= 0 && ld < (1L << 2
 
 // The epilogue of a wave block: the whole-block paths above where they
 // apply, epilogue() otherwise (ragged blocks, fp32 store beside the BF16
-// output, bias along rows, the baseline bias rounding, no bias).
+// output, the baseline bias rounding, no bias, a bias along rows with GELU
+// or a residual).
 template <int TM, int TN>
 __device__ __forceinline__ void finish(const GemmArgs& p, f32x16 (&acc)[TM][TN], int mb, int nb, int half,
                                        int l32) {
@@ -221,17 +227,22 @@ __device__ __forceinline__ void finish(const GemmArgs& p, f32x16 (&acc)[TM][TN],
     store_acc_full<TM, TN>(p, acc, mb, nb, half, l32);
     return;
   }
-  if (full && p.out && !p.acc_out && p.bias && !p.bias_on_m && !p.baseline_bias && ld_ok(p.ldo) &&
-      (!p.resid || ld_ok(p.ldr))) {
+  if (full && p.out && !p.acc_out && p.bias && !p.baseline_bias && ld_ok(p.ldo) && (!p.resid || ld_ok(p.ldr))) {
     const bool gelu = p.epi == EPI_GELU;
-    if (p.resid) {
-      if (gelu) epilogue_full<TM, TN, true, true>(p, acc, mb, nb, half, l32);
-      else epilogue_full<TM, TN, false, true>(p, acc, mb, nb, half, l32);
+    if (p.bias_on_m) {
+      if (!gelu && !p.resid) {
+        epilogue_full<TM, TN, false, false, true>(p, acc, mb, nb, half, l32);
+        return;
+      }
+    } else if (p.resid) {
+      if (gelu) epilogue_full<TM, TN, true, true, false>(p, acc, mb, nb, half, l32);
+      else epilogue_full<TM, TN, false, true, false>(p, acc, mb, nb, half, l32);
+      return;
     } else {
-      if (gelu) epilogue_full<TM, TN, true, false>(p, acc, mb, nb, half, l32);
-      else epilogue_full<TM, TN, false, false>(p, acc, mb, nb, half, l32);
+      if (gelu) epilogue_full<TM, TN, true, false, false>(p, acc, mb, nb, half, l32);
+      else epilogue_full<TM, TN, false, false, false>(p, acc, mb, nb, half, l32);
+      return;
     }
-    return;
   }
   epilogue<TM, TN>(p, acc, mb, nb, half, l32);
 }
@@ -392,6 +403,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_kernel_dma(GemmArgs p,
   f32x16 acc[TM][TN];
   init_acc<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, half, l32);
 
+  // k16 step of tile kt after whose MFMAs stage kt+S-1 is issued; always
+  // before the wait for stage kt+1 in the last step, so the vmcnt counts
+  // hold.  Measured on MI355X: one step in is 1.5% faster with 3 stages and
+  // 3-7% slower with 4.
+  constexpr int kIssueStep = S == 3 ? 1 : 0;
+  static_assert(kIssueStep < KS - 1, "stage issue must precede the last step's wait");
   const int nk = p.K / BK;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_kernel_dma(GemmArgs p,
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-      if (ks == 0 && kt + S - 1 < nk) issue(kt + S - 1);
+      if (ks == kIssueStep && kt + S - 1 < nk) issue(kt + S - 1);
     }
   }
   __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0));
