@@ -448,3 +448,41 @@ def test_device_timeline_structure(P):
         assert np.array_equal(host(y), run_ffn(P, c, 256, chunks=2))
     finally:
         P.psi_arena_destroy(ar)
+
+
+def test_zero_tokens_enqueue_nothing(P):
+    """M = 0 on a live arena: every operator returns PSI_OK without a kernel
+    launch or a page copy, and the output buffers keep their bytes;
+    cross-attention over zero keys is an argument error, raised before
+    anything is enqueued."""
+    rng = np.random.default_rng(12)
+    d, h, heads = 256, 1024, 2
+    w = synth.block_weights(12, 0, d, h)
+    a = make_arena(16 * MiB, 512 * KiB, 2)
+    try:
+        x = dev(synth.normal_bf16(rng, (8, d), 1.0))
+        y = dev(synth.normal_bf16(rng, (8, d), 1.0))
+        y0 = host(y).copy()
+        xt = empty_bf16(8, d)
+        acc = torch.zeros(8, d, dtype=torch.float32, device="cuda")
+        Wq = P.pinned_matrix(w["Wq"], w["bq"], P.PSI_SPLIT_ROWS, 128)
+        Wk = P.pinned_matrix(w["Wk"], w["bk"], P.PSI_SPLIT_ROWS, 128)
+        Wv = P.pinned_matrix(w["Wv"], w["bv"], P.PSI_SPLIT_ROWS, 128)
+        Wo = P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, 128)
+        U = P.pinned_matrix(w["U"], w["a"], P.PSI_SPLIT_ROWS, 256)
+        V = P.pinned_matrix(w["V"], w["b"], P.PSI_SPLIT_COLS, 256)
+        P.psi_linear_paged(a, x, 0, d, Wq, acc, y, P.PSI_OP_RESIDUAL)
+        P.psi_ffn_paged(a, x, 0, d, U, V, 1, acc, y, P.PSI_OP_RESIDUAL)
+        P.psi_attn_paged(a, x, 0, None, 0, heads, 128, Wq, Wk, Wv, Wo, acc, y, P.PSI_OP_RESIDUAL)
+        P.psi_attn_paged(a, x, 0, x, 1, heads, 128, Wq, Wk, Wv, Wo, acc, y, P.PSI_OP_RESIDUAL)
+        with pytest.raises(P.PsiError) as e:  # cross-attention over no key is refused
+            P.psi_attn_paged(a, x, 4, x, 0, heads, 128, Wq, Wk, Wv, Wo, acc, y, P.PSI_OP_RESIDUAL)
+        assert e.value.status == P.PSI_E_INVALID
+        P.psi_block_paged(a, y, xt, 0, heads, 128, P.block_weights(w, 128, 256), 1, acc, None, 0)
+        P.psi_arena_sync(a)
+        s = P.psi_arena_stats(a)
+        assert s.kernel_launches == 0 and s.page_copies == 0
+        assert np.array_equal(host(y), y0)
+        assert torch.count_nonzero(acc).item() == 0
+    finally:
+        P.psi_arena_destroy(a)
