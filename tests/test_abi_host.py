@@ -129,7 +129,7 @@ def cfg5_ffn(tile=1024):
 def test_capacity_outcomes_like_table_v(arena, page, expect):
     """[PSI] Table V lists six arena/page capacities for one block with tiles
     held fixed: 48/8 and 64/8 exhaust scratch, 80/8, 96/8, 96/16 complete,
-    80/4 fails because a weight tile exceeds the page.  With this build's
+    80/4 fails because a weight tile exceeds the page.  With the stack's
     tiles (8-head groups, 1,024-channel FFN tiles, 8,192 tokens, 8 MiB
     workspace) the same six settings give the same outcome pattern."""
     d = desc(arena, page, 2, 8, 0)
