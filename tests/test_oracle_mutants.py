@@ -64,6 +64,20 @@ EXT_MUTANTS = {
 }
 
 
+# Mistakes in the residual write y = B(f(x) + f(Y)).
+RESIDUAL_PINS = "residual"
+_RES = "x[i] = orc_bf16_from_float(orc_f(x[i]) + orc_f(y[i]));"
+RESIDUAL_MUTANTS = {
+    "residual_wrong_operand": (_RES, "x[i] = orc_bf16_from_float(orc_f(y[i]) + orc_f(y[i]));"),
+    "residual_subtracts": (_RES, "x[i] = orc_bf16_from_float(orc_f(x[i]) - orc_f(y[i]));"),
+    "residual_truncates": (_RES, "{ float s_ = orc_f(x[i]) + orc_f(y[i]); uint32_t w_; "
+                                 "memcpy(&w_, &s_, sizeof w_); x[i] = (uint16_t)(w_ >> 16); }"),
+    "residual_drops_sublayer": (_RES, "x[i] = x[i];"),
+    "residual_ties_away": (_RES, "{ float s_ = orc_f(x[i]) + orc_f(y[i]); uint32_t w_; "
+                                 "memcpy(&w_, &s_, sizeof w_); x[i] = (uint16_t)((w_ + 0x8000u) >> 16); }"),
+}
+
+
 def _run_mutant(old, new, tmp_path, select=None):
     src = open(SRC).read()
     assert src.count(old) >= 1, "mutation pattern not found"
@@ -103,4 +117,11 @@ def test_pins_reject_mutant(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins accepted mutant {name}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(RESIDUAL_MUTANTS))
+def test_pins_reject_residual_mutant(name, tmp_path):
+    old, new = RESIDUAL_MUTANTS[name]
+    r = _run_mutant(old, new, tmp_path, RESIDUAL_PINS)
     assert r.returncode != 0, f"pins accepted mutant {name}:\n{r.stdout[-2000:]}"

@@ -498,6 +498,57 @@ def test_block_is_composition_of_sublayers():
     assert np.array_equal(y, y2)
 
 
+# ------------------------------------------------------------- residual
+
+def test_residual_is_sum_rounded_once():
+    """The residual write y = B(f(x) + f(Y)) (reading R7: the sub-block
+    output is a declared BF16 value, then the sum is rounded once, [PSI]
+    sec. III-A).  Every output equals the exact rational sum of its two
+    BF16 operands rounded to the nearest BF16 value, ties to even, on random
+    pairs, pairs with a large exponent gap, cancellations and hand-built
+    ties; and the special cases: x + 0 = x, x + (-x) = +0, commutativity."""
+    rng = np.random.default_rng(31)
+    n = 4000
+    x = synth.normal_bf16(rng, (n,), 1.0)
+    y = synth.normal_bf16(rng, (n,), 1.0)
+    # exponent gaps up to 2^30: the smaller operand falls below every BF16
+    # half-ulp of the larger one, or just touches it
+    scale = synth.f32_to_bf16_bits(np.float32(2.0) ** rng.integers(-30, 31, size=n).astype(np.float32))
+    y = synth.f32_to_bf16_bits(f(y) * f(scale))
+    # cancellations: y = -x nudged by a few BF16 ulps
+    k = n // 8
+    y[:k] = (x[:k] ^ 0x8000) + rng.integers(-3, 4, size=k).astype(np.uint16)
+    # ties: x = 1 + m 2^-7, y = 2^-8 puts x + y on a BF16 midpoint
+    m = np.arange(64, dtype=np.float32)
+    xt = synth.f32_to_bf16_bits(1.0 + m * 2.0 ** -7)
+    yt = synth.f32_to_bf16_bits(np.full(64, 2.0 ** -8, np.float32))
+    x = np.concatenate([x, xt])
+    y = np.concatenate([y, yt])
+    got = oracle.residual(x, y)
+    exact = [exact_bf16_round(frac_of_bits(a) + frac_of_bits(b)) for a, b in zip(x, y)]
+    assert [frac_of_bits(g) for g in got] == exact
+    # the midpoint cases round to the even neighbour: up for odd m, down for even m
+    tie = f(got[-64:]).astype(np.float64)
+    assert np.array_equal(tie, 1.0 + (m + (m % 2)) * 2.0 ** -7)
+    assert np.array_equal(oracle.residual(x, np.zeros_like(x)), np.where(x == 0x8000, 0, x).astype(np.uint16))
+    cancel = oracle.residual(x, x ^ 0x8000)
+    assert np.all(cancel == 0)  # exactly +0 under round-to-nearest
+    assert np.array_equal(got, oracle.residual(y, x))
+
+
+def test_residual_vs_library_bf16_add():
+    """Library cross-check: torch's BF16 tensor addition (widen, add in
+    fp32, round to nearest even) gives the oracle's residual bits on a
+    full-size row block of the block-output distribution."""
+    rng = np.random.default_rng(32)
+    x = synth.normal_bf16(rng, (64, 4096), 1.0)
+    y = synth.normal_bf16(rng, (64, 4096), 0.3)
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    ty = torch.from_numpy(y.view(np.int16)).view(torch.bfloat16)
+    ref = (tx + ty).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.residual(x, y), ref)
+
+
 # --------------------------------------------- RMS normalisation and RoPE
 
 def _bits(vals) -> np.ndarray:
