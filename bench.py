@@ -117,9 +117,8 @@ def build_workload(args, torch, psi, synth):
         log(f"bench: generated and pinned {nblk} blocks in {time.time() - t0:.1f}s")
         x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
         x = torch.empty_like(x0)
-        xt = torch.empty_like(x0)
         acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
-        live += [x0, x, xt, acc]
+        live += [x0, x, acc]
         journal = None
         if not args.no_journal:
             store = (args.steps + args.warmup) * nblk * M * d * 2
@@ -136,7 +135,8 @@ def build_workload(args, torch, psi, synth):
             x.copy_(x0)
             s = state["step"]
             for b in range(nblk):
-                psi.psi_block_paged(arena, x, xt, M, heads, 128, blocks[b], 1, acc, journal, 0)
+                psi.psi_block_paged(arena, x, None, M, heads, 128, blocks[b], args.token_chunks, acc,
+                                    journal, 0)
                 if journal:
                     psi.psi_journal_commit(journal, psi.key(s, b, 0, 0), x, M * d * 2, stream)
             state["step"] += 1
@@ -147,7 +147,8 @@ def build_workload(args, torch, psi, synth):
                             "tokens": M, "d_model": d, "heads": heads, "head_dim": 128,
                             "ffn_hidden": hid, "blocks": nblk, "arena_MiB": 80, "page_MiB": 8,
                             "pages": args.pages, "workspace_MiB": ws // MiB, "head_group": 8,
-                            "ffn_tile": 1024, "o_projection": "output tiles" if otiles else "K-split",
+                            "ffn_tile": 1024, "token_chunks": args.token_chunks,
+                            "o_projection": "output tiles" if otiles else "K-split",
                             "journal": not args.no_journal, "resident_weights": args.resident})
     if args.workload in ("ffn2048", "ffn4096"):
         if args.workload == "ffn2048":
@@ -539,6 +540,9 @@ def main():
     ap.add_argument("--pages", type=int, default=None,
                     help="page slots in the 80 MiB stack arena (default 7 with output-tile "
                          "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
+    ap.add_argument("--token-chunks", type=int, default=1,
+                    help="stack: token chunks of each FFN (each page serves every chunk; the hidden "
+                         "tile holds one chunk's rows)")
     ap.add_argument("--o-proj", choices=("tiles", "ksplit"), default="tiles",
                     help="stack, attn4096, audio8: attention O-projection over output tiles of Wo rows "
                          "from every head "

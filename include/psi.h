@@ -262,7 +262,9 @@ psi_status psi_arena_device_base(psi_arena* a, void** base_out, size_t* bytes_ou
  *                     (Wo split by columns); with Wo split into output
  *                     tiles, every group's outputs at once, [M, d], under
  *                     branch -1
- *   PSI_ROLE_FFN_H    FFN hidden tile H_J (after GELU), [M, tile]
+ *   PSI_ROLE_FFN_H    FFN hidden tile H_J (after GELU), [M, tile]; with
+ *                     token_chunks > 1, chunk c's rows under branch
+ *                     J * token_chunks + c
  * and the compute stream waits for each copy before the scratch holding
  * the tensor is reused (probes cost time; they are a diagnostic).  Pass
  * NULL to detach.  Errors: PSI_E_INVALID. */
@@ -304,9 +306,11 @@ psi_status psi_page_release(psi_arena* a, int page);
  *      PSI_SPLIT_COLS -> K-split, fp32 accumulator carried in page order in
  *      acc_dev (or arena scratch when acc_dev is NULL and it fits), bias
  *      added once after the last page.
- *   acc_dev nullable [M, N] fp32; y_dev [M, N] bf16 (N = W->rows).
+ *   acc_dev nullable [M, N] fp32; y_dev [M, N] bf16 (N = W->rows).  y must
+ *   not overlap x: every page launch reads x while earlier launches have
+ *   written y (PSI_E_INVALID otherwise).
  *   flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL (y = B(x + ...), needs
- *   K == N; y may alias x), PSI_OP_STORE_ACC. */
+ *   K == N), PSI_OP_STORE_ACC. */
 psi_status psi_linear_paged(psi_arena* a, const uint16_t* x_dev, int M, int K,
                             const psi_matrix* W, float* acc_dev, uint16_t* y_dev,
                             unsigned flags);
@@ -316,12 +320,21 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x_dev, int M, int K,
  * B(phi(.)), output B(ACC + b).
  *   U: [h, d] PSI_SPLIT_ROWS with block t_h (hidden tile J); bias a [h].
  *   V: [d, h] PSI_SPLIT_COLS with the same block t_h; bias b [d].
- *   Each U_J page, then each V_J page, serves all token_chunks chunks of x
- *   before release (page reuse across token chunks); the hidden tile H_J
- *   holds every token and lives in arena scratch, so all chunks of a page
- *   go into one launch (per row the same arithmetic); the fp32 accumulator
- *   lives in acc_dev or scratch.
- *   y_dev may alias x_dev (with PSI_OP_RESIDUAL: y = B(x + F(x))). */
+ *   token_chunks >= 1: x is cut into contiguous chunks of ceil(M/chunks)
+ *   rows.  With one chunk every page is one launch over all tokens.  With
+ *   several, U_J and V_J are held together (two page slots) while every
+ *   chunk runs its up-projection into H_J and its carried down-projection,
+ *   so each page is streamed once and serves all chunks (page reuse across
+ *   token chunks); H_J [ceil(M/chunks), t_h] BF16 lives in arena scratch,
+ *   so the scratch bound does not grow with M.  Rows are independent: the
+ *   result is bitwise the same for every chunk count.
+ *   The fp32 accumulator [M, d] lives in acc_dev or scratch.
+ *   y_dev may be x_dev itself (with PSI_OP_RESIDUAL: y = B(x + F(x))) or
+ *   must not overlap it.
+ * Errors: PSI_E_INVALID (shapes, token_chunks < 1, several chunks in a
+ * one-slot arena with streamed weights, y partly overlapping x),
+ * PSI_E_SCRATCH_EXHAUSTED (one chunk's H_J, plus the accumulator without
+ * acc_dev, exceeds the scratch), PSI_E_PAGE_TOO_SMALL, PSI_E_NOT_PINNED. */
 psi_status psi_ffn_paged(psi_arena* a, const uint16_t* x_dev, int M, int d,
                          const psi_matrix* U, const psi_matrix* V, int token_chunks,
                          float* acc_dev, uint16_t* y_dev, unsigned flags);
@@ -468,12 +481,14 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x_dev, int M, const uint
                           unsigned flags);
 
 /* One synthetic transformer block in place: x_tmp = x + Attn(x) (self),
- * then x = x_tmp + FFN(x_tmp), both with the residual write.  w->Wo may be
- * split by columns or by rows (psi_attn_paged's two O-projection layouts);
- * acc_dev serves both sub-blocks in turn.  If `fence`
- * is non-NULL, the FFN's output write first waits for every journal copy
- * enqueued so far (the journal's reads of x are previous consumers,
- * [PSI] sec. II-D). */
+ * then x = x_tmp + FFN(x_tmp), both with the residual write.  x_tmp_dev
+ * NULL (or x_dev) runs both sub-blocks in place on x with the same bits, so
+ * x is the only [M, d] BF16 live state; otherwise x_tmp must not overlap x.
+ * w->Wo may be split by columns or by rows (psi_attn_paged's two
+ * O-projection layouts); acc_dev serves both sub-blocks in turn;
+ * token_chunks as psi_ffn_paged.  If `fence` is non-NULL, the first launch
+ * that writes x first waits for every journal copy enqueued so far (the
+ * journal's reads of x are previous consumers, [PSI] sec. II-D). */
 typedef struct psi_block_weights {
   psi_matrix Wq, Wk, Wv, Wo; /* attention projections */
   psi_matrix U, V;           /* FFN */

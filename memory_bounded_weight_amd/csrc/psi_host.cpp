@@ -205,9 +205,15 @@ psi_status psi_ffn_plan(const psi_arena_desc* d, int M, int dmodel, const psi_ma
   if (U->block % 8 != 0) return fail(PSI_E_ALIGN, "ffn: hidden tile must be a multiple of 8");
   if (token_chunks < 1) return fail(PSI_E_INVALID, "ffn: token_chunks must be >= 1");
   if ((st = page_fit(d, U, "U")) || (st = page_fit(d, V, "V"))) return st;
+  // several chunks hold U_J and V_J in two slots at once (every chunk's
+  // up-projection is followed by its down-projection)
+  if (token_chunks > 1 && d->n_pages < 2 && !(U->resident && V->resident))
+    return fail(PSI_E_INVALID, "ffn: token chunks keep U_J and V_J acquired together: need two page slots");
   const psi_matrix* uv[2] = {U, V};
   if ((st = bias_fit(L, uv, 2))) return st;
-  size_t need = align_up((size_t)M * U->block * 2, kAlign);  // hidden tile H_J, all rows
+  // hidden tile H_J for the rows of one token chunk
+  const size_t rows = ffn_chunk_rows(M, token_chunks);
+  size_t need = align_up(rows * U->block * 2, kAlign);
   if (!acc_external) need += align_up((size_t)M * dmodel * 4, kAlign);
   if ((st = scratch_fit(L, need, "FFN hidden tile and accumulator"))) return st;
   if (scratch_needed) *scratch_needed = need;

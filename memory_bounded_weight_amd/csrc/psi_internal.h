@@ -110,6 +110,13 @@ inline bool qk_stage_active(const psi_qk_norm_rope* nr) {
   return nr && (nr->gamma_q || nr->gamma_k || nr->cos_q || nr->sin_q || nr->cos_k || nr->sin_k);
 }
 MatrixInfo matrix_info(const psi_matrix* m);
+// Rows of one FFN token chunk: ceil(M / chunks) (the last chunk may be
+// shorter); chunks < 1 is treated as 1.
+inline size_t ffn_chunk_rows(int M, int chunks) {
+  if (M <= 0) return 0;
+  if (chunks < 1) chunks = 1;
+  return ((size_t)M + chunks - 1) / chunks;
+}
 const void* matrix_page_ptr(const psi_matrix* m, int p);
 int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COLS) in page p
 

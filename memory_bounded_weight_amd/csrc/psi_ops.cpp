@@ -135,6 +135,19 @@ psi_status check_ptr(const void* p, const char* what, bool allow_null = false) {
   return PSI_OK;
 }
 
+// Output and input ranges: disjoint, or (where the operator reads each
+// element of x before writing the same element of y, and every other read
+// of x comes earlier on the stream) exactly the same buffer.
+psi_status check_alias(const void* x, size_t xbytes, const void* y, size_t ybytes, bool allow_same,
+                       const char* op) {
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+  if (!x || !y || xbytes == 0 || ybytes == 0) return PSI_OK;
+  if (x0 + xbytes <= y0 || y0 + ybytes <= x0) return PSI_OK;
+  if (allow_same && x0 == y0 && xbytes == ybytes) return PSI_OK;
+  return fail(PSI_E_INVALID, std::string(op) + (allow_same ? ": y must be x itself or not overlap it"
+                                                           : ": y must not overlap x"));
+}
+
 psi_status check_matrix_pinned(psi_arena* a, const psi_matrix* m, const char* name) {
   if (a->dry) return PSI_OK;
   if (m->resident) {
@@ -287,6 +300,9 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
   const bool resid = flags & PSI_OP_RESIDUAL;
   if (resid && K != N) return fail(PSI_E_INVALID, "linear residual needs K == N");
   if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  // every page reads all of x (output-column pages) or x's next columns
+  // (K-split) while earlier launches have written y: no in-place form
+  if ((st = check_alias(x, (size_t)M * K * 2, y, (size_t)M * N * 2, false, "linear"))) return st;
   if (!a->dry) {
     if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(acc_dev, "acc", true)))
       return st;
@@ -361,6 +377,7 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
   psi_status st = psi_ffn_plan(&a->desc, M, d, U, V, token_chunks, acc_dev != nullptr, &need);
   if (st) return st;
   if ((flags & PSI_OP_STORE_ACC) && !acc_dev) return fail(PSI_E_INVALID, "PSI_OP_STORE_ACC needs acc_dev");
+  if ((st = check_alias(x, (size_t)M * d * 2, y, (size_t)M * d * 2, true, "ffn"))) return st;
   if (!a->dry) {
     if ((st = check_ptr(x, "x")) || (st = check_ptr(y, "y")) || (st = check_ptr(acc_dev, "acc", true)))
       return st;
@@ -370,8 +387,18 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
   if (M == 0) return PSI_OK;
   const bool resid = flags & PSI_OP_RESIDUAL;
   const int th = U->block;
+  // Token chunks: contiguous row ranges of x of `rows_per` rows.  One chunk
+  // (the default) runs every page in a single launch over all tokens.  With
+  // several, U_J and V_J stay acquired while every chunk runs its
+  // up-projection and its carried down-projection, so each page is streamed
+  // once and serves all chunks (page reuse across token chunks, [PSI]
+  // sec. II-B eq. (2) with the bounded scratch of sec. II-A eq. (1)): the
+  // hidden tile H_J holds one chunk's rows.  Rows are independent, so the
+  // arithmetic of every output is the same whatever the chunk count.
+  const int rows_per = (int)ffn_chunk_rows(M, token_chunks);
+  const int nC = (M + rows_per - 1) / rows_per;
   ScratchMark mark(a);
-  uint16_t* H = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
+  uint16_t* H = static_cast<uint16_t*>(scratch_alloc(a, (size_t)rows_per * th * 2, &st));
   if (st) return st;
   float* acc = acc_dev;
   if (!acc) {
@@ -382,7 +409,7 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
   OpBiases bias;
   if ((st = bias.stage(a, ms, 2))) return st;
   // Request order U_0, V_0, U_1, V_1, ...: each hidden tile J is produced
-  // for all tokens from U_J, then consumed by V_J ([PSI] eq. (2)).
+  // from U_J, then consumed by V_J ([PSI] eq. (2)).
   std::vector<PageReq> ru, rv, reqs;
   matrix_requests(U, ru);
   matrix_requests(V, rv);
@@ -391,58 +418,75 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
     reqs.push_back(ru[J]);
     reqs.push_back(rv[J]);
   }
-  // The hidden tile holds every token, so each page serves all token chunks
-  // (contiguous row ranges of x and H) in one launch: per row the
-  // arithmetic is that of a chunk-by-chunk loop, and the page is streamed
-  // once whatever the number of chunks ([PSI] sec. III-B page reuse).
-  (void)token_chunks;
-  const int rows_per = M;
   LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
   const uint16_t *ba = nullptr, *bb = nullptr;
+  const unsigned baseline = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  // H[0:mr] = B(phi(B(x[r0:r0+mr] U_J^T + a_J)))
+  auto up = [&](int J, const uint16_t* page, int r0, int mr) -> psi_status {
+    GemmArgs g = gemm_args();
+    g.A = x + (size_t)r0 * d; g.lda = d;
+    g.B = page; g.ldb = d;
+    g.M = mr; g.N = matrix_page_extent(U, J); g.K = d;
+    g.bias = ba ? ba + (size_t)J * th : nullptr;
+    g.out = H; g.ldo = th;
+    g.epi = EPI_GELU;
+    g.baseline_bias = baseline;
+    return run_gemm(a, g);
+  };
+  // ACC[r0:r0+mr] (+)= H V_J^T; after the last tile y = B(ACC + b) (+ x)
+  auto down = [&](int J, const uint16_t* page, int r0, int mr) -> psi_status {
+    const int ext = matrix_page_extent(U, J);
+    const bool last = J == nJ - 1;
+    GemmArgs g = gemm_args();
+    g.A = H; g.lda = th;
+    g.B = page; g.ldb = ext;
+    g.M = mr; g.N = d; g.K = ext;
+    float* ar = acc + (size_t)r0 * d;
+    if (J > 0) { g.acc_in = ar; g.ld_acc_in = d; }
+    if (last) {
+      g.bias = bb;
+      g.out = y + (size_t)r0 * d; g.ldo = d;
+      if (resid) { g.resid = x + (size_t)r0 * d; g.ldr = d; }
+      if (flags & PSI_OP_STORE_ACC) { g.acc_out = ar; g.ld_acc_out = d; }
+    } else {
+      g.epi = EPI_ACC;
+      g.acc_out = ar; g.ld_acc_out = d;
+    }
+    return run_gemm(a, g);
+  };
   for (int J = 0; J < nJ; ++J) {
     const int ext = matrix_page_extent(U, J);
     const bool last = J == nJ - 1;
-    const uint16_t* page;
-    // up-projection + bias + BF16 + GELU + BF16 for every token chunk
-    if ((st = feeder.take(2 * J, &page))) return st;
-    if ((st = bias.get(0, &ba))) return st;
-    for (int r0 = 0; r0 < M; r0 += rows_per) {
-      const int mr = M - r0 < rows_per ? M - r0 : rows_per;
-      GemmArgs g = gemm_args();
-      g.A = x + (size_t)r0 * d; g.lda = d;
-      g.B = page; g.ldb = d;
-      g.M = mr; g.N = ext; g.K = d;
-      g.bias = ba ? ba + (size_t)J * th : nullptr;
-      g.out = H + (size_t)r0 * th; g.ldo = th;
-      g.epi = EPI_GELU;
-      g.baseline_bias = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
-      if ((st = run_gemm(a, g))) return st;
+    const uint16_t *upage, *vpage;
+    if ((st = feeder.take(2 * J, &upage)) || (st = bias.get(0, &ba))) return st;
+    if (nC == 1) {
+      // up-projection + bias + BF16 + GELU + BF16 for all tokens; U_J goes
+      // back before V_J is waited for, so the next copy overlaps the GEMMs
+      if ((st = up(J, upage, 0, M)) || (st = feeder.give_back(2 * J))) return st;
+      const int branch = token_chunks > 1 ? J * token_chunks : J;
+      if (ext == th && (st = probe_commit(a, branch, PSI_ROLE_FFN_H, H, (size_t)M * th * 2))) return st;
+      if ((st = feeder.take(2 * J + 1, &vpage))) return st;
+      if (last && (st = bias.get(1, &bb))) return st;
+      if (last && out_fence && !a->dry && (st = psi_journal_fence(out_fence, a->compute))) return st;
+      if ((st = down(J, vpage, 0, M)) || (st = feeder.give_back(2 * J + 1))) return st;
+      continue;
     }
-    if ((st = feeder.give_back(2 * J))) return st;
-    if (ext == th && (st = probe_commit(a, J, PSI_ROLE_FFN_H, H, (size_t)M * th * 2))) return st;
-    // down-projection: carried fp32 accumulator, bias once after the last tile
-    if ((st = feeder.take(2 * J + 1, &page))) return st;
+    // several chunks: both pages of tile J held across the chunk launches
+    if ((st = feeder.take(2 * J + 1, &vpage))) return st;
     if (last && (st = bias.get(1, &bb))) return st;
     if (last && out_fence && !a->dry && (st = psi_journal_fence(out_fence, a->compute))) return st;
-    for (int r0 = 0; r0 < M; r0 += rows_per) {
+    for (int c = 0; c < nC; ++c) {
+      const int r0 = c * rows_per;
       const int mr = M - r0 < rows_per ? M - r0 : rows_per;
-      GemmArgs g = gemm_args();
-      g.A = H + (size_t)r0 * th; g.lda = th;
-      g.B = page; g.ldb = ext;
-      g.M = mr; g.N = d; g.K = ext;
-      if (J > 0) { g.acc_in = acc + (size_t)r0 * d; g.ld_acc_in = d; }
-      if (last) {
-        g.bias = bb;
-        g.out = y + (size_t)r0 * d; g.ldo = d;
-        if (resid) { g.resid = x + (size_t)r0 * d; g.ldr = d; }
-        if (flags & PSI_OP_STORE_ACC) { g.acc_out = acc + (size_t)r0 * d; g.ld_acc_out = d; }
-      } else {
-        g.epi = EPI_ACC;
-        g.acc_out = acc + (size_t)r0 * d; g.ld_acc_out = d;
-      }
-      if ((st = run_gemm(a, g))) return st;
+      if ((st = up(J, upage, r0, mr))) return st;
+      // U_J's last use is the last chunk's up-projection
+      if (c == nC - 1 && (st = feeder.give_back(2 * J))) return st;
+      if (ext == th &&
+          (st = probe_commit(a, J * token_chunks + c, PSI_ROLE_FFN_H, H, (size_t)mr * th * 2)))
+        return st;
+      if ((st = down(J, vpage, r0, mr))) return st;
     }
     if ((st = feeder.give_back(2 * J + 1))) return st;
   }
@@ -464,6 +508,7 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   if (schedule == PSI_FFN_REUSE && !j) return fail(PSI_E_INVALID, "ffn tiled: FFN reuse needs a journal");
   if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "ffn tiled: no full accumulator to store");
   const int nO = psi_matrix_pages(Vo);
+  if ((st = check_alias(x, (size_t)M * d * 2, y, (size_t)M * d * 2, true, "ffn tiled"))) return st;
   if (x == y && nO > 1 && schedule != PSI_FFN_REUSE)
     return fail(PSI_E_INVALID, "ffn tiled: with recomputation y may alias x only with a single output tile");
   if (!a->dry) {
@@ -603,10 +648,13 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   return bias.release();
 }
 
-psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
-                          int heads, int head_dim, const psi_matrix* Wq, const psi_matrix* Wk,
-                          const psi_matrix* Wv, const psi_matrix* Wo, float* acc_dev, uint16_t* y,
-                          unsigned flags) {
+// The attention sub-block; with out_fence, the compute stream first waits
+// for every journal copy enqueued so far right before the first launch that
+// writes y (as in ffn_paged).
+static psi_status attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc, int heads,
+                             int head_dim, const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
+                             const psi_matrix* Wo, float* acc_dev, uint16_t* y, unsigned flags,
+                             psi_journal* out_fence) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
   if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
   if (!ctx) Mc = 0;
@@ -619,13 +667,17 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
   if (otiles && (reinterpret_cast<uintptr_t>(acc_dev) & 15))
     return fail(PSI_E_ALIGN, "attention: acc_dev must be 16-byte aligned when it holds the head-group outputs");
   if ((st = check_attn_args(a, x, y, ctx, acc_dev, Wq, Wk, Wv, Wo))) return st;
-  if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
+  if ((st = check_alias(x, (size_t)M * dm * 2, y, (size_t)M * dm * 2, true, "attention"))) return st;
+  if (M == 0) return PSI_OK;
   const int gw = Wq->block;
   const uint16_t* src = ctx ? ctx : x;
   const int Ms = ctx ? Mc : M;
   const long ldvt = (long)align_up((size_t)Ms, 64);
   const int bbase = (flags & PSI_OP_BASELINE_BIAS) ? 1 : 0;
+  auto fence = [&]() -> psi_status {
+    return out_fence && !a->dry ? psi_journal_fence(out_fence, a->compute) : PSI_OK;
+  };
   ScratchMark mark(a);
   // Q_g, overwritten by O_g: one group's tile [M, gw] for the K-split, or
   // columns g of an [M, dm] buffer that keeps every group's O for the
@@ -712,7 +764,7 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     if ((st = attend(a, Qg, ldq, Kb, gw, Vt, ldvt, M, Ms, ext / head_dim, head_dim, flags))) return st;
     if (otiles) continue;
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, (size_t)M * gw * 2))) return st;
-    if ((st = feeder.take(r0 + 3, &page)) ||
+    if ((st = feeder.take(r0 + 3, &page)) || (g == nG - 1 && (st = fence())) ||
         (st = oproj_ksplit(a, Q, gw, M, dm, page, ext, g == 0, g == nG - 1, acc, bq[3], y, x, flags, bbase)) ||
         (st = feeder.give_back(r0 + 3)))
       return st;
@@ -722,13 +774,20 @@ psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t
     const size_t r0 = (size_t)per * nG;
     const uint16_t* page;
     for (int o = 0; o < (int)ro.size(); ++o)
-      if ((st = feeder.take(r0 + o, &page)) ||
+      if ((st = feeder.take(r0 + o, &page)) || (o == 0 && (st = fence())) ||
           (st = oproj_tile(a, Q, M, dm, page, matrix_page_extent(Wo, o), (size_t)o * Wo->block, bq[3], y, x,
                            flags, bbase)) ||
           (st = feeder.give_back(r0 + o)))
         return st;
   }
   return bias.release();
+}
+
+psi_status psi_attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
+                          int heads, int head_dim, const psi_matrix* Wq, const psi_matrix* Wk,
+                          const psi_matrix* Wv, const psi_matrix* Wo, float* acc_dev, uint16_t* y,
+                          unsigned flags) {
+  return attn_paged(a, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_dev, y, flags, nullptr);
 }
 
 psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc,
@@ -753,8 +812,9 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
       if ((st = Wq->resident ? check_ptr(g, "gamma") : check_pinned(g, "gamma"))) return st;
     }
   }
-  if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
+  if ((st = check_alias(x, (size_t)M * dm * 2, y, (size_t)M * dm * 2, true, "attention"))) return st;
+  if (M == 0) return PSI_OK;
   const int gw = Wq->block;
   const uint16_t* src = ctx ? ctx : x;
   const int Ms = ctx ? Mc : M;
@@ -869,8 +929,9 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
   if (!j) return fail(PSI_E_INVALID, "attention tiled: needs a journal for the head-group outputs");
   if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "attention tiled: no full accumulator to store");
   if ((st = check_attn_args(a, x, y, ctx, nullptr, Wq, Wk, Wv, Wo))) return st;
-  if (M == 0) return PSI_OK;
   const int dm = heads * head_dim;
+  if ((st = check_alias(x, (size_t)M * dm * 2, y, (size_t)M * dm * 2, true, "attention tiled"))) return st;
+  if (M == 0) return PSI_OK;
   const int gw = Wq->block, to = Wo->block;
   const uint16_t* src = ctx ? ctx : x;
   const int Ms = ctx ? Mc : M;
@@ -992,7 +1053,6 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
                            const psi_block_weights* w, int token_chunks, float* acc_dev,
                            psi_journal* fence, unsigned flags) {
   if (!a || !w) return fail(PSI_E_INVALID, "null argument");
-  if (x == xt && M > 0) return fail(PSI_E_INVALID, "block: x_tmp must be a separate buffer");
   const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2)) | PSI_OP_RESIDUAL;
   // validate both halves before enqueueing anything
   const int dm = heads * head_dim;
@@ -1001,8 +1061,20 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
   if (st) return st;
   if ((st = psi_ffn_plan(&a->desc, M, dm, &w->U, &w->V, token_chunks, acc_dev != nullptr, nullptr)))
     return st;
-  if ((st = psi_attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo,
-                           acc_dev, xt, f)))
+  const size_t xbytes = (size_t)M * dm * 2;
+  if (xt && xt != x && (st = check_alias(x, xbytes, xt, xbytes, false, "block x_tmp"))) return st;
+  if (!xt || xt == x) {
+    // in place: the attention sub-block's output tiles write x after its
+    // last read of x, and the FFN's last down-projection writes each row
+    // after every read of that row; the journal's reads of x's previous
+    // contents precede the attention's first write
+    if ((st = attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, acc_dev, x, f,
+                         fence)))
+      return st;
+    return ffn_paged(a, x, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, nullptr);
+  }
+  if ((st = attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, acc_dev, xt, f,
+                       nullptr)))
     return st;
   return ffn_paged(a, xt, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, fence);
 }

@@ -200,10 +200,11 @@ def test_page_lifecycle_dry_run():
 
 
 def test_ffn_streams_every_page_once_dry_run():
-    """Page reuse across token chunks: with 4 chunks of 1,024 tokens each
-    U_J and V_J page is copied exactly once (32 pages = 256 MiB of weights,
-    plus the bias slices), never once per chunk; the hidden tile holds every
-    token, so one launch per page serves all four chunks."""
+    """Page reuse across token chunks ([PSI] sec. II-B eq. (2)): with 4
+    chunks of 1,024 tokens each U_J and V_J page is copied exactly once (32
+    pages = 256 MiB of weights, plus the bias slices), never once per chunk;
+    every chunk runs its own up- and down-projection launch (16 tiles x 4
+    chunks x 2), and the hidden tile holds one chunk's rows."""
     a = psi.psi_arena_create(desc(80, 8, 2, 8))
     try:
         U, V = cfg5_ffn()
@@ -212,8 +213,98 @@ def test_ffn_streams_every_page_once_dry_run():
         s = psi.psi_arena_stats(a)
         assert s.page_copies == 32
         assert s.bytes_h2d == 256 * MiB + 16384 * 2 + 4096 * 2
-        assert s.kernel_launches == 32
+        assert s.kernel_launches == 16 * 4 * 2
+        assert s.scratch_high_water == 1024 * 1024 * 2
+        psi.psi_arena_reset_stats(a)
+        psi.psi_ffn_paged(a, fake, 4096, 4096, U, V, 1, fake, fake, psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 32 and s.kernel_launches == 32
         assert s.scratch_high_water == 4096 * 1024 * 2
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_ffn_token_chunks_bound_scratch_dry_run():
+    """The hidden tile is sized from one token chunk, so the FFN's scratch
+    stays bounded at any token count ([PSI] sec. II-A eq. (1)).  In the
+    benchmark's arena (80 MiB: seven 8 MiB pages, no workspace, about 23.9
+    MiB of scratch) the FFN of 16,384 tokens is refused in one chunk (32 MiB
+    hidden tile) and fits in two or more; ragged chunk counts round the
+    chunk up; several chunks need two page slots unless the weights are
+    resident."""
+    U, V = cfg5_ffn()
+    d = desc(80, 8, 7, 0)
+    assert psi.psi_ffn_plan(d, 16384, 4096, U, V, token_chunks=1)[0] == psi.PSI_E_SCRATCH_EXHAUSTED
+    for chunks, rows in ((2, 8192), (3, 5462), (16, 1024), (16384, 1), (20000, 1)):
+        assert psi.psi_ffn_plan(d, 16384, 4096, U, V, token_chunks=chunks) == \
+            (psi.PSI_OK, -(-rows * 1024 * 2 // 256) * 256)
+    assert psi.psi_ffn_plan(desc(80, 8, 1, 0), 4096, 4096, U, V, token_chunks=2)[0] == psi.PSI_E_INVALID
+    Ur = psi.make_matrix(0x1000, 0x2000, 16384, 4096, psi.PSI_SPLIT_ROWS, 1024, 1)
+    Vr = psi.make_matrix(0x1000, 0x2000, 4096, 16384, psi.PSI_SPLIT_COLS, 1024, 1)
+    assert psi.psi_ffn_plan(desc(80, 8, 1, 0), 4096, 4096, Ur, Vr, token_chunks=2) == \
+        (psi.PSI_OK, 2048 * 1024 * 2)
+
+
+def test_stack_16384_tokens_plans_in_benchmark_arena_dry_run():
+    """The 8-block stack at 16,384 tokens (twice the benchmarked count) runs
+    inside the same 80 MiB arena of seven pages once the FFN uses two token
+    chunks: attention keeps its head-group outputs, K and V^T in the
+    caller's accumulator memory (no arena scratch) and the FFN's hidden tile
+    is 16 MiB.  In one chunk it is refused before anything is enqueued."""
+    Wq, Wk, Wv, _ = cfg5_attn()
+    Wo_t = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 1024)
+    U, V = cfg5_ffn()
+    bw = psi.psi_block_weights(Wq, Wk, Wv, Wo_t, U, V)
+    a = psi.psi_arena_create(desc(80, 8, 7, 0))
+    try:
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_block_paged(a, 0x10000, None, 16384, 32, 128, bw, 1, 0x30000, None, 0)
+        assert e.value.status == psi.PSI_E_SCRATCH_EXHAUSTED
+        assert psi.psi_arena_stats(a).page_copies == 0
+        for _ in range(8):
+            psi.psi_block_paged(a, 0x10000, None, 16384, 32, 128, bw, 2, 0x30000, None, 0)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 8 * 48
+        assert s.scratch_high_water == 8192 * 1024 * 2
+        assert s.arena_bytes == 80 * MiB
+    finally:
+        psi.psi_arena_destroy(a)
+
+
+def test_output_overlap_rules_dry_run():
+    """The projection reads x in every page launch while earlier launches
+    have written y, so y must not overlap x.  The FFN, attention and block
+    write each element after every read of it: y may be x itself, but not a
+    partly overlapping range.  Refusals happen before anything is enqueued."""
+    a = psi.psi_arena_create(desc(8, 1, 2, 0))
+    try:
+        M, K = 64, 256
+        W = fake_matrix(256, 256, psi.PSI_SPLIT_ROWS, 128)
+        base = 0x100000
+        for y in (base, base + 2 * K * 16):
+            with pytest.raises(psi.PsiError) as e:
+                psi.psi_linear_paged(a, base, M, K, W, None, y, psi.PSI_OP_RESIDUAL)
+            assert e.value.status == psi.PSI_E_INVALID
+        psi.psi_linear_paged(a, base, M, K, W, None, base + M * K * 2, 0)  # adjacent: fine
+        U = fake_matrix(512, 256, psi.PSI_SPLIT_ROWS, 256)
+        V = fake_matrix(256, 512, psi.PSI_SPLIT_COLS, 256)
+        psi.psi_ffn_paged(a, base, M, K, U, V, 2, None, base, psi.PSI_OP_RESIDUAL)
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_ffn_paged(a, base, M, K, U, V, 2, None, base + 16, psi.PSI_OP_RESIDUAL)
+        assert e.value.status == psi.PSI_E_INVALID
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 2 + 4
+    finally:
+        psi.psi_arena_destroy(a)
+    Wq, Wk, Wv, Wo = cfg5_attn()
+    U, V = cfg5_ffn()
+    bw = psi.psi_block_weights(Wq, Wk, Wv, Wo, U, V)
+    a = psi.psi_arena_create(desc(80, 8, 2, 8))
+    try:
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_block_paged(a, 0x10000, 0x10000 + 4096, 8192, 32, 128, bw, 1, 0x30000, None, 0)
+        assert e.value.status == psi.PSI_E_INVALID
+        assert psi.psi_arena_stats(a).page_copies == 0
     finally:
         psi.psi_arena_destroy(a)
 
@@ -250,7 +341,7 @@ def test_checkpoint_size_independence_dry_run():
             U, V = cfg5_ffn()
             bw = psi.psi_block_weights(Wq, Wk, Wv, Wo, U, V)
             for _ in range(nblocks):
-                psi.psi_block_paged(a, 0x10000, 0x20000, 8192, 32, 128, bw, 1, 0x30000, None, 0)
+                psi.psi_block_paged(a, 0x10000, 1 << 40, 8192, 32, 128, bw, 1, 0x30000, None, 0)
             s = psi.psi_arena_stats(a)
             peaks.append((s.arena_bytes, s.scratch_high_water))
             streamed.append(s.bytes_h2d)
@@ -322,7 +413,7 @@ def test_ffn_tiled_plans_and_recompute_stream_dry_run():
         with pytest.raises(psi.PsiError) as e:  # y aliasing x over 16 output tiles
             psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE, None, 0, 0, fake)
         assert e.value.status == psi.PSI_E_INVALID
-        psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE, None, 0, 0, 2 * fake)
+        psi.psi_ffn_tiled(a, fake, 512, 4096, U, Vo, psi.PSI_FFN_RECOMPUTE, None, 0, 0, 1 << 40)
         s = psi.psi_arena_stats(a)
         n_o, n_j = 4096 // 256, 16384 // 1024
         assert s.page_copies == n_o * (1 + n_j)

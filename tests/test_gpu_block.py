@@ -42,7 +42,7 @@ def stack():
 
 
 def run_stack(P, blocks_host, x0, steps=1, n_pages=2, arena_flags=0, journal_flags=0,
-              group_heads=1, tile=256):
+              group_heads=1, tile=256, chunks=2, in_place=False):
     gw = group_heads * 128
     bws = [P.block_weights(w, gw, tile) for w in blocks_host]
     page = max(gw * D * 2, tile * D * 2)
@@ -59,7 +59,7 @@ def run_stack(P, blocks_host, x0, steps=1, n_pages=2, arena_flags=0, journal_fla
             P.psi_journal_fence(j, s)
             x.copy_(xd0)
             for b, bw in enumerate(bws):
-                P.psi_block_paged(ar, x, xt, M, HEADS, 128, bw, 2, acc, j, 0)
+                P.psi_block_paged(ar, x, None if in_place else xt, M, HEADS, 128, bw, chunks, acc, j, 0)
                 P.psi_journal_commit(j, P.key(st, b), x, M * D * 2, s)
         P.psi_arena_sync(ar)
         outs = []
@@ -112,6 +112,10 @@ def test_stack_invocations_and_controls_bitwise(P, stack):
         "sync journal": dict(journal_flags=P.PSI_JOURNAL_SYNC),
         "2-head groups": dict(group_heads=2),
         "hidden tile 128": dict(tile=128),
+        "one token chunk": dict(chunks=1),
+        "three token chunks": dict(chunks=3),
+        "in place (no x_tmp)": dict(in_place=True),
+        "in place, 3 pages, sync copies": dict(in_place=True, n_pages=3, arena_flags=P.PSI_ARENA_SYNC_COPY),
     }
     for name, kw in variants.items():
         got = run_stack(P, blocks, x0, **kw)[0]

@@ -7,9 +7,12 @@ pages + 8 MiB workspace, K-split O-projection).
 Rows of an FFN are independent, so sampled rows of x go through the
 oracle directly.  Attention rows depend on every key; the paged operator's
 stage probes journal each head group's output O_g, so the oracle checks
-(a) head 0 of O on sampled query rows against its own projections of that
-head, and (b) the output projection + residual on the GPU's O (identical
-inputs, as the paper's same-input probes do, [PSI] sec. IV-B).
+(a) one head of every head-group page (heads 0, 9, 18, 31 of the 8-head
+groups) on the sampled query rows against its own projections of that head
+over all keys, and (b) the output projection + residual on the GPU's O
+(identical inputs, as the paper's same-input probes do, [PSI] sec. IV-B).
+The sampled rows hit every 256-row tile of the GEMM and attention
+workgroups (one random row per tile, plus the first and the last row).
 
 [PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
 Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
@@ -30,10 +33,16 @@ def P(psi_lib):
     return psi_lib
 
 
-def sample_rows(M, n, seed=0):
+def sample_rows(M, n=None, seed=0, tile=256):
+    """One random row in every `tile`-row block of [0, M), plus rows 0 and
+    M - 1 (n is ignored: kept for call sites that name a count)."""
     rng = np.random.default_rng(seed)
-    rows = set(rng.choice(M, size=n - 2, replace=False).tolist()) | {0, M - 1}
+    rows = {int(t + rng.integers(0, min(tile, M - t))) for t in range(0, M, tile)} | {0, M - 1}
     return np.array(sorted(rows))
+
+
+# one head of each of the four 8-head groups
+CHECK_HEADS = (0, 9, 18, 31)
 
 
 def read_probe(P, j, role, branch, M, cols, step=0, block=0):
@@ -43,9 +52,10 @@ def read_probe(P, j, role, branch, M, cols, step=0, block=0):
 
 
 def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0, otiles=False):
-    """(a) head 0 on sampled rows against the oracle's own projections of
-    head 0; (b) output projection + residual on the journaled O (per head
-    group for the K-split, all groups at once for output tiles)."""
+    """(a) one head of every head group on the sampled rows against the
+    oracle's own projections of that head (its Q on those rows, its K and V
+    over every key); (b) output projection + residual on the journaled O
+    (per head group for the K-split, all groups at once for output tiles)."""
     M, d = x_in.shape
     if otiles:
         O = read_probe(P, j, P.PSI_ROLE_ATTN_O, -1, M, d, step)
@@ -53,13 +63,17 @@ def check_attention(P, j, x_in, y, w, heads, gw, rows, ctx=None, step=0, otiles=
         O = np.concatenate([read_probe(P, j, P.PSI_ROLE_ATTN_O, g, M, gw, step) for g in range(d // gw)],
                            axis=1)
     src = x_in if ctx is None else ctx
-    h0 = slice(0, 128)
-    K0 = oracle.linear(src, np.ascontiguousarray(w["Wk"][h0]), w["bk"][h0].copy())
-    V0 = oracle.linear(src, np.ascontiguousarray(w["Wv"][h0]), w["bv"][h0].copy())
-    Q0 = oracle.linear(np.ascontiguousarray(x_in[rows]), np.ascontiguousarray(w["Wq"][h0]),
-                       w["bq"][h0].copy())
-    O0 = oracle.attention(Q0, K0, V0, 1, 128)
-    assert_bf16_close(O[rows][:, h0], O0, what="attention head 0")
+    xr = np.ascontiguousarray(x_in[rows])
+    groups = set()
+    for h in CHECK_HEADS:
+        hs = slice(h * 128, (h + 1) * 128)
+        groups.add(h * 128 // gw)
+        Kh = oracle.linear(src, np.ascontiguousarray(w["Wk"][hs]), w["bk"][hs].copy())
+        Vh = oracle.linear(src, np.ascontiguousarray(w["Wv"][hs]), w["bv"][hs].copy())
+        Qh = oracle.linear(xr, np.ascontiguousarray(w["Wq"][hs]), w["bq"][hs].copy())
+        Oh = oracle.attention(Qh, Kh, Vh, 1, 128)
+        assert_bf16_close(O[rows][:, hs], Oh, what=f"attention head {h}")
+    assert groups == set(range(d // gw)), "every head-group page is checked"
     ref = oracle.residual(x_in[rows], oracle.linear(np.ascontiguousarray(O[rows]), w["Wo"], w["bo"]))
     assert_bf16_close(y[rows], ref, what="output projection + residual")
 
@@ -86,7 +100,7 @@ def test_fullsize_block_8192_tokens(P, layout):
         P.psi_arena_sync(ar)
         P.psi_journal_sync(j)
         y_attn, y = host(xt), host(x)
-        rows = sample_rows(M, 12)
+        rows = sample_rows(M)
         check_attention(P, j, x0, y_attn, w, heads, 1024, rows, otiles=otiles)
         # FFN on the GPU's own attention output (identical inputs), and its
         # first hidden tile from the stage probe
@@ -131,7 +145,7 @@ def test_fullsize_attention_self_and_cross(P, layout):
         P.psi_attn_paged(ar, y1, M, ctx, Mc, heads, 128, *mats["cross"], acc, y2, P.PSI_OP_RESIDUAL)
         P.psi_arena_sync(ar)
         P.psi_journal_sync(j)
-        rows = sample_rows(M, 12, seed=1)
+        rows = sample_rows(M, seed=1)
         y1h, y2h = host(y1), host(y2)
         check_attention(P, j, c["x"], y1h, c["self"], heads, 1024, rows, step=0, otiles=otiles)
         check_attention(P, j, y1h, y2h, c["cross"], heads, 1024, rows, ctx=c["ctx"], step=1, otiles=otiles)
@@ -162,8 +176,51 @@ def test_fullsize_ffn(P, cfg):
         P.psi_arena_sync(ar)
         s = P.psi_arena_stats(ar)
         assert s.page_copies == 2 * hid // tile  # every page streamed exactly once
-        rows = sample_rows(M, 10, seed=2)
+        rows = sample_rows(M, seed=2)
         yr = oracle.ffn(np.ascontiguousarray(c["x"][rows]), c["U"], c["a"], c["V"], c["b"])
         assert_bf16_close(host(y)[rows], yr, what=f"FFN {cfg}")
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+def test_fullsize_ffn_token_chunks_16384_tokens(P):
+    """Page reuse across token chunks at twice the stack's token count: the
+    FFN of 16,384 tokens (d 4,096, hidden 16,384, 1,024-channel tiles) in the
+    benchmark's arena (80 MiB, seven 8 MiB pages, no workspace, fp32
+    accumulator as declared live state) is refused in one chunk (its 32 MiB
+    hidden tile exceeds the scratch) and runs in two, each page streamed
+    once; sampled rows of every 256-row tile match the oracle.  At 8,192
+    tokens, where one chunk fits, one and four chunks give the same bits."""
+    d, hid = 4096, 16384
+    c = synth.ffn_case(0, 16384, d, hid)
+    U = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, 1024)
+    V = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, 1024)
+    ar = make_arena(80 * MiB, 8 * MiB, 7, 0)
+    try:
+        M = 16384
+        x = dev(c["x"])
+        y = torch.empty_like(x)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        with pytest.raises(P.PsiError) as e:
+            P.psi_ffn_paged(ar, x, M, d, U, V, 1, acc, y, P.PSI_OP_RESIDUAL)
+        assert e.value.status == P.PSI_E_SCRATCH_EXHAUSTED
+        P.psi_arena_reset_stats(ar)
+        P.psi_ffn_paged(ar, x, M, d, U, V, 2, acc, y, P.PSI_OP_RESIDUAL)
+        P.psi_arena_sync(ar)
+        s = P.psi_arena_stats(ar)
+        assert s.page_copies == 2 * hid // 1024
+        assert s.scratch_high_water == 8192 * 1024 * 2
+        rows = sample_rows(M, seed=3)
+        yr = oracle.ffn(np.ascontiguousarray(c["x"][rows]), c["U"], c["a"], c["V"], c["b"], residual=True)
+        assert_bf16_close(host(y)[rows], yr, what="FFN 16,384 tokens in two chunks")
+        half = 8192
+        outs = []
+        for ch in (1, 4):
+            y2 = torch.empty(half, d, dtype=torch.int16, device="cuda")
+            P.psi_ffn_paged(ar, x[:half], half, d, U, V, ch, acc[:half], y2, P.PSI_OP_RESIDUAL)
+            P.psi_arena_sync(ar)
+            outs.append(host(y2))
+        assert np.array_equal(outs[0], outs[1])
+        assert np.array_equal(outs[0], host(y)[:half])  # rows do not depend on the other rows
     finally:
         P.psi_arena_destroy(ar)

@@ -238,13 +238,46 @@ def test_ffn_parity_residual_inplace(P, residual):
 
 def test_ffn_partitions_bitwise_gpu(P):
     """[PSI] eq. (2) on the GPU: hidden tiles of 128/256/512 channels and
-    1/2/4 token chunks give bitwise-identical outputs."""
-    c = synth.ffn_case(seed=3, M=256, d=256, hidden=1024)
+    1/2/3/4/7 token chunks (ragged: 250 rows) give bitwise-identical
+    outputs; with several chunks each chunk runs its own launches over a
+    hidden tile of one chunk's rows."""
+    c = synth.ffn_case(seed=3, M=250, d=256, hidden=1024)
     ref = run_ffn(P, c, 512, chunks=1)
     for tile in (256, 128):
-        for ch in (1, 2, 4):
+        for ch in (1, 2, 3, 4, 7):
             assert np.array_equal(run_ffn(P, c, tile, chunks=ch), ref), (tile, ch)
     assert np.array_equal(run_ffn(P, c, 256, chunks=2, acc_external=False), ref)
+    assert_bf16_close(ref, oracle.ffn(c["x"], c["U"], c["a"], c["V"], c["b"]))
+
+
+def test_ffn_token_chunks_reuse_pages_gpu(P):
+    """Page reuse across token chunks: U_J and V_J are held while every chunk
+    runs, so the page copies and bytes do not depend on the chunk count;
+    the launches do (2 per tile and chunk); the hidden-tile scratch shrinks
+    to one chunk; in place (y = x, residual) the chunked result equals the
+    one-launch result bitwise."""
+    M, d, h, tile = 301, 256, 1024, 256
+    c = synth.ffn_case(seed=9, M=M, d=d, hidden=h)
+    mu = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, tile)
+    mv = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, tile)
+    ar = make_arena(4 * MiB, 256 * KiB, 3)
+    outs, stats = {}, {}
+    try:
+        for ch in (1, 4):
+            xd = dev(c["x"])
+            P.psi_arena_reset_stats(ar)
+            P.psi_ffn_paged(ar, xd, M, d, mu, mv, ch, None, xd, P.PSI_OP_RESIDUAL)
+            P.psi_arena_sync(ar)
+            outs[ch] = host(xd)
+            stats[ch] = P.psi_arena_stats(ar)
+    finally:
+        P.psi_arena_destroy(ar)
+    assert np.array_equal(outs[1], outs[4])
+    assert stats[1].page_copies == stats[4].page_copies == 2 * h // tile
+    assert stats[1].bytes_h2d == stats[4].bytes_h2d
+    assert stats[4].kernel_launches == 4 * stats[1].kernel_launches
+    assert stats[4].scratch_high_water < stats[1].scratch_high_water
+    assert_bf16_close(outs[4], oracle.ffn(c["x"], c["U"], c["a"], c["V"], c["b"], residual=True))
 
 
 def test_ffn_baseline_bias_variant(P):
@@ -420,10 +453,10 @@ def test_operators_back_to_back_share_arena(P):
 
 def test_device_timeline_structure(P):
     """The profiled arena's device timeline ([PSI] sec. II-D page lifecycle):
-    one copy per page on the two copy streams, one GEMM per page (both
-    token chunks in one launch), ordered events with positive durations;
-    kernel-only profiling
-    keeps copy events off the copy streams until a trace is started."""
+    one copy per page on the two copy streams, one GEMM per page and token
+    chunk (two chunks: 16 launches for 8 pages), ordered events with
+    positive durations; kernel-only profiling keeps copy events off the
+    copy streams until a trace is started."""
     c = synth.ffn_case(seed=4, M=192, d=256, hidden=1024)
     mu = P.pinned_matrix(c["U"], c["a"], P.PSI_SPLIT_ROWS, 256)
     mv = P.pinned_matrix(c["V"], c["b"], P.PSI_SPLIT_COLS, 256)
@@ -434,12 +467,12 @@ def test_device_timeline_structure(P):
         P.psi_ffn_paged(ar, xd, 192, 256, mu, mv, 2, None, y, 0)
         P.psi_arena_sync(ar)
         st = P.psi_arena_stats(ar)
-        assert st.gemm_launches == 8 and st.copy_ms == 0.0  # one launch per page; copies untimed
+        assert st.gemm_launches == 16 and st.copy_ms == 0.0  # one launch per page and chunk; copies untimed
         P.psi_arena_trace_start(ar, 1024)
         P.psi_ffn_paged(ar, xd, 192, 256, mu, mv, 2, None, y, 0)
         ev = P.psi_arena_trace_read(ar, 1024)
         kinds = [e[0] for e in ev]
-        assert kinds.count(0) == 8 and kinds.count(1) == 0
+        assert kinds.count(0) == 16 and kinds.count(1) == 0
         assert kinds.count(2) + kinds.count(3) == 8 and kinds.count(2) >= 1 and kinds.count(3) >= 1
         assert all(e[1] >= 0.0 and e[2] > 0.0 for e in ev)
         gemm_starts = [e[1] for e in ev if e[0] == 0]
