@@ -315,6 +315,30 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x_dev, int M, int K,
                             const psi_matrix* W, float* acc_dev, uint16_t* y_dev,
                             unsigned flags);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * projection of psi_linear_paged over RESIDENT weight pages (W->resident
+ * = 1: image and bias are device pointers) with no arena.  The K-split's
+ * fp32 accumulator lives in a library-owned static device array of
+ * PSI_NOALLOC_SCRATCH_BYTES per device (held until the process ends); the
+ * call allocates nothing and enqueues only GEMM launches on `stream`
+ * (hipStream_t; NULL = null stream), in the page order of
+ * psi_linear_paged, so its bits equal psi_linear_paged's on the same
+ * resident matrix.
+ *   x_dev [M, K] bf16, y_dev [M, N] bf16 (N = W->rows), y must not overlap x;
+ *   W split by ROWS (no scratch used) or COLS (M * N * 4 bytes of scratch).
+ *   flags: PSI_OP_BASELINE_BIAS, PSI_OP_RESIDUAL (needs K == N).
+ * Every call on a device shares that device's array and finds the last
+ * call's contents in it (the first K-split page never reads them): calls
+ * that overlap on one device (two streams, two threads) race and must be
+ * ordered by the caller.
+ * Errors (before anything is enqueued): PSI_E_INVALID (not resident,
+ * shapes, flags, y overlapping x), PSI_E_SCRATCH_EXHAUSTED (M * N * 4 >
+ * PSI_NOALLOC_SCRATCH_BYTES for a K-split), PSI_E_ALIGN, PSI_E_HIP. */
+#define PSI_NOALLOC_SCRATCH_BYTES (16u << 20)
+psi_status psi_linear_resident_noalloc(const uint16_t* x_dev, int M, int K, const psi_matrix* W,
+                                       uint16_t* y_dev, unsigned flags, void* stream);
+
 /* Paged FFN F(X) = phi(X U^T + a) V^T + b ([PSI] sec. II-B eq. (2)) with the
  * declared BF16 writes of sec. III-A: pre-GELU B(acc + a), post-GELU
  * B(phi(.)), output B(ACC + b).

@@ -41,6 +41,23 @@ psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split)
   return PSI_OK;
 }
 
+psi_status check_ptr(const void* p, const char* what, bool allow_null) {
+  if (!p) return allow_null ? PSI_OK : fail(PSI_E_INVALID, std::string(what) + " is null");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(PSI_E_ALIGN, std::string(what) + " must be 16-byte aligned");
+  return PSI_OK;
+}
+
+psi_status check_alias(const void* x, size_t xbytes, const void* y, size_t ybytes, bool allow_same,
+                       const char* op) {
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+  if (!x || !y || xbytes == 0 || ybytes == 0) return PSI_OK;
+  if (x0 + xbytes <= y0 || y0 + ybytes <= x0) return PSI_OK;
+  if (allow_same && x0 == y0 && xbytes == ybytes) return PSI_OK;
+  return fail(PSI_E_INVALID, std::string(op) + (allow_same ? ": y must be x itself or not overlap it"
+                                                           : ": y must not overlap x"));
+}
+
 int matrix_page_extent(const psi_matrix* m, int p) {
   int total = m->split == PSI_SPLIT_ROWS ? m->rows : m->cols;
   int start = p * m->block;

@@ -105,6 +105,14 @@ struct MatrixInfo {
   size_t max_page_bytes;
 };
 psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split);
+// A device pointer that must be 16-byte aligned (and non-null unless
+// allow_null): PSI_E_INVALID / PSI_E_ALIGN otherwise.
+psi_status check_ptr(const void* p, const char* what, bool allow_null = false);
+// Output and input ranges: disjoint, or (where the operator reads each
+// element of x before writing the same element of y, and every other read
+// of x comes earlier on the stream) exactly the same buffer.
+psi_status check_alias(const void* x, size_t xbytes, const void* y, size_t ybytes, bool allow_same,
+                       const char* op);
 // True when the query/key normalisation-rotary stage does any work.
 inline bool qk_stage_active(const psi_qk_norm_rope* nr) {
   return nr && (nr->gamma_q || nr->gamma_k || nr->cos_q || nr->sin_q || nr->cos_k || nr->sin_k);

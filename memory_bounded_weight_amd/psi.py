@@ -177,6 +177,7 @@ _sig("psi_page_submit", [_vp, _vp, _sz, _P(_i)])
 _sig("psi_page_acquire", [_vp, _i, _P(_vp)])
 _sig("psi_page_release", [_vp, _i])
 _sig("psi_linear_paged", [_vp, _vp, _i, _i, _P(psi_matrix), _vp, _vp, _u])
+_sig("psi_linear_resident_noalloc", [_vp, _i, _i, _P(psi_matrix), _vp, _u, _vp])
 _sig("psi_ffn_paged", [_vp, _vp, _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _vp, _vp, _u])
 _sig("psi_ffn_tiled_plan", [_P(psi_arena_desc), _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _P(_sz)])
 _sig("psi_ffn_tiled", [_vp, _vp, _i, _i, _P(psi_matrix), _P(psi_matrix), _i, _vp, ctypes.c_int32,
@@ -210,7 +211,8 @@ EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_
            "psi_arena_stats",
            "psi_arena_reset_stats", "psi_arena_trace_start", "psi_arena_trace_read",
            "psi_arena_device_base", "psi_arena_set_probe", "psi_page_submit",
-           "psi_page_acquire", "psi_page_release", "psi_linear_paged", "psi_ffn_paged",
+           "psi_page_acquire", "psi_page_release", "psi_linear_paged",
+           "psi_linear_resident_noalloc", "psi_ffn_paged",
            "psi_attn_paged", "psi_block_paged", "psi_ffn_tiled_plan", "psi_ffn_tiled",
            "psi_attn_ext_plan", "psi_attn_paged_ext", "psi_attn_tiled_plan", "psi_attn_tiled",
            "psi_block_lowlive", "psi_journal_reset",
@@ -416,6 +418,16 @@ def psi_linear_paged(arena, x, M, K, W: psi_matrix, acc, y, flags=0):
     _hold(arena, W)
     return _check(_lib.psi_linear_paged(arena, _ptr(x), M, K, ctypes.byref(W), _ptr(acc), _ptr(y),
                                         flags), "psi_linear_paged")
+
+
+PSI_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def psi_linear_resident_noalloc(x, M, K, W: psi_matrix, y, flags=0, stream=None):
+    """Projection over resident pages with no arena and no allocation (the
+    K-split accumulator is the library's static per-device array)."""
+    return _check(_lib.psi_linear_resident_noalloc(_ptr(x), M, K, ctypes.byref(W), _ptr(y), flags,
+                                                   stream), "psi_linear_resident_noalloc")
 
 
 def psi_ffn_paged(arena, x, M, d, U: psi_matrix, V: psi_matrix, token_chunks, acc, y, flags=0):
