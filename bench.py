@@ -3,15 +3,19 @@
 
 Default workload: a stack of 8 synthetic transformer blocks (d 4096, 32
 heads of 128, FFN 16384, biases; ~3.2 GB of random BF16 weights in pinned
-host memory), 8192 tokens, fixed 80 MiB arena (2 x 8 MiB pages, 8 MiB
-workspace, scratch), each block output journaled to the host.  One step is
-one invocation of the stack (all 8 blocks); the default 11 timed steps
-mirror the paper's eleven transformer invocations, all on the same input.
+host memory), 8192 tokens, fixed 80 MiB arena (seven 8 MiB page slots, no
+workspace, the FFN's 16 MiB hidden tile in scratch), blocks run in place on
+x, each block output journaled to the host.  One step is one invocation of
+the stack (all 8 blocks); the default 11 timed steps mirror the paper's
+eleven transformer invocations, all on the same input.
 
 Every step streams every weight page from pinned host memory into the
 arena: the metric is TFLOP/s of the paged block operators, reported with
 the fraction of the binding roofline min(MFMA BF16 peak, H2D GB/s x
-FLOP/byte), where H2D GB/s is measured in the same run.
+FLOP/byte), where H2D GB/s is measured in the same run.  The same line
+carries the resident-weight run of the same stack (weights already in HBM,
+no H2D) against the MFMA peak, the dominant kernel against its roofline,
+and the oracle's per-invocation estimate on the host's cores.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported (the build
 runs on one GPU) and exits with a message.
@@ -29,7 +33,7 @@ MiB = 1 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix peak
 HBM_PEAK_GBPS = 8000.0
 
-WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity", "lowlive", "audio8")
+WORKLOADS = ("stack8", "ffn2048", "ffn4096", "attn4096", "ffnsched", "capacity", "lowlive", "audio8", "kernels")
 
 
 def log(*a):
@@ -141,8 +145,57 @@ def build_workload(args, torch, psi, synth):
                     psi.psi_journal_commit(journal, psi.key(s, b, 0, 0), x, M * d * 2, stream)
             state["step"] += 1
 
+        def resident_run():
+            """The same stack with every weight already in HBM (no H2D, no
+            journal): MFMA-bound, reported against the MFMA peak.  Per-launch
+            events time the last of its steps."""
+            rblocks = [psi.resident_block_weights(bw) for bw in blocks]
+            ar = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, args.pages, ws, 0, stream,
+                                                     psi.PSI_ARENA_PROFILE))
+            n = max(3, min(args.steps, 6))
+
+            def rstep():
+                x.copy_(x0)
+                for b in range(nblk):
+                    psi.psi_block_paged(ar, x, None, M, heads, 128, rblocks[b], args.token_chunks, acc, None, 0)
+
+            psi.psi_arena_set_timing(ar, False)
+            rstep()
+            psi.psi_arena_sync(ar)
+            torch.cuda.synchronize()
+            psi.psi_arena_reset_stats(ar)
+            t0 = time.perf_counter()
+            for i in range(n):
+                psi.psi_arena_set_timing(ar, i == n - 1)
+                rstep()
+            torch.cuda.synchronize()
+            psi.psi_arena_sync(ar)
+            dt = time.perf_counter() - t0
+            st = psi.psi_arena_stats(ar)
+            psi.psi_arena_destroy(ar)
+            same = None
+            if journal:
+                ref = np.empty(M * d, np.uint16)
+                psi.psi_journal_read(journal, psi.key(args.warmup + args.steps - 1, nblk - 1), ref, ref.nbytes)
+                same = bool(np.array_equal(ref, x.cpu().numpy().view(np.uint16).ravel()))
+            del rblocks
+            torch.cuda.empty_cache()
+            tf = flops_block * nblk * n / dt / 1e12
+            out = {"value": round(tf, 2), "unit": "TFLOP/s", "ms_per_step": round(dt * 1e3 / n, 3), "steps": n,
+                   "bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "h2d_bytes_per_step": 0, "bitwise_equal_to_paged": same}
+            for name, ms, k, fl in (("gemm", st.gemm_ms, st.gemm_launches, st.gemm_flops),
+                                    ("attention", st.attn_ms, st.attn_launches, st.attn_flops)):
+                if k:
+                    a = fl / (ms * 1e-3) / 1e12
+                    out[name] = {"avg_launch_us": round(ms * 1e3 / k, 2), "launches": k,
+                                 "achieved": round(a, 2), "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+            return out
+
         return dict(step=step, arena=arena, journal=journal, flops=flops_block * nblk,
                     h2d=h2d_block * nblk, live=live, keep=blocks,
+                    after=None if (args.resident or args.no_resident_run) else resident_run,
+                    after_name="resident_weights",
                     config={"workload": "stack of 8 synthetic blocks (self-attention + FFN)",
                             "tokens": M, "d_model": d, "heads": heads, "head_dim": 128,
                             "ffn_hidden": hid, "blocks": nblk, "arena_MiB": 80, "page_MiB": 8,
@@ -372,8 +425,11 @@ def build_workload(args, torch, psi, synth):
                     "weight_h2d_per_block": wh2d_block}
 
         flops_block = (4 * 2.0 * M * d * d) + 4.0 * M * M * 128 * heads + 2 * 2.0 * M * d * hid
+        # algorithmic H2D bytes are the weights; the journal's reloads are the
+        # mode's overhead (reported beside the fraction, not inside it)
         return dict(step=step, arena=arena, journal=journal, flops=flops_block * nblk,
-                    h2d=(wh2d_block + jh2d_block) * nblk, live=live, keep=(low, reg), after=compare,
+                    h2d=wh2d_block * nblk, overhead_h2d=jh2d_block * nblk, live=live, keep=(low, reg),
+                    after=compare,
                     after_name="lowlive",
                     config={"workload": "low-live-state blocks (x the only device state)", "tokens": M,
                             "d_model": d, "heads": heads, "head_dim": 128, "ffn_hidden": hid,
@@ -493,33 +549,130 @@ def committed_traffic(kernel_source, profile):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(seed, budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the default workload:
-    the FFN sub-block of block 0 (Linear 4096->16384, GELU, Linear
-    16384->4096, residual) on a few token rows.  Returns TFLOP/s."""
+def kernel_microbench(torch, psi, synth, reps=20):
+    """Per-launch times of the hot kernels on the stack's shapes, through the
+    C ABI with resident weights in a profiled arena (HIP events around each
+    launch; warm caches, no page copies):
+      gemm_page      y = B(x W^T + b): 8192 x 1024 x 4096, one output-column page
+      gemm_ksplit    fp32 accumulator carried over three K pages of 1024:
+                     8192 x 4096 x 1024 per launch (first page stores the
+                     accumulator, the middle one loads and stores it, the last
+                     loads it and writes B(acc + b))
+      attention_*    8 heads x 8192 queries x 8192 keys, head_dim 128, with
+                     fp32 weights (three BF16 terms), two terms, BF16 weights
+    Returns a dict of {name: {avg_launch_us, achieved TFLOP/s, frac}}."""
+    import numpy as np
+    stream = torch.cuda.current_stream().cuda_stream
+    M = 8192
+    out = {}
+    rng = np.random.default_rng(7)
+
+    def arena():
+        return psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, psi.PSI_ARENA_PROFILE))
+
+    def measure(name, call, kind):
+        a = arena()
+        try:
+            psi.psi_arena_set_timing(a, False)
+            call(a)
+            psi.psi_arena_sync(a)
+            psi.psi_arena_reset_stats(a)
+            psi.psi_arena_set_timing(a, True)
+            for _ in range(reps):
+                call(a)
+            st = psi.psi_arena_stats(a)
+        finally:
+            psi.psi_arena_destroy(a)
+        ms, n, fl = (st.gemm_ms, st.gemm_launches, st.gemm_flops) if kind == "gemm" else \
+            (st.attn_ms, st.attn_launches, st.attn_flops)
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"avg_launch_us": round(ms * 1e3 / n, 2), "launches": n, "achieved": round(tf, 1),
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl / n}
+
+    x = torch.from_numpy(synth.normal_bf16(rng, (M, 4096), 1.0).view("int16")).cuda()
+    Wp = psi.resident_matrix(psi.pinned_matrix(synth.normal_bf16(rng, (1024, 4096), 1.0 / 4096),
+                                               synth.normal_bf16(rng, (1024,), 0.02), psi.PSI_SPLIT_ROWS, 1024))
+    y = torch.empty(M, 1024, dtype=torch.int16, device="cuda")
+    measure("gemm_page_8192x1024x4096", lambda a: psi.psi_linear_paged(a, x, M, 4096, Wp, None, y, 0), "gemm")
+    Wk = psi.resident_matrix(psi.pinned_matrix(synth.normal_bf16(rng, (4096, 3072), 1.0 / 3072),
+                                               synth.normal_bf16(rng, (4096,), 0.02), psi.PSI_SPLIT_COLS, 1024))
+    xk = torch.from_numpy(synth.normal_bf16(rng, (M, 3072), 1.0).view("int16")).cuda()
+    acc = torch.empty(M, 4096, dtype=torch.float32, device="cuda")
+    y2 = torch.empty(M, 4096, dtype=torch.int16, device="cuda")
+    measure("gemm_ksplit_8192x4096x1024", lambda a: psi.psi_linear_paged(a, xk, M, 3072, Wk, acc, y2, 0), "gemm")
+    d, heads = 1024, 8
+    w = synth.attn_weights(rng, d)
+    mats = [psi.resident_matrix(psi.pinned_matrix(w["W" + n], w["b" + n], psi.PSI_SPLIT_ROWS, d)) for n in "qkvo"]
+    xa = torch.from_numpy(synth.normal_bf16(rng, (M, d), 1.0).view("int16")).cuda()
+    ya = torch.empty_like(xa)
+    acc_a = torch.empty(M, d, dtype=torch.float32, device="cuda")
+    for name, fl in (("attention_fp32_weights", 0), ("attention_two_terms", psi.PSI_OP_ATTN_P2),
+                     ("attention_bf16_weights", psi.PSI_OP_BF16_SOFTMAX)):
+        measure(name, lambda a, fl=fl: psi.psi_attn_paged(a, xa, M, None, 0, heads, 128, *mats, acc_a, ya, fl),
+                "attn")
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(seed, budget_s=20.0):
+    """The oracle, as it stands, on bounded samples of one invocation of the
+    default stack, scaled to the whole invocation.  One block is 4
+    projections 4096 -> 4096 over 8,192 rows, attention of 32 heads over
+    8,192 queries x 8,192 keys, and the FFN 4096 -> 16384 -> 4096 over 8,192
+    rows; each part is linear in its row count, so each is timed on a few
+    rows (every thread busy) and scaled.  Returns the estimate in TFLOP/s of
+    the invocation's algorithmic FLOPs."""
     import numpy as np
 
     import oracle
     from memory_bounded_weight_amd import synth
     threads = oracle.threads()
+    M, d, heads, dh, hid, nblk = 8192, 4096, 32, 128, 16384, 8
     w = synth.block_weights(seed, 0)
     x = synth.stack_input(seed)
-    per_row = 2 * 2.0 * 4096 * 16384
-    rows = max(threads, 8)
-    t0 = time.perf_counter()
-    oracle.ffn(np.ascontiguousarray(x[:rows]), w["U"], w["a"], w["V"], w["b"], residual=True)
-    dt = time.perf_counter() - t0
-    if dt < budget_s / 4:
-        rows2 = int(rows * min(budget_s / max(dt, 1e-3), 64)) // threads * threads
-        rows2 = max(rows2, rows)
+    rows = 4 * max(threads, 8)
+    hs = slice(0, dh)
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.ffn(np.ascontiguousarray(x[:rows2]), w["U"], w["a"], w["V"], w["b"], residual=True)
-        dt = time.perf_counter() - t0
-        rows = rows2
-    return {"value": per_row * rows / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"FFN sub-block of block 0 (4096->16384->4096, residual) on {rows} of 8192 "
-                      f"token rows; {dt:.1f} s"}
+        fn()
+        return time.perf_counter() - t0
+
+    # keys and values of head 0 over all 8,192 tokens: the attention sample's inputs
+    t0 = time.perf_counter()
+    K0 = oracle.linear(x, np.ascontiguousarray(w["Wk"][hs]), w["bk"][hs].copy())
+    V0 = oracle.linear(x, np.ascontiguousarray(w["Wv"][hs]), w["bv"][hs].copy())
+    t_kv = time.perf_counter() - t0
+    xr = np.ascontiguousarray(x[:rows])
+    t_q = timed(lambda: oracle.linear(xr, w["Wq"], w["bq"]))
+    per_row_proj = t_q / rows  # seconds per 4096 -> 4096 row
+    Q0 = oracle.linear(xr, np.ascontiguousarray(w["Wq"][hs]), w["bq"][hs].copy())
+    att_rows = rows * 8
+    Qa = np.ascontiguousarray(np.resize(Q0, (att_rows, dh)))
+    t_att = timed(lambda: oracle.attention(Qa, K0, V0, 1, dh))
+    per_row_head_att = t_att / att_rows
+    t_ffn = timed(lambda: oracle.ffn(xr, w["U"], w["a"], w["V"], w["b"], residual=True))
+    per_row_ffn = t_ffn / rows
+    block_s = 4 * M * per_row_proj + heads * M * per_row_head_att + M * per_row_ffn
+    inv_s = nblk * block_s
+    flops_block = 4 * 2.0 * M * d * d + 4.0 * M * M * dh * heads + 2 * 2.0 * M * d * hid
+    sampled = t_kv + t_q + t_att + t_ffn
+    return {"value": nblk * flops_block / inv_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "ms_per_invocation_estimate": round(inv_s * 1e3, 1),
+            "sample": (f"one invocation of the 8-block stack estimated from timed oracle samples of block 0 "
+                       f"({sampled:.1f} s): projections ({rows} rows x 4096->4096 and head-0 K/V over {M} "
+                       f"rows), attention of {att_rows} query rows of one head over {M} keys, FFN on {rows} "
+                       f"rows; per block 4 x {M} projection rows + {heads} x {M} head rows + {M} FFN rows")}
 
 
 def main():
@@ -537,6 +690,8 @@ def main():
     ap.add_argument("--no-journal", action="store_true")
     ap.add_argument("--sync-copy", action="store_true", help="page copies on the compute stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-resident-run", action="store_true",
+                    help="stack: skip the resident-weight run of the same stack after the timed steps")
     ap.add_argument("--pages", type=int, default=None,
                     help="page slots in the 80 MiB stack arena (default 7 with output-tile "
                          "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
@@ -575,6 +730,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": 512 * MiB,
                           "bytes_written": 512 * MiB, "launches": 3}))
+        return
+    if args.workload == "kernels":
+        ks = kernel_microbench(torch, psi, synth, reps=max(args.steps, 5))
+        print(json.dumps({"workload": "kernel micro-benchmark (resident weights, per-launch HIP events)",
+                          "unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFLOPS, "kernels": ks}), flush=True)
         return
     h2d_gbps, h2d_one, h2d_two = measure_h2d_gbps(torch)
     log(f"bench: pinned H2D {h2d_gbps:.1f} GB/s (one stream {h2d_one:.1f}, two streams {h2d_two:.1f})")
@@ -636,6 +796,12 @@ def main():
                    "h2d_GBps_two_streams": round(h2d_two, 2), "flop_per_h2d_byte": round(ai, 1),
                    "roof_tflops": round(roof, 2), "frac": round(value / roof, 4),
                    "h2d_bytes_per_step": wl["h2d"]}
+        if wl.get("overhead_h2d"):
+            # the same time against the copies' whole traffic (weights plus the
+            # journal reloads the mode adds): how close the link itself runs
+            t_link = (wl["h2d"] + wl["overhead_h2d"]) / (h2d_gbps * 1e9)
+            binding["overhead_h2d_bytes_per_step"] = wl["overhead_h2d"]
+            binding["link_busy_frac_incl_overhead"] = round(t_link / (ms_per_step * 1e-3), 4)
 
     roofline = None
     if not args.no_profile:

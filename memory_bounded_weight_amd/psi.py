@@ -578,6 +578,14 @@ def resident_matrix(m: psi_matrix) -> psi_matrix:
     return r
 
 
+def resident_block_weights(bw: psi_block_weights) -> psi_block_weights:
+    """Device-resident copy of a pinned psi_block_weights (same packing)."""
+    mats = {n: resident_matrix(m) for n, m in bw._keepalive.items()}
+    r = psi_block_weights(mats["Wq"], mats["Wk"], mats["Wv"], mats["Wo"], mats["U"], mats["V"])
+    r._keepalive = mats
+    return r
+
+
 def block_weights(w: dict, group_cols: int, hidden_tile: int, resident: bool = False,
                   attn_out_tile: int = 0, ffn_out_tile: int = 0) -> psi_block_weights:
     """psi_block_weights from a dict of host bf16 arrays (Wq..bo, U, a, V, b);
