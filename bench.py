@@ -367,16 +367,26 @@ def build_workload(args, torch, psi, synth):
         # Low-live-state mode ([PSI] sec. III-B: intermediate state retained on
         # device or stored in the host journal): x is the only device state;
         # head-group outputs and FFN hidden tiles live in the journal and are
-        # reloaded for every output tile.  4,991 tokens: one [4991, 16384] BF16
+        # reloaded once per output tile.  4,991 tokens: one [4991, 16384] BF16
         # hidden state is 163,545,088 B, the per-block journal figure the paper
-        # reports (sec. IV).  Two blocks per step; afterwards the same blocks
-        # run as psi_block_paged (device-resident intermediates) for the
-        # footprint, time and bitwise comparison.
+        # reports (sec. IV).  The output tiles are wide and cut into 8 MiB 2-D
+        # page tiles (attention: 2,048 rows x 2 head groups; FFN: 1,024 rows x
+        # 4 hidden tiles), so each head-group output is reloaded twice and
+        # each hidden state four times per block (--lowlive-rows: the
+        # row-split pages of 512 and 256 rows, 8 and 16 reloads).  Two blocks
+        # per step; afterwards the same blocks run as psi_block_paged
+        # (device-resident intermediates) for the footprint, time and bitwise
+        # comparison.
         M, d, heads, hid, nblk = 4991, 4096, 32, 16384, 2
-        gw, th, to_a, to_f = 1024, 1024, 512, 256
+        gw, th = 1024, 1024
+        if args.lowlive_rows:
+            to_a, to_f, tc_a, tc_f = 512, 256, 0, 0
+        else:
+            to_a, to_f, tc_a, tc_f = 2048, 1024, 2048, 4096
         arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, flags))
         ws = [synth.block_weights(args.seed, b, d, hid) for b in range(nblk)]
-        low = [psi.block_weights(w, gw, th, attn_out_tile=to_a, ffn_out_tile=to_f) for w in ws]
+        low = [psi.block_weights(w, gw, th, attn_out_tile=to_a, ffn_out_tile=to_f, attn_out_cols=tc_a,
+                                 ffn_out_cols=tc_f) for w in ws]
         reg = [psi.block_weights(w, gw, th) for w in ws]
         del ws
         x0 = torch.from_numpy(synth.stack_input(args.seed, M, d).view("int16")).cuda()
@@ -435,7 +445,8 @@ def build_workload(args, torch, psi, synth):
                             "d_model": d, "heads": heads, "head_dim": 128, "ffn_hidden": hid,
                             "blocks_per_step": nblk, "arena_MiB": 80, "page_MiB": 8, "pages": 2,
                             "head_group": 8, "ffn_tile": th, "attn_output_tile": to_a,
-                            "ffn_output_tile": to_f, "resident_weights": False})
+                            "ffn_output_tile": to_f, "attn_page_cols": tc_a or d, "ffn_page_cols": tc_f or hid,
+                            "resident_weights": False})
     if args.workload == "audio8":
         # Audio-branch shape ([PSI] sec. II-B, sec. III-A): 8 blocks of 126
         # tokens at d 2,048 (32 heads of 64) with RMS-normalised, rotated Q/K
@@ -695,6 +706,8 @@ def main():
     ap.add_argument("--pages", type=int, default=None,
                     help="page slots in the 80 MiB stack arena (default 7 with output-tile "
                          "O-projection, 3 with the K-split; 2 = the paper's 2 pages + 8 MiB workspace)")
+    ap.add_argument("--lowlive-rows", action="store_true",
+                    help="lowlive: row-split output tiles (512 / 256 rows) instead of 2-D page tiles")
     ap.add_argument("--token-chunks", type=int, default=1,
                     help="stack: token chunks of each FFN (each page serves every chunk; the hidden "
                          "tile holds one chunk's rows)")

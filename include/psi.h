@@ -87,6 +87,11 @@ typedef int psi_status;
 #define PSI_SPLIT_COLS 1 /* page p = columns [p*block, (p+1)*block) of W stored as a
                             contiguous [rows, block] slice: a K-split with a carried fp32
                             accumulator ([PSI] sec. II-B eq. (2), bias added once) */
+#define PSI_SPLIT_TILES 2 /* 2-D page tiles: page (o, q) = rows [o*block, ...) x columns
+                             [q*block_cols, ...) of W stored as a contiguous [rows, cols]
+                             block; pages ordered o-major (p = o * ceil(cols/block_cols) + q).
+                             An output tile of `block` rows may then span several pages
+                             (the output-tile schedules of psi_ffn_tiled and psi_attn_tiled) */
 
 #define PSI_MAX_PAGES 8
 
@@ -143,20 +148,24 @@ typedef struct psi_stats {
 } psi_stats;
 
 /* A weight matrix W[rows, cols] in pinned host memory, already packed into
- * page-contiguous slices by psi_pack_matrix ([PSI] Fig. 1 "checkpoint
- * slices"): page p starts at byte offset p * block * (split == ROWS ? cols :
- * rows) * 2.  The last page may be narrower (ragged). */
+ * page-contiguous slices by psi_pack_matrix or psi_pack_tiles ([PSI] Fig. 1
+ * "checkpoint slices"): for ROWS / COLS page p starts at byte offset
+ * p * block * (split == ROWS ? cols : rows) * 2; for TILES page (o, q) starts
+ * at (o * block * cols + e_o * q * block_cols) * 2 with e_o the rows of row
+ * tile o.  The last page of a row or column may be narrower (ragged). */
 typedef struct psi_matrix {
   const void* pages_host;   /* pinned, packed image of W (rows*cols bf16) */
   const uint16_t* bias_host;/* pinned [rows] bf16, or NULL for no bias */
   int rows;                 /* output features */
   int cols;                 /* input features */
-  int split;                /* PSI_SPLIT_ROWS or PSI_SPLIT_COLS */
-  int block;                /* rows (ROWS) or columns (COLS) per page */
+  int split;                /* PSI_SPLIT_ROWS, PSI_SPLIT_COLS or PSI_SPLIT_TILES */
+  int block;                /* rows (ROWS, TILES) or columns (COLS) per page */
   int resident;             /* 0: streamed through the arena pages.  1: the image and
                                bias are DEVICE pointers (weights already resident in
                                HBM); pages are consumed in place, nothing is copied and
                                no page slot is used (the resident-weight comparison) */
+  int block_cols;           /* TILES: columns per page (a multiple of 8); ignored (0) for
+                               ROWS and COLS */
 } psi_matrix;
 
 /* ------------------------------------------------------------ host utils */
@@ -165,6 +174,12 @@ typedef struct psi_matrix {
  * layout of psi_matrix; dst must hold rows*cols bf16.  Host-only. */
 psi_status psi_pack_matrix(const uint16_t* W, int rows, int cols, int split, int block,
                            void* dst);
+
+/* Pack a row-major W[rows, cols] into the PSI_SPLIT_TILES page image of
+ * block_rows x block_cols pages (row tiles in order, each row tile's column
+ * blocks in order, each page row-major); dst (rows*cols bf16) must not
+ * overlap W.  Host-only.  Errors: PSI_E_INVALID. */
+psi_status psi_pack_tiles(const uint16_t* W, int rows, int cols, int block_rows, int block_cols, void* dst);
 
 /* Number of pages and bytes of page p of a matrix.  Host-only. */
 int psi_matrix_pages(const psi_matrix* m);

@@ -29,16 +29,48 @@ psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split)
   if (!m) return fail(PSI_E_INVALID, std::string(name) + ": null matrix");
   if (m->rows <= 0 || m->cols <= 0 || m->block <= 0)
     return fail(PSI_E_INVALID, std::string(name) + ": non-positive rows/cols/block");
-  if (m->split != PSI_SPLIT_ROWS && m->split != PSI_SPLIT_COLS)
+  if (m->split != PSI_SPLIT_ROWS && m->split != PSI_SPLIT_COLS && m->split != PSI_SPLIT_TILES)
     return fail(PSI_E_INVALID, std::string(name) + ": unknown split");
-  if (expect_split >= 0 && m->split != expect_split)
+  if (expect_split == kSplitOutputTiles) {
+    if (m->split == PSI_SPLIT_COLS)
+      return fail(PSI_E_INVALID, std::string(name) + ": must be split into output tiles (by rows or 2-D tiles)");
+  } else if (m->split == PSI_SPLIT_TILES) {
+    return fail(PSI_E_INVALID, std::string(name) + ": 2-D page tiles serve only the output-tile schedules");
+  } else if (expect_split >= 0 && m->split != expect_split) {
     return fail(PSI_E_INVALID, std::string(name) + (expect_split == PSI_SPLIT_ROWS
                                                          ? ": must be split by rows (output columns)"
                                                          : ": must be split by columns (K-split)"));
+  }
+  if (m->split == PSI_SPLIT_TILES && (m->block_cols <= 0 || m->block_cols % 8 != 0))
+    return fail(PSI_E_ALIGN, std::string(name) + ": 2-D page tiles need block_cols a positive multiple of 8");
   if (m->cols % 8 != 0 || (m->split == PSI_SPLIT_COLS && m->block % 8 != 0))
     return fail(PSI_E_ALIGN, std::string(name) + ": K extents must be multiples of 8 (16-byte rows)");
   if (!m->pages_host) return fail(PSI_E_INVALID, std::string(name) + ": null page image");
   return PSI_OK;
+}
+
+// Column blocks per row tile of a TILES matrix (1 otherwise).
+static int tile_cols_per_row(const psi_matrix* m) {
+  return m->split == PSI_SPLIT_TILES ? (m->cols + m->block_cols - 1) / m->block_cols : 1;
+}
+
+int matrix_page_cols(const psi_matrix* m, int p) {
+  if (m->split == PSI_SPLIT_ROWS) return m->cols;
+  if (m->split == PSI_SPLIT_COLS) return matrix_page_extent(m, p);
+  const int q = p % tile_cols_per_row(m);
+  const int ext = m->cols - q * m->block_cols;
+  return ext < m->block_cols ? ext : m->block_cols;
+}
+
+int matrix_page_col0(const psi_matrix* m, int p) {
+  if (m->split == PSI_SPLIT_ROWS) return 0;
+  if (m->split == PSI_SPLIT_COLS) return p * m->block;
+  return (p % tile_cols_per_row(m)) * m->block_cols;
+}
+
+int matrix_page_row0(const psi_matrix* m, int p) {
+  if (m->split == PSI_SPLIT_COLS) return 0;
+  return (p / tile_cols_per_row(m)) * m->block;
 }
 
 psi_status check_ptr(const void* p, const char* what, bool allow_null) {
@@ -59,7 +91,8 @@ psi_status check_alias(const void* x, size_t xbytes, const void* y, size_t ybyte
 }
 
 int matrix_page_extent(const psi_matrix* m, int p) {
-  int total = m->split == PSI_SPLIT_ROWS ? m->rows : m->cols;
+  if (m->split == PSI_SPLIT_TILES) p /= tile_cols_per_row(m);  // row tile of page p
+  int total = m->split == PSI_SPLIT_COLS ? m->cols : m->rows;
   int start = p * m->block;
   int ext = total - start;
   return ext < m->block ? ext : m->block;
@@ -67,6 +100,13 @@ int matrix_page_extent(const psi_matrix* m, int p) {
 
 MatrixInfo matrix_info(const psi_matrix* m) {
   MatrixInfo mi;
+  if (m->split == PSI_SPLIT_TILES) {
+    const int nq = tile_cols_per_row(m);
+    mi.pages = (m->rows + m->block - 1) / m->block * nq;
+    mi.max_page_bytes = (size_t)(m->block < m->rows ? m->block : m->rows) *
+                        (size_t)(m->block_cols < m->cols ? m->block_cols : m->cols) * 2;
+    return mi;
+  }
   int total = m->split == PSI_SPLIT_ROWS ? m->rows : m->cols;
   mi.pages = (total + m->block - 1) / m->block;
   size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
@@ -75,6 +115,11 @@ MatrixInfo matrix_info(const psi_matrix* m) {
 }
 
 const void* matrix_page_ptr(const psi_matrix* m, int p) {
+  if (m->split == PSI_SPLIT_TILES) {
+    const int nq = tile_cols_per_row(m), o = p / nq, q = p % nq;
+    const size_t off = (size_t)o * m->block * m->cols + (size_t)matrix_page_extent(m, p) * q * m->block_cols;
+    return static_cast<const char*>(m->pages_host) + off * 2;
+  }
   size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
   return static_cast<const char*>(m->pages_host) + (size_t)p * m->block * other * 2;
 }
@@ -111,6 +156,26 @@ psi_status psi_pack_matrix(const uint16_t* W, int rows, int cols, int split, int
   return PSI_OK;
 }
 
+psi_status psi_pack_tiles(const uint16_t* W, int rows, int cols, int block_rows, int block_cols, void* dst) {
+  if (!W || !dst || rows <= 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0)
+    return fail(PSI_E_INVALID, "psi_pack_tiles: bad arguments");
+  uint16_t* out = static_cast<uint16_t*>(dst);
+  const size_t n = (size_t)rows * cols;
+  if (!(out + n <= W || W + n <= out)) return fail(PSI_E_INVALID, "psi_pack_tiles: dst overlaps W");
+  size_t off = 0;
+  for (int r0 = 0; r0 < rows; r0 += block_rows) {
+    const int er = rows - r0 < block_rows ? rows - r0 : block_rows;
+    for (int c0 = 0; c0 < cols; c0 += block_cols) {
+      const int ec = cols - c0 < block_cols ? cols - c0 : block_cols;
+      for (int r = 0; r < er; ++r) {
+        std::memcpy(out + off, W + (size_t)(r0 + r) * cols + c0, (size_t)ec * 2);
+        off += (size_t)ec;
+      }
+    }
+  }
+  return PSI_OK;
+}
+
 int psi_matrix_pages(const psi_matrix* m) {
   if (!m || m->block <= 0) return 0;
   return matrix_info(m).pages;
@@ -118,6 +183,7 @@ int psi_matrix_pages(const psi_matrix* m) {
 
 size_t psi_matrix_page_bytes(const psi_matrix* m, int p) {
   if (!m || p < 0 || p >= psi_matrix_pages(m)) return 0;
+  if (m->split == PSI_SPLIT_TILES) return (size_t)matrix_page_extent(m, p) * matrix_page_cols(m, p) * 2;
   size_t other = m->split == PSI_SPLIT_ROWS ? (size_t)m->cols : (size_t)m->rows;
   return (size_t)matrix_page_extent(m, p) * other * 2;
 }
@@ -245,10 +311,12 @@ psi_status psi_ffn_tiled_plan(const psi_arena_desc* d, int M, int dmodel, const 
   if (schedule != PSI_FFN_REUSE && schedule != PSI_FFN_RECOMPUTE)
     return fail(PSI_E_INVALID, "ffn tiled: unknown schedule");
   if ((st = check_matrix(U, "U", PSI_SPLIT_ROWS))) return st;
-  if ((st = check_matrix(Vo, "V", PSI_SPLIT_ROWS))) return st;
+  if ((st = check_matrix(Vo, "V", kSplitOutputTiles))) return st;
   if (M < 0 || dmodel <= 0 || U->cols != dmodel || Vo->rows != dmodel || Vo->cols != U->rows)
     return fail(PSI_E_INVALID, "ffn tiled: need U [h, d] and V [d, h]");
   if (U->block % 8 != 0) return fail(PSI_E_ALIGN, "ffn tiled: hidden tile must be a multiple of 8");
+  if (Vo->split == PSI_SPLIT_TILES && Vo->block_cols % U->block != 0)
+    return fail(PSI_E_INVALID, "ffn tiled: V's page columns must hold whole hidden tiles");
   if ((st = page_fit(d, U, "U")) || (st = page_fit(d, Vo, "V"))) return st;
   if (schedule == PSI_FFN_RECOMPUTE && d->n_pages < 2 && !(U->resident && Vo->resident))
     return fail(PSI_E_INVALID, "ffn tiled: the recompute schedule holds an output tile while U streams: "
@@ -324,7 +392,7 @@ psi_status psi_attn_tiled_plan(const psi_arena_desc* d, int M, int Mc, int heads
   if ((st = check_matrix(Wq, "Wq", PSI_SPLIT_ROWS)) || (st = check_matrix(Wk, "Wk", PSI_SPLIT_ROWS)) ||
       (st = check_matrix(Wv, "Wv", PSI_SPLIT_ROWS)))
     return st;
-  if ((st = check_matrix(Wo, "Wo", PSI_SPLIT_ROWS))) return st;  // output tiles of the O-projection
+  if ((st = check_matrix(Wo, "Wo", kSplitOutputTiles))) return st;  // output tiles of the O-projection
   const psi_matrix* ms[4] = {Wq, Wk, Wv, Wo};
   for (const psi_matrix* m : ms)
     if (m->rows != dm || m->cols != dm)
@@ -334,6 +402,8 @@ psi_status psi_attn_tiled_plan(const psi_arena_desc* d, int M, int Mc, int heads
     return fail(PSI_E_INVALID, "attention: Wq, Wk, Wv need the same head-group block (a multiple of head_dim)");
   if (gw % 8 != 0 || Wo->block % 8 != 0)
     return fail(PSI_E_ALIGN, "attention: head-group and output tiles must be multiples of 8");
+  if (Wo->split == PSI_SPLIT_TILES && Wo->block_cols % gw != 0)
+    return fail(PSI_E_INVALID, "attention tiled: Wo's page columns must hold whole head groups");
   const char* names[4] = {"Wq", "Wk", "Wv", "Wo"};
   for (int i = 0; i < 4; ++i)
     if ((st = page_fit(d, ms[i], names[i]))) return st;

@@ -104,6 +104,10 @@ struct MatrixInfo {
   int pages;
   size_t max_page_bytes;
 };
+// expect_split: PSI_SPLIT_ROWS / PSI_SPLIT_COLS, -1 for either of the two,
+// or kSplitOutputTiles for the output-tile schedules (ROWS or TILES).
+// TILES is refused everywhere else.
+constexpr int kSplitOutputTiles = -2;
 psi_status check_matrix(const psi_matrix* m, const char* name, int expect_split);
 // A device pointer that must be 16-byte aligned (and non-null unless
 // allow_null): PSI_E_INVALID / PSI_E_ALIGN otherwise.
@@ -126,7 +130,10 @@ inline size_t ffn_chunk_rows(int M, int chunks) {
   return ((size_t)M + chunks - 1) / chunks;
 }
 const void* matrix_page_ptr(const psi_matrix* m, int p);
-int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS) or cols (COLS) in page p
+int matrix_page_extent(const psi_matrix* m, int p);  // rows (ROWS, TILES) or cols (COLS) in page p
+int matrix_page_cols(const psi_matrix* m, int p);    // columns held by page p
+int matrix_page_col0(const psi_matrix* m, int p);    // first column of W in page p
+int matrix_page_row0(const psi_matrix* m, int p);    // first row of W in page p
 
 }  // namespace psi
 

@@ -487,7 +487,10 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   if (st) return st;
   if (schedule == PSI_FFN_REUSE && !j) return fail(PSI_E_INVALID, "ffn tiled: FFN reuse needs a journal");
   if (flags & PSI_OP_STORE_ACC) return fail(PSI_E_INVALID, "ffn tiled: no full accumulator to store");
-  const int nO = psi_matrix_pages(Vo);
+  // output tiles: row tiles of Vo (a page each when split by rows, several
+  // pages of whole hidden tiles each with 2-D page tiles)
+  const int nO = (Vo->rows + Vo->block - 1) / Vo->block;
+  const int nP = psi_matrix_pages(Vo);
   if ((st = check_alias(x, (size_t)M * d * 2, y, (size_t)M * d * 2, true, "ffn tiled"))) return st;
   if (x == y && nO > 1 && schedule != PSI_FFN_REUSE)
     return fail(PSI_E_INVALID, "ffn tiled: with recomputation y may alias x only with a single output tile");
@@ -498,9 +501,13 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
   }
   if (M == 0) return PSI_OK;
   const bool resid = flags & PSI_OP_RESIDUAL;
-  const int th = U->block, to = Vo->block, h = U->rows;
+  const int th = U->block, to = Vo->block;
   const int nJ = psi_matrix_pages(U);
   const bool reuse = schedule == PSI_FFN_REUSE;
+  // hidden tiles J of page p: J * th in [col0, col0 + cols) (whole tiles,
+  // checked by the plan)
+  auto j_first = [&](int p) { return matrix_page_col0(Vo, p) / th; };
+  auto j_end = [&](int p) { return (matrix_page_col0(Vo, p) + matrix_page_cols(Vo, p) + th - 1) / th; };
   ScratchMark mark(a);
   uint16_t* Hb[2];
   Hb[0] = static_cast<uint16_t*>(scratch_alloc(a, (size_t)M * th * 2, &st));
@@ -522,9 +529,9 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
     reqs = ru;
     reqs.insert(reqs.end(), rv.begin(), rv.end());
   } else {
-    for (int o = 0; o < nO; ++o) {
-      reqs.push_back(rv[o]);
-      reqs.insert(reqs.end(), ru.begin(), ru.end());
+    for (int p = 0; p < nP; ++p) {
+      reqs.push_back(rv[p]);
+      for (int J = j_first(p); J < j_end(p); ++J) reqs.push_back(ru[J]);
     }
   }
   // not with the journal's reloads: more pages in flight delay the hidden
@@ -552,19 +559,20 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
     g.baseline_bias = baseline;
     return run_gemm(a, g);
   };
-  // ACC_o (+)= H_J V_o[:, J]^T; the last hidden tile writes y[:, o]
-  auto down = [&](int o, int J, const uint16_t* vpage, const uint16_t* H) -> psi_status {
-    const int eo = matrix_page_extent(Vo, o), ej = matrix_page_extent(U, J);
+  // ACC_o (+)= H_J V[o rows, J cols]^T from page p of row tile o; the last
+  // hidden tile writes y[:, o rows]
+  auto down = [&](int p, int J, const uint16_t* vpage, const uint16_t* H) -> psi_status {
+    const int eo = matrix_page_extent(Vo, p), ej = matrix_page_extent(U, J);
     const bool last = J == nJ - 1;
     GemmArgs g = gemm_args();
     g.A = H; g.lda = ej;
-    g.B = vpage + (size_t)J * th; g.ldb = h;
+    g.B = vpage + ((size_t)J * th - matrix_page_col0(Vo, p)); g.ldb = matrix_page_cols(Vo, p);
     g.M = M; g.N = eo; g.K = ej;
     if (J > 0) { g.acc_in = acc; g.ld_acc_in = eo; }
     if (last) {
       psi_status s2 = bias.get(1, &bb);
       if (s2) return s2;
-      const size_t c0 = (size_t)o * to;
+      const size_t c0 = (size_t)matrix_page_row0(Vo, p);
       g.bias = bb ? bb + c0 : nullptr;
       g.out = y + c0; g.ldo = d;
       if (resid) { g.resid = x + c0; g.ldr = d; }
@@ -589,38 +597,42 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
       if ((st = feeder.take(J, &page)) || (st = up(J, page, Hb[b])) || (st = feeder.give_back(J))) return st;
       if (!a->dry && (st = journal_commit_ev(j, hkey(J), Hb[b], hbytes(J), a->compute, rd[b]))) return st;
     }
-    // down-projection steps t = o * nJ + J read buffer t % 2; the reload of
-    // step t + 1 is issued before the GEMM of step t (after the GEMM of
-    // step t - 1, the buffer's previous reader), so copies overlap GEMMs
-    const int T = nO * nJ;
+    // down-projection steps t (over the pages in order, the hidden tiles of
+    // each page in order) read buffer t % 2; the reload of step t + 1 is
+    // issued before the GEMM of step t (after the GEMM of step t - 1, the
+    // buffer's previous reader), so copies overlap GEMMs
+    std::vector<int> step_j;
+    for (int p = 0; p < nP; ++p)
+      for (int J = j_first(p); J < j_end(p); ++J) step_j.push_back(J);
+    const int T = (int)step_j.size();
     auto issue = [&](int t) -> psi_status {
-      const int J = t % nJ;
+      const int J = step_j[t];
       return journal_reload_ev(j, hkey(J), Hb[t % 2], hbytes(J), a->compute, ld[t % 2]);
     };
     if (!a->dry && (st = issue(0))) return st;
-    for (int o = 0; o < nO; ++o) {
+    int t = 0;
+    for (int p = 0; p < nP; ++p) {
       const uint16_t* vpage;
-      if ((st = feeder.take(nJ + o, &vpage))) return st;
-      for (int J = 0; J < nJ; ++J) {
-        const int t = o * nJ + J;
+      if ((st = feeder.take(nJ + p, &vpage))) return st;
+      for (int J = j_first(p); J < j_end(p); ++J, ++t) {
         if (!a->dry) {
           if (t + 1 < T && (st = issue(t + 1))) return st;
           PSI_HIP(hipStreamWaitEvent(a->compute, ld[t % 2], 0));
         }
-        if ((st = down(o, J, vpage, Hb[t % 2]))) return st;
+        if ((st = down(p, J, vpage, Hb[t % 2]))) return st;
       }
-      if ((st = feeder.give_back(nJ + o))) return st;
+      if ((st = feeder.give_back(nJ + p))) return st;
     }
   } else {
     size_t r = 0;
-    for (int o = 0; o < nO; ++o) {
+    for (int p = 0; p < nP; ++p) {
       const size_t vi = r++;
       const uint16_t* vpage;
       if ((st = feeder.take(vi, &vpage))) return st;
-      for (int J = 0; J < nJ; ++J) {
+      for (int J = j_first(p); J < j_end(p); ++J) {
         const size_t ui = r++;
         if ((st = feeder.take(ui, &page)) || (st = up(J, page, Hb[0])) || (st = feeder.give_back(ui))) return st;
-        if ((st = down(o, J, vpage, Hb[0]))) return st;
+        if ((st = down(p, J, vpage, Hb[0]))) return st;
       }
       if ((st = feeder.give_back(vi))) return st;
     }
@@ -936,7 +948,7 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
   matrix_requests(Wk, rk);
   matrix_requests(Wv, rv);
   matrix_requests(Wo, ro);
-  const int nG = (int)rq.size(), nO = (int)ro.size();
+  const int nG = (int)rq.size(), nP = (int)ro.size();
   for (int g = 0; g < nG; ++g) {
     reqs.push_back(rq[g]);
     reqs.push_back(rk[g]);
@@ -975,30 +987,38 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
     if (ext == gw && (st = probe_commit(a, g, PSI_ROLE_ATTN_O, Q, obytes(g)))) return st;
     if (!a->dry && (st = journal_commit_ev(j, okey(g), Q, obytes(g), a->compute, rd[g % 2]))) return st;
   }
-  // per output tile o: ACC_o = sum over g ascending of O_g Wo[o, g]^T, then
-  // y[:, o] = B(ACC_o + bo_o) (+ x[:, o]); O_g reloads alternate buffers
+  // per output tile o (rows of Wo: one page, or several pages of whole head
+  // groups with 2-D page tiles): ACC_o = sum over g ascending of
+  // O_g Wo[o, g]^T, then y[:, o] = B(ACC_o + bo_o) (+ x[:, o]); O_g reloads
+  // alternate buffers
   scratch_reset(a, phase_mark);
   float* acc = static_cast<float*>(scratch_alloc(a, (size_t)M * to * 4, &st));
   if (st) return st;
-  const int T = nO * nG;
+  auto g_first = [&](int p) { return matrix_page_col0(Wo, p) / gw; };
+  auto g_end = [&](int p) { return (matrix_page_col0(Wo, p) + matrix_page_cols(Wo, p) + gw - 1) / gw; };
+  std::vector<int> step_g;
+  for (int p = 0; p < nP; ++p)
+    for (int g = g_first(p); g < g_end(p); ++g) step_g.push_back(g);
+  const int T = (int)step_g.size();
   auto issue = [&](int t) -> psi_status {
-    const int g = t % nG;
+    const int g = step_g[t];
     return journal_reload_ev(j, okey(g), Ob[t % 2], obytes(g), a->compute, ld[t % 2]);
   };
   if (!a->dry && (st = issue(0))) return st;
-  for (int o = 0; o < nO; ++o) {
-    const int eo = matrix_page_extent(Wo, o);
-    const size_t c0 = (size_t)o * to;
-    if ((st = feeder.take(3 * nG + o, &page))) return st;
-    for (int g = 0; g < nG; ++g) {
-      const int t = o * nG + g;
+  int t = 0;
+  for (int p = 0; p < nP; ++p) {
+    const int eo = matrix_page_extent(Wo, p);
+    const size_t c0 = (size_t)matrix_page_row0(Wo, p);
+    if ((st = feeder.take(3 * nG + p, &page))) return st;
+    for (int g = g_first(p); g < g_end(p); ++g, ++t) {
       const int ext = matrix_page_extent(Wq, g);
       if (!a->dry) {
         if (t + 1 < T && (st = issue(t + 1))) return st;
         PSI_HIP(hipStreamWaitEvent(a->compute, ld[t % 2], 0));
       }
       GemmArgs G = gemm_args();
-      G.A = Ob[t % 2]; G.lda = ext; G.B = page + (size_t)g * gw; G.ldb = dm;
+      G.A = Ob[t % 2]; G.lda = ext;
+      G.B = page + ((size_t)g * gw - matrix_page_col0(Wo, p)); G.ldb = matrix_page_cols(Wo, p);
       G.M = M; G.N = eo; G.K = ext;
       G.baseline_bias = bbase;
       if (g > 0) { G.acc_in = acc; G.ld_acc_in = eo; }
@@ -1010,7 +1030,7 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
       }
       if ((st = run_gemm(a, G))) return st;
     }
-    if ((st = feeder.give_back(3 * nG + o))) return st;
+    if ((st = feeder.give_back(3 * nG + p))) return st;
   }
   return bias.release();
 }

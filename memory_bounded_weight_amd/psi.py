@@ -65,6 +65,7 @@ PSI_FFN_RECOMPUTE = 2
 
 PSI_SPLIT_ROWS = 0
 PSI_SPLIT_COLS = 1
+PSI_SPLIT_TILES = 2
 PSI_MAX_PAGES = 8
 PSI_JOURNAL_SYNC = 0x1
 PSI_JOURNAL_RING = 0x2
@@ -111,7 +112,7 @@ class psi_trace_event(ctypes.Structure):
 
 class psi_matrix(ctypes.Structure):
     _fields_ = [("pages_host", _vp), ("bias_host", _vp), ("rows", _i), ("cols", _i),
-                ("split", _i), ("block", _i), ("resident", _i)]
+                ("split", _i), ("block", _i), ("resident", _i), ("block_cols", _i)]
 
 
 class psi_block_weights(ctypes.Structure):
@@ -154,6 +155,7 @@ def _sig(name, args, res=_i):
 
 
 _sig("psi_pack_matrix", [_vp, _i, _i, _i, _i, _vp])
+_sig("psi_pack_tiles", [_vp, _i, _i, _i, _i, _vp])
 _sig("psi_matrix_pages", [_P(psi_matrix)])
 _sig("psi_matrix_page_bytes", [_P(psi_matrix), _i], _sz)
 _sig("psi_arena_plan", [_P(psi_arena_desc), _P(psi_arena_layout)])
@@ -205,7 +207,7 @@ _sig("psi_journal_read", [_vp, psi_key, _vp, _sz])
 _sig("psi_journal_counters", [_vp, _P(ctypes.c_uint64), _P(ctypes.c_uint64), _P(ctypes.c_uint64)])
 
 #: every symbol the header declares (checked by the CPU test suite)
-EXPORTS = ["psi_pack_matrix", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_arena_plan",
+EXPORTS = ["psi_pack_matrix", "psi_pack_tiles", "psi_matrix_pages", "psi_matrix_page_bytes", "psi_arena_plan",
            "psi_linear_plan", "psi_ffn_plan", "psi_attn_plan", "psi_last_error", "psi_version",
            "psi_arena_create", "psi_arena_destroy", "psi_arena_sync", "psi_arena_set_timing",
            "psi_arena_stats",
@@ -262,8 +264,13 @@ def psi_pack_matrix(W, rows, cols, split, block, dst):
     return _check(_lib.psi_pack_matrix(_ptr(W), rows, cols, split, block, _ptr(dst)), "psi_pack_matrix")
 
 
-def make_matrix(pages_host, bias_host, rows, cols, split, block, resident=0) -> psi_matrix:
-    return psi_matrix(_ptr(pages_host), _ptr(bias_host), rows, cols, split, block, int(resident))
+def psi_pack_tiles(W, rows, cols, block_rows, block_cols, dst):
+    return _check(_lib.psi_pack_tiles(_ptr(W), rows, cols, block_rows, block_cols, _ptr(dst)), "psi_pack_tiles")
+
+
+def make_matrix(pages_host, bias_host, rows, cols, split, block, resident=0, block_cols=0) -> psi_matrix:
+    return psi_matrix(_ptr(pages_host), _ptr(bias_host), rows, cols, split, block, int(resident),
+                      int(block_cols))
 
 
 def psi_matrix_pages(m: psi_matrix) -> int:
@@ -545,23 +552,27 @@ def psi_journal_counters(j):
 
 # ------------------------------------------------------ pinned weight images
 
-def pinned_matrix(W, bias, split, block) -> psi_matrix:
+def pinned_matrix(W, bias, split, block, block_cols=0) -> psi_matrix:
     """Pack a host bf16 matrix (numpy uint16 [rows, cols]) into a pinned page
     image (torch pinned memory is plumbing only) and describe it as a
-    psi_matrix.  The returned structure keeps the pinned buffers alive."""
+    psi_matrix (``block_cols`` for PSI_SPLIT_TILES).  The returned structure
+    keeps the pinned buffers alive."""
     import numpy as np
     import torch
     W = np.ascontiguousarray(W, dtype=np.uint16)
     rows, cols = W.shape
     img = torch.empty(rows * cols, dtype=torch.int16, pin_memory=True)
-    psi_pack_matrix(W, rows, cols, split, block, img)
+    if split == PSI_SPLIT_TILES:
+        psi_pack_tiles(W, rows, cols, block, block_cols, img)
+    else:
+        psi_pack_matrix(W, rows, cols, split, block, img)
     b = None
     if bias is not None:
         bias = np.ascontiguousarray(bias, dtype=np.uint16)
         assert bias.shape == (rows,)
         b = torch.empty(rows, dtype=torch.int16, pin_memory=True)
         b.copy_(torch.from_numpy(bias.view(np.int16)))
-    m = make_matrix(img, b, rows, cols, split, block)
+    m = make_matrix(img, b, rows, cols, split, block, 0, block_cols)
     m._keepalive = (img, b)
     return m
 
@@ -573,7 +584,7 @@ def resident_matrix(m: psi_matrix) -> psi_matrix:
     img, b = m._keepalive
     dimg = img.to("cuda", non_blocking=False)
     db = b.to("cuda", non_blocking=False) if b is not None else None
-    r = make_matrix(dimg, db, m.rows, m.cols, m.split, m.block, 1)
+    r = make_matrix(dimg, db, m.rows, m.cols, m.split, m.block, 1, m.block_cols)
     r._keepalive = (dimg, db)
     return r
 
@@ -587,19 +598,26 @@ def resident_block_weights(bw: psi_block_weights) -> psi_block_weights:
 
 
 def block_weights(w: dict, group_cols: int, hidden_tile: int, resident: bool = False,
-                  attn_out_tile: int = 0, ffn_out_tile: int = 0) -> psi_block_weights:
+                  attn_out_tile: int = 0, ffn_out_tile: int = 0, attn_out_cols: int = 0,
+                  ffn_out_cols: int = 0) -> psi_block_weights:
     """psi_block_weights from a dict of host bf16 arrays (Wq..bo, U, a, V, b);
     ``resident`` places the page images in device memory instead.  With
     ``attn_out_tile`` / ``ffn_out_tile`` set, Wo / V are split by rows into
-    output tiles of that many rows (the layout psi_block_lowlive takes);
-    otherwise by columns (psi_block_paged).  The returned structure holds
-    (copies of) the six psi_matrix values and keeps the Python objects that
-    own their buffers alive."""
+    output tiles of that many rows (the layout psi_block_lowlive takes), and
+    with ``attn_out_cols`` / ``ffn_out_cols`` also set into 2-D page tiles of
+    that many columns; otherwise by columns (psi_block_paged).  The returned
+    structure holds (copies of) the six psi_matrix values and keeps the
+    Python objects that own their buffers alive."""
+    def out_tiles(W, b, rows, cols):
+        if cols:
+            return pinned_matrix(W, b, PSI_SPLIT_TILES, rows, cols)
+        return pinned_matrix(W, b, PSI_SPLIT_ROWS, rows)
+
     mats = {n: pinned_matrix(w[n], w["b" + n[1]], PSI_SPLIT_ROWS, group_cols) for n in ("Wq", "Wk", "Wv")}
-    mats["Wo"] = (pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_ROWS, attn_out_tile) if attn_out_tile else
+    mats["Wo"] = (out_tiles(w["Wo"], w["bo"], attn_out_tile, attn_out_cols) if attn_out_tile else
                   pinned_matrix(w["Wo"], w["bo"], PSI_SPLIT_COLS, group_cols))
     mats["U"] = pinned_matrix(w["U"], w["a"], PSI_SPLIT_ROWS, hidden_tile)
-    mats["V"] = (pinned_matrix(w["V"], w["b"], PSI_SPLIT_ROWS, ffn_out_tile) if ffn_out_tile else
+    mats["V"] = (out_tiles(w["V"], w["b"], ffn_out_tile, ffn_out_cols) if ffn_out_tile else
                  pinned_matrix(w["V"], w["b"], PSI_SPLIT_COLS, hidden_tile))
     if resident:
         mats = {n: resident_matrix(m) for n, m in mats.items()}

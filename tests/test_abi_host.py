@@ -607,3 +607,68 @@ def test_scratch_lent_as_page_slots_dry_run():
             assert s.scratch_high_water == 8192 * 1024 * 2
         finally:
             psi.psi_arena_destroy(a)
+
+
+def test_pack_tiles_layout():
+    """PSI_SPLIT_TILES page image: row tiles in order, each row tile's column
+    blocks in order, each page a contiguous row-major block (ragged last row
+    tile and column block); page counts and sizes follow."""
+    rows, cols, br, bc = 10, 24, 4, 16
+    W = np.arange(rows * cols, dtype=np.uint16).reshape(rows, cols)
+    img = np.empty(rows * cols, np.uint16)
+    psi.psi_pack_tiles(W, rows, cols, br, bc, img)
+    expect = np.concatenate([W[r0:r0 + br, c0:c0 + bc].ravel() for r0 in range(0, rows, br)
+                             for c0 in range(0, cols, bc)])
+    assert np.array_equal(img, expect)
+    m = psi.make_matrix(img, None, rows, cols, psi.PSI_SPLIT_TILES, br, 0, bc)
+    assert psi.psi_matrix_pages(m) == 3 * 2
+    sizes = [psi.psi_matrix_page_bytes(m, p) for p in range(6)]
+    assert sizes == [4 * 16 * 2, 4 * 8 * 2, 4 * 16 * 2, 4 * 8 * 2, 2 * 16 * 2, 2 * 8 * 2]
+    assert sum(sizes) == rows * cols * 2
+    with pytest.raises(psi.PsiError):
+        psi.psi_pack_tiles(W, rows, cols, br, bc, W)  # in place is refused
+
+
+def test_two_d_page_tiles_rules_and_lowlive_traffic_dry_run():
+    """2-D page tiles serve only the output-tile schedules: the projection,
+    the paged attention and the paged FFN refuse them; the tiled FFN needs
+    whole hidden tiles per page and the tiled attention whole head groups.
+    In a low-live block, output tiles of 1,024 (FFN, 4 pages each) and 2,048
+    rows (attention, 2 pages each) stream the same pages as narrow tiles but
+    reload each hidden state 4 times instead of 16 and each head-group output
+    2 times instead of 8 ([PSI] sec. IV-C quantifies this journal traffic)."""
+    d, h, M, gw, th = 4096, 16384, 4991, 1024, 1024
+    T = lambda r, c, br, bc: psi.make_matrix(0x1000, 0x2000, r, c, psi.PSI_SPLIT_TILES, br, 0, bc)
+    dsc = desc(80, 8, 2)
+    q, k, v = [fake_matrix(d, d, psi.PSI_SPLIT_ROWS, gw) for _ in range(3)]
+    U = fake_matrix(h, d, psi.PSI_SPLIT_ROWS, th)
+    Vt, Wot = T(d, h, 1024, 4096), T(d, d, 2048, 2048)
+    assert psi.psi_linear_plan(dsc, 64, d, Wot)[0] == psi.PSI_E_INVALID
+    assert psi.psi_attn_plan(dsc, 64, 0, 32, 128, q, k, v, Wot)[0] == psi.PSI_E_INVALID
+    assert psi.psi_ffn_tiled_plan(dsc, M, d, U, T(d, h, 1024, 3072), psi.PSI_FFN_REUSE)[0] == psi.PSI_OK
+    assert psi.psi_ffn_tiled_plan(dsc, M, d, U, T(d, h, 1024, 2040), psi.PSI_FFN_REUSE)[0] == psi.PSI_E_INVALID
+    assert psi.psi_ffn_tiled_plan(dsc, M, d, U, T(d, h, 1024, 8192), psi.PSI_FFN_REUSE)[0] == \
+        psi.PSI_E_PAGE_TOO_SMALL
+    assert psi.psi_attn_tiled_plan(dsc, M, 0, 32, 128, q, k, v, T(d, d, 2048, 1536))[0] == psi.PSI_E_INVALID
+    st, need_f = psi.psi_ffn_tiled_plan(dsc, M, d, U, Vt, psi.PSI_FFN_REUSE)
+    assert st == psi.PSI_OK and need_f == 2 * (-(-M * th * 2 // 256) * 256) + -(-M * 1024 * 4 // 256) * 256
+    st, need_a = psi.psi_attn_tiled_plan(dsc, M, 0, 32, 128, q, k, v, Wot)
+    assert st == psi.PSI_OK
+    counts = {}
+    for name, Wo, V in (("rows", fake_matrix(d, d, psi.PSI_SPLIT_ROWS, 512), fake_matrix(d, h, psi.PSI_SPLIT_ROWS, 256)),
+                        ("tiles", Wot, Vt)):
+        a = psi.psi_arena_create(dsc)
+        try:
+            psi.psi_block_lowlive(a, 0x10000, M, 32, 128, psi.psi_block_weights(q, k, v, Wo, U, V), 0x20000, 0)
+            s = psi.psi_arena_stats(a)
+            counts[name] = (s.page_copies, s.bytes_h2d, s.kernel_launches)
+        finally:
+            psi.psi_arena_destroy(a)
+    nG, nJ = d // gw, h // th
+    weights = 4 * d * d * 2 + 2 * d * h * 2 + (4 * d + h + d) * 2
+    assert counts["rows"][:2] == (3 * nG + 8 + nJ + 16, weights)  # Wo in 8 pages of 4 MiB
+    assert counts["tiles"][:2] == (3 * nG + 4 + nJ + 16, weights)  # Wo in 4 pages of 8 MiB
+    # GEMMs: per group Q, K, V^T (+ attention); O-projection one per (row tile, group);
+    # FFN one up per hidden tile and one down per (row tile, hidden tile)
+    assert counts["rows"][2] == 4 * nG + 8 * nG + nJ + 16 * nJ
+    assert counts["tiles"][2] == 4 * nG + 2 * nG + nJ + 4 * nJ

@@ -185,3 +185,62 @@ def test_lowlive_block_ragged_medium_size_matches_paged(P):
     finally:
         P.psi_journal_destroy(j)
         P.psi_arena_destroy(ar)
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+def test_two_d_page_tiles_bitwise(P, recompute):
+    """2-D page tiles (PSI_SPLIT_TILES): wide output tiles cut into pages of
+    whole hidden tiles / head groups, with ragged row tiles, ragged column
+    pages and a ragged last hidden tile, give the bits of the row-split
+    output tiles and of psi_block_paged, and reload each journaled hidden
+    state once per row tile (777 tokens, d 1,024, FFN 3,960 in 800-channel
+    tiles, the last 760: V in 320 x 2,400 pages, Wo in 384 x 512 pages)."""
+    M, d, heads, h, gw, th = 777, 1024, 8, 3960, 256, 800
+    x0 = synth.stack_input(49, M, d)
+    w = synth.block_weights(49, 0, d, h)
+    ar = make_arena(32 * MiB, 4 * MiB, 3)
+    j = P.psi_journal_create(MiB, 2, M * (d + h) * 2 + MiB)
+    try:
+        xr = dev(x0)
+        xt = torch.empty_like(xr)
+        acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
+        P.psi_block_paged(ar, xr, xt, M, heads, 128, P.block_weights(w, gw, th), 1, acc, None, 0)
+        ref = host(xr)
+        # the FFN alone, row-split against 2-D tiles, on the same input
+        U = P.pinned_matrix(w["U"], w["a"], P.PSI_SPLIT_ROWS, th)
+        Vr = P.pinned_matrix(w["V"], w["b"], P.PSI_SPLIT_ROWS, 320)
+        Vt = P.pinned_matrix(w["V"], w["b"], P.PSI_SPLIT_TILES, 320, 2400)
+        assert P.psi_matrix_pages(Vt) == 4 * 2
+        sched = P.PSI_FFN_RECOMPUTE if recompute else P.PSI_FFN_REUSE
+        outs, reloads = [], []
+        for V in (Vr, Vt):
+            P.psi_journal_reset(j)
+            P.psi_journal_sync(j)
+            _, h2d0, _ = P.psi_journal_counters(j)
+            y = empty_bf16(M, d)
+            P.psi_ffn_tiled(ar, dev(x0), M, d, U, V, sched, j, 0, 1, y, P.PSI_OP_RESIDUAL)
+            P.psi_arena_sync(ar)
+            P.psi_journal_sync(j)
+            outs.append(host(y))
+            reloads.append(P.psi_journal_counters(j)[1] - h2d0)
+        assert np.array_equal(outs[0], outs[1])
+        if not recompute:
+            assert reloads == [4 * M * h * 2, 4 * M * h * 2]  # one reload per row tile (4 either way)
+        if recompute:
+            return
+        # the whole low-live block with 2-D tiles in both output-tile schedules
+        xl = dev(x0)
+        bw = P.block_weights(w, gw, th, attn_out_tile=384, ffn_out_tile=1024, attn_out_cols=512,
+                             ffn_out_cols=1600)
+        P.psi_journal_reset(j)
+        P.psi_journal_sync(j)
+        _, h2d0, _ = P.psi_journal_counters(j)
+        P.psi_block_lowlive(ar, xl, M, heads, 128, bw, j, 0)
+        P.psi_arena_sync(ar)
+        P.psi_journal_sync(j)
+        assert np.array_equal(host(xl), ref)
+        _, h2d1, _ = P.psi_journal_counters(j)
+        assert h2d1 - h2d0 == 3 * M * d * 2 + 1 * M * h * 2  # 3 attention row tiles, 1 FFN row tile
+    finally:
+        P.psi_journal_destroy(j)
+        P.psi_arena_destroy(ar)
