@@ -318,12 +318,17 @@ def build_workload(args, torch, psi, synth):
         U = psi.pinned_matrix(c["U"], c["a"], psi.PSI_SPLIT_ROWS, th)
         V = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_COLS, th)
         Vo = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_ROWS, to)
+        # the same schedules over output tiles of 1,024 rows in 2-D page tiles
+        # of two hidden tiles (1,024 x 4,096 = 8 MiB): half the row tiles, so
+        # half the reloads (reuse) or half the U re-streaming (recompute)
+        to2, tc2 = 1024, 4096
+        Vo2 = psi.pinned_matrix(c["V"], c["b"], psi.PSI_SPLIT_TILES, to2, tc2)
         arena = psi.psi_arena_create(psi.arena_desc(32 * MiB, 8 * MiB, 2, 0, 0, stream, flags))
         x = torch.from_numpy(c["x"].view("int16")).cuda()
         y = torch.empty_like(x)
         live += [x, y]
         runs = args.warmup + args.steps
-        journal = psi.psi_journal_create(8 * MiB, 2, runs * hid * M * 2)
+        journal = psi.psi_journal_create(8 * MiB, 2, hid * M * 2 + MiB)
 
         def step():
             psi.psi_ffn_paged(arena, x, M, d, U, V, 1, None, y, 0)
@@ -333,7 +338,9 @@ def build_workload(args, torch, psi, synth):
             psi.psi_arena_sync(arena)
             ref = y.cpu().numpy()
             res = {}
-            for name, sched in (("reuse", psi.PSI_FFN_REUSE), ("recompute", psi.PSI_FFN_RECOMPUTE)):
+            for name, sched, vm in (("reuse", psi.PSI_FFN_REUSE, Vo), ("recompute", psi.PSI_FFN_RECOMPUTE, Vo),
+                                    ("reuse_2d_tiles", psi.PSI_FFN_REUSE, Vo2),
+                                    ("recompute_2d_tiles", psi.PSI_FFN_RECOMPUTE, Vo2)):
                 yt = torch.empty_like(x)
                 s0 = psi.psi_arena_stats(arena)
                 j0 = psi.psi_journal_counters(journal)
@@ -341,8 +348,8 @@ def build_workload(args, torch, psi, synth):
                 for r in range(runs):
                     torch.cuda.synchronize()
                     t = time.perf_counter()
-                    psi.psi_ffn_tiled(arena, x, M, d, U, Vo, sched, journal, r, 0 if name == "reuse" else 1,
-                                      yt, 0)
+                    psi.psi_journal_reset(journal)
+                    psi.psi_ffn_tiled(arena, x, M, d, U, vm, sched, journal, r, 0, yt, 0)
                     psi.psi_arena_sync(arena)
                     psi.psi_journal_sync(journal)
                     torch.cuda.synchronize()
@@ -358,10 +365,11 @@ def build_workload(args, torch, psi, synth):
             return res
 
         return dict(step=step, arena=arena, journal=None, flops=2 * 2.0 * M * d * hid,
-                    h2d=2 * d * hid * 2 + (hid + d) * 2, live=live, keep=(U, V, Vo, journal),
+                    h2d=2 * d * hid * 2 + (hid + d) * 2, live=live, keep=(U, V, Vo, Vo2, journal),
                     after=schedules, after_name="schedules", close=lambda: psi.psi_journal_destroy(journal),
                     config={"workload": f"FFN schedules d={d} hidden={hid}", "tokens": M,
-                            "ffn_tile": th, "output_tile": to, "arena_MiB": 32, "page_MiB": 8,
+                            "ffn_tile": th, "output_tile": to, "output_tile_2d": [to2, tc2], "arena_MiB": 32,
+                            "page_MiB": 8,
                             "pages": 2, "resident_weights": False})
     if args.workload == "lowlive":
         # Low-live-state mode ([PSI] sec. III-B: intermediate state retained on
