@@ -80,6 +80,11 @@ typedef int psi_status;
 #define PSI_OP_ATTN_P2 0x10u      /* attention: fp32 weights carried as two BF16 terms
                                      (about 17 significant bits; one MFMA fewer per
                                      step); ignored with PSI_OP_BF16_SOFTMAX */
+#define PSI_OP_ATTN_PIPELINED 0x20u /* attention: run the lock-step pipelined kernel at
+                                       every size instead of the automatic choice (the
+                                       ping-pong kernel for 256 or more workgroups of
+                                       256 queries, else 128-query workgroups); the
+                                       same bits, a comparison path */
 
 /* -------------------------------------------------------- matrix layouts */
 #define PSI_SPLIT_ROWS 0 /* page p = rows [p*block, (p+1)*block) of W: an output-column

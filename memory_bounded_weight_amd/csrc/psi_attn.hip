@@ -517,10 +517,371 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
   }
 }
 
+// Ping-pong variant.  The vector work of a key tile (mask, maximum, exp2,
+// normaliser, rescale, BF16 split) and its matrix work (P.V of the tile and
+// the scores of the next) are separate phases, and the two waves that share
+// a SIMD run opposite phases: waves 0-3 (queries 0-127 of the workgroup)
+// run the vector phase of tile t while waves 4-7 (queries 128-255) run the
+// matrix phase of tile t-1 and the scores of tile t, then they swap at a
+// workgroup barrier.  A SIMD's matrix core then works on one wave's MFMAs
+// while its vector unit works on the other wave's softmax, where in
+// attn_kernel_pipe both waves of a SIMD reach the same phase together.
+// Per query the arithmetic and its order are those of attn_kernel_pipe (same
+// score chains, softmax updates, split and P.V sequence per accumulator), so
+// the bits are the same.
+//
+// Half-iteration h (one barrier after each): group A (waves 0-3) runs the
+// vector phase V(t) at h = 2t and the matrix phase M(t) = P.V(t) + S(t+1) at
+// h = 2t+1; group B runs S(0) at h = 0, V(t) at h = 2t+1 and M(t) at
+// h = 2t+2.  Tile i's K is read at h = 2i-1 and 2i (the groups' S(i)), its
+// V^T at h = 2i+1 and 2i+2 (their P.V(i)); three LDS buffers of each hold
+// the tiles.  Group A stages K: the global loads of K(i) at the start of
+// its M(i-2) (h = 2i-3), the LDS stores at the end of its V(i-1)
+// (h = 2i-2), after K(i-3) was last read at h = 2i-6.  Group B stages V^T
+// the same way one half-iteration later: loads at the start of its M(i-2)
+// (h = 2i-2), stores at the end of its V(i-1) (h = 2i-1), after V^T(i-3)
+// was last read at h = 2i-4.  Each group runs its own loop (2 ntiles + 2
+// barriers in both), so that the compiler allocates registers for one
+// group's phases at a time.
+template <int NP, int DH>
+__global__ __launch_bounds__(512) void attn_kernel_pp(AttnArgs p) {
+  constexpr int QB = 256;
+  constexpr int KS = DH + 8;
+  constexpr int CPRK = DH / 8;
+  constexpr int NT = QB;                  // the 256 threads of one group stage a part
+  constexpr int KCH = KT * DH / 8 / NT;   // 16-byte K chunks per thread of group A
+  constexpr int VCH = DH * KT / 8 / NT;   // 16-byte V^T chunks per thread of group B
+  constexpr int NB = 3;
+  constexpr int KSTEPS = DH / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NB][KT * KS];
+  // V^T rows of 72 elements (144 B: 16-byte aligned, 16 lanes reading
+  // 16 bytes each at row stride 36 banks touch all 64 banks once)
+  constexpr int VP = KT + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NB][DH * VP];
+
+  const int tid = threadIdx.x;
+  const int gtid = tid & (NT - 1);  // thread index inside its group
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool group_a = wave < 4;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int h = blockIdx.y;
+  const int qrow = blockIdx.x * QB + wave * 32 + l32;
+  const bool qvalid = qrow < p.Mq;
+  const float c = p.alpha * 1.4426950408889634f;
+
+  bf16x8 qf[KSTEPS];
+  {
+    const int qr = qvalid ? qrow : p.Mq - 1;
+    const uint16_t* qp = p.q + (long)qr * p.ldq + h * DH + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qp + kk * 16));
+  }
+
+  // Tile staging as attn_kernel_pipe's, split by operand: K rows past Mk are
+  // clamped (their scores are masked), V^T entries past Mk are zeroed.
+  uint4 rs[KCH > VCH ? KCH : VCH];
+  const uint16_t* kbase = p.k + h * DH;
+  const uint16_t* vbase = p.vt + (long)h * DH * p.ldvt;
+  // Byte offsets of this thread's chunks inside a full tile, so that a tile
+  // costs one wave-uniform base address (scalar arithmetic) plus these.
+  uint32_t koff[KCH > VCH ? KCH : VCH];
+#pragma unroll
+  for (int i = 0; i < (KCH > VCH ? KCH : VCH); ++i) {
+    const int c2 = gtid + i * NT;
+    koff[i] = group_a ? (uint32_t)(((long)(c2 / CPRK) * p.ldk + (c2 % CPRK) * 8) * 2)
+                      : (uint32_t)(((long)(c2 >> 3) * p.ldvt + (c2 & 7) * 8) * 2);
+  }
+  auto load_k = [&](int key0) {
+    if (key0 + KT <= p.Mk) {
+      const char* base = reinterpret_cast<const char*>(kbase + (long)key0 * p.ldk);
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) rs[i] = *reinterpret_cast<const uint4*>(base + koff[i]);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = gtid + i * NT;
+      int key = key0 + c2 / CPRK;
+      key = key < p.Mk ? key : p.Mk - 1;
+      rs[i] = *reinterpret_cast<const uint4*>(kbase + (long)key * p.ldk + (c2 % CPRK) * 8);
+    }
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      int c2 = gtid + i * NT;
+      *reinterpret_cast<uint4*>(&k_lds[buf][(c2 / CPRK) * KS + (c2 % CPRK) * 8]) = rs[i];
+    }
+  };
+  auto load_v = [&](int key0) {
+    if (key0 + KT <= p.Mk) {
+      const char* base = reinterpret_cast<const char*>(vbase + key0);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) rs[i] = *reinterpret_cast<const uint4*>(base + koff[i]);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = gtid + i * NT;
+      int vr = c2 >> 3, vkey = key0 + (c2 & 7) * 8;
+      {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (vkey < p.Mk) {
+          v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+          const int keep = p.Mk - vkey;
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t mlo = (2 * q < keep) ? 0x0000FFFFu : 0u;
+            const uint32_t mhi = (2 * q + 1 < keep) ? 0xFFFF0000u : 0u;
+            w[q] &= (mlo | mhi);
+          }
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        rs[i] = v;
+      }
+    }
+  };
+  // Within each 16-key group the V^T row holds the keys in the order of the
+  // P^T operand's lanes: keys 0-3 and 8-11 (read by lanes 0-31), then 4-7
+  // and 12-15 (lanes 32-63), so that one fragment is one 16-byte read.  A
+  // chunk of 8 keys starting at an even multiple of 8 puts keys 0-3 at
+  // positions 0-3 and 4-7 at 8-11; an odd one puts 8-11 at 4-7 and 12-15
+  // at 12-15.
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      int c2 = gtid + i * NT;
+      uint16_t* row = &v_lds[buf][(c2 >> 3) * VP + ((c2 & 7) >> 1) * 16 + (c2 & 1) * 4];
+      *reinterpret_cast<uint2*>(row) = make_uint2(rs[i].x, rs[i].y);
+      *reinterpret_cast<uint2*>(row + 8) = make_uint2(rs[i].z, rs[i].w);
+    }
+  };
+  auto kfrag = [&](int buf, int kb, int kk) {
+    return *reinterpret_cast<const bf16x8*>(&k_lds[buf][(kb * 32 + l32) * KS + kk * 16 + half * 8]);
+  };
+  auto vfrag = [&](int buf, int g, int dt) {
+    return *reinterpret_cast<const bf16x8*>(&v_lds[buf][(dt * 32 + l32) * VP + 16 * g + 8 * half]);
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+  f32x16 s[2];
+  bf16x8 bt[NP][4];
+
+  // The matrix phase runs one wave's MFMAs with no other MFMA stream on its
+  // SIMD to hide LDS latency behind, so fragments are read well ahead: the
+  // reads of P.V group g+1 are issued with the MFMAs of group g, the K
+  // fragments of score step kk+KPF before the MFMAs of step kk (held there
+  // by sched_barrier fences), and the first V^T group during the vector
+  // phase.  Fencing the P.V reads as well measured slower with three terms.
+  constexpr int KPF = KSTEPS < 3 ? KSTEPS : 3;  // score steps read ahead
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+
+  // S^T of the tile in buffer kb: the two 32-key chains alternate (as in
+  // attn_kernel_pipe); f holds the fragments of steps 0 .. KPF-1 on entry
+  auto scores = [&](int kb, bf16x8 (&f)[KPF][2]) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int cur = kk % KPF;
+      const bf16x8 a0 = f[cur][0], a1 = f[cur][1];
+      if (kk + KPF < KSTEPS) {
+        f[cur][0] = kfrag(kb, 0, kk + KPF);
+        f[cur][1] = kfrag(kb, 1, kk + KPF);
+      }
+      fence();
+      if (kk == 0) {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], f32x16{}, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], f32x16{}, 0, 0, 0);
+      } else {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s[1], 0, 0, 0);
+      }
+      fence();
+    }
+  };
+
+  // vector phase of the tile starting at key0: the online-softmax update and
+  // the BF16 terms of the weights (attn_kernel_pipe's arithmetic, in order);
+  // va receives group 0 of the V^T tile in buffer vb for the next matrix phase
+  auto vector_phase = [&](int key0, int vb, bf16x8 (&va)[DH / 32]) {
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt) va[dt] = vfrag(vb, 0, dt);
+    fence();
+    if (key0 + KT > p.Mk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + 8 * (r / 4) + 4 * half + (r % 4) >= p.Mk) s[kb][r] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float mc = m_new * c;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+        s[kb][r] = e;
+        lsum += e;
+      }
+    lsum += __shfl_xor(lsum, 32);
+    if (__any(m_new != m_run)) {
+      const float eta = __builtin_amdgcn_exp2f(m_run * c - mc);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= eta;
+      l_run *= eta;
+    }
+    l_run += lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        f32x2 pv = {s[g >> 1][(g & 1) * 8 + j], s[g >> 1][(g & 1) * 8 + j + 1]};
+        bf16x2 t[3];
+        split_p<NP>(pv, t);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          bt[n][g][j] = t[n][0];
+          bt[n][g][j + 1] = t[n][1];
+        }
+      }
+    }
+  };
+  // matrix phase: O^T += V^T P^T of the tile in buffer vb (attn_kernel_pipe's
+  // MFMA order per accumulator; va holds its group 0), then the scores of
+  // the tile in buffer kb.  Without a next tile kb = vb: the scores are
+  // computed from a valid buffer and never used, so that the phase has no
+  // branch.
+  auto matrix_phase = [&](int vb, int kb, bf16x8 (&va)[DH / 32]) {
+    bf16x8 kf[KPF][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x8 vn[DH / 32];
+      if (g + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) vn[dt] = vfrag(vb, g + 1, dt);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KPF; ++kk) {
+          kf[kk][0] = kfrag(kb, 0, kk);
+          kf[kk][1] = kfrag(kb, 1, kk);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NP; ++n)
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], bt[n][g], o[dt], 0, 0, 0);
+      if (g + 1 < 4) {
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) va[dt] = vn[dt];
+      }
+    }
+    scores(kb, kf);
+  };
+  // the stores of this half-iteration are visible after it
+  auto barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  const int ntiles = (p.Mk + KT - 1) / KT;
+  // tiles 0 and 1: K by group A, V^T by group B
+  if (group_a) {
+    load_k(0);
+    store_k(0);
+    if (ntiles > 1) {
+      load_k(KT);
+      store_k(1);
+    }
+  } else {
+    load_v(0);
+    store_v(0);
+    if (ntiles > 1) {
+      load_v(KT);
+      store_v(1);
+    }
+  }
+  barrier();
+  {
+    bf16x8 kf[KPF][2];
+#pragma unroll
+    for (int kk = 0; kk < KPF; ++kk) {
+      kf[kk][0] = kfrag(0, 0, kk);
+      kf[kk][1] = kfrag(0, 1, kk);
+    }
+    bf16x8 va[DH / 32];
+    if (group_a) {
+      scores(0, kf);
+      for (int t = 0; t < ntiles; ++t) {
+        vector_phase(t * KT, t % NB, va);                     // h = 2t
+        if (t >= 1 && t + 1 < ntiles) store_k((t + 1) % NB);  // loaded in M(t-1)
+        barrier();
+        if (t + 2 < ntiles) load_k((t + 2) * KT);             // h = 2t+1
+        matrix_phase(t % NB, t + 1 < ntiles ? (t + 1) % NB : t % NB, va);
+        barrier();
+      }
+      barrier();  // h = 2 ntiles: group B's last matrix phase
+    } else {
+      scores(0, kf);  // h = 0
+      barrier();
+      for (int t = 0; t < ntiles; ++t) {
+        vector_phase(t * KT, t % NB, va);                     // h = 2t+1
+        if (t >= 1 && t + 1 < ntiles) store_v((t + 1) % NB);  // loaded in M(t-1)
+        barrier();
+        if (t + 2 < ntiles) load_v((t + 2) * KT);             // h = 2t+2
+        matrix_phase(t % NB, t + 1 < ntiles ? (t + 1) % NB : t % NB, va);
+        barrier();
+      }
+    }
+  }
+
+  if (qvalid) {
+    uint16_t* op = p.q + (long)qrow * p.ldq + h * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c0 = dt * 32 + 8 * rg + 4 * half;
+        uint16_t b0 = f2bf(o[dt][rg * 4 + 0] / l_run);
+        uint16_t b1 = f2bf(o[dt][rg * 4 + 1] / l_run);
+        uint16_t b2 = f2bf(o[dt][rg * 4 + 2] / l_run);
+        uint16_t b3 = f2bf(o[dt][rg * 4 + 3] / l_run);
+        uint2 w = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16));
+        *reinterpret_cast<uint2*>(op + c0) = w;
+      }
+  }
+}
+
 template <int QB, int NP, int DH>
 hipError_t launch_pipe(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
   hipLaunchKernelGGL((attn_kernel_pipe<QB, NP, DH>), grid, dim3(QB * 2), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int NP, int DH>
+hipError_t launch_pp(const AttnArgs& a, hipStream_t s) {
+  // the kernel addresses a tile's chunks by 32-bit byte offsets
+  if ((long)KT * a.ldk * 2 >= (1L << 32) || (long)DH * a.ldvt * 2 >= (1L << 32))
+    return launch_pipe<256, NP, DH>(a, s);
+  dim3 grid((a.Mq + 255) / 256, a.heads);
+  hipLaunchKernelGGL((attn_kernel_pp<NP, DH>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -536,6 +897,7 @@ hipError_t launch_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
   switch (cfg) {
     case 2: return launch_q<256, NP, DH>(a, s);
     case 3: return launch_pipe<256, NP, DH>(a, s);
+    case 4: return launch_pp<NP, DH>(a, s);
     default: return launch_q<128, NP, DH>(a, s);
   }
 }
@@ -554,12 +916,14 @@ hipError_t launch_dh(const AttnArgs& a, int cfg, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Mq <= 0) return hipSuccess;
-  // 256-query workgroups (8 waves sharing each K/V tile, software-pipelined)
-  // when they still give every CU a workgroup, else 128-query ones.
-  // Configurations: 1 = 128-query, 2 = 256-query, 3 = 256-query pipelined;
-  // all give identical bits.  Head dimension 128 or 64.
+  if (a.Mk <= 0) return hipErrorInvalidValue;  // softmax over no keys
+  // 256-query workgroups (8 waves sharing each K/V tile, the two wave
+  // groups in ping-pong) when they still give every CU a workgroup, else
+  // 128-query ones.  Configurations: 1 = 128-query, 2 = 256-query, 3 =
+  // 256-query pipelined in lock step, 4 = 256-query ping-pong; all give
+  // identical bits.  Head dimension 128 or 64.
   int cfg = a.config;
-  if (cfg == 0) cfg = ((a.Mq + 255) / 256) * a.heads >= 256 ? 3 : 1;
+  if (cfg == 0) cfg = a.lockstep ? 3 : ((a.Mq + 255) / 256) * a.heads >= 256 ? 4 : 1;
   if (a.dh == 64) return launch_dh<64>(a, cfg, s);
   if (a.dh != 128) return hipErrorInvalidValue;
   return launch_dh<128>(a, cfg, s);

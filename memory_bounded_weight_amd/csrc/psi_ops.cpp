@@ -212,6 +212,7 @@ psi_status attend(psi_arena* a, uint16_t* q, long ldq, const uint16_t* k, long l
   A.Mq = Mq; A.Mk = Mk; A.heads = heads; A.dh = dh;
   A.alpha = (float)(1.0 / std::sqrt((double)dh));
   A.p_terms = attn_p_terms(flags);
+  A.lockstep = (flags & PSI_OP_ATTN_PIPELINED) ? 1 : 0;
   return run_attention(a, A);
 }
 
@@ -1038,7 +1039,8 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
 psi_status psi_block_lowlive(psi_arena* a, uint16_t* x, int M, int heads, int head_dim,
                              const psi_block_weights* w, psi_journal* j, unsigned flags) {
   if (!a || !w || !j) return fail(PSI_E_INVALID, "null argument");
-  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2)) | PSI_OP_RESIDUAL;
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_PIPELINED)) |
+                     PSI_OP_RESIDUAL;
   const int dm = heads * head_dim;
   psi_status st = psi_attn_tiled_plan(&a->desc, M, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, nullptr);
   if (st) return st;
@@ -1053,7 +1055,8 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
                            const psi_block_weights* w, int token_chunks, float* acc_dev,
                            psi_journal* fence, unsigned flags) {
   if (!a || !w) return fail(PSI_E_INVALID, "null argument");
-  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2)) | PSI_OP_RESIDUAL;
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_PIPELINED)) |
+                     PSI_OP_RESIDUAL;
   // validate both halves before enqueueing anything
   const int dm = heads * head_dim;
   psi_status st = psi_attn_plan(&a->desc, M, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo,

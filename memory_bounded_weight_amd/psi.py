@@ -55,6 +55,7 @@ PSI_OP_RESIDUAL = 0x2
 PSI_OP_STORE_ACC = 0x4
 PSI_OP_BF16_SOFTMAX = 0x8
 PSI_OP_ATTN_P2 = 0x10
+PSI_OP_ATTN_PIPELINED = 0x20
 
 PSI_ROLE_ATTN_O = 16
 PSI_ROLE_FFN_H = 17

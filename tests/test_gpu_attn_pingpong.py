@@ -1,0 +1,74 @@
+"""The ping-pong attention kernel against the lock-step pipelined one.
+
+Launches of 256 or more 256-query workgroups run the ping-pong kernel (the
+two wave groups of a workgroup alternate softmax and matrix phases); the
+flag PSI_OP_ATTN_PIPELINED runs the pipelined kernel instead.  Both compute
+every query's scores, online-softmax updates and P.V accumulation in the
+same order, so the outputs are compared bit for bit: self- and
+cross-attention with ragged query and key counts, head dimensions 128 and
+64, and the three softmax-weight precisions (fp32 weights as three BF16
+terms, two terms, BF16 numerator weights).  Parity with the oracle at the
+benchmark's shape, where the ping-pong kernel runs, is checked by the
+full-size tests.
+
+[PSI] = "Precision-Preserving Subtensor Inference for a 22B Joint Audio-Video
+Generator under a Fixed GPU Working Set" (arXiv 2611.08023); attention
+sub-block of sec. II-B, softmax weights of sec. III-A.
+"""
+import numpy as np
+import pytest
+
+from memory_bounded_weight_amd import synth
+from tests.gpu_util import dev, empty_bf16, f, host, make_arena
+
+pytestmark = pytest.mark.gpu
+
+KiB = 1024
+
+
+@pytest.fixture(scope="module")
+def P(psi_lib):
+    return psi_lib
+
+
+def run(P, x, ctx, w, heads, dh, flags):
+    """psi_attn_paged with every head in one group (one attention launch)."""
+    M, d = x.shape
+    Mc = 0 if ctx is None else ctx.shape[0]
+    Ms = Mc or M
+    gw = heads * dh
+    ms = (P.pinned_matrix(w["Wq"], w["bq"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wk"], w["bk"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wv"], w["bv"], P.PSI_SPLIT_ROWS, gw),
+          P.pinned_matrix(w["Wo"], w["bo"], P.PSI_SPLIT_COLS, gw))
+    pb = gw * d * 2
+    ldvt = (Ms + 63) // 64 * 64
+    scratch = (M + Ms) * d * 2 + gw * ldvt * 2 + M * d * 4 + 16 * KiB
+    ar = make_arena(2 * pb + 2 * 64 * KiB + scratch, pb, 2)
+    try:
+        xd = dev(x)
+        cd = dev(ctx) if ctx is not None else None
+        y = empty_bf16(M, d)
+        P.psi_attn_paged(ar, xd, M, cd, Mc, heads, dh, *ms, None, y, flags | P.PSI_OP_RESIDUAL)
+        P.psi_arena_sync(ar)
+        return host(y)
+    finally:
+        P.psi_arena_destroy(ar)
+
+
+@pytest.mark.parametrize("dh,heads,M,Mc", [(128, 8, 7990, 0), (128, 8, 7990, 3000),
+                                           (64, 16, 7990, 0), (64, 16, 4000, 2999)])
+def test_pingpong_matches_pipelined_bitwise(P, dh, heads, M, Mc):
+    assert -(-M // 256) * heads >= 256  # the automatic choice is the ping-pong kernel
+    rng = np.random.default_rng(1000 + dh + M + Mc)
+    d = heads * dh
+    x = synth.normal_bf16(rng, (M, d), 1.0)
+    ctx = synth.normal_bf16(rng, (Mc, d), 1.0) if Mc else None
+    w = synth.attn_weights(rng, d)
+    for fl in (0, P.PSI_OP_ATTN_P2, P.PSI_OP_BF16_SOFTMAX):
+        y_pp = run(P, x, ctx, w, heads, dh, fl)
+        y_ls = run(P, x, ctx, w, heads, dh, fl | P.PSI_OP_ATTN_PIPELINED)
+        assert np.isfinite(f(y_pp)).all()
+        diff = np.flatnonzero(y_pp != y_ls)
+        assert diff.size == 0, (f"dh {dh} M {M} Mc {Mc} flags {fl:#x}: {diff.size} outputs differ, "
+                                f"first at {np.unravel_index(diff[0], y_pp.shape)}")
