@@ -578,7 +578,9 @@ def kernel_microbench(torch, psi, synth, reps=20):
                      accumulator, the middle one loads and stores it, the last
                      loads it and writes B(acc + b))
       attention_*    8 heads x 8192 queries x 8192 keys, head_dim 128, with
-                     fp32 weights (three BF16 terms), two terms, BF16 weights
+                     fp32 weights (three BF16 terms), two terms, BF16 weights;
+                     the default (ping-pong) kernel, then with the suffix
+                     _lockstep the pipelined kernel (PSI_OP_ATTN_PIPELINED)
     Returns a dict of {name: {avg_launch_us, achieved TFLOP/s, frac}}."""
     import numpy as np
     stream = torch.cuda.current_stream().cuda_stream
@@ -625,10 +627,12 @@ def kernel_microbench(torch, psi, synth, reps=20):
     xa = torch.from_numpy(synth.normal_bf16(rng, (M, d), 1.0).view("int16")).cuda()
     ya = torch.empty_like(xa)
     acc_a = torch.empty(M, d, dtype=torch.float32, device="cuda")
-    for name, fl in (("attention_fp32_weights", 0), ("attention_two_terms", psi.PSI_OP_ATTN_P2),
-                     ("attention_bf16_weights", psi.PSI_OP_BF16_SOFTMAX)):
-        measure(name, lambda a, fl=fl: psi.psi_attn_paged(a, xa, M, None, 0, heads, 128, *mats, acc_a, ya, fl),
-                "attn")
+    # the default (ping-pong) kernel, then the lock-step pipelined one
+    for kern, kf in (("", 0), ("_lockstep", psi.PSI_OP_ATTN_PIPELINED)):
+        for name, fl in (("attention_fp32_weights", 0), ("attention_two_terms", psi.PSI_OP_ATTN_P2),
+                         ("attention_bf16_weights", psi.PSI_OP_BF16_SOFTMAX)):
+            measure(name + kern, lambda a, fl=fl | kf: psi.psi_attn_paged(a, xa, M, None, 0, heads, 128, *mats,
+                                                                          acc_a, ya, fl), "attn")
     return out
 
 
