@@ -378,10 +378,10 @@ def build_workload(args, torch, psi, synth):
         # reloaded once per output tile.  4,991 tokens: one [4991, 16384] BF16
         # hidden state is 163,545,088 B, the per-block journal figure the paper
         # reports (sec. IV).  The output tiles are wide and cut into 8 MiB 2-D
-        # page tiles (attention: 2,048 rows x 2 head groups; FFN: 1,024 rows x
-        # 4 hidden tiles), so each head-group output is reloaded twice and
-        # each hidden state four times per block (--lowlive-rows: the
-        # row-split pages of 512 and 256 rows, 8 and 16 reloads).  Two blocks
+        # page tiles (attention: 2,048 rows x 2 head groups; FFN: 2,048 rows x
+        # 2 hidden tiles), so each head-group output and each hidden state is
+        # reloaded twice per block (--lowlive-rows: the row-split pages of 512
+        # and 256 rows, 8 and 16 reloads).  Two blocks
         # per step; afterwards the same blocks run as psi_block_paged
         # (device-resident intermediates) for the footprint, time and bitwise
         # comparison.
@@ -390,7 +390,7 @@ def build_workload(args, torch, psi, synth):
         if args.lowlive_rows:
             to_a, to_f, tc_a, tc_f = 512, 256, 0, 0
         else:
-            to_a, to_f, tc_a, tc_f = 2048, 1024, 2048, 4096
+            to_a, to_f, tc_a, tc_f = 2048, 2048, 2048, 2048
         arena = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, flags))
         ws = [synth.block_weights(args.seed, b, d, hid) for b in range(nblk)]
         low = [psi.block_weights(w, gw, th, attn_out_tile=to_a, ffn_out_tile=to_f, attn_out_cols=tc_a,
@@ -417,7 +417,6 @@ def build_workload(args, torch, psi, synth):
             psi.psi_journal_sync(journal)
             out_low = x.cpu().numpy()
             xr = torch.empty_like(x0)
-            xt = torch.empty_like(x0)
             acc = torch.empty(M, d, dtype=torch.float32, device="cuda")
             a2 = psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, 0))
             times = []
@@ -426,7 +425,7 @@ def build_workload(args, torch, psi, synth):
                 torch.cuda.synchronize()
                 t = time.perf_counter()
                 for b in range(nblk):
-                    psi.psi_block_paged(a2, xr, xt, M, heads, 128, reg[b], 1, acc, None, 0)
+                    psi.psi_block_paged(a2, xr, None, M, heads, 128, reg[b], 1, acc, None, 0)
                 psi.psi_arena_sync(a2)
                 torch.cuda.synchronize()
                 times.append(time.perf_counter() - t)
@@ -436,7 +435,7 @@ def build_workload(args, torch, psi, synth):
             return {"regular_ms_per_step": round(1e3 * sum(times[1:]) / args.steps, 3),
                     "bitwise_equal_to_regular": same,
                     "device_state_bytes": {"lowlive": {"x": act},
-                                           "regular": {"x": act, "x_tmp": act, "fp32_acc": 2 * act}},
+                                           "regular": {"x": act, "fp32_acc": 2 * act}},
                     "journal_per_block": {"d2h_bytes": jd2h_block, "h2d_bytes": jh2d_block,
                                           "hidden_state_bytes": M * hid * 2,
                                           "attn_output_tiles": n_oa, "ffn_output_tiles": n_of},
