@@ -534,8 +534,9 @@ __global__ __launch_bounds__(QB * 2) void attn_kernel_pipe(AttnArgs p) {
 // vector phase V(t) at h = 2t and the matrix phase M(t) = P.V(t) + S(t+1) at
 // h = 2t+1; group B runs S(0) at h = 0, V(t) at h = 2t+1 and M(t) at
 // h = 2t+2.  Tile i's K is read at h = 2i-1 and 2i (the groups' S(i)), its
-// V^T at h = 2i+1 and 2i+2 (their P.V(i)); three LDS buffers of each hold
-// the tiles.  Group A stages K: the global loads of K(i) at the start of
+// V^T at h = 2i to 2i+2 (the groups' P.V(i), whose first fragment group each
+// reads during its vector phase V(i)); three LDS buffers of each hold the
+// tiles.  Group A stages K: the global loads of K(i) at the start of
 // its M(i-2) (h = 2i-3), the LDS stores at the end of its V(i-1)
 // (h = 2i-2), after K(i-3) was last read at h = 2i-6.  Group B stages V^T
 // the same way one half-iteration later: loads at the start of its M(i-2)
@@ -627,22 +628,20 @@ __global__ __launch_bounds__(512) void attn_kernel_pp(AttnArgs p) {
     for (int i = 0; i < VCH; ++i) {
       int c2 = gtid + i * NT;
       int vr = c2 >> 3, vkey = key0 + (c2 & 7) * 8;
-      {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (vkey < p.Mk) {
-          v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
-          const int keep = p.Mk - vkey;
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (vkey < p.Mk) {
+        v = *reinterpret_cast<const uint4*>(vbase + (long)vr * p.ldvt + vkey);
+        const int keep = p.Mk - vkey;
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t mlo = (2 * q < keep) ? 0x0000FFFFu : 0u;
-            const uint32_t mhi = (2 * q + 1 < keep) ? 0xFFFF0000u : 0u;
-            w[q] &= (mlo | mhi);
-          }
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t mlo = (2 * q < keep) ? 0x0000FFFFu : 0u;
+          const uint32_t mhi = (2 * q + 1 < keep) ? 0xFFFF0000u : 0u;
+          w[q] &= (mlo | mhi);
         }
-        rs[i] = v;
+        v = make_uint4(w[0], w[1], w[2], w[3]);
       }
+      rs[i] = v;
     }
   };
   // Within each 16-key group the V^T row holds the keys in the order of the
