@@ -82,9 +82,9 @@ typedef int psi_status;
                                      step); ignored with PSI_OP_BF16_SOFTMAX */
 #define PSI_OP_ATTN_PIPELINED 0x20u /* attention: run the lock-step pipelined kernel at
                                        every size instead of the automatic choice (the
-                                       ping-pong kernel for 256 or more workgroups of
-                                       256 queries, else 128-query workgroups); the
-                                       same bits, a comparison path */
+                                       ping-pong kernel for 512 or more keys or 256 or
+                                       more workgroups of 256 queries, else 128-query
+                                       workgroups); the same bits, a comparison path */
 
 /* -------------------------------------------------------- matrix layouts */
 #define PSI_SPLIT_ROWS 0 /* page p = rows [p*block, (p+1)*block) of W: an output-column

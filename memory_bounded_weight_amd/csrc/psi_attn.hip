@@ -917,12 +917,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.Mq <= 0) return hipSuccess;
   if (a.Mk <= 0) return hipErrorInvalidValue;  // softmax over no keys
   // 256-query workgroups (8 waves sharing each K/V tile, the two wave
-  // groups in ping-pong) when they still give every CU a workgroup, else
-  // 128-query ones.  Configurations: 1 = 128-query, 2 = 256-query, 3 =
-  // 256-query pipelined in lock step, 4 = 256-query ping-pong; all give
-  // identical bits.  Head dimension 128 or 64.
+  // groups in ping-pong) when there are at least 512 keys or the grid gives
+  // every CU a workgroup, else 128-query ones (measured on MI355X: with 8 or
+  // more key tiles the ping-pong kernel is faster even on grids of 64
+  // workgroups; with fewer, more and smaller workgroups win unless the grid
+  // is large).  Configurations: 1 = 128-query, 2 = 256-query, 3 = 256-query
+  // pipelined in lock step, 4 = 256-query ping-pong; all give identical
+  // bits.  Head dimension 128 or 64.
   int cfg = a.config;
-  if (cfg == 0) cfg = a.lockstep ? 3 : ((a.Mq + 255) / 256) * a.heads >= 256 ? 4 : 1;
+  if (cfg == 0) cfg = a.lockstep ? 3 : (a.Mk >= 512 || ((a.Mq + 255) / 256) * a.heads >= 256) ? 4 : 1;
   if (a.dh == 64) return launch_dh<64>(a, cfg, s);
   if (a.dh != 128) return hipErrorInvalidValue;
   return launch_dh<128>(a, cfg, s);

@@ -1,8 +1,9 @@
 """The ping-pong attention kernel against the lock-step pipelined one.
 
-Launches of 256 or more 256-query workgroups run the ping-pong kernel (the
-two wave groups of a workgroup alternate softmax and matrix phases); the
-flag PSI_OP_ATTN_PIPELINED runs the pipelined kernel instead.  Both compute
+Launches over 512 or more keys, or of 256 or more 256-query workgroups, run
+the ping-pong kernel (the two wave groups of a workgroup alternate softmax
+and matrix phases); the flag PSI_OP_ATTN_PIPELINED runs the pipelined
+kernel instead.  Both compute
 every query's scores, online-softmax updates and P.V accumulation in the
 same order, so the outputs are compared bit for bit: self- and
 cross-attention with ragged query and key counts, head dimensions 128 and
@@ -57,9 +58,12 @@ def run(P, x, ctx, w, heads, dh, flags):
 
 
 @pytest.mark.parametrize("dh,heads,M,Mc", [(128, 8, 7990, 0), (128, 8, 7990, 3000),
-                                           (64, 16, 7990, 0), (64, 16, 4000, 2999)])
+                                           (64, 16, 7990, 0), (64, 16, 4000, 2999),
+                                           (128, 2, 777, 0), (64, 4, 300, 1000), (128, 2, 1000, 513)])
 def test_pingpong_matches_pipelined_bitwise(P, dh, heads, M, Mc):
-    assert -(-M // 256) * heads >= 256  # the automatic choice is the ping-pong kernel
+    # the automatic choice is the ping-pong kernel: 512 or more keys, or 256 or
+    # more workgroups of 256 queries (small grids included)
+    assert (Mc or M) >= 512 or -(-M // 256) * heads >= 256
     rng = np.random.default_rng(1000 + dh + M + Mc)
     d = heads * dh
     x = synth.normal_bf16(rng, (M, d), 1.0)
