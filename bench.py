@@ -570,7 +570,8 @@ def committed_traffic(kernel_source, profile):
 def kernel_microbench(torch, psi, synth, reps=20):
     """Per-launch times of the hot kernels on the stack's shapes, through the
     C ABI with resident weights in a profiled arena (HIP events around each
-    launch; warm caches, no page copies):
+    launch; warm caches, no page copies; after about a second of launches,
+    each entry is timed in two rounds of opposite order and keeps the faster):
       gemm_page      y = B(x W^T + b): 8192 x 1024 x 4096, one output-column page
       gemm_ksplit    fp32 accumulator carried over three K pages of 1024:
                      8192 x 4096 x 1024 per launch (first page stores the
@@ -580,6 +581,10 @@ def kernel_microbench(torch, psi, synth, reps=20):
                      fp32 weights (three BF16 terms), two terms, BF16 weights;
                      the default (ping-pong) kernel, then with the suffix
                      _lockstep the pipelined kernel (PSI_OP_ATTN_PIPELINED)
+      attention_kernels_us   per-launch time of each attention kernel
+                     (PSI_OP_ATTN_CONFIG 1-4, fp32 weights), 8 heads of 128:
+                     self-attention of 8,192, 4,991, 2,048 and 512 tokens,
+                     cross-attention of 1,024 and 4,991 queries over 126 keys
     Returns a dict of {name: {avg_launch_us, achieved TFLOP/s, frac}}."""
     import numpy as np
     stream = torch.cuda.current_stream().cuda_stream
@@ -590,7 +595,12 @@ def kernel_microbench(torch, psi, synth, reps=20):
     def arena():
         return psi.psi_arena_create(psi.arena_desc(80 * MiB, 8 * MiB, 2, 0, 0, stream, psi.PSI_ARENA_PROFILE))
 
+    tasks = []
+
     def measure(name, call, kind):
+        tasks.append((name, call, kind))
+
+    def timed(call, kind):
         a = arena()
         try:
             psi.psi_arena_set_timing(a, False)
@@ -603,11 +613,26 @@ def kernel_microbench(torch, psi, synth, reps=20):
             st = psi.psi_arena_stats(a)
         finally:
             psi.psi_arena_destroy(a)
-        ms, n, fl = (st.gemm_ms, st.gemm_launches, st.gemm_flops) if kind == "gemm" else \
+        return (st.gemm_ms, st.gemm_launches, st.gemm_flops) if kind == "gemm" else \
             (st.attn_ms, st.attn_launches, st.attn_flops)
-        tf = fl / (ms * 1e-3) / 1e12
-        out[name] = {"avg_launch_us": round(ms * 1e3 / n, 2), "launches": n, "achieved": round(tf, 1),
-                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl / n}
+
+    def run_tasks():
+        # about a second of launches first (the clocks settle), then two
+        # rounds in opposite orders; each entry keeps its faster round
+        t_end = time.time() + 1.0
+        while time.time() < t_end:
+            timed(tasks[0][1], tasks[0][2])
+        best = {}
+        for order in (tasks, tasks[::-1]):
+            for name, call, kind in order:
+                r = timed(call, kind)
+                if name not in best or r[0] / r[1] < best[name][0] / best[name][1]:
+                    best[name] = r
+        for name, _, _ in tasks:
+            ms, n, fl = best[name]
+            tf = fl / (ms * 1e-3) / 1e12
+            out[name] = {"avg_launch_us": round(ms * 1e3 / n, 2), "launches": n, "achieved": round(tf, 1),
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl / n}
 
     x = torch.from_numpy(synth.normal_bf16(rng, (M, 4096), 1.0).view("int16")).cuda()
     Wp = psi.resident_matrix(psi.pinned_matrix(synth.normal_bf16(rng, (1024, 4096), 1.0 / 4096),
@@ -632,6 +657,21 @@ def kernel_microbench(torch, psi, synth, reps=20):
                          ("attention_bf16_weights", psi.PSI_OP_BF16_SOFTMAX)):
             measure(name + kern, lambda a, fl=fl | kf: psi.psi_attn_paged(a, xa, M, None, 0, heads, 128, *mats,
                                                                           acc_a, ya, fl), "attn")
+    # every attention kernel (fp32 weights) on 8 heads of 8,192, 4,991 and
+    # 2,048 tokens: 256, 160 and 64 workgroups of 256 queries
+    # (queries, keys): self-attention, and cross-attention over the first
+    # rows of the same activations as the context
+    kernels = ((1, "128_query"), (2, "256_query"), (3, "lockstep"), (4, "ping_pong"))
+    shapes = ((8192, 8192), (4991, 4991), (2048, 2048), (512, 512), (1024, 126), (4991, 126))
+    for mq, mk in shapes:
+        for c, kname in kernels:
+            ctx, mc = (None, 0) if mk == mq else (xa, mk)
+            measure(f"attention_{mq}x{mk}_{kname}",
+                    lambda a, mq=mq, ctx=ctx, mc=mc, c=c: psi.psi_attn_paged(
+                        a, xa, mq, ctx, mc, heads, 128, *mats, acc_a, ya, psi.PSI_OP_ATTN_CONFIG(c)), "attn")
+    run_tasks()
+    out["attention_kernels_us"] = {f"{mq}x{mk}": {kname: out.pop(f"attention_{mq}x{mk}_{kname}")["avg_launch_us"]
+                                                  for _, kname in kernels} for mq, mk in shapes}
     return out
 
 

@@ -80,11 +80,16 @@ typedef int psi_status;
 #define PSI_OP_ATTN_P2 0x10u      /* attention: fp32 weights carried as two BF16 terms
                                      (about 17 significant bits; one MFMA fewer per
                                      step); ignored with PSI_OP_BF16_SOFTMAX */
-#define PSI_OP_ATTN_PIPELINED 0x20u /* attention: run the lock-step pipelined kernel at
-                                       every size instead of the automatic choice (the
-                                       ping-pong kernel for 512 or more keys or 256 or
-                                       more workgroups of 256 queries, else 128-query
-                                       workgroups); the same bits, a comparison path */
+/* Attention kernel (bits 8-10 of the flags): 0 = the automatic choice (the
+   ping-pong kernel for 512 or more keys or 256 or more workgroups of 256
+   queries, else 128-query workgroups); 1 = 128-query workgroups; 2 = 256-query
+   workgroups; 3 = 256-query, software-pipelined with the waves in lock step;
+   4 = 256-query ping-pong (the two wave groups alternate softmax and matrix
+   phases).  Every choice gives the same bits (a comparison path); other
+   values are PSI_E_INVALID. */
+#define PSI_OP_ATTN_CONFIG(c) (((unsigned)(c) & 7u) << 8)
+#define PSI_OP_ATTN_CONFIG_MASK 0x700u
+#define PSI_OP_ATTN_PIPELINED PSI_OP_ATTN_CONFIG(3) /* the lock-step kernel at every size */
 
 /* -------------------------------------------------------- matrix layouts */
 #define PSI_SPLIT_ROWS 0 /* page p = rows [p*block, (p+1)*block) of W: an output-column

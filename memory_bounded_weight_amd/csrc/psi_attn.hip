@@ -925,7 +925,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // pipelined in lock step, 4 = 256-query ping-pong; all give identical
   // bits.  Head dimension 128 or 64.
   int cfg = a.config;
-  if (cfg == 0) cfg = a.lockstep ? 3 : (a.Mk >= 512 || ((a.Mq + 255) / 256) * a.heads >= 256) ? 4 : 1;
+  if (cfg == 0) cfg = (a.Mk >= 512 || ((a.Mq + 255) / 256) * a.heads >= 256) ? 4 : 1;
   if (a.dh == 64) return launch_dh<64>(a, cfg, s);
   if (a.dh != 128) return hipErrorInvalidValue;
   return launch_dh<128>(a, cfg, s);

@@ -76,7 +76,6 @@ struct AttnArgs {
                        // 2 = hi + lo (about 17 bits), 1 = BF16 numerator weights
   int config;          // 0: chosen from the shape; 1: 128-query, 2: 256-query, 3: 256-query
                        // pipelined (waves in lock step), 4: 256-query ping-pong
-  int lockstep;        // with config 0: configuration 3 at every size
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -149,6 +149,13 @@ struct ScratchMark {
   ~ScratchMark() { scratch_reset(a, mark); }
 };
 
+// The attention kernel choice in the flags: 0 (automatic) to 4.
+psi_status check_attn_config(unsigned flags) {
+  if ((flags & PSI_OP_ATTN_CONFIG_MASK) > PSI_OP_ATTN_CONFIG(4))
+    return fail(PSI_E_INVALID, "attention kernel choice (PSI_OP_ATTN_CONFIG) must be 0-4");
+  return PSI_OK;
+}
+
 int attn_p_terms(unsigned flags) {
   if (flags & PSI_OP_BF16_SOFTMAX) return 1;
   return (flags & PSI_OP_ATTN_P2) ? 2 : 3;
@@ -212,7 +219,7 @@ psi_status attend(psi_arena* a, uint16_t* q, long ldq, const uint16_t* k, long l
   A.Mq = Mq; A.Mk = Mk; A.heads = heads; A.dh = dh;
   A.alpha = (float)(1.0 / std::sqrt((double)dh));
   A.p_terms = attn_p_terms(flags);
-  A.lockstep = (flags & PSI_OP_ATTN_PIPELINED) ? 1 : 0;
+  A.config = (int)((flags & PSI_OP_ATTN_CONFIG_MASK) >> 8);  // 0-4, checked at the operator's entry
   return run_attention(a, A);
 }
 
@@ -649,6 +656,7 @@ static psi_status attn_paged(psi_arena* a, const uint16_t* x, int M, const uint1
                              const psi_matrix* Wo, float* acc_dev, uint16_t* y, unsigned flags,
                              psi_journal* out_fence) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (psi_status st = check_attn_config(flags)) return st;
   if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
   if (!ctx) Mc = 0;
   size_t need = 0;
@@ -787,6 +795,7 @@ psi_status psi_attn_paged_ext(psi_arena* a, const uint16_t* x, int M, const uint
                               int heads, int head_dim, const psi_matrix* Wq, const psi_matrix* Wk,
                               const psi_matrix* Wv, const psi_matrix* Wo, const psi_qk_norm_rope* nr,
                               float* acc_dev, uint16_t* y, unsigned flags) {
+  if (psi_status st = check_attn_config(flags)) return st;
   if (!qk_stage_active(nr))
     return psi_attn_paged(a, x, M, ctx, Mc, heads, head_dim, Wq, Wk, Wv, Wo, acc_dev, y, flags);
   if (!a) return fail(PSI_E_INVALID, "null arena");
@@ -915,6 +924,7 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
                           const psi_matrix* Wo, psi_journal* j, int32_t step, int32_t block, uint16_t* y,
                           unsigned flags) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
+  if (psi_status st = check_attn_config(flags)) return st;
   if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
   if (!ctx) Mc = 0;
   psi_status st = psi_attn_tiled_plan(&a->desc, M, Mc, heads, head_dim, Wq, Wk, Wv, Wo, nullptr);
@@ -1039,7 +1049,8 @@ psi_status psi_attn_tiled(psi_arena* a, const uint16_t* x, int M, const uint16_t
 psi_status psi_block_lowlive(psi_arena* a, uint16_t* x, int M, int heads, int head_dim,
                              const psi_block_weights* w, psi_journal* j, unsigned flags) {
   if (!a || !w || !j) return fail(PSI_E_INVALID, "null argument");
-  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_PIPELINED)) |
+  if (psi_status st = check_attn_config(flags)) return st;
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_CONFIG_MASK)) |
                      PSI_OP_RESIDUAL;
   const int dm = heads * head_dim;
   psi_status st = psi_attn_tiled_plan(&a->desc, M, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, nullptr);
@@ -1055,7 +1066,8 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
                            const psi_block_weights* w, int token_chunks, float* acc_dev,
                            psi_journal* fence, unsigned flags) {
   if (!a || !w) return fail(PSI_E_INVALID, "null argument");
-  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_PIPELINED)) |
+  if (psi_status st = check_attn_config(flags)) return st;
+  const unsigned f = (flags & (PSI_OP_BASELINE_BIAS | PSI_OP_BF16_SOFTMAX | PSI_OP_ATTN_P2 | PSI_OP_ATTN_CONFIG_MASK)) |
                      PSI_OP_RESIDUAL;
   // validate both halves before enqueueing anything
   const int dm = heads * head_dim;

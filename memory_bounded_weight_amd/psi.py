@@ -55,7 +55,16 @@ PSI_OP_RESIDUAL = 0x2
 PSI_OP_STORE_ACC = 0x4
 PSI_OP_BF16_SOFTMAX = 0x8
 PSI_OP_ATTN_P2 = 0x10
-PSI_OP_ATTN_PIPELINED = 0x20
+PSI_OP_ATTN_CONFIG_MASK = 0x700
+
+
+def PSI_OP_ATTN_CONFIG(c):
+    """Attention kernel choice in the flags: 0 automatic, 1 128-query, 2
+    256-query, 3 lock-step pipelined, 4 ping-pong (all give the same bits)."""
+    return (c & 7) << 8
+
+
+PSI_OP_ATTN_PIPELINED = PSI_OP_ATTN_CONFIG(3)
 
 PSI_ROLE_ATTN_O = 16
 PSI_ROLE_FFN_H = 17

@@ -329,6 +329,33 @@ def test_attention_page_order_dry_run():
         psi.psi_arena_destroy(a)
 
 
+def test_attention_kernel_choice_checked_first_dry_run():
+    """PSI_OP_ATTN_CONFIG(c): 0-4 accepted, anything else refused before any
+    page copy or launch, for the attention operators and the block driver."""
+    a = psi.psi_arena_create(desc(80, 8, 2, 8))
+    try:
+        Wq, Wk, Wv, Wo = cfg5_attn()
+        fake = 0x10000
+        for c in range(5):
+            psi.psi_attn_paged(a, fake, 6144, None, 0, 32, 128, Wq, Wk, Wv, Wo, fake, fake,
+                               psi.PSI_OP_RESIDUAL | psi.PSI_OP_ATTN_CONFIG(c))
+        s0 = psi.psi_arena_stats(a)
+        for c in (5, 7):
+            with pytest.raises(psi.PsiError) as e:
+                psi.psi_attn_paged(a, fake, 6144, None, 0, 32, 128, Wq, Wk, Wv, Wo, fake, fake,
+                                   psi.PSI_OP_RESIDUAL | psi.PSI_OP_ATTN_CONFIG(c))
+            assert e.value.status == psi.PSI_E_INVALID
+        U, V = cfg5_ffn()
+        bw = psi.psi_block_weights(Wq, Wk, Wv, Wo, U, V)
+        with pytest.raises(psi.PsiError) as e:
+            psi.psi_block_paged(a, 0x10000, None, 8192, 32, 128, bw, 1, 1 << 40, None, psi.PSI_OP_ATTN_CONFIG(6))
+        assert e.value.status == psi.PSI_E_INVALID
+        s1 = psi.psi_arena_stats(a)
+        assert (s1.page_copies, s1.kernel_launches) == (s0.page_copies, s0.kernel_launches)
+    finally:
+        psi.psi_arena_destroy(a)
+
+
 def test_checkpoint_size_independence_dry_run():
     """[PSI] sec. II-A: the managed footprint does not depend on checkpoint
     size -- stacks of 2, 4 and 8 blocks give the same arena peak and scratch
