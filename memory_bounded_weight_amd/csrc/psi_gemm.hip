@@ -64,15 +64,20 @@ __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 // tanh-GELU, phi(v) = v/2 (1 + tanh(z)), z = sqrt(2/pi) (v + 0.044715 v^3),
-// through 1 + tanh(z) = 2 / (1 + e^(-2z)) = 2 e^(2z) / (1 + e^(2z)); the
-// second form for z < 0 neither cancels nor overflows, so the tiny negative
-// values of the left tail keep their relative precision.
+// through 1 + tanh(z) = 2 / (1 + e^(-2z)) = 2 e^(2z) / (1 + e^(2z)); with
+// e = e^(-2|z|) <= 1 that is v / (1 + e) for z >= 0 and v e / (1 + e) for
+// z < 0, which neither cancels nor overflows, so the tiny negative values of
+// the left tail keep their relative precision.  e comes from exp2f (which
+// keeps denormal results) of -2 log2(e) |z|, and 1 / (1 + e) (in [1/2, 1])
+// from the reciprocal instruction: about 2^-18 relative error against the
+// exact function, well inside the BF16 rounding that follows (a result moves
+// by one BF16 ulp only next to a rounding boundary).
 __device__ __forceinline__ float gelu_tanh(float v) {
   const float c = 0.7978845608028654f;
   const float z = c * (v + 0.044715f * v * v * v);
-  if (z >= 0.0f) return v / (1.0f + expf(-2.0f * z));
-  const float e = expf(2.0f * z);
-  return v * e / (1.0f + e);
+  const float e = exp2f(-2.8853900817779268f * fabsf(z));
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  return z >= 0.0f ? v * r : (v * e) * r;
 }
 
 // Epilogue of one wave's TM x TN block of 32x32 accumulator tiles.  C layout
