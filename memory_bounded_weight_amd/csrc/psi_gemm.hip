@@ -27,6 +27,8 @@
 // the same bits on every run and for every page partition of the output;
 // all tile configurations below give identical bits (each output sees the
 // same ascending sequence of k16 MFMA steps with the same lane mapping).
+#include <atomic>
+
 #include "psi_internal.h"
 
 namespace psi {
@@ -298,9 +300,8 @@ __device__ __forceinline__ void init_acc(const GemmArgs& p, f32x16 (&acc)[TM][TN
 // column.  The tiles an XCD runs at the same time then cover about gm rows
 // x (concurrent / gm) columns, and share both operands' K slices in its L2
 // (gm = 1 walks whole rows, N fastest).
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords_of(int t, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
   const int nt = tiles_m * tiles_n;
-  int t = blockIdx.x;
   if (nt % 8 == 0) t = (t % 8) * (nt / 8) + t / 8;
   const int per_group = gm * tiles_n;
   const int first_m = (t / per_group) * gm;
@@ -308,6 +309,9 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, in
   const int r = t % per_group;
   tm = first_m + r % rows;
   tn = r / rows;
+}
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  tile_coords_of(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
 }
 
 // s_waitcnt immediate for gfx9: vmcnt = n (6 bits), expcnt and lgkmcnt not
@@ -447,6 +451,276 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_kernel_dma(GemmArgs p,
 }
 
 // ---------------------------------------------------------------------------
+// Carried-chain kernel: a middle step of a K-split chain (fp32 accumulator in
+// and out, no bias, no BF16 output) over whole 256 x 128 tiles, K = 1024,
+// with the waves and LDS ring of the direct-to-LDS kernel (8 waves of
+// 64 x 64, three stages).  In that kernel each workgroup loads its 128 KiB
+// of acc_in before its first MFMA and stores 128 KiB after its last, with
+// the matrix cores idle in both.  Here each workgroup stays resident and
+// walks T tiles (t = blockIdx.x + i * gridDim.x, in the same XCD-local tile
+// order), and two accumulator register sets alternate: while the MFMAs of
+// tile i run on one, the other first gives up tile i-1's result (stores)
+// and then takes tile i+1's acc_in (loads into the same registers), four
+// or five elements in each of the first fourteen K tiles.  The LDS ring runs on across
+// tiles: the first two stages of tile i+1 are issued during the last two K
+// tiles of tile i.  Every output still starts from its acc_in and sees the
+// same ascending k16 MFMA steps with the same lane mapping, so the bits are
+// those of the other kernels.  The accumulator moves with non-temporal loads
+// and stores, which leaves more of each XCD's L2 to the operand tiles.
+//
+// Wait counts.  One counter covers loads and stores, retired in issue order.
+// In K tile kt, stage kt+2 is issued after the MFMAs of the second k16 step
+// and the accumulator operations right after it; the wait for stage kt+1
+// before the last step leaves in flight exactly what was issued after stage
+// kt+1: the accumulator operations of K tile kt-1, stage kt+2 and the
+// accumulator operations of K tile kt.  A store or load thus has two K tiles
+// to complete.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {  // immediates only; folded once the K loop is unrolled
+    case 1: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(15)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(16)); break;
+    case 17: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(17)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(18)); break;
+    case 19: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(19)); break;
+    case 20: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(20)); break;
+    case 21: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(21)); break;
+    case 22: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(22)); break;
+    case 23: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(23)); break;
+    case 24: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(24)); break;
+    case 25: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(25)); break;
+    case 26: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(26)); break;
+    case 27: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(27)); break;
+    case 28: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(28)); break;
+    case 29: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(29)); break;
+    case 30: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(30)); break;
+    case 31: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(31)); break;
+    case 32: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(32)); break;
+    case 33: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(33)); break;
+    case 34: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(34)); break;
+    case 35: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(35)); break;
+    case 36: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(36)); break;
+    case 37: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(37)); break;
+    case 38: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(38)); break;
+    case 39: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(39)); break;
+    case 40: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(40)); break;
+    default: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0)); break;  // fewer in flight is always safe
+  }
+}
+
+constexpr int kChainNK = 16;  // K tiles of 64 per step: K = 1024
+// The accumulator traffic of a tile (64 elements per lane each way) is
+// spread over its first 14 K tiles: element range [chain_e0(kt),
+// chain_e0(kt + 1)) in K tile kt, 4 or 5 elements.  Over 8 K tiles it asked
+// for about twice the HBM bandwidth the chip has and slowed the MFMAs; the
+// last two K tiles stay free so that the next tile's accumulator has
+// arrived before its first MFMA.
+constexpr int kChainAccTiles = 14;
+__host__ __device__ constexpr int chain_e0(int kt) { return kt * 64 / kChainAccTiles; }
+
+template <int KIND>
+struct ChainKind {  // 0: first tile (no previous), 1: middle, 2: last (no next)
+  static constexpr bool prev = KIND != 0, next = KIND != 2;
+};
+
+__global__ __launch_bounds__(512, 2) void gemm_kernel_chain(GemmArgs p, int tiles_m, int tiles_n, int gm, int T) {
+  constexpr int BM = 256, BN = 128, WGN = 2, NW = 8, S = 3, BK = 64, NK = kChainNK;
+  constexpr int CPR = BK / 8, RPI = 64 / CPR, STAGE = (BM + BN) * BK;
+  constexpr int LA = BM / RPI / NW, LB = BN / RPI / NW, NL = LA + LB;
+  constexpr int WM = 64, WN = 64, TM = 2, TN = 2, KS = BK / 16;
+  static_assert(kChainAccTiles + 2 <= NK, "accumulator traffic must end two K tiles before a tile's end");
+  static_assert(chain_e0(kChainAccTiles) == TM * TN * 16, "every accumulator element is moved");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // Tile i of this workgroup: operand bases (scalar) and the wave block's origin.
+  struct Tile {
+    const uint16_t* a;
+    const uint16_t* b;
+    int mb, nb;
+  };
+  auto tile = [&](int i) {
+    int tm, tn;
+    tile_coords_of(blockIdx.x + i * gridDim.x, tiles_m, tiles_n, gm, tm, tn);
+    Tile t;
+    t.a = p.A + (long)(tm * BM) * p.lda;
+    t.b = p.B + (long)(tn * BN) * p.ldb;
+    t.mb = __builtin_amdgcn_readfirstlane(tm * BM + wm * WM);
+    t.nb = __builtin_amdgcn_readfirstlane(tn * BN + wn * WN);
+    return t;
+  };
+  // Per-lane element offsets of the stage loads within a tile's operand rows
+  // (32-bit: the dispatcher bounds lda and ldb).
+  uint32_t oa[LA], ob[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int r = (j * NW + wave) * RPI + lane / CPR;
+    oa[j] = (uint32_t)r * (uint32_t)p.lda + (uint32_t)((lane % CPR) ^ ((r / 2) % CPR)) * 8u;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int r = (j * NW + wave) * RPI + lane / CPR;
+    ob[j] = (uint32_t)r * (uint32_t)p.ldb + (uint32_t)((lane % CPR) ^ ((r / 2) % CPR)) * 8u;
+  }
+  auto issue = [&](const Tile& t, int kk, int buf) {
+    uint16_t* st = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(t.a + oa[j] + kk * BK),
+                                       PSI_LDS(st + (j * NW + wave) * RPI * BK), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(t.b + ob[j] + kk * BK),
+                                       PSI_LDS(st + BM * BK + (j * NW + wave) * RPI * BK), 16, 0, 0);
+  };
+  int offa[TM], offb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) offa[i] = (wm * WM + i * 32 + l32) * BK;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) offb[j] = BM * BK + (wn * WN + j * 32 + l32) * BK;
+  const int swz = (l32 / 2) % CPR;
+  auto frags = [&](const uint16_t* st, int ks, bf16x8* af, bf16x8* bf) {
+    const int pc = ((ks * 2 + half) ^ swz) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + offa[i] + pc);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(st + offb[j] + pc);
+  };
+  // Accumulator element e of a wave block: tile (e / 32, e % 2), register
+  // (e % 32) / 2; row and column as in the MFMA C layout.  Addresses: the
+  // wave block's origin (scalar, per tile) plus a 32-bit byte offset, the
+  // row's (scalar) and the lane's (the dispatcher bounds the leading
+  // dimensions so that both fit).
+  const uint32_t ld_in = (uint32_t)p.ld_acc_in * 4u, ld_out = (uint32_t)p.ld_acc_out * 4u;
+  const uint32_t lane_in = 4u * (uint32_t)half * ld_in + (uint32_t)l32 * 4u;
+  const uint32_t lane_out = 4u * (uint32_t)half * ld_out + (uint32_t)l32 * 4u;
+  auto acc_src = [&](const char* base, uint32_t ld, int i, int r, int j) {
+    const char* row = base + (uint32_t)block_row(0, i, r) * ld;  // scalar
+    return (const float*)(row + lane_in + j * 128);
+  };
+  auto acc_dst = [&](char* base, uint32_t ld, int i, int r, int j) {
+    char* row = base + (uint32_t)block_row(0, i, r) * ld;  // scalar
+    return (float*)(row + lane_out + j * 128);
+  };
+  auto src_base = [&](const Tile& t) { return (const char*)(p.acc_in + (long)t.mb * p.ld_acc_in + t.nb); };
+  auto dst_base = [&](const Tile& t) { return (char*)(p.acc_out + (long)t.mb * p.ld_acc_out + t.nb); };
+
+  bf16x8 fa[2][TM], fb[2][TN];
+  f32x16 P[TM][TN], Q[TM][TN];
+
+  // One tile: MFMAs into cur; side gives up tile i-1 and takes tile i+1's
+  // acc_in; the ring index of the tile's first K tile is (i * NK) % S.
+  auto body = [&](auto kind, int i, f32x16 (&cur)[TM][TN], f32x16 (&side)[TM][TN]) {
+    constexpr bool has_prev = decltype(kind)::prev, has_next = decltype(kind)::next;
+    constexpr int OPS = (has_prev ? 1 : 0) + (has_next ? 1 : 0);  // per element
+    // accumulator operations issued in K tile x of this tile
+    auto acc_ops = [&](int x) { return (x >= 0 && x < kChainAccTiles) ? OPS * (chain_e0(x + 1) - chain_e0(x)) : 0; };
+    const Tile tc = tile(i);
+    Tile tn = tc;
+    char* dst = nullptr;
+    const char* src = nullptr;
+    if (has_prev) dst = dst_base(tile(i - 1));
+    if (has_next) {
+      tn = tile(i + 1);
+      src = src_base(tn);
+    }
+    const int b0 = (i * NK) % S;
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      const int bc = (b0 + kt) % S, bn = (b0 + kt + 1) % S, bi = (b0 + kt + 2) % S;
+      const uint16_t* st = smem + bc * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks & 1, n = c ^ 1;
+        if (ks + 1 < KS) {
+          frags(st, ks + 1, fa[n], fb[n]);
+        } else if (kt + 1 < NK || has_next) {
+          const bool issued = kt + 2 < NK || has_next;
+          wait_vmcnt(acc_ops(kt - 1) + (issued ? NL : 0) + acc_ops(kt));
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          frags(smem + bn * STAGE, 0, fa[n], fb[n]);
+        }
+#pragma unroll
+        for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+          for (int tj = 0; tj < TN; ++tj)
+            cur[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][ti], fb[c][tj], cur[ti][tj], 0, 0, 0);
+        if (ks == 1) {
+          // The wait counts above need every accumulator operation of a K
+          // tile issued after that tile's stage loads: the scheduler may not
+          // move instructions across this fence.
+          __builtin_amdgcn_sched_barrier(0);
+          if (kt + 2 < NK) issue(tc, kt + 2, bi);
+          else if (has_next) issue(tn, kt + 2 - NK, bi);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // Accumulator operations: half after the MFMAs of the second k16
+        // step, half after the third (both before the wait in the last).
+        if (kt < kChainAccTiles && (ks == 1 || ks == 2)) {
+          // row offsets computed here, not hoisted (they would hold 128 scalar registers)
+          uint32_t li = ld_in, lo = ld_out;
+          asm volatile("" : "+s"(li), "+s"(lo));
+          const int e0 = chain_e0(kt), e1 = chain_e0(kt + 1), em = (e0 + e1) / 2;
+#pragma unroll
+          for (int e = ks == 1 ? e0 : em; e < (ks == 1 ? em : e1); ++e) {
+            const int ei = e / 32, er = (e % 32) / 2, ej = e % 2;
+            if (has_prev) __builtin_nontemporal_store(side[ei][ej][er], acc_dst(dst, lo, ei, er, ej));
+            if (has_next) side[ei][ej][er] = __builtin_nontemporal_load(acc_src(src, li, ei, er, ej));
+          }
+        }
+      }
+    }
+  };
+
+  // Prologue: tile 0's acc_in, then its first two stages.
+  {
+    const Tile t0 = tile(0);
+    const char* src = src_base(t0);
+#pragma unroll
+    for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int tj = 0; tj < TN; ++tj) P[ti][tj][r] = __builtin_nontemporal_load(acc_src(src, ld_in, ti, r, tj));
+    issue(t0, 0, 0);
+    issue(t0, 1, 1);
+    wait_vmcnt(NL);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    frags(smem, 0, fa[0], fb[0]);
+  }
+  body(ChainKind<0>{}, 0, P, Q);
+  int i = 1;
+  for (; i + 2 < T; i += 2) {  // T is even: tiles 1 .. T-2 in pairs
+    body(ChainKind<1>{}, i, Q, P);
+    body(ChainKind<1>{}, i + 1, P, Q);
+  }
+  body(ChainKind<2>{}, i, Q, P);
+  char* dst = dst_base(tile(i));
+#pragma unroll
+  for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int tj = 0; tj < TN; ++tj) __builtin_nontemporal_store(Q[ti][tj][r], acc_dst(dst, ld_out, ti, r, tj));
+}
+
+// ---------------------------------------------------------------------------
 // Register-staged kernel for any K and 8-element-aligned rows: 128 x 128 x 64
 // tile, 2 x 2 waves of 64 x 64, padded LDS rows (BK + 8), the next K tile
 // loaded into registers while the current one is multiplied, K tail zeroed.
@@ -566,11 +840,52 @@ bool dma_ok(const GemmArgs& a) {
   return a.K > 0 && a.K % 64 == 0 && (al & 15) == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of the carried-chain kernel for this step, or 0 where it does
+// not apply: a middle step of a K-split chain (fp32 accumulator in and out
+// only) of K = 1024 over whole 256 x 128 tiles, one workgroup per CU, each
+// with an even number of tiles; operand rows of the stage loads addressed
+// with 32-bit offsets.
+int chain_workgroups(const GemmArgs& a) {
+  if (!a.acc_in || !a.acc_out || a.out || a.bias || a.resid || !dma_ok(a)) return 0;
+  if (a.K != kChainNK * 64 || a.M % 256 != 0 || a.N % 128 != 0) return 0;
+  if (a.lda >= (1L << 22) || a.ldb >= (1L << 22) || !(a.ld_acc_in >= 0 && a.ld_acc_in < (1L << 24)) ||
+      !(a.ld_acc_out >= 0 && a.ld_acc_out < (1L << 24)))
+    return 0;
+  const int G = device_cus();
+  const long nt = (long)(a.M / 256) * (a.N / 128);
+  if (G <= 0 || G % 8 != 0 || nt % G != 0 || (nt / G) % 2 != 0) return 0;
+  return G;
+}
+
+hipError_t launch_chain(const GemmArgs& a, int G, hipStream_t s) {
+  const int tiles_m = a.M / 256, tiles_n = a.N / 128;
+  const int gm = group_rows(tiles_m, kXcdCUs, 256, 128);
+  const int T = (int)((long)tiles_m * tiles_n / G);
+  hipLaunchKernelGGL(gemm_kernel_chain, dim3(G), dim3(512), 0, s, a, tiles_m, tiles_n, gm, T);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Tile configurations (all give identical bits):
 //   1: direct-to-LDS 256 x 128, 8 waves of 64 x 64, 3 LDS stages (144 KiB,
-//      one workgroup per CU);
+//      one workgroup per CU); a middle step of a carried K-split chain
+//      that fits the carried-chain kernel runs on that kernel instead
+//      (same tile and waves, resident workgroups) unless configuration 1
+//      is asked for explicitly;
 //   2: direct-to-LDS 128 x 128, 4 waves of 64 x 64, 2 LDS stages (64 KiB,
 //      two workgroups per CU);
 //   3: register-staged 128 x 128 (any K, 8-element-aligned rows).
@@ -594,6 +909,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   int cfg = a.config > 0 ? a.config : gemm_auto_config(a);
   if (cfg != 3 && !dma_ok(a)) cfg = 3;
+  if (a.config == 0 && cfg == 1)
+    if (const int G = chain_workgroups(a)) return launch_chain(a, G, s);
   switch (cfg) {
     case 1: return launch_dma<256, 128, 4, 2, 3>(a, s);
     case 2: return launch_dma<128, 128, 2, 2, 2>(a, s);
