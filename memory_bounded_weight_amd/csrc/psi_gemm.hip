@@ -460,74 +460,44 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_kernel_dma(GemmArgs p,
 // walks T tiles (t = blockIdx.x + i * gridDim.x, in the same XCD-local tile
 // order), and two accumulator register sets alternate: while the MFMAs of
 // tile i run on one, the other first gives up tile i-1's result (stores)
-// and then takes tile i+1's acc_in (loads into the same registers), four
-// or five elements in each of the first fourteen K tiles.  The LDS ring runs on across
-// tiles: the first two stages of tile i+1 are issued during the last two K
-// tiles of tile i.  Every output still starts from its acc_in and sees the
-// same ascending k16 MFMA steps with the same lane mapping, so the bits are
-// those of the other kernels.  The accumulator moves with non-temporal loads
-// and stores, which leaves more of each XCD's L2 to the operand tiles.
+// and then takes tile i+1's acc_in (loads into the same registers), four or
+// five elements in each of the first fourteen K tiles.  The LDS ring runs on
+// across tiles: the first two stages of tile i+1 are issued during the last
+// two K tiles of tile i.  Every output still starts from its acc_in and sees
+// the same ascending k16 MFMA steps with the same lane mapping, so the bits
+// are those of the other kernels.  The accumulator moves with non-temporal
+// loads and stores, which leaves more of each XCD's L2 to the operand tiles.
 //
 // Wait counts.  One counter covers loads and stores, retired in issue order.
-// In K tile kt, stage kt+2 is issued after the MFMAs of the second k16 step
-// and the accumulator operations right after it; the wait for stage kt+1
-// before the last step leaves in flight exactly what was issued after stage
-// kt+1: the accumulator operations of K tile kt-1, stage kt+2 and the
-// accumulator operations of K tile kt.  A store or load thus has two K tiles
-// to complete.
+// In K tile kt, stage kt+2 is issued after the MFMAs of the second k16 step;
+// the accumulator operations follow, half after that step and half after
+// the third, and the wait for stage kt+1 before the last step leaves in
+// flight exactly what was issued after stage kt+1: the accumulator
+// operations of K tile kt-1, stage kt+2 and the accumulator operations of
+// K tile kt.  A store or load thus has about two K tiles to complete.
+#define PSI_VM_CASE(n) \
+  case n: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(n)); break;
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {  // immediates only; folded once the K loop is unrolled
-    case 1: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(7)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(9)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(10)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(11)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(12)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(13)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(14)); break;
-    case 15: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(15)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(16)); break;
-    case 17: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(17)); break;
-    case 18: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(18)); break;
-    case 19: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(19)); break;
-    case 20: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(20)); break;
-    case 21: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(21)); break;
-    case 22: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(22)); break;
-    case 23: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(23)); break;
-    case 24: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(24)); break;
-    case 25: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(25)); break;
-    case 26: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(26)); break;
-    case 27: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(27)); break;
-    case 28: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(28)); break;
-    case 29: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(29)); break;
-    case 30: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(30)); break;
-    case 31: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(31)); break;
-    case 32: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(32)); break;
-    case 33: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(33)); break;
-    case 34: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(34)); break;
-    case 35: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(35)); break;
-    case 36: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(36)); break;
-    case 37: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(37)); break;
-    case 38: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(38)); break;
-    case 39: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(39)); break;
-    case 40: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(40)); break;
+    PSI_VM_CASE(1) PSI_VM_CASE(2) PSI_VM_CASE(3) PSI_VM_CASE(4) PSI_VM_CASE(5) PSI_VM_CASE(6) PSI_VM_CASE(7)
+    PSI_VM_CASE(8) PSI_VM_CASE(9) PSI_VM_CASE(10) PSI_VM_CASE(11) PSI_VM_CASE(12) PSI_VM_CASE(13)
+    PSI_VM_CASE(14) PSI_VM_CASE(15) PSI_VM_CASE(16) PSI_VM_CASE(17) PSI_VM_CASE(18) PSI_VM_CASE(19)
+    PSI_VM_CASE(20) PSI_VM_CASE(21) PSI_VM_CASE(22) PSI_VM_CASE(23) PSI_VM_CASE(24) PSI_VM_CASE(25)
+    PSI_VM_CASE(26) PSI_VM_CASE(27) PSI_VM_CASE(28) PSI_VM_CASE(29) PSI_VM_CASE(30) PSI_VM_CASE(31)
+    PSI_VM_CASE(32) PSI_VM_CASE(33) PSI_VM_CASE(34) PSI_VM_CASE(35) PSI_VM_CASE(36) PSI_VM_CASE(37)
+    PSI_VM_CASE(38) PSI_VM_CASE(39) PSI_VM_CASE(40)
     default: __builtin_amdgcn_s_waitcnt(PSI_VMCNT(0)); break;  // fewer in flight is always safe
   }
 }
+#undef PSI_VM_CASE
 
 constexpr int kChainNK = 16;  // K tiles of 64 per step: K = 1024
 // The accumulator traffic of a tile (64 elements per lane each way) is
 // spread over its first 14 K tiles: element range [chain_e0(kt),
-// chain_e0(kt + 1)) in K tile kt, 4 or 5 elements.  Over 8 K tiles it asked
-// for about twice the HBM bandwidth the chip has and slowed the MFMAs; the
-// last two K tiles stay free so that the next tile's accumulator has
-// arrived before its first MFMA.
+// chain_e0(kt + 1)) in K tile kt, 4 or 5 elements.  The last two K tiles
+// stay free, so the next tile's accumulator has arrived before its first
+// MFMA without a wait.  (Over the first 8 K tiles the kernel measured the
+// same.)
 constexpr int kChainAccTiles = 14;
 __host__ __device__ constexpr int chain_e0(int kt) { return kt * 64 / kChainAccTiles; }
 
