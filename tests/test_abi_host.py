@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 from memory_bounded_weight_amd import psi
+from tests import golden
 
 MiB = 1 << 20
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -118,20 +119,18 @@ def cfg5_ffn(tile=1024):
             fake_matrix(4096, 16384, psi.PSI_SPLIT_COLS, tile))
 
 
-@pytest.mark.parametrize("arena,page,expect", [
-    (48, 8, psi.PSI_E_SCRATCH_EXHAUSTED),
-    (64, 8, psi.PSI_E_SCRATCH_EXHAUSTED),
-    (80, 8, psi.PSI_OK),
-    (96, 8, psi.PSI_OK),
-    (80, 4, psi.PSI_E_PAGE_TOO_SMALL),
-    (96, 16, psi.PSI_OK),
-])
+TABLE_V_OUTCOME = {"scratch_exhausted": psi.PSI_E_SCRATCH_EXHAUSTED, "complete": psi.PSI_OK,
+                   "weight_tile_exceeds_page": psi.PSI_E_PAGE_TOO_SMALL}
+
+
+@pytest.mark.parametrize("arena,page,expect", [(int(a), int(p), TABLE_V_OUTCOME[o])
+                                               for a, p, o in golden.rows("table_v_capacity.txt")])
 def test_capacity_outcomes_like_table_v(arena, page, expect):
-    """[PSI] Table V lists six arena/page capacities for one block with tiles
-    held fixed: 48/8 and 64/8 exhaust scratch, 80/8, 96/8, 96/16 complete,
-    80/4 fails because a weight tile exceeds the page.  With the stack's
-    tiles (8-head groups, 1,024-channel FFN tiles, 8,192 tokens, 8 MiB
-    workspace) the same six settings give the same outcome pattern."""
+    """[PSI] Table V (tests/golden) lists six arena/page capacities for one
+    block with tiles held fixed: 48/8 and 64/8 exhaust scratch, 80/8, 96/8,
+    96/16 complete, 80/4 fails because a weight tile exceeds the page.  With
+    the stack's tiles (8-head groups, 1,024-channel FFN tiles, 8,192 tokens,
+    8 MiB workspace) the same six settings give the same outcome pattern."""
     d = desc(arena, page, 2, 8, 0)
     Wq, Wk, Wv, Wo = cfg5_attn()
     st_a, need_a = psi.psi_attn_plan(d, 8192, 0, 32, 128, Wq, Wk, Wv, Wo, True)
@@ -654,6 +653,17 @@ def test_pack_tiles_layout():
     assert sum(sizes) == rows * cols * 2
     with pytest.raises(psi.PsiError):
         psi.psi_pack_tiles(W, rows, cols, br, bc, W)  # in place is refused
+
+
+def test_lowlive_hidden_state_is_the_journal_figure():
+    """[PSI] sec. IV-C prints a per-block journal figure (tests/golden).  It
+    factors as one BF16 FFN hidden state of 4,991 tokens at width 16,384, the
+    token count of the low-live workload, whose tiled FFN commits exactly that
+    many bytes of hidden tiles per block (16 tiles of 4,991 x 1,024)."""
+    fig = golden.values("journal_block_bytes.txt")["bytes_per_block"]
+    M, h, th = 4991, 16384, 1024
+    assert fig == M * h * 2
+    assert fig == (h // th) * M * th * 2
 
 
 def test_two_d_page_tiles_rules_and_lowlive_traffic_dry_run():

@@ -15,7 +15,10 @@ import torch
 
 import oracle
 from memory_bounded_weight_amd import synth
+from tests import golden
 from tests.gpu_util import MiB, assert_bf16_close, dev, empty_bf16, f, host, make_arena, rel_err
+
+EQ5 = golden.values("eq5_write_boundary.txt")  # [PSI] sec. II-C eq. (5)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +66,7 @@ def test_linear_single_paged_case(P):
     assert rel_err(acc, accr).max() <= 1e-4  # identical inputs: fp32 accumulators
 
 
-@pytest.mark.parametrize("variant,expect", [(0, 129 / 128), (1, 1.0)])
+@pytest.mark.parametrize("variant,expect", [(0, float(EQ5["B(z + b)"])), (1, float(EQ5["B(B(z) + b)"]))])
 def test_linear_eq5_bitwise(P, variant, expect):
     """[PSI] eq. (5) through the GPU epilogue: the accumulator is exactly
     257/256, so the fp32-bias variant gives 129/128 and the baseline variant

@@ -16,8 +16,10 @@ import torch
 
 import oracle
 from memory_bounded_weight_amd import synth
+from tests import golden
 
 f = oracle.bf16_to_float
+EQ5 = golden.values("eq5_write_boundary.txt")  # [PSI] sec. II-C eq. (5)
 
 
 def torch_bf16_bits(a64) -> np.ndarray:
@@ -55,12 +57,13 @@ def frac_of_bits(u) -> Fraction:
 # ----------------------------------------------------------------- rounding
 
 def test_eq5_write_boundary_scalars():
-    """[PSI] sec. II-C eq. (5): B(B(257/256) + 1/256) = 1 but B(257/256 + 1/256) = 129/128."""
-    z, b = 257 / 256, 1 / 256
+    """[PSI] sec. II-C eq. (5), the worked example in tests/golden: B(B(z) + b)
+    and B(z + b) for z = 257/256, b = 1/256."""
+    z, b = float(EQ5["z"]), float(EQ5["b"])
     once = oracle.bf16_from_float_scalar(z + b)
     twice = oracle.bf16_from_float_scalar(float(f(oracle.bf16_from_float_scalar(z))) + b)
-    assert float(f(np.uint16(once))) == 129 / 128
-    assert float(f(np.uint16(twice))) == 1.0
+    assert Fraction(float(f(np.uint16(once)))) == EQ5["B(z + b)"]
+    assert Fraction(float(f(np.uint16(twice)))) == EQ5["B(B(z) + b)"]
 
 
 def test_eq5_linear_bias_variants():
@@ -72,9 +75,9 @@ def test_eq5_linear_bias_variants():
     b = synth.f32_to_bf16_bits(np.array([2.0 ** -8], np.float32))
     y_mod, acc = oracle.linear(x, W, b, variant=0, want_acc=True)
     y_base = oracle.linear(x, W, b, variant=1)
-    assert acc[0, 0] == np.float32(257 / 256)
-    assert f(y_mod)[0, 0] == np.float32(129 / 128)
-    assert f(y_base)[0, 0] == np.float32(1.0)
+    assert Fraction(float(acc[0, 0])) == EQ5["z"]
+    assert Fraction(float(f(y_mod)[0, 0])) == EQ5["B(z + b)"]
+    assert Fraction(float(f(y_base)[0, 0])) == EQ5["B(B(z) + b)"]
 
 
 def test_bf16_from_float_matches_torch_rounding():
