@@ -97,10 +97,10 @@ static psi_status wait_release(psi_arena* a, psi_page_slot& slot) {
   return PSI_OK;
 }
 
-int first_free_slot(const psi_arena* a) {
+int first_free_slot(const psi_arena* a, int skip) {
   for (int i = 0; i < a->desc.n_pages; ++i) {
     const int c = (a->next_slot + i) % a->desc.n_pages;
-    if (a->slots[c].state == psi_page_slot::FREE) return c;
+    if (c != skip && a->slots[c].state == psi_page_slot::FREE) return c;
   }
   return -1;
 }
@@ -131,16 +131,27 @@ static int ready_lent_slot(psi_arena* a) {
 }
 
 // A free lent slot whose fill needs a host wait, or -1.
-static int free_lent_slot(const psi_arena* a) {
+static int free_lent_slot(const psi_arena* a, int skip) {
   for (int i = 0; i < a->n_lent; ++i)
-    if (a->lent[i].state == psi_page_slot::FREE) return a->desc.n_pages + i;
+    if (a->desc.n_pages + i != skip && a->lent[i].state == psi_page_slot::FREE) return a->desc.n_pages + i;
   return -1;
 }
 
-int submit_slot(psi_arena* a) {
+// The held slot while its consumer may still run, else -1 (dry runs keep
+// the plain order).
+static int pending_hold(psi_arena* a) {
+  const int h = a->hold_slot;
+  if (h < 0 || a->dry) return -1;
+  psi_page_slot* p = slot_ptr(a, h);
+  if (!p || p->state != psi_page_slot::FREE || !p->released_once) return -1;
+  return event_done(p->release) ? -1 : h;
+}
+
+int submit_slot(psi_arena* a, bool avoid_hold) {
+  const int skip = avoid_hold ? pending_hold(a) : -1;
   int s = ready_lent_slot(a);
-  if (s < 0) s = first_free_slot(a);
-  if (s < 0) s = free_lent_slot(a);
+  if (s < 0) s = first_free_slot(a, skip);
+  if (s < 0) s = free_lent_slot(a, skip);
   return s;
 }
 
@@ -163,6 +174,7 @@ int lend_scratch_slots(psi_arena* a) {
     l.dev = a->dry ? nullptr : a->base + a->layout.scratch_off + start + i * stride;
     a->lent_fresh[i] = true;
   }
+  if (a->hold_slot >= a->desc.n_pages) a->hold_slot = -1;
   a->n_lent = (int)n;
   if (n) {
     // the scratch's earlier users (previous operators) precede any copy into
@@ -178,13 +190,14 @@ int lend_scratch_slots(psi_arena* a) {
 psi_status return_lent_slots(psi_arena* a) {
   bool busy = false;
   for (int i = 0; i < a->n_lent; ++i) busy |= a->lent[i].state != psi_page_slot::FREE;
+  if (a->hold_slot >= a->desc.n_pages) a->hold_slot = -1;
   a->n_lent = 0;
   if (busy) return fail(PSI_E_STATE, "a lent page slot is still in use at the end of the operator");
   return PSI_OK;
 }
 
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
-                          bool pinned_check) {
+                          bool pinned_check, bool avoid_hold) {
   if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
   if (bytes > a->desc.page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
@@ -193,7 +206,7 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
   // round-robin position on (a page held across many requests does not
   // stall the others)
   // (a lent slot that is not ready comes last and then takes a host wait)
-  const int s = submit_slot(a);
+  const int s = submit_slot(a, avoid_hold);
   if (s < 0) return fail(PSI_E_PAGE_BUSY, "every page slot still has an unreleased request");
   const bool lent = s >= a->desc.n_pages;
   psi_page_slot& slot = *slot_ptr(a, s);
@@ -370,6 +383,12 @@ static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (
   if (t0) {
     PSI_HIP(hipEventRecord(t1, a->compute));
     a->pending.push_back({t0, t1, kind, work});
+  }
+  // A consumer enqueued after the held slot's one: fills of that slot no
+  // longer leave the compute stream empty.
+  if (a->hold_slot >= 0) {
+    a->hold_slot = -1;
+    if (a->refill) return a->refill(a->refill_ctx);
   }
   return PSI_OK;
 }

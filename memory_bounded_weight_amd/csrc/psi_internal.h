@@ -165,6 +165,14 @@ struct psi_arena {
   int next_copy = 0;            // copy stream of the next page
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
+  // The slot freed by the consumer the host enqueued last.  While that
+  // consumer may still run, page fills that are not needed yet go elsewhere:
+  // filling it would make the host wait for the kernel it has just
+  // enqueued, and the compute stream would run dry until the next launch.
+  int hold_slot = -1;
+  // the running operator's page feeder, called after a launch that ends a hold
+  psi_status (*refill)(void*) = nullptr;
+  void* refill_ctx = nullptr;
   // Page slots lent by the running operator from the whole pages of scratch
   // above its own allocations (indices n_pages .. n_pages + n_lent - 1).
   // A lent slot is filled only when no host wait is needed: on first use
@@ -206,7 +214,7 @@ void scratch_reset(psi_arena* a, size_t mark);
 
 // Page request (slice copy into a lent slot that is ready, else into the
 // next round-robin page slot).
-int first_free_slot(const psi_arena* a);  // -1 when every slot is taken
+int first_free_slot(const psi_arena* a, int skip = -1);  // -1 when every slot is taken
 // Lends the whole pages of scratch above scratch_top as page slots to the
 // running operator (none in a sync-copy arena); returns how many.  The
 // operator must not allocate scratch afterwards, and returns them with
@@ -215,10 +223,10 @@ int lend_scratch_slots(psi_arena* a);
 psi_status return_lent_slots(psi_arena* a);
 // The slot the next page_submit_ex would fill (-1: none free), and the
 // device address of slot s (regular or lent).
-int submit_slot(psi_arena* a);
+int submit_slot(psi_arena* a, bool avoid_hold = false);
 void* slot_dev(psi_arena* a, int s);
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
-                          bool check_pinned);
+                          bool check_pinned, bool avoid_hold = false);
 psi_status page_acquire(psi_arena* a, int page);
 psi_status page_release(psi_arena* a, int page);
 

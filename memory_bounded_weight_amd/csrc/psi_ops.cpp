@@ -75,24 +75,44 @@ class OpBiases {
 // the round-robin slot), so the copy of the next pages overlaps the
 // consumers of the current one; with two slots this is the paper's two
 // alternating pages ([PSI] sec. III-B weight prefetch).  Refilling a slot
-// waits on the host for its last consumer (see page_submit_ex); submitting
-// only slots whose consumer had already finished, to keep the host further
-// ahead of the compute stream, started each copy later after its slot's
-// release and cost the copy-bound workloads 2-6%.
+// waits on the host for its last consumer (see page_submit_ex), so each copy
+// starts right after that consumer ends (submitting only slots whose
+// consumer had already finished started copies later and cost the
+// copy-bound workloads 2-6%).  The one exception is the slot freed by the
+// consumer enqueued last: waiting for that kernel would leave the compute
+// stream empty until the host enqueues the next one.  A page not needed yet
+// goes to another slot, and that slot is refilled right after the next
+// launch (the arena's hold, ended in its launch path through `refill`).
 class PageFeeder {
  public:
-  PageFeeder(psi_arena* a, std::vector<PageReq> reqs) : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {}
+  PageFeeder(psi_arena* a, std::vector<PageReq> reqs) : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {
+    a_->refill = &PageFeeder::refill_cb;
+    a_->refill_ctx = this;
+  }
+  ~PageFeeder() {
+    if (a_->refill_ctx == this) {
+      a_->refill = nullptr;
+      a_->refill_ctx = nullptr;
+    }
+  }
+  PageFeeder(const PageFeeder&) = delete;
+  PageFeeder& operator=(const PageFeeder&) = delete;
+  static psi_status refill_cb(void* self) { return static_cast<PageFeeder*>(self)->feed(); }
 
-  psi_status feed() {
+  // Submits requests in order while a slot is free.  Requests below `need`
+  // are wanted now and may take any slot; later ones avoid the slot freed by
+  // the last enqueued consumer while it may still run.
+  psi_status feed(size_t need = 0) {
     while (submitted_ < reqs_.size()) {
       const PageReq& r = reqs_[submitted_];
       if (r.resident) {  // consumed in place: no copy, no slot
         ++submitted_;
         continue;
       }
-      if (submit_slot(a_) < 0) break;
+      const bool avoid = submitted_ >= need;
+      if (submit_slot(a_, avoid) < 0) break;
       int s = -1;
-      psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false);
+      psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false, avoid);
       if (st) return st;
       slot_[submitted_++] = s;
     }
@@ -100,7 +120,7 @@ class PageFeeder {
   }
   // Waits (on the compute stream) for request i and returns its page.
   psi_status take(size_t i, const uint16_t** page) {
-    psi_status st = feed();
+    psi_status st = feed(i + 1);
     if (st) return st;
     const PageReq& r = reqs_[i];
     if (r.resident) {
@@ -117,6 +137,7 @@ class PageFeeder {
     if (!reqs_[i].resident) {
       psi_status st = page_release(a_, slot_[i]);
       if (st) return st;
+      a_->hold_slot = slot_[i];
     }
     return feed();
   }
