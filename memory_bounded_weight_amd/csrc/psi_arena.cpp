@@ -11,13 +11,20 @@
 // wait on `ready`; release records `release` on the compute stream after
 // every enqueued use, and the next copy into the slot is enqueued once the
 // host has seen `release` complete (a host wait when it has not: see
-// wait_release).  Inside an operator, whole pages of idle scratch serve as
-// extra (lent) slots, filled only when that needs no wait.
+// wait_release).  An operator's own release right after the consuming
+// kernel takes that kernel's end event instead of recording one (see
+// psi_arena::stop_ring).  Inside an operator, whole pages of idle scratch
+// serve as extra (lent) slots, filled only when that needs no wait.
 #include <cstring>
 
 #include "psi_internal.h"
 
 namespace psi {
+
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
 
 psi_status probe_commit(psi_arena* a, int32_t branch, int32_t role, const void* dev, size_t bytes) {
   if (!a->probe || a->dry) return PSI_OK;
@@ -88,11 +95,19 @@ static hipEvent_t pool_event(psi_arena* a) {
 // for 8 MiB pages in a slot/event pipeline).  With the wait on the host the
 // host stays at most one slot round ahead of the consumers, which keeps the
 // compute stream fed.
+static hipEvent_t release_event(const psi_arena* a, const psi_page_slot& slot) {
+  // a ring entry bound again has seen its earlier kernel end
+  if (slot.rel_ring >= 0 && a->stop_seq[slot.rel_ring] != slot.rel_seq) return nullptr;
+  return slot.rel_ev;
+}
+
 static psi_status wait_release(psi_arena* a, psi_page_slot& slot) {
-  hipError_t q = hipEventQuery(slot.release);
+  hipEvent_t ev = release_event(a, slot);
+  if (!ev) return PSI_OK;
+  hipError_t q = hipEventQuery(ev);
   if (q == hipSuccess) return PSI_OK;
   if (q != hipErrorNotReady) return hip_fail(q, "hipEventQuery(release)");
-  PSI_HIP(hipEventSynchronize(slot.release));
+  PSI_HIP(hipEventSynchronize(ev));
   a->stats.host_syncs++;
   return PSI_OK;
 }
@@ -112,10 +127,33 @@ static psi_page_slot* slot_ptr(psi_arena* a, int s) {
 }
 
 static bool event_done(hipEvent_t e) {
+  if (!e) return true;
   const hipError_t q = hipEventQuery(e);
   if (q == hipSuccess) return true;
   if (q != hipErrorNotReady) (void)hipGetLastError();  // not ready for this purpose; the waits report it
   return false;
+}
+
+static bool release_done(const psi_arena* a, const psi_page_slot& slot) {
+  return !slot.released_once || event_done(release_event(a, slot));
+}
+
+// Marks the slot's release after every use enqueued so far: with `borrow`,
+// and a kernel launched after the slot's consumers were ordered, the end
+// event of the last launch (which follows them in stream order); else an
+// event recorded on the compute stream now.
+static psi_status mark_release(psi_arena* a, psi_page_slot& slot, bool borrow) {
+  if (a->dry) return PSI_OK;
+  if (borrow && a->last_stop && a->launches > slot.acq_launch) {
+    slot.rel_ev = a->last_stop;
+    slot.rel_ring = a->last_stop_ring;
+    slot.rel_seq = a->launches;
+    return PSI_OK;
+  }
+  PSI_HIP(hipEventRecord(slot.release, a->compute));
+  slot.rel_ev = slot.release;
+  slot.rel_ring = -1;
+  return PSI_OK;
 }
 
 // A lent slot that can be filled without a host wait, or -1.
@@ -124,7 +162,7 @@ static int ready_lent_slot(psi_arena* a) {
     const psi_page_slot& l = a->lent[i];
     if (l.state != psi_page_slot::FREE) continue;
     if (a->dry) return a->desc.n_pages + i;
-    if (a->lent_fresh[i] ? event_done(a->scratch_free) : (!l.released_once || event_done(l.release)))
+    if (a->lent_fresh[i] ? event_done(a->scratch_free) : release_done(a, l))
       return a->desc.n_pages + i;
   }
   return -1;
@@ -144,7 +182,7 @@ static int pending_hold(psi_arena* a) {
   if (h < 0 || a->dry) return -1;
   psi_page_slot* p = slot_ptr(a, h);
   if (!p || p->state != psi_page_slot::FREE || !p->released_once) return -1;
-  return event_done(p->release) ? -1 : h;
+  return release_done(a, *p) ? -1 : h;
 }
 
 int submit_slot(psi_arena* a, bool avoid_hold) {
@@ -231,10 +269,14 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
       a->next_copy = ci ^ 1;
       if (lent) {
         const int li = s - a->desc.n_pages;
-        hipEvent_t w = a->lent_fresh[li] ? a->scratch_free : (slot.released_once ? slot.release : nullptr);
-        if (w && !event_done(w)) {
-          PSI_HIP(hipEventSynchronize(w));
-          a->stats.host_syncs++;
+        if (a->lent_fresh[li]) {
+          if (!event_done(a->scratch_free)) {
+            PSI_HIP(hipEventSynchronize(a->scratch_free));
+            a->stats.host_syncs++;
+          }
+        } else if (slot.released_once) {
+          psi_status st = wait_release(a, slot);
+          if (st) return st;
         }
       } else if (slot.released_once) {
         psi_status st = wait_release(a, slot);
@@ -316,11 +358,12 @@ psi_status bias_acquire(psi_arena* a, int s) {
       a->stats.event_waits++;
     }
     slot.state = psi_page_slot::CONSUMING;
+    slot.acq_launch = a->launches;
   }
   return PSI_OK;
 }
 
-psi_status bias_release(psi_arena* a, int s) {
+psi_status bias_release(psi_arena* a, int s, bool borrow) {
   if (s < 0) return PSI_OK;
   psi_page_slot& slot = a->bias_slots[s];
   if (slot.state == psi_page_slot::FREE) return PSI_OK;
@@ -328,7 +371,7 @@ psi_status bias_release(psi_arena* a, int s) {
     psi_status st = bias_acquire(a, s);
     if (st) return st;
   }
-  if (!a->dry) PSI_HIP(hipEventRecord(slot.release, a->compute));
+  if (psi_status st = mark_release(a, slot, borrow)) return st;
   slot.released_once = true;
   slot.state = psi_page_slot::FREE;
   return PSI_OK;
@@ -346,10 +389,11 @@ psi_status page_acquire(psi_arena* a, int page) {
     a->stats.event_waits++;
   }
   slot.state = psi_page_slot::CONSUMING;
+  slot.acq_launch = a->launches;
   return PSI_OK;
 }
 
-psi_status page_release(psi_arena* a, int page) {
+psi_status page_release(psi_arena* a, int page, bool borrow) {
   psi_page_slot* sp = slot_ptr(a, page);
   if (!sp) return fail(PSI_E_INVALID, "bad page index");
   psi_page_slot& slot = *sp;
@@ -359,7 +403,7 @@ psi_status page_release(psi_arena* a, int page) {
     psi_status st = page_acquire(a, page);
     if (st) return st;
   }
-  if (!a->dry) PSI_HIP(hipEventRecord(slot.release, a->compute));
+  if (psi_status st = mark_release(a, slot, borrow)) return st;
   slot.released_once = true;
   slot.state = psi_page_slot::FREE;
   return PSI_OK;
@@ -370,18 +414,47 @@ static psi_status timed_launch(psi_arena* a, int kind, double work, hipError_t (
   a->stats.kernel_launches++;
   if (a->dry) return PSI_OK;
   if (psi_status st = jitter(a, a->compute)) return st;  // delays the consumer, not the copies
+  a->last_stop = nullptr;
+  LaunchEvents& ev = launch_events();
+  ev = LaunchEvents{};
   hipEvent_t t0 = nullptr, t1 = nullptr;
+  int ring = -1;
   if ((a->desc.flags & PSI_ARENA_PROFILE) && !a->timing_off) {
+    // bound to the kernel: its own start and end, as a kernel trace has them
     t0 = pool_event(a);
     t1 = pool_event(a);
     if (!t0 || !t1) return fail(PSI_E_HIP, "event pool");
-    PSI_HIP(hipEventRecord(t0, a->compute));
+    ev.start = t0;
+    ev.stop = t1;
+  } else {
+    const int j = a->stop_next;
+    if (a->stop_seq[j] == 0 || event_done(a->stop_ring[j])) {
+      ring = j;
+      ev.stop = a->stop_ring[j];
+    }
   }
-  hipError_t e = fn(args, a->compute);
+  const hipError_t e = fn(args, a->compute);
+  const bool launched = ev.launched;
+  ev = LaunchEvents{};
   if (e != hipSuccess)
     return hip_fail(e, kind == 0 ? "gemm launch" : kind == 1 ? "attention launch" : "norm/rope launch");
+  if (launched) {
+    a->launches++;
+    if (ring >= 0) {
+      a->stop_seq[ring] = a->launches;
+      a->stop_next = (ring + 1) % psi_arena::kStopRing;
+      a->last_stop = a->stop_ring[ring];
+      a->last_stop_ring = ring;
+    } else if (t1) {
+      a->last_stop = t1;
+      a->last_stop_ring = -1;
+    }
+  }
   if (t0) {
-    PSI_HIP(hipEventRecord(t1, a->compute));
+    if (!launched) {  // nothing to bind (an empty launch): time the empty interval
+      PSI_HIP(hipEventRecord(t0, a->compute));
+      PSI_HIP(hipEventRecord(t1, a->compute));
+    }
     a->pending.push_back({t0, t1, kind, work});
   }
   // A consumer enqueued after the held slot's one: fills of that slot no
@@ -426,6 +499,14 @@ static psi_status harvest(psi_arena* a) {
   PSI_HIP(hipStreamSynchronize(a->copy1));
   PSI_HIP(hipStreamSynchronize(a->compute));
   a->stats.host_syncs += 3;
+  // every release is complete now; profiling events go back to the pool
+  auto drop = [](psi_page_slot& sl) {
+    if (sl.rel_ring < 0 && sl.rel_ev != sl.release) sl.rel_ev = nullptr;
+  };
+  for (int i = 0; i < a->desc.n_pages; ++i) drop(a->slots[i]);
+  for (psi_page_slot& sl : a->lent) drop(sl);
+  for (psi_page_slot& sl : a->bias_slots) drop(sl);
+  if (a->last_stop_ring < 0) a->last_stop = nullptr;
   for (const psi_timed& t : a->pending) {
     float ms = 0.0f;
     PSI_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
@@ -499,6 +580,8 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->lent[i].release, hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&a->scratch_free, hipEventDisableTiming);
+    for (int i = 0; e == hipSuccess && i < psi_arena::kStopRing; ++i)
+      e = hipEventCreateWithFlags(&a->stop_ring[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       psi_status r = hip_fail(e, "psi_arena_create");
       psi_arena_destroy(a);
@@ -537,6 +620,8 @@ psi_status psi_arena_destroy(psi_arena* a) {
       if (l.release) (void)hipEventDestroy(l.release);
     }
     if (a->scratch_free) (void)hipEventDestroy(a->scratch_free);
+    for (hipEvent_t e : a->stop_ring)
+      if (e) (void)hipEventDestroy(e);
     if (a->copy) (void)hipStreamDestroy(a->copy);
     if (a->copy1) (void)hipStreamDestroy(a->copy1);
     if (a->base) {

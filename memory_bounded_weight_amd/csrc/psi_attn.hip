@@ -870,8 +870,7 @@ __global__ __launch_bounds__(512) void attn_kernel_pp(AttnArgs p) {
 template <int QB, int NP, int DH>
 hipError_t launch_pipe(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel_pipe<QB, NP, DH>), grid, dim3(QB * 2), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(attn_kernel_pipe<QB, NP, DH>, grid, dim3(QB * 2), s, a);
 }
 
 template <int NP, int DH>
@@ -880,15 +879,13 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t s) {
   if ((long)KT * a.ldk * 2 >= (1L << 32) || (long)DH * a.ldvt * 2 >= (1L << 32))
     return launch_pipe<256, NP, DH>(a, s);
   dim3 grid((a.Mq + 255) / 256, a.heads);
-  hipLaunchKernelGGL((attn_kernel_pp<NP, DH>), grid, dim3(512), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(attn_kernel_pp<NP, DH>, grid, dim3(512), s, a);
 }
 
 template <int QB, int NP, int DH>
 hipError_t launch_q(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.Mq + QB - 1) / QB, a.heads);
-  hipLaunchKernelGGL((attn_kernel<QB, NP, DH>), grid, dim3(QB * 2), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(attn_kernel<QB, NP, DH>, grid, dim3(QB * 2), s, a);
 }
 
 template <int NP, int DH>

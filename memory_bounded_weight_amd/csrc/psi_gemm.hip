@@ -792,17 +792,15 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int tiles_n = (a.N + BN - 1) / BN;
   constexpr int per_cu = (160 * 1024) / (S * (BM + BN) * 64 * 2);  // workgroups per CU by LDS
   const int gm = group_rows(tiles_m, kXcdCUs * per_cu, BM, BN);
-  hipLaunchKernelGGL((gemm_kernel_dma<BM, BN, WGM, WGN, S>), dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), 0, s,
-                     a, tiles_m, tiles_n, gm);
-  return hipGetLastError();
+  return launch_kernel(gemm_kernel_dma<BM, BN, WGM, WGN, S>, dim3(tiles_m * tiles_n), dim3(64 * WGM * WGN), s, a,
+                       tiles_m, tiles_n, gm);
 }
 
 hipError_t launch_reg(const GemmArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + 127) / 128;
   const int tiles_n = (a.N + 127) / 128;
   const int gm = group_rows(tiles_m, kXcdCUs * 2, 128, 128);
-  hipLaunchKernelGGL(gemm_kernel_reg, dim3(tiles_m * tiles_n), dim3(kRegThreads), 0, s, a, tiles_m, tiles_n, gm);
-  return hipGetLastError();
+  return launch_kernel(gemm_kernel_reg, dim3(tiles_m * tiles_n), dim3(kRegThreads), s, a, tiles_m, tiles_n, gm);
 }
 
 bool dma_ok(const GemmArgs& a) {
@@ -844,8 +842,7 @@ hipError_t launch_chain(const GemmArgs& a, int G, hipStream_t s) {
   const int tiles_m = a.M / 256, tiles_n = a.N / 128;
   const int gm = group_rows(tiles_m, kXcdCUs, 256, 128);
   const int T = (int)((long)tiles_m * tiles_n / G);
-  hipLaunchKernelGGL(gemm_kernel_chain, dim3(G), dim3(512), 0, s, a, tiles_m, tiles_n, gm, T);
-  return hipGetLastError();
+  return launch_kernel(gemm_kernel_chain, dim3(G), dim3(512), s, a, tiles_m, tiles_n, gm, T);
 }
 
 }  // namespace

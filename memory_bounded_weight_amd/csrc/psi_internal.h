@@ -4,6 +4,7 @@
 // Audio-Video Generator under a Fixed GPU Working Set" (arXiv 2611.08023).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -29,6 +30,29 @@ constexpr size_t kAlign = 256;
 constexpr size_t kDefaultSide = 64 * 1024;
 
 // ------------------------------------------------------------- kernels
+// Events that the next kernel launch binds to its own start and end
+// (hipExtLaunchKernelGGL), set by the arena around one launch: bound to the
+// kernel they time the kernel alone, and they add no packet to the stream.
+// `launched` is set once a kernel has taken them; a launch function that
+// launches several kernels binds `start` to the first and `stop` to the last.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool launched = false;
+};
+LaunchEvents& launch_events();  // this host thread's
+
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchEvents& ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    ev.launched = true;
+    ev.start = nullptr;
+  }
+  return e;
+}
+
 enum GemmEpilogue : int {
   EPI_ACC = 0,   // store fp32 accumulator only
   EPI_BIAS = 1,  // out = B(acc + bias)  [+ residual]
@@ -144,6 +168,15 @@ struct psi_page_slot {
   State state = FREE;
   hipEvent_t ready = nullptr;    // recorded on the copy stream after the copy
   hipEvent_t release = nullptr;  // recorded on the compute stream after the last consumer
+  // The event that marks the last release: `release`, or the end event bound
+  // to the consuming kernel's launch (entry `rel_ring` of the arena's ring
+  // while that entry still carries launch number `rel_seq`; a profiling
+  // event when `rel_ring` is -1, dropped once harvested); nullptr once known
+  // to be complete.
+  hipEvent_t rel_ev = nullptr;
+  int rel_ring = -1;
+  uint64_t rel_seq = 0;
+  uint64_t acq_launch = 0;  // kernel launches before the slot's consumers were ordered after its copy
   bool released_once = false;
   void* dev = nullptr;
 };
@@ -205,6 +238,19 @@ struct psi_arena {
   uint32_t jitter_state = 0x9E3779B9u;  // PSI_ARENA_JITTER sequence
   bool timing_off = false;               // psi_arena_set_timing(a, 0)
   int device = 0;
+  // End events bound to the kernels the arena launches (launch_kernel).  A
+  // release made by an operator right after its consuming kernel borrows
+  // that kernel's end event instead of recording one more event on the
+  // compute stream: each recorded event delays the next kernel by a few
+  // microseconds (measured on MI355X), one bound to a launch does not.  An
+  // entry is bound again only after its previous kernel has ended.
+  static constexpr int kStopRing = 32;
+  hipEvent_t stop_ring[kStopRing] = {};
+  uint64_t stop_seq[kStopRing] = {};  // launch number an entry is bound to (0: never)
+  int stop_next = 0;
+  uint64_t launches = 0;              // kernels launched through the arena
+  hipEvent_t last_stop = nullptr;     // end event of the last launch, if it has one
+  int last_stop_ring = -1;            // its ring entry, or -1 for a profiling event
 };
 
 namespace psi {
@@ -228,7 +274,10 @@ void* slot_dev(psi_arena* a, int s);
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
                           bool check_pinned, bool avoid_hold = false);
 psi_status page_acquire(psi_arena* a, int page);
-psi_status page_release(psi_arena* a, int page);
+// `borrow`: the caller releases right after launching the slot's last
+// consumer (an operator's own sequence, nothing of the caller's between), so
+// the release may take that kernel's end event (see psi_arena::stop_ring).
+psi_status page_release(psi_arena* a, int page, bool borrow = false);
 
 // An operator's biases: one request into the next bias slot (several
 // pinned host arrays, each placed 256-byte aligned); *dev_out[i] receives
@@ -240,7 +289,7 @@ struct BiasPart {
 psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_t** dev_out,
                        int* slot_out);
 psi_status bias_acquire(psi_arena* a, int slot);
-psi_status bias_release(psi_arena* a, int slot);
+psi_status bias_release(psi_arena* a, int slot, bool borrow = false);
 
 // Kernel launch through the arena (profiling, counters).
 psi_status run_gemm(psi_arena* a, const GemmArgs& g);

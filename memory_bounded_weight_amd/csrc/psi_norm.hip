@@ -134,8 +134,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void qk_norm_rope_kernel(NormRo
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t s) {
   if (a.M <= 0 || (!a.gamma && !a.cs)) return hipSuccess;
   const dim3 grid((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL(qk_norm_rope_kernel, grid, dim3(64 * kRowsPerBlock), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(qk_norm_rope_kernel, grid, dim3(64 * kRowsPerBlock), s, a);
 }
 
 }  // namespace psi

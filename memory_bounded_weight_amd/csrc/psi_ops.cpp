@@ -61,7 +61,8 @@ class OpBiases {
     *out = ptr_[i];
     return PSI_OK;
   }
-  psi_status release() { return bias_release(a_, slot_); }
+  // called by the operator right after its last kernel
+  psi_status release() { return bias_release(a_, slot_, true); }
 
  private:
   static constexpr int kMax = 6;
@@ -135,7 +136,7 @@ class PageFeeder {
   }
   psi_status give_back(size_t i) {
     if (!reqs_[i].resident) {
-      psi_status st = page_release(a_, slot_[i]);
+      psi_status st = page_release(a_, slot_[i], true);
       if (st) return st;
       a_->hold_slot = slot_[i];
     }
