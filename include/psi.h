@@ -155,6 +155,7 @@ typedef struct psi_stats {
                                (PSI_ARENA_PROFILE_COPIES or while tracing) */
   uint64_t copy_bytes_timed;
   uint64_t lent_page_copies; /* page copies into slots lent from an operator's idle scratch */
+  uint64_t ahead_page_copies; /* page copies of a block's FFN started during its attention sub-block */
 } psi_stats;
 
 /* A weight matrix W[rows, cols] in pinned host memory, already packed into
@@ -223,8 +224,8 @@ const char* psi_version(void);
 
 /* [PSI] sec. II-A, Fig. 1: one device allocation of arena_bytes carved into
  * n_pages page slots, two bias slots (the bounded metadata term eps of
- * eq. (1)), the workspace and scratch.  Creates the copy stream and the
- * per-slot events.  While an operator runs, the whole pages of scratch
+ * eq. (1)), the workspace and scratch.  Creates two page-copy streams, a
+ * bias-copy stream and the per-slot events.  While an operator runs, the whole pages of scratch
  * above its own allocations serve as extra page slots for its requests
  * (psi_stats.lent_page_copies; not in a PSI_ARENA_SYNC_COPY arena).
  * *out is the caller's handle until psi_arena_destroy.

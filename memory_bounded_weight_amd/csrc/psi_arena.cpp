@@ -185,8 +185,9 @@ static int pending_hold(psi_arena* a) {
   return release_done(a, *p) ? -1 : h;
 }
 
-int submit_slot(psi_arena* a, bool avoid_hold) {
+int submit_slot(psi_arena* a, bool avoid_hold, bool regular_only) {
   const int skip = avoid_hold ? pending_hold(a) : -1;
+  if (regular_only) return first_free_slot(a, skip);
   int s = ready_lent_slot(a);
   if (s < 0) s = first_free_slot(a, skip);
   if (s < 0) s = free_lent_slot(a, skip);
@@ -235,7 +236,7 @@ psi_status return_lent_slots(psi_arena* a) {
 }
 
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
-                          bool pinned_check, bool avoid_hold) {
+                          bool pinned_check, bool avoid_hold, bool regular_only) {
   if (!host || bytes == 0) return fail(PSI_E_INVALID, "page submit: empty slice");
   if (bytes > a->desc.page_bytes)
     return fail(PSI_E_PAGE_TOO_SMALL, "weight tile exceeds page: " + std::to_string(bytes) +
@@ -244,7 +245,7 @@ psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* pag
   // round-robin position on (a page held across many requests does not
   // stall the others)
   // (a lent slot that is not ready comes last and then takes a host wait)
-  const int s = submit_slot(a, avoid_hold);
+  const int s = submit_slot(a, avoid_hold, regular_only);
   if (s < 0) return fail(PSI_E_PAGE_BUSY, "every page slot still has an unreleased request");
   const bool lent = s >= a->desc.n_pages;
   psi_page_slot& slot = *slot_ptr(a, s);
@@ -327,7 +328,7 @@ psi_status bias_submit(psi_arena* a, const BiasPart* parts, int n, const uint16_
   if (slot.state != psi_page_slot::FREE)
     return fail(PSI_E_STATE, "bias slot " + std::to_string(s) + " still in use");
   const bool sync = a->desc.flags & PSI_ARENA_SYNC_COPY;
-  hipStream_t cs = sync ? a->compute : a->copy;
+  hipStream_t cs = sync ? a->compute : a->copyb;
   if (!a->dry && !sync && slot.released_once) {
     psi_status st = wait_release(a, slot);
     if (st) return st;
@@ -497,8 +498,9 @@ static psi_status harvest(psi_arena* a) {
   if (a->dry) return PSI_OK;
   PSI_HIP(hipStreamSynchronize(a->copy));
   PSI_HIP(hipStreamSynchronize(a->copy1));
+  PSI_HIP(hipStreamSynchronize(a->copyb));
   PSI_HIP(hipStreamSynchronize(a->compute));
-  a->stats.host_syncs += 3;
+  a->stats.host_syncs += 4;
   // every release is complete now; profiling events go back to the pool
   auto drop = [](psi_page_slot& sl) {
     if (sl.rel_ring < 0 && sl.rel_ev != sl.release) sl.rel_ev = nullptr;
@@ -563,6 +565,7 @@ psi_status psi_arena_create(const psi_arena_desc* d, psi_arena** out) {
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&a->base), d->arena_bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copy1, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->copyb, hipStreamNonBlocking);
     for (int i = 0; e == hipSuccess && i < d->n_pages; ++i) {
       e = hipEventCreateWithFlags(&a->slots[i].ready, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&a->slots[i].release, hipEventDisableTiming);
@@ -598,6 +601,7 @@ psi_status psi_arena_destroy(psi_arena* a) {
   if (!a->dry) {
     if (a->copy) (void)hipStreamSynchronize(a->copy);
     if (a->copy1) (void)hipStreamSynchronize(a->copy1);
+    if (a->copyb) (void)hipStreamSynchronize(a->copyb);
     (void)hipStreamSynchronize(a->compute);
     for (psi_timed& t : a->pending) {
       a->event_pool.push_back(t.start);
@@ -624,6 +628,7 @@ psi_status psi_arena_destroy(psi_arena* a) {
       if (e) (void)hipEventDestroy(e);
     if (a->copy) (void)hipStreamDestroy(a->copy);
     if (a->copy1) (void)hipStreamDestroy(a->copy1);
+    if (a->copyb) (void)hipStreamDestroy(a->copyb);
     if (a->base) {
       hipError_t e = hipFree(a->base);
       if (e != hipSuccess) st = hip_fail(e, "hipFree(arena)");
@@ -638,8 +643,9 @@ psi_status psi_arena_sync(psi_arena* a) {
   if (a->dry) return PSI_OK;
   PSI_HIP(hipStreamSynchronize(a->copy));
   PSI_HIP(hipStreamSynchronize(a->copy1));
+  PSI_HIP(hipStreamSynchronize(a->copyb));
   PSI_HIP(hipStreamSynchronize(a->compute));
-  a->stats.host_syncs += 3;
+  a->stats.host_syncs += 4;
   return PSI_OK;
 }
 

@@ -160,6 +160,13 @@ int matrix_page_cols(const psi_matrix* m, int p);    // columns held by page p
 int matrix_page_col0(const psi_matrix* m, int p);    // first column of W in page p
 int matrix_page_row0(const psi_matrix* m, int p);    // first row of W in page p
 
+// One weight-page request of an operator, in consumption order.
+struct PageReq {
+  const void* host;  // device address when `resident`
+  size_t bytes;
+  bool resident;
+};
+
 }  // namespace psi
 
 // ------------------------------------------------------------- arena
@@ -195,6 +202,7 @@ struct psi_arena {
   hipStream_t compute = nullptr;
   hipStream_t copy = nullptr;   // even page copies and bias copies
   hipStream_t copy1 = nullptr;  // odd page copies (a second DMA engine)
+  hipStream_t copyb = nullptr;  // bias copies: small, never queued behind page copies
   int next_copy = 0;            // copy stream of the next page
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
@@ -251,6 +259,15 @@ struct psi_arena {
   uint64_t launches = 0;              // kernels launched through the arena
   hipEvent_t last_stop = nullptr;     // end event of the last launch, if it has one
   int last_stop_ring = -1;            // its ring entry, or -1 for a profiling event
+  // Page requests of the operator that runs next, set by a block driver for
+  // the operator before it.  Once that operator's feeder has submitted all
+  // of its own requests, page slots it frees (never lent ones: those are its
+  // scratch) take these in order, so the copy engines keep working through
+  // the end of a compute-bound operator; the next operator's feeder adopts
+  // the submitted ones (`ahead_slot`, -1 for a resident page).
+  std::vector<psi::PageReq> ahead;
+  std::vector<int> ahead_slot;
+  bool ahead_producing = false;  // the running operator's feeder still submits them
 };
 
 namespace psi {
@@ -269,10 +286,11 @@ int lend_scratch_slots(psi_arena* a);
 psi_status return_lent_slots(psi_arena* a);
 // The slot the next page_submit_ex would fill (-1: none free), and the
 // device address of slot s (regular or lent).
-int submit_slot(psi_arena* a, bool avoid_hold = false);
+// `regular_only`: never a lent slot.
+int submit_slot(psi_arena* a, bool avoid_hold = false, bool regular_only = false);
 void* slot_dev(psi_arena* a, int s);
 psi_status page_submit_ex(psi_arena* a, const void* host, size_t bytes, int* page_out,
-                          bool check_pinned, bool avoid_hold = false);
+                          bool check_pinned, bool avoid_hold = false, bool regular_only = false);
 psi_status page_acquire(psi_arena* a, int page);
 // `borrow`: the caller releases right after launching the slot's last
 // consumer (an operator's own sequence, nothing of the caller's between), so

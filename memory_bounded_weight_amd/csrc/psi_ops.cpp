@@ -12,13 +12,6 @@
 namespace psi {
 namespace {
 
-// One weight-page request of an operator, in consumption order.
-struct PageReq {
-  const void* host;  // device address when `resident`
-  size_t bytes;
-  bool resident;
-};
-
 void matrix_requests(const psi_matrix* m, std::vector<PageReq>& out) {
   const int n = psi_matrix_pages(m);
   for (int p = 0; p < n; ++p)
@@ -84,9 +77,37 @@ class OpBiases {
 // stream empty until the host enqueues the next one.  A page not needed yet
 // goes to another slot, and that slot is refilled right after the next
 // launch (the arena's hold, ended in its launch path through `refill`).
+//
+// Given the next operator's requests (`next`), the feeder goes on with them
+// once its own are all submitted, into regular slots only, and leaves them
+// in the arena, where the next operator's feeder adopts them: a
+// compute-bound operator (attention) then no longer leaves the copy engines
+// idle while its last kernels run.
 class PageFeeder {
  public:
-  PageFeeder(psi_arena* a, std::vector<PageReq> reqs) : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {
+  PageFeeder(psi_arena* a, std::vector<PageReq> reqs, const std::vector<PageReq>* next = nullptr)
+      : a_(a), reqs_(std::move(reqs)), slot_(reqs_.size(), -1) {
+    if (!a_->ahead.empty() && !a_->ahead_producing) {
+      // pages the previous operator submitted for this one
+      const size_t n = a_->ahead_slot.size();
+      for (size_t i = 0; i < n && !mismatch_; ++i) {
+        const PageReq& q = a_->ahead[i];
+        mismatch_ = i >= reqs_.size() || reqs_[i].host != q.host || reqs_[i].bytes != q.bytes ||
+                    reqs_[i].resident != q.resident;
+      }
+      if (!mismatch_) {
+        for (size_t i = 0; i < n; ++i) slot_[i] = a_->ahead_slot[i];
+        submitted_ = n;
+        a_->ahead.clear();
+        a_->ahead_slot.clear();
+      }
+    }
+    if (next && !next->empty() && !mismatch_) {
+      a_->ahead = *next;
+      a_->ahead_slot.clear();
+      a_->ahead_producing = true;
+      producer_ = true;
+    }
     a_->refill = &PageFeeder::refill_cb;
     a_->refill_ctx = this;
   }
@@ -95,6 +116,7 @@ class PageFeeder {
       a_->refill = nullptr;
       a_->refill_ctx = nullptr;
     }
+    if (producer_) a_->ahead_producing = false;  // from now on the next feeder adopts them
   }
   PageFeeder(const PageFeeder&) = delete;
   PageFeeder& operator=(const PageFeeder&) = delete;
@@ -104,6 +126,7 @@ class PageFeeder {
   // are wanted now and may take any slot; later ones avoid the slot freed by
   // the last enqueued consumer while it may still run.
   psi_status feed(size_t need = 0) {
+    if (mismatch_) return fail(PSI_E_STATE, "pages submitted ahead do not match the operator's requests");
     while (submitted_ < reqs_.size()) {
       const PageReq& r = reqs_[submitted_];
       if (r.resident) {  // consumed in place: no copy, no slot
@@ -117,6 +140,7 @@ class PageFeeder {
       if (st) return st;
       slot_[submitted_++] = s;
     }
+    if (producer_ && submitted_ == reqs_.size()) return feed_ahead();
     return PSI_OK;
   }
   // Waits (on the compute stream) for request i and returns its page.
@@ -144,11 +168,47 @@ class PageFeeder {
   }
 
  private:
+  // The next operator's requests, into free regular slots; none of them is
+  // wanted yet.
+  psi_status feed_ahead() {
+    while (a_->ahead_slot.size() < a_->ahead.size()) {
+      const PageReq& r = a_->ahead[a_->ahead_slot.size()];
+      if (r.resident) {
+        a_->ahead_slot.push_back(-1);
+        continue;
+      }
+      if (submit_slot(a_, true, true) < 0) break;
+      int s = -1;
+      psi_status st = page_submit_ex(a_, r.host, r.bytes, &s, false, true, true);
+      if (st) return st;
+      a_->ahead_slot.push_back(s);
+      a_->stats.ahead_page_copies++;
+    }
+    return PSI_OK;
+  }
+
   psi_arena* a_;
   std::vector<PageReq> reqs_;
   std::vector<int> slot_;
   size_t submitted_ = 0;
+  bool producer_ = false;
+  bool mismatch_ = false;
 };
+
+// Releases the pages submitted ahead for an operator that did not adopt
+// them (an error before it ran), so that their slots serve again.
+psi_status drop_ahead(psi_arena* a) {
+  psi_status first = PSI_OK;
+  for (int s : a->ahead_slot) {
+    if (s < 0) continue;
+    psi_status st = page_release(a, s);
+    if (st && !first) first = st;
+  }
+  a->ahead.clear();
+  a->ahead_slot.clear();
+  a->ahead_producing = false;
+  return first;
+}
 
 psi_status check_matrix_pinned(psi_arena* a, const psi_matrix* m, const char* name) {
   if (a->dry) return PSI_OK;
@@ -379,6 +439,19 @@ psi_status psi_linear_paged(psi_arena* a, const uint16_t* x, int M, int K, const
 // The FFN; with out_fence, the compute stream first waits for every journal
 // copy enqueued so far right before the first launch that writes y (the
 // journal's reads of y's previous contents are earlier consumers).
+// The FFN's page requests, U_0, V_0, U_1, V_1, ...: each hidden tile J is
+// produced from U_J, then consumed by V_J ([PSI] eq. (2)).
+std::vector<PageReq> ffn_requests(const psi_matrix* U, const psi_matrix* V) {
+  std::vector<PageReq> ru, rv, reqs;
+  matrix_requests(U, ru);
+  matrix_requests(V, rv);
+  for (size_t J = 0; J < ru.size(); ++J) {
+    reqs.push_back(ru[J]);
+    reqs.push_back(rv[J]);
+  }
+  return reqs;
+}
+
 static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const psi_matrix* U,
                             const psi_matrix* V, int token_chunks, float* acc_dev, uint16_t* y,
                             unsigned flags, psi_journal* out_fence) {
@@ -418,16 +491,8 @@ static psi_status ffn_paged(psi_arena* a, const uint16_t* x, int M, int d, const
   const psi_matrix* ms[2] = {U, V};
   OpBiases bias;
   if ((st = bias.stage(a, ms, 2))) return st;
-  // Request order U_0, V_0, U_1, V_1, ...: each hidden tile J is produced
-  // from U_J, then consumed by V_J ([PSI] eq. (2)).
-  std::vector<PageReq> ru, rv, reqs;
-  matrix_requests(U, ru);
-  matrix_requests(V, rv);
-  const int nJ = (int)ru.size();
-  for (int J = 0; J < nJ; ++J) {
-    reqs.push_back(ru[J]);
-    reqs.push_back(rv[J]);
-  }
+  const std::vector<PageReq> reqs = ffn_requests(U, V);
+  const int nJ = (int)reqs.size() / 2;
   LentSlots lent(a);
   PageFeeder feeder(a, reqs);
   if ((st = feeder.feed())) return st;
@@ -676,7 +741,7 @@ psi_status psi_ffn_tiled(psi_arena* a, const uint16_t* x, int M, int d, const ps
 static psi_status attn_paged(psi_arena* a, const uint16_t* x, int M, const uint16_t* ctx, int Mc, int heads,
                              int head_dim, const psi_matrix* Wq, const psi_matrix* Wk, const psi_matrix* Wv,
                              const psi_matrix* Wo, float* acc_dev, uint16_t* y, unsigned flags,
-                             psi_journal* out_fence) {
+                             psi_journal* out_fence, const std::vector<PageReq>* next = nullptr) {
   if (!a) return fail(PSI_E_INVALID, "null arena");
   if (psi_status st = check_attn_config(flags)) return st;
   if (ctx && Mc < 1) return fail(PSI_E_INVALID, "attention: cross-attention needs Mc >= 1 keys");
@@ -758,7 +823,7 @@ static psi_status attn_paged(psi_arena* a, const uint16_t* x, int M, const uint1
   }
   if (otiles) reqs.insert(reqs.end(), ro.begin(), ro.end());
   LentSlots lent(a);
-  PageFeeder feeder(a, reqs);
+  PageFeeder feeder(a, reqs, next);
   if ((st = feeder.feed())) return st;
   const uint16_t* bq[4];
   for (int g = 0; g < nG; ++g) {
@@ -1100,20 +1165,21 @@ psi_status psi_block_paged(psi_arena* a, uint16_t* x, uint16_t* xt, int M, int h
     return st;
   const size_t xbytes = (size_t)M * dm * 2;
   if (xt && xt != x && (st = check_alias(x, xbytes, xt, xbytes, false, "block x_tmp"))) return st;
-  if (!xt || xt == x) {
-    // in place: the attention sub-block's output tiles write x after its
-    // last read of x, and the FFN's last down-projection writes each row
-    // after every read of that row; the journal's reads of x's previous
-    // contents precede the attention's first write
-    if ((st = attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, acc_dev, x, f,
-                         fence)))
-      return st;
-    return ffn_paged(a, x, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, nullptr);
-  }
-  if ((st = attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, acc_dev, xt, f,
-                       nullptr)))
-    return st;
-  return ffn_paged(a, xt, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, fence);
+  // The FFN's first pages are copied while the attention sub-block's last
+  // kernels run (PageFeeder lookahead).
+  const std::vector<PageReq> ffn_reqs = ffn_requests(&w->U, &w->V);
+  const bool inplace = !xt || xt == x;
+  // In place, the attention sub-block's output tiles write x after its last
+  // read of x, and the FFN's last down-projection writes each row after
+  // every read of that row; the journal's reads of x's previous contents
+  // precede the attention's first write.
+  st = attn_paged(a, x, M, nullptr, 0, heads, head_dim, &w->Wq, &w->Wk, &w->Wv, &w->Wo, acc_dev, inplace ? x : xt,
+                  f, inplace ? fence : nullptr, &ffn_reqs);
+  if (!st)
+    st = inplace ? ffn_paged(a, x, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, nullptr)
+                 : ffn_paged(a, xt, M, dm, &w->U, &w->V, token_chunks, acc_dev, x, f, fence);
+  if (st && !a->ahead.empty()) (void)drop_ahead(a);  // the error is the one to report
+  return st;
 }
 
 }  // extern "C"

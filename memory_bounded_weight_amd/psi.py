@@ -109,7 +109,8 @@ class psi_stats(ctypes.Structure):
                 ("attn_ms", ctypes.c_double), ("attn_launches", ctypes.c_uint64),
                 ("attn_flops", ctypes.c_double),
                 ("copy_ms", ctypes.c_double), ("copy_bytes_timed", ctypes.c_uint64),
-                ("lent_page_copies", ctypes.c_uint64)]
+                ("lent_page_copies", ctypes.c_uint64),
+                ("ahead_page_copies", ctypes.c_uint64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

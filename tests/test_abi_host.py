@@ -606,6 +606,35 @@ def test_attention_output_tiles_plan_and_page_order_dry_run():
         psi.psi_arena_destroy(a)
 
 
+def test_block_copies_ffn_pages_during_attention_dry_run():
+    """psi_block_paged hands the FFN's page requests to the attention
+    sub-block's feeder: once every attention page is submitted, page slots
+    freed by attention kernels take the FFN's first pages, and the FFN's
+    feeder adopts them.  Every page is still copied exactly once per block
+    (48 in the benchmarked layout), blocks in a row stay consistent, and
+    the two operators called on their own copy nothing ahead."""
+    Wq, Wk, Wv, _ = cfg5_attn()
+    Wo_t = fake_matrix(4096, 4096, psi.PSI_SPLIT_ROWS, 1024)
+    U, V = cfg5_ffn()
+    bw = psi.psi_block_weights(Wq, Wk, Wv, Wo_t, U, V)
+    a = psi.psi_arena_create(desc(80, 8, 7, 0))
+    try:
+        for n in range(1, 4):
+            psi.psi_block_paged(a, 0x10000, None, 8192, 32, 128, bw, 1, 0x30000, None, 0)
+            s = psi.psi_arena_stats(a)
+            assert s.page_copies == 48 * n
+            assert 0 < s.ahead_page_copies <= 32 * n
+            assert s.ahead_page_copies % n == 0 and s.ahead_page_copies // n <= 7 + 9
+        psi.psi_arena_reset_stats(a)
+        psi.psi_attn_paged(a, 0x10000, 8192, None, 0, 32, 128, Wq, Wk, Wv, Wo_t, 0x30000, 0x10000,
+                           psi.PSI_OP_RESIDUAL)
+        psi.psi_ffn_paged(a, 0x10000, 8192, 4096, U, V, 1, 0x30000, 0x10000, psi.PSI_OP_RESIDUAL)
+        s = psi.psi_arena_stats(a)
+        assert s.page_copies == 48 and s.ahead_page_copies == 0
+    finally:
+        psi.psi_arena_destroy(a)
+
+
 def test_scratch_lent_as_page_slots_dry_run():
     """An operator lends the whole pages of scratch above its own allocations
     as page slots for its requests: in the stack's 80 MiB arena (7 pages),
