@@ -164,6 +164,44 @@ def test_capacity_settings_outcomes_and_bitwise(P, stack):
                         "small scratch": "PSI_E_SCRATCH_EXHAUSTED", "small pages": "PSI_E_PAGE_TOO_SMALL"}, outcomes
 
 
+def test_block_mixed_residency_bitwise(P, stack):
+    """A block whose FFN matrices are resident while its attention pages
+    stream, and the reverse, gives the bits of the all-paged block.  In the
+    first case the attention sub-block's feeder hands the FFN requests that
+    need no copy or slot; the FFN's feeder adopts them.  In the second the
+    attention feeder has no copies of its own and starts on the FFN's pages
+    at once."""
+    blocks, x0 = stack
+    w = blocks[0]
+    bw = P.block_weights(w, 128, 256)
+    mats = bw._keepalive
+    res = {n: P.resident_matrix(m) for n, m in mats.items()}
+
+    def run(sel):
+        ms = [sel[n] for n in ("Wq", "Wk", "Wv", "Wo", "U", "V")]
+        b = P.psi_block_weights(*ms)
+        ar = make_arena(4 * MiB, 256 * KiB, 2)
+        try:
+            x = dev(x0)
+            acc = torch.empty(M, D, dtype=torch.float32, device="cuda")
+            P.psi_block_paged(ar, x, None, M, HEADS, 128, b, 1, acc, None, 0)
+            P.psi_arena_sync(ar)
+            return host(x), P.psi_arena_stats(ar)
+        finally:
+            P.psi_arena_destroy(ar)
+
+    ref, s_ref = run(mats)
+    assert s_ref.ahead_page_copies > 0
+    for name, sel in (("resident FFN", {**mats, "U": res["U"], "V": res["V"]}),
+                      ("resident attention", {**mats, **{n: res[n] for n in ("Wq", "Wk", "Wv", "Wo")}})):
+        got, s = run(sel)
+        assert np.array_equal(got, ref), name
+        if name == "resident FFN":
+            assert s.ahead_page_copies == 0 and s.page_copies < s_ref.page_copies
+        else:
+            assert s.ahead_page_copies > 0
+
+
 @pytest.mark.parametrize("n_pages", [2, 3])
 def test_transport_jitter_keeps_bits(P, n_pages):
     """[PSI] sec. II-D transport control: with every page/bias copy and every
