@@ -224,8 +224,8 @@ const char* psi_version(void);
 
 /* [PSI] sec. II-A, Fig. 1: one device allocation of arena_bytes carved into
  * n_pages page slots, two bias slots (the bounded metadata term eps of
- * eq. (1)), the workspace and scratch.  Creates two page-copy streams, a
- * bias-copy stream and the per-slot events.  While an operator runs, the whole pages of scratch
+ * eq. (1)), the workspace and scratch.  Creates two page-copy streams and
+ * the per-slot events (a bias-copy stream follows on the first bias copy).  While an operator runs, the whole pages of scratch
  * above its own allocations serve as extra page slots for its requests
  * (psi_stats.lent_page_copies; not in a PSI_ARENA_SYNC_COPY arena).
  * *out is the caller's handle until psi_arena_destroy.

@@ -202,7 +202,7 @@ struct psi_arena {
   hipStream_t compute = nullptr;
   hipStream_t copy = nullptr;   // even page copies and bias copies
   hipStream_t copy1 = nullptr;  // odd page copies (a second DMA engine)
-  hipStream_t copyb = nullptr;  // bias copies: small, never queued behind page copies
+  hipStream_t copyb = nullptr;  // bias copies: small, never queued behind page copies (created on first use)
   int next_copy = 0;            // copy stream of the next page
   psi_page_slot slots[PSI_MAX_PAGES];
   int next_slot = 0;
